@@ -1,0 +1,180 @@
+"""Throughput of the cone-beam forward + matched backprojection pair on one MI355X.
+
+Workload: the 512^3 anisotropic circular cone beam (volume stored z-fastest, spacing
+(dz, dy, dx) = (1.5, 1, 1), SID 1000, SDD 1500, 720 views, 768 x 512 detector, 20 seeded
+ellipsoids plus U[0, 0.05) background). One step = one forward projection of the phantom and
+one matched backprojection of the resulting sinogram (every row of the hot path: frame
+staging is done once per plan, ray setup, forward walk, adjoint walk; this workload needs no
+layout conversion and fits one view launch).
+
+Metric: ray/voxel segments of positive length walked per second, forward plus adjoint,
+divided by the time of both (G ray-segments/s). The segment count comes from the library's
+counting kernel. Timing: W untimed warm-up steps, then K timed steps between device
+synchronisations; per-operation kernel time from HIP events recorded on the stream the
+kernels run on.
+
+Printed: one JSON line with the metric, a roofline object for the dominant kernel
+(algorithmic bytes per launch / average launch time, against the 8 TB/s HBM peak) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, traj, x_dhw, views=(0, 180, 360, 540)):
+    """The fp64 oracle on all rays of a few views: forward, then adjoint of its output."""
+    import numpy as np
+    from oracle import oracle as O
+
+    geom = O.geom_from_config(cfg)
+    sub = {k: (None if v is None else np.ascontiguousarray(v[list(views)])) for k, v in traj.items()}
+    sgeom = dict(geom, views=len(views))
+    threads = O.max_threads()
+    t0 = time.perf_counter()
+    sino, counts = O.project(sgeom, sub, x_dhw, counts=True)
+    t1 = time.perf_counter()
+    O.backproject(sgeom, sub, sino.astype(np.float32))
+    t2 = time.perf_counter()
+    segs = int(counts.sum())
+    value = 2 * segs / (t2 - t0) / 1e9
+    log(f"cpu oracle: {segs} segments per op, forward {t1 - t0:.2f} s, adjoint {t2 - t1:.2f} s, "
+        f"{threads} threads")
+    return {"value": value, "unit": "Gray-segments/s", "cores": threads, "kind": "oracle",
+            "sample": (f"views {list(views)} of {cfg.views} (all {cfg.rows}x{cfg.cols} rays each), "
+                       f"fp64 forward then adjoint; {segs} segments per op; "
+                       f"{t2 - t0:.1f} s total")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is "
+              "a design, not part of this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import matched_backprojection_amd as mbp
+    from workloads import CONFIGS, config_phantom, config_trajectory
+
+    cfg = CONFIGS["c4_cone512_aniso"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = time.perf_counter()
+    traj = config_trajectory(cfg)
+    x = config_phantom(cfg)
+    log(f"phantom {cfg.shape} built in {time.perf_counter() - t:.1f} s")
+    plan = mbp.Plan("cone", cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols), (cfg.dv, cfg.du),
+                    layout="WHD")
+    info = plan.info
+    # the z-fastest volume: a (D, H, W) tensor with strides (1, D, D*H)
+    xd = torch.from_numpy(np.ascontiguousarray(x.transpose(2, 1, 0))).to(dev).permute(2, 1, 0)
+    sino = torch.empty((cfg.views, cfg.rows, cfg.cols), dtype=torch.float32, device=dev)
+    vol = plan.empty_volume(device=dev)
+    segs = plan.segment_count()
+    log(f"plan: {info}; {segs} positive-length segments per op")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        plan.project(xd, out=sino)
+        if ev is not None:
+            ev[1].record()
+        plan.backproject(sino, out=vol)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    value = 2.0 * segs * args.steps / wall / 1e9
+    f_avg, b_avg = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+    log(f"forward {f_avg:.2f} ms (median {np.median(fwd_ms):.2f}), adjoint {b_avg:.2f} ms "
+        f"(median {np.median(bwd_ms):.2f}), step {ms_per_step:.2f} ms wall")
+
+    io_bytes = 4.0 * (cfg.n_voxels + cfg.n_rays) + 96.0 * cfg.views
+    alg_bytes = 4.0 * segs + io_bytes
+    dominant = "column_adjoint_kernel" if b_avg >= f_avg else "column_forward_kernel"
+    dom_ms = max(b_avg, f_avg)
+    achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
+    pair_gbs = 2 * alg_bytes / ((f_avg + b_avg) * 1e-3) / 1e9
+    log(f"algorithmic bytes per launch {alg_bytes / 1e9:.1f} GB; dominant {dominant}: "
+        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak; pair {pair_gbs:.0f} GB/s")
+
+    result = {
+        "metric": "cone forward+backproject Gray-segments/s at 512^3 on 1 MI355X; % HBM peak",
+        "value": value,
+        "unit": "Gray-segments/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("c4_cone512_aniso: circular cone beam, 512^3 volume stored "
+                         "(W,H,D)-contiguous, spacing (dz,dy,dx)=(1.5,1,1), SID 1000, SDD 1500, "
+                         "720 views, 768 cols x 512 rows, pitch 1; 20 seeded ellipsoids + "
+                         "U[0,0.05) background; forward + matched backprojection"),
+            "segments_per_op": segs,
+            "rays_per_op": cfg.n_rays,
+            "path": info["path"],
+            "forward_ms": f_avg,
+            "adjoint_ms": b_avg,
+            "rays_per_s": 2.0 * cfg.n_rays * args.steps / wall,
+            "pct_hbm_peak_pair": 100.0 * pair_gbs / HBM_PEAK_GBS,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dominant,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, traj, x)
+    print(json.dumps(result), flush=True)
+    plan.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,172 @@
+/*
+ * mbp.h -- C ABI of the MI355X ray-driven X-ray transform pair.
+ *
+ * The pair (diffct pages, "diffct 2.1.0 -> 2.2.1", README "Why diffct", bullet "Matched
+ * operators"): project() and backproject() form an exact adjoint pair for the cell-constant
+ * Siddon model.
+ *
+ *   project      P[b, view, row, col] = sum_v len(ray, v) * volume[b, v]
+ *   backproject  volume[b, v]        (+)= sum_rays len(ray, v) * sinogram[b, ray]
+ *
+ * len(ray, v) is the physical length of the ray inside voxel v. Each view has its own source
+ * (or ray direction), detector centre and detector axes (page "diffct 2.2.1 -> 2.4.0",
+ * README "Why diffct", bullet "Arbitrary trajectories"; the per-view tuples are on page
+ * "diffct 2.1.0 -> 2.2.1", diffct/analytical.py). Geometry readings taken where the pages
+ * are silent: the volume box is centred on `center`; world x <-> W, y <-> H, z <-> D; pixel
+ * (row k, col j) sits at det + ((j - (cols-1)/2) du) eu + ((k - (rows-1)/2) dv) ev; fan and
+ * cone rays are the segments source -> pixel; parallel rays are infinite lines through the
+ * pixel along the view's ray direction; cells are half-open.
+ *
+ * Memory and ownership. Volume and sinogram pointers are HIP device pointers on the current
+ * device, owned by the caller; the library never frees or reallocates them. Trajectory
+ * arrays are host pointers, copied at plan creation. Calls that take a `stream` enqueue work
+ * on that HIP stream (NULL = the default stream) and return without synchronising, except
+ * mbp_segment_count, which waits for its own result. A plan may be used from one host
+ * thread and one stream at a time; plans are independent of each other.
+ *
+ * Layouts. Volumes of one batch member are dense and either MBP_LAYOUT_DHW (C order of the
+ * tensor shape (D, H, W), W fastest) or MBP_LAYOUT_WHD (the same (D, H, W) tensor with
+ * z-fastest strides: element (z, y, x) at (x*H + y)*D + z; page "diffct 2.2.1 -> 2.4.0",
+ * CHANGELOG 2.4.0, native_volume_layout). Sinograms are dense [views][rows][cols]. A leading
+ * batch of B members is dense too: member b starts at b * D*H*W (volumes) and at
+ * b * views*rows*cols (sinograms). B may be 0 (page "diffct 2.2.1 -> 2.3.0", CHANGELOG
+ * 2.3.0, "Added": leading batch dimensions including empty batches).
+ *
+ * Errors. Every function validates all of its arguments before any device work and returns
+ * MBP_OK (0) or a negative mbp_status; mbp_last_error() then holds a message for the calling
+ * thread. A geometry that fails validation never produces a plan.
+ */
+#ifndef MBP_H
+#define MBP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MBP_ABI_VERSION 1
+
+typedef enum mbp_status {
+    MBP_OK = 0,
+    MBP_EINVAL = -1,       /* bad enum, shape, pointer, batch, or 2-D with D != 1 / rows != 1 */
+    MBP_ENONFINITE = -2,   /* NaN or Inf in spacing, centre, pitch or trajectory ("must be finite") */
+    MBP_ECOINCIDENT = -3,  /* source on a pixel, zero ray direction or detector axis, parallel
+                              detector axes ("must differ") */
+    MBP_ERANGE = -4,       /* voxel pitch outside [1e-6, 1e6] or max/min pitch > 1e4; source
+                              nearer than 1e-6 min pitch to the detector ("near"); a coordinate
+                              farther than 1e15 min pitch from the volume centre ("far") */
+    MBP_ETOOLARGE = -5,    /* one batch member's volume or sinogram has >= 2^31 elements */
+    MBP_EHIP = -6,         /* a HIP runtime call failed; mbp_last_error() has its message */
+    MBP_ENOMEM = -7        /* host or device allocation failed, or a workspace is too small */
+} mbp_status;
+
+typedef enum mbp_beam {
+    MBP_PARALLEL = 0,      /* 2-D parallel beam: volume (H, W), D = 1, rows = 1             */
+    MBP_FAN = 1,           /* 2-D fan beam, flat (line) detector: D = 1, rows = 1           */
+    MBP_CONE = 2           /* 3-D cone beam, flat detector                                   */
+} mbp_beam;
+
+typedef enum mbp_layout {
+    MBP_LAYOUT_DHW = 0,    /* W fastest (C order of (D, H, W))                               */
+    MBP_LAYOUT_WHD = 1     /* D fastest; cone beams only                                     */
+} mbp_layout;
+
+typedef enum mbp_path {
+    MBP_PATH_AUTO = 0,     /* pick the column walk when the geometry allows it               */
+    MBP_PATH_GENERIC = 1,  /* one lane per ray, full 3-D walk, any flat-detector geometry    */
+    MBP_PATH_COLUMN = 2    /* cone beam whose detector row axis is parallel to z: the rows of
+                              a detector column share their xy walk                          */
+} mbp_path;
+
+typedef struct mbp_geometry {
+    int32_t beam;          /* mbp_beam                                                       */
+    int32_t layout;        /* mbp_layout of the caller's volumes                            */
+    int64_t D, H, W;       /* volume shape in tensor order; 2-D beams: D = 1                */
+    double spacing[3];     /* (dz, dy, dx): voxel pitch in tensor axis order, physical units
+                              (page "diffct 2.4.3 -> 2.4.4", README "Per-axis voxel
+                              spacing"); 2-D beams ignore dz                                 */
+    double center[3];      /* world (x, y, z) of the volume centre; 2-D beams ignore z      */
+    int64_t views, rows, cols;   /* sinogram [views][rows][cols]; 2-D beams: rows = 1       */
+    double du, dv;         /* detector pitch along eu (columns) and ev (rows); > 0           */
+} mbp_geometry;
+
+typedef struct mbp_plan mbp_plan;
+
+typedef struct mbp_plan_info {
+    int32_t path;              /* MBP_PATH_GENERIC or MBP_PATH_COLUMN (the one that runs)   */
+    int32_t column_capable;    /* 1 if the geometry allows the column walk                  */
+    int64_t views_per_launch;  /* view batch of one kernel launch                           */
+    int64_t launches;          /* kernel launches per member group and operation            */
+    int64_t rays;              /* views * rows * cols                                       */
+    int64_t voxels;            /* D * H * W                                                 */
+    int64_t members_per_pass;  /* batch members one walk serves (volume interleave)         */
+} mbp_plan_info;
+
+/* Validate the geometry and trajectory and build a plan. Trajectory arrays are host fp64,
+   row-major [views][rank] with rank 3 for cone and 2 for 2-D beams: src = source position
+   (fan/cone) or ray direction (parallel); det = detector centre; eu, ev = detector axes
+   (ev NULL for 2-D beams). The arrays are copied; no device call is made here (frames are
+   staged to device memory on first use on each device). On success *out owns the plan. */
+int mbp_plan_create(const mbp_geometry* geometry, const double* src, const double* det,
+                    const double* eu, const double* ev, mbp_plan** out);
+
+/* Free a plan and its device frames and library-owned workspace. NULL is a no-op. The
+   caller must make sure no enqueued work still uses the plan. */
+void mbp_plan_destroy(mbp_plan* plan);
+
+/* Fill *info (host only, no device call). */
+int mbp_plan_get_info(const mbp_plan* plan, mbp_plan_info* info);
+
+/* Force a walk (MBP_PATH_AUTO restores the automatic choice). Forcing MBP_PATH_COLUMN on a
+   geometry that cannot use it returns MBP_EINVAL. Both walks visit the same segments. */
+int mbp_plan_set_path(mbp_plan* plan, int32_t path);
+
+/* Limit the views of one kernel launch (0 = automatic: as many as index and grid limits
+   allow). Results do not depend on it (page "diffct 2.1.0 -> 2.2.1", CHANGELOG 2.2.0,
+   "Changed": backprojection accumulators span all contributing view batches). */
+int mbp_plan_set_view_batch(mbp_plan* plan, int64_t views_per_launch);
+
+/* Forward projection of `batch` volumes (caller's layout) into `sinogram` [batch][views]
+   [rows][cols]. Every sinogram element is written; rays that miss the volume get 0. */
+int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinogram,
+                void* stream);
+
+/* Matched backprojection: volume = sum over rays of len * sinogram (accumulate = 0), or
+   volume += that sum (accumulate = 1), in the caller's layout, for `batch` members. The
+   segments are exactly those of mbp_project. Floating-point atomics make the summation
+   order, and so the last bits, vary from run to run. */
+int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
+                    int32_t accumulate, void* stream);
+
+/* Number of positive-length ray/voxel segments one projection of one member walks (the
+   work unit of the throughput metric). Runs a counting kernel on `stream`, then waits. */
+int mbp_segment_count(mbp_plan* plan, int64_t* count, void* stream);
+
+/* Device workspace the plan needs for `batch` members (layout conversion for the column
+   walk). 0 when none is needed. */
+int mbp_workspace_size(const mbp_plan* plan, int64_t batch, size_t* bytes);
+
+/* Hand the plan a caller-owned device workspace (NULL, 0 = let the library allocate its
+   own on first use). The caller keeps ownership and must keep it alive while work that uses
+   it is enqueued. A call that needs more than `bytes` returns MBP_ENOMEM. */
+int mbp_set_workspace(mbp_plan* plan, void* device_ptr, size_t bytes);
+
+/* Convert `batch` volumes between MBP_LAYOUT_DHW and MBP_LAYOUT_WHD (to_whd = 1: DHW ->
+   WHD). `in` and `out` must not overlap. Lets a caller keep volumes in the z-fastest layout
+   across repeated operator applications (page "diffct 2.2.1 -> 2.4.0", CHANGELOG 2.4.0:
+   keeping the native layout saves two whole-volume copies per normal-operator
+   application). */
+int mbp_convert_layout(const float* in, int64_t batch, int64_t D, int64_t H, int64_t W,
+                       int32_t to_whd, float* out, void* stream);
+
+const char* mbp_status_string(int status);
+const char* mbp_last_error(void);
+int mbp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBP_H */

@@ -1,0 +1,177 @@
+// hostcheck.cpp -- CPU replay of the GPU walks (test harness, not part of the library).
+//
+// Compiles traverse.h for the host and runs the generic and the column walk over every ray
+// of a geometry, checking each visited cell index against the volume bounds and each length
+// for sign. Tests use it to show that a launch configuration stays in bounds before it runs
+// on a GPU, and to check the walk logic against the fp64 oracle on the CPU. It shares the
+// traversal code with the HIP kernels, so agreement here is a logic check, not parity.
+#include <stdint.h>
+
+#include <cmath>
+#include <vector>
+
+#include "traverse.h"
+
+using namespace mbp;
+
+namespace {
+
+struct Checked {
+    const Box* B;
+    long long* violations;
+    bool ok(int32_t cx, int32_t cy, int32_t cz, float len) const {
+        const bool in = cx >= 0 && cx < B->n[0] && cy >= 0 && cy < B->n[1] && cz >= 0 && cz < B->n[2];
+        if (!in || !(len >= 0.0f) || !std::isfinite(len)) {
+            ++*violations;
+            return false;
+        }
+        return true;
+    }
+};
+
+void frames_from(const double* f, int views, std::vector<Frame>& out) {
+    out.resize((size_t)views);
+    for (int i = 0; i < views; ++i)
+        for (int a = 0; a < 3; ++a) {
+            out[i].s[a] = f[i * 12 + a];
+            out[i].c[a] = f[i * 12 + 3 + a];
+            out[i].u[a] = f[i * 12 + 6 + a];
+            out[i].v[a] = f[i * 12 + 9 + a];
+        }
+}
+
+Box box_from(const double* lo, const double* pitch, const int32_t* n) {
+    Box B;
+    for (int a = 0; a < 3; ++a) {
+        B.lo[a] = lo[a];
+        B.pitch[a] = pitch[a];
+        B.n[a] = n[a];
+        B.hi[a] = lo[a] + (double)n[a] * pitch[a];
+    }
+    return B;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Forward projection with the generic (path 1) or column (path 2) walk. frames: views x 12
+// doubles (s, c, u, v); volume element (x, y, z) at x*sx + y*sy + z*sz. Outputs the fp32
+// sinogram [views][rows][cols], per-ray counts of positive-length segments, and the number of bound violations.
+int mbph_project(int path, const double* frames, int beam, const double* lo, const double* hi,
+                 const double* pitch, const int32_t* n, int views, int rows, int cols,
+                 double du, double dv, const float* vol, int64_t sx, int64_t sy, int64_t sz,
+                 float* sino, int64_t* counts, long long* violations) {
+    (void)hi;
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *violations = 0;
+    Checked chk{&B, violations};
+    for (int i = 0; i < views; ++i) {
+        for (int j = 0; j < cols; ++j) {
+            ColumnWalk c;
+            if (path == 2) column_setup(F[i], B, beam, centred(j, cols, du), c);
+            for (int k = 0; k < rows; ++k) {
+                float acc = 0.0f;
+                int64_t cnt = 0;
+                auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+                    if (len > 0.0f) ++cnt;
+                    if (!chk.ok(cx, cy, cz, len)) return;
+                    acc = fmaf(len, vol[cx * sx + cy * sy + cz * sz], acc);
+                };
+                float scale = 1.0f;
+                if (path == 2) {
+                    RowWalk r;
+                    row_setup(c, B, centred(k, rows, dv), F[i].v[2], r);
+                    walk_column_row(c, r, visit);
+                    scale = r.kappa;
+                } else {
+                    RayWalk r;
+                    ray_setup(F[i], B, beam, centred(j, cols, du), centred(k, rows, dv), r);
+                    walk_ray(r, visit);
+                }
+                const int64_t ray = ((int64_t)i * rows + k) * cols + j;
+                sino[ray] = acc * scale;
+                if (counts) counts[ray] = cnt;
+            }
+        }
+    }
+    return 0;
+}
+
+// Adjoint with the same walks, accumulated in fp64 on the host (order is deterministic).
+int mbph_backproject(int path, const double* frames, int beam, const double* lo,
+                     const double* hi, const double* pitch, const int32_t* n, int views,
+                     int rows, int cols, double du, double dv, const float* sino, double* vol,
+                     int64_t sx, int64_t sy, int64_t sz, long long* violations) {
+    (void)hi;
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *violations = 0;
+    Checked chk{&B, violations};
+    for (int i = 0; i < views; ++i) {
+        for (int j = 0; j < cols; ++j) {
+            ColumnWalk c;
+            if (path == 2) column_setup(F[i], B, beam, centred(j, cols, du), c);
+            for (int k = 0; k < rows; ++k) {
+                const int64_t ray = ((int64_t)i * rows + k) * cols + j;
+                double w = sino[ray];
+                auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+                    if (!chk.ok(cx, cy, cz, len)) return;
+                    vol[cx * sx + cy * sy + cz * sz] += (double)len * w;
+                };
+                if (path == 2) {
+                    RowWalk r;
+                    row_setup(c, B, centred(k, rows, dv), F[i].v[2], r);
+                    w *= (double)r.kappa;
+                    walk_column_row(c, r, visit);
+                } else {
+                    RayWalk r;
+                    ray_setup(F[i], B, beam, centred(j, cols, du), centred(k, rows, dv), r);
+                    walk_ray(r, visit);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+// Bounds-only sweep of selected rays (flat ids) with either walk; returns visits.
+int64_t mbph_check_rays(int path, const double* frames, int beam, const double* lo,
+                        const double* pitch, const int32_t* n, int views, int rows, int cols,
+                        double du, double dv, const int64_t* ray_ids, int64_t nrays,
+                        long long* violations) {
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *violations = 0;
+    Checked chk{&B, violations};
+    int64_t visits = 0;
+    for (int64_t q = 0; q < nrays; ++q) {
+        const int64_t id = ray_ids[q];
+        const int i = (int)(id / ((int64_t)rows * cols));
+        const int k = (int)((id / cols) % rows);
+        const int j = (int)(id % cols);
+        if (i < 0 || i >= views) { ++*violations; continue; }
+        auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+            ++visits;
+            chk.ok(cx, cy, cz, len);
+        };
+        if (path == 2) {
+            ColumnWalk c;
+            column_setup(F[i], B, beam, centred(j, cols, du), c);
+            RowWalk r;
+            row_setup(c, B, centred(k, rows, dv), F[i].v[2], r);
+            walk_column_row(c, r, visit);
+        } else {
+            RayWalk r;
+            ray_setup(F[i], B, beam, centred(j, cols, du), centred(k, rows, dv), r);
+            walk_ray(r, visit);
+        }
+    }
+    return visits;
+}
+
+}  // extern "C"

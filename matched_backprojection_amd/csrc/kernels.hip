@@ -1,0 +1,501 @@
+// kernels.hip -- gfx950 kernels of the ray-driven X-ray transform pair.
+//
+// Forward (diffct pages, "diffct 2.1.0 -> 2.2.1", README "Why diffct", bullet "Matched
+// operators"): each detector pixel's value is the line integral of the cell-constant volume
+// along its ray. Adjoint: each ray's value is scattered back along exactly the same segments,
+// weighted by length, with global float atomics.
+//
+// Kernels:
+//  * generic_*: one lane per ray, full 3-D walk from an fp64 entry (any flat detector, and
+//    2-D beams with a single z cell); lanes of a wave are adjacent detector columns.
+//  * column_*: for cone beams whose detector row axis is parallel to z. A wave takes 64
+//    adjacent rows of one detector column of one view. Their rays share the xy line, so the
+//    xy walk is wave-uniform, and every lane steps its own z crossings inside each xy cell
+//    (diffct pages, "diffct 2.2.1 -> 2.4.0", CHANGELOG 2.4.0, "Changed": z crossings of each
+//    xy cell stepped in an inner loop, adjacent detector rows grouped in a warp so that the
+//    atomic additions hit neighbouring voxels of one column). On a z-fastest volume the 64
+//    lanes then load from, or add into, a few consecutive cache lines.
+//  * layout conversion between the caller's (D, H, W) order and the z-fastest order with up
+//    to four batch members interleaved innermost, so one walk serves four volumes.
+//
+// Block-to-work mapping is XCD-aware: consecutive block ids are dealt round-robin to the
+// eight XCDs, so the mapping hands each XCD one contiguous range of work (neighbouring
+// columns of the same view share most voxels, and so each XCD's L2).
+#include <hip/hip_runtime.h>
+
+#include "mbp_internal.h"
+
+namespace mbp {
+
+namespace {
+
+constexpr uint32_t kXcds = 8;
+
+struct Ptrs4 { const float* p[4]; };
+struct MPtrs4 { float* p[4]; };
+
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
+    const uint32_t xcd = b % kXcds, idx = b / kXcds;
+    const uint32_t base = n / kXcds, rem = n % kXcds;
+    return xcd * base + (xcd < rem ? xcd : rem) + idx;
+}
+
+__device__ __forceinline__ void atomic_add_f32(float* p, float v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// ------------------------------------------------------------------------------------------
+// Generic walk
+
+__global__ void __launch_bounds__(256) generic_forward_kernel(const GenericLaunch A,
+                                                              const Ptrs4 vol, const MPtrs4 sino) {
+    const uint32_t per_view = (uint32_t)A.rows * (uint32_t)A.cols;
+    const uint32_t rid = blockIdx.x * 256u + threadIdx.x;
+    if (rid >= (uint32_t)A.nviews * per_view) return;
+    const uint32_t vl = rid / per_view;
+    const uint32_t rem = rid - vl * per_view;
+    const int32_t k = (int32_t)(rem / (uint32_t)A.cols);
+    const int32_t j = (int32_t)(rem - (uint32_t)k * (uint32_t)A.cols);
+    const int32_t view = A.view0 + (int32_t)vl;
+    const Frame F = A.frames[view];
+    RayWalk r;
+    ray_setup(F, A.box, A.beam, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), r);
+    float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+    const int nb = A.nb;
+    auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+        const int32_t idx = cx * A.sx + cy * A.sy + cz * A.sz;
+        acc0 = fmaf(len, vol.p[0][idx], acc0);
+        if (nb > 1) acc1 = fmaf(len, vol.p[1][idx], acc1);
+        if (nb > 2) acc2 = fmaf(len, vol.p[2][idx], acc2);
+        if (nb > 3) acc3 = fmaf(len, vol.p[3][idx], acc3);
+    };
+    walk_ray(r, visit);
+    const int64_t ray = (int64_t)view * per_view + rem;
+    sino.p[0][ray] = acc0;
+    if (nb > 1) sino.p[1][ray] = acc1;
+    if (nb > 2) sino.p[2][ray] = acc2;
+    if (nb > 3) sino.p[3][ray] = acc3;
+}
+
+__global__ void __launch_bounds__(256) generic_adjoint_kernel(const GenericLaunch A,
+                                                              const Ptrs4 sino, const MPtrs4 vol) {
+    const uint32_t per_view = (uint32_t)A.rows * (uint32_t)A.cols;
+    const uint32_t rid = blockIdx.x * 256u + threadIdx.x;
+    if (rid >= (uint32_t)A.nviews * per_view) return;
+    const uint32_t vl = rid / per_view;
+    const uint32_t rem = rid - vl * per_view;
+    const int32_t k = (int32_t)(rem / (uint32_t)A.cols);
+    const int32_t j = (int32_t)(rem - (uint32_t)k * (uint32_t)A.cols);
+    const int32_t view = A.view0 + (int32_t)vl;
+    const int64_t ray = (int64_t)view * per_view + rem;
+    const int nb = A.nb;
+    const float w0 = sino.p[0][ray];
+    const float w1 = nb > 1 ? sino.p[1][ray] : 0.0f;
+    const float w2 = nb > 2 ? sino.p[2][ray] : 0.0f;
+    const float w3 = nb > 3 ? sino.p[3][ray] : 0.0f;
+    if (w0 == 0.0f && w1 == 0.0f && w2 == 0.0f && w3 == 0.0f) return;
+    const Frame F = A.frames[view];
+    RayWalk r;
+    ray_setup(F, A.box, A.beam, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), r);
+    auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+        if (!(len > 0.0f)) return;
+        const int32_t idx = cx * A.sx + cy * A.sy + cz * A.sz;
+        atomic_add_f32(vol.p[0] + idx, len * w0);
+        if (nb > 1) atomic_add_f32(vol.p[1] + idx, len * w1);
+        if (nb > 2) atomic_add_f32(vol.p[2] + idx, len * w2);
+        if (nb > 3) atomic_add_f32(vol.p[3] + idx, len * w3);
+    };
+    walk_ray(r, visit);
+}
+
+// Segment counts: positive-length segments of the generic walk, grid-stride over rays, one
+// 64-bit atomic per block.
+__device__ __forceinline__ void block_count_add(unsigned long long local, unsigned long long* count) {
+    __shared__ unsigned long long part[256];
+    part[threadIdx.x] = local;
+    __syncthreads();
+    for (uint32_t s = 128; s > 0; s >>= 1) {
+        if (threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0 && part[0]) atomicAdd(count, part[0]);
+}
+
+__global__ void __launch_bounds__(256) generic_count_kernel(const GenericLaunch A,
+                                                            unsigned long long* count) {
+    const uint32_t per_view = (uint32_t)A.rows * (uint32_t)A.cols;
+    const uint32_t n = (uint32_t)A.nviews * per_view;
+    unsigned long long local = 0;
+    for (uint32_t rid = blockIdx.x * 256u + threadIdx.x; rid < n; rid += gridDim.x * 256u) {
+        const uint32_t vl = rid / per_view;
+        const uint32_t rem = rid - vl * per_view;
+        const int32_t k = (int32_t)(rem / (uint32_t)A.cols);
+        const int32_t j = (int32_t)(rem - (uint32_t)k * (uint32_t)A.cols);
+        const Frame F = A.frames[A.view0 + (int32_t)vl];
+        RayWalk r;
+        ray_setup(F, A.box, A.beam, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), r);
+        uint32_t c = 0;
+        auto visit = [&](int32_t, int32_t, int32_t, float len) { c += len > 0.0f ? 1u : 0u; };
+        walk_ray(r, visit);
+        local += c;
+    }
+    block_count_add(local, count);
+}
+
+// ------------------------------------------------------------------------------------------
+// Column walk
+
+template <int NB> struct VecOf;
+template <> struct VecOf<1> { using T = float; };
+template <> struct VecOf<2> { using T = float2; };
+template <> struct VecOf<4> { using T = float4; };
+
+template <int NB>
+__device__ __forceinline__ void load_acc(const float* __restrict__ p, float len, float* acc) {
+    if constexpr (NB == 1) {
+        acc[0] = fmaf(len, p[0], acc[0]);
+    } else if constexpr (NB == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        acc[0] = fmaf(len, v.x, acc[0]);
+        acc[1] = fmaf(len, v.y, acc[1]);
+    } else {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        acc[0] = fmaf(len, v.x, acc[0]);
+        acc[1] = fmaf(len, v.y, acc[1]);
+        acc[2] = fmaf(len, v.z, acc[2]);
+        acc[3] = fmaf(len, v.w, acc[3]);
+    }
+}
+
+struct ColumnTask {
+    int32_t view, col, row;
+    bool valid;
+    bool live;
+};
+
+__device__ __forceinline__ ColumnTask column_task(const ColumnLaunch& A) {
+    ColumnTask t;
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
+    const uint32_t task = blk * 4u + wave;
+    t.live = task < A.tasks;
+    const uint32_t rb = task % (uint32_t)A.row_blocks;
+    const uint32_t vc = task / (uint32_t)A.row_blocks;
+    t.col = (int32_t)(vc % (uint32_t)A.cols);
+    t.view = A.view0 + (int32_t)(vc / (uint32_t)A.cols);
+    t.row = (int32_t)(rb * 64u + lane);
+    t.valid = t.live && t.row < A.rows;
+    return t;
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch A,
+                                                             const float* __restrict__ vol,
+                                                             const MPtrs4 sino) {
+    const ColumnTask t = column_task(A);
+    if (!t.live) return;
+    const Frame F = A.frames[t.view];
+    ColumnWalk c;
+    column_setup(F, A.box, A.beam, centred(t.col, A.cols, A.du), c);
+    RowWalk r;
+    row_setup(c, A.box, centred(t.row, A.rows, A.dv), F.v[2], r);
+    if (!t.valid) { r.t_lo = 0.0f; r.t_hi = 0.0f; }
+    float acc[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) acc[m] = 0.0f;
+    const uint32_t H = (uint32_t)A.H, D = (uint32_t)A.D;
+    auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+        const uint32_t base = (((uint32_t)cx * H + (uint32_t)cy) * D + (uint32_t)cz) * NB;
+        load_acc<NB>(vol + base, len, acc);
+    };
+    walk_column_row(c, r, visit);
+    if (t.valid) {
+        const int64_t ray = ((int64_t)t.view * A.rows + t.row) * A.cols + t.col;
+#pragma unroll
+        for (int m = 0; m < NB; ++m) sino.p[m][ray] = acc[m] * r.kappa;
+    }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) column_adjoint_kernel(const ColumnLaunch A,
+                                                             const Ptrs4 sino,
+                                                             float* __restrict__ vol) {
+    const ColumnTask t = column_task(A);
+    if (!t.live) return;
+    const Frame F = A.frames[t.view];
+    ColumnWalk c;
+    column_setup(F, A.box, A.beam, centred(t.col, A.cols, A.du), c);
+    RowWalk r;
+    row_setup(c, A.box, centred(t.row, A.rows, A.dv), F.v[2], r);
+    float w[NB];
+    bool any = false;
+    const int64_t ray = ((int64_t)t.view * A.rows + t.row) * A.cols + t.col;
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        w[m] = t.valid ? sino.p[m][ray] * r.kappa : 0.0f;
+        any = any || w[m] != 0.0f;
+    }
+    if (!any) { r.t_lo = 0.0f; r.t_hi = 0.0f; }
+    const uint32_t H = (uint32_t)A.H, D = (uint32_t)A.D;
+    auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+        const uint32_t base = (((uint32_t)cx * H + (uint32_t)cy) * D + (uint32_t)cz) * NB;
+#pragma unroll
+        for (int m = 0; m < NB; ++m) atomic_add_f32(vol + base + m, len * w[m]);
+    };
+    walk_column_row(c, r, visit);
+}
+
+__global__ void __launch_bounds__(256) column_count_kernel(const ColumnLaunch A,
+                                                           unsigned long long* count) {
+    const ColumnTask t = column_task(A);
+    uint32_t c = 0;
+    if (t.live) {
+        const Frame F = A.frames[t.view];
+        ColumnWalk cw;
+        column_setup(F, A.box, A.beam, centred(t.col, A.cols, A.du), cw);
+        RowWalk r;
+        row_setup(cw, A.box, centred(t.row, A.rows, A.dv), F.v[2], r);
+        if (!t.valid) { r.t_lo = 0.0f; r.t_hi = 0.0f; }
+        auto visit = [&](int32_t, int32_t, int32_t, float len) { c += len > 0.0f ? 1u : 0u; };
+        walk_column_row(cw, r, visit);
+    }
+    block_count_add(c, count);
+}
+
+// ------------------------------------------------------------------------------------------
+// Layout conversion. DHW member m: element (z, y, x) at m*ms + (z*H + y)*W + x.
+// Native: element (x, y, z, m) at ((x*H + y)*D + z)*NB + m.
+
+template <int NB>
+__global__ void __launch_bounds__(256) dhw_to_native_kernel(const float* __restrict__ in,
+                                                            int64_t ms, int32_t D, int32_t H,
+                                                            int32_t W, int32_t y0,
+                                                            float* __restrict__ out) {
+    __shared__ float tile[NB][32][33];
+    const int32_t x0 = blockIdx.x * 32, z0 = blockIdx.y * 32, y = y0 + (int32_t)blockIdx.z;
+    const int32_t tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t z = z0 + ty + 8 * i, x = x0 + tx;
+            if (z < D && x < W) tile[m][ty + 8 * i][tx] = in[m * ms + ((int64_t)z * H + y) * W + x];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t x = x0 + ty + 8 * i, z = z0 + tx;
+        if (x < W && z < D) {
+            const int64_t o = (((int64_t)x * H + y) * D + z) * NB;
+#pragma unroll
+            for (int m = 0; m < NB; ++m) out[o + m] = tile[m][tx][ty + 8 * i];
+        }
+    }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) native_to_dhw_kernel(const float* __restrict__ in,
+                                                            int32_t D, int32_t H, int32_t W,
+                                                            int32_t y0, float* __restrict__ out,
+                                                            int64_t ms, int32_t accumulate) {
+    __shared__ float tile[NB][32][33];
+    const int32_t x0 = blockIdx.x * 32, z0 = blockIdx.y * 32, y = y0 + (int32_t)blockIdx.z;
+    const int32_t tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t x = x0 + ty + 8 * i, z = z0 + tx;
+        if (x < W && z < D) {
+            const int64_t o = (((int64_t)x * H + y) * D + z) * NB;
+#pragma unroll
+            for (int m = 0; m < NB; ++m) tile[m][tx][ty + 8 * i] = in[o + m];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t z = z0 + ty + 8 * i, x = x0 + tx;
+            if (z < D && x < W) {
+                float* q = out + m * ms + ((int64_t)z * H + y) * W + x;
+                const float v = tile[m][ty + 8 * i][tx];
+                *q = accumulate ? *q + v : v;
+            }
+        }
+}
+
+// z-fastest member volumes <-> interleaved: element i of member m <-> native i*NB + m.
+template <int NB>
+__global__ void __launch_bounds__(256) interleave_kernel(const float* __restrict__ in, int64_t ms,
+                                                         int64_t n, float* __restrict__ out) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) out[i * NB + m] = in[m * ms + i];
+    }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) deinterleave_kernel(const float* __restrict__ in, int64_t n,
+                                                           float* __restrict__ out, int64_t ms,
+                                                           int32_t accumulate) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            const float v = in[i * NB + m];
+            float* q = out + m * ms + i;
+            *q = accumulate ? *q + v : v;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0.0f;
+}
+
+constexpr int32_t kMaxGridYZ = 65535;
+
+template <int NB>
+hipError_t to_native_nb(const float* in, int64_t ms, int32_t D, int32_t H, int32_t W, int whd_in,
+                        float* ws, hipStream_t s) {
+    if (whd_in) {
+        const int64_t n = (int64_t)D * H * W;
+        const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+        interleave_kernel<NB><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(in, ms, n, ws);
+        return hipGetLastError();
+    }
+    for (int32_t y0 = 0; y0 < H; y0 += kMaxGridYZ) {
+        const int32_t ny = H - y0 < kMaxGridYZ ? H - y0 : kMaxGridYZ;
+        dim3 grid((W + 31) / 32, (D + 31) / 32, ny);
+        dhw_to_native_kernel<NB><<<grid, dim3(256), 0, s>>>(in, ms, D, H, W, y0, ws);
+    }
+    return hipGetLastError();
+}
+
+template <int NB>
+hipError_t from_native_nb(const float* ws, int32_t D, int32_t H, int32_t W, int whd_out, float* out,
+                          int64_t ms, int accumulate, hipStream_t s) {
+    if (whd_out) {
+        const int64_t n = (int64_t)D * H * W;
+        const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+        deinterleave_kernel<NB><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(ws, n, out, ms, accumulate);
+        return hipGetLastError();
+    }
+    for (int32_t y0 = 0; y0 < H; y0 += kMaxGridYZ) {
+        const int32_t ny = H - y0 < kMaxGridYZ ? H - y0 : kMaxGridYZ;
+        dim3 grid((W + 31) / 32, (D + 31) / 32, ny);
+        native_to_dhw_kernel<NB><<<grid, dim3(256), 0, s>>>(ws, D, H, W, y0, out, ms, accumulate);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+// Launchers
+
+hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vol,
+                                  float* const* sino, hipStream_t s) {
+    const int64_t n = (int64_t)a.nviews * a.rows * a.cols;
+    if (n == 0) return hipSuccess;
+    Ptrs4 v{};
+    MPtrs4 o{};
+    for (int m = 0; m < a.nb; ++m) { v.p[m] = vol[m]; o.p[m] = sino[m]; }
+    generic_forward_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a, v, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_generic_adjoint(const GenericLaunch& a, const float* const* sino,
+                                  float* const* vol, hipStream_t s) {
+    const int64_t n = (int64_t)a.nviews * a.rows * a.cols;
+    if (n == 0) return hipSuccess;
+    Ptrs4 y{};
+    MPtrs4 o{};
+    for (int m = 0; m < a.nb; ++m) { y.p[m] = sino[m]; o.p[m] = vol[m]; }
+    generic_adjoint_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a, y, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol,
+                                 float* const* sino, hipStream_t s) {
+    if (a.tasks == 0) return hipSuccess;
+    MPtrs4 o{};
+    for (int m = 0; m < nb; ++m) o.p[m] = sino[m];
+    const dim3 grid((a.tasks + 3) / 4);
+    switch (nb) {
+        case 1: column_forward_kernel<1><<<grid, dim3(256), 0, s>>>(a, vol, o); break;
+        case 2: column_forward_kernel<2><<<grid, dim3(256), 0, s>>>(a, vol, o); break;
+        case 4: column_forward_kernel<4><<<grid, dim3(256), 0, s>>>(a, vol, o); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* const* sino,
+                                 float* vol, hipStream_t s) {
+    if (a.tasks == 0) return hipSuccess;
+    Ptrs4 y{};
+    for (int m = 0; m < nb; ++m) y.p[m] = sino[m];
+    const dim3 grid((a.tasks + 3) / 4);
+    switch (nb) {
+        case 1: column_adjoint_kernel<1><<<grid, dim3(256), 0, s>>>(a, y, vol); break;
+        case 2: column_adjoint_kernel<2><<<grid, dim3(256), 0, s>>>(a, y, vol); break;
+        case 4: column_adjoint_kernel<4><<<grid, dim3(256), 0, s>>>(a, y, vol); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_count(const GenericLaunch& a, unsigned long long* count, hipStream_t s) {
+    const int64_t n = (int64_t)a.nviews * a.rows * a.cols;
+    if (n == 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    generic_count_kernel<<<dim3((unsigned)(want < 8192 ? want : 8192)), dim3(256), 0, s>>>(a, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_column_count(const ColumnLaunch& a, unsigned long long* count, hipStream_t s) {
+    if (a.tasks == 0) return hipSuccess;
+    column_count_kernel<<<dim3((a.tasks + 3) / 4), dim3(256), 0, s>>>(a, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_native(const float* in, int64_t ms, int nb, int32_t D, int32_t H, int32_t W,
+                            int whd_in, float* ws, hipStream_t s) {
+    switch (nb) {
+        case 1: return to_native_nb<1>(in, ms, D, H, W, whd_in, ws, s);
+        case 2: return to_native_nb<2>(in, ms, D, H, W, whd_in, ws, s);
+        case 4: return to_native_nb<4>(in, ms, D, H, W, whd_in, ws, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_from_native(const float* ws, int nb, int32_t D, int32_t H, int32_t W, int whd_out,
+                              float* out, int64_t ms, int accumulate, hipStream_t s) {
+    switch (nb) {
+        case 1: return from_native_nb<1>(ws, D, H, W, whd_out, out, ms, accumulate, s);
+        case 2: return from_native_nb<2>(ws, D, H, W, whd_out, out, ms, accumulate, s);
+        case 4: return from_native_nb<4>(ws, D, H, W, whd_out, out, ms, accumulate, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_convert(const float* in, int32_t D, int32_t H, int32_t W, int to_whd, float* out,
+                          hipStream_t s) {
+    if (to_whd) return to_native_nb<1>(in, 0, D, H, W, 0, out, s);
+    return from_native_nb<1>(in, D, H, W, 0, out, 0, 0, s);
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    fill_zero_kernel<<<dim3((unsigned)(want < 65536 ? want : 65536)), dim3(256), 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+}  // namespace mbp

@@ -1,0 +1,70 @@
+// mbp_internal.h -- launch interface between the host plan (plan.cpp) and the kernels
+// (kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "traverse.h"
+
+namespace mbp {
+
+// Arguments of one generic-walk launch: rays [view0, view0 + nviews) x rows x cols, for `nb`
+// batch members (1..4) whose volumes and sinograms start at vol[m] and sino[m].
+struct GenericLaunch {
+    const Frame* frames;      // device, all views of the plan
+    int32_t view0, nviews;
+    int32_t rows, cols;
+    double du, dv;
+    int32_t beam;
+    int32_t nb;
+    Box box;
+    int32_t sx, sy, sz;       // volume element strides along world x, y, z
+    int32_t pad_;
+};
+
+// Arguments of one column-walk launch: waves over (view, column, block of 64 rows). The
+// volume is z-fastest with `NB` members interleaved innermost: element (x, y, z, m) at
+// ((x*H + y)*D + z)*NB + m.
+struct ColumnLaunch {
+    const Frame* frames;
+    int32_t view0, nviews;
+    int32_t rows, cols;
+    int32_t row_blocks;       // ceil(rows / 64)
+    int32_t beam;
+    double du, dv;
+    Box box;
+    int32_t H, D;
+    uint32_t tasks;           // nviews * cols * row_blocks
+    uint32_t pad_;
+};
+
+// Forward: sino[m][ray] for rays of the launch; adjoint: atomically adds into vol.
+hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vol,
+                                  float* const* sino, hipStream_t s);
+hipError_t launch_generic_adjoint(const GenericLaunch& a, const float* const* sino,
+                                  float* const* vol, hipStream_t s);
+hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol,
+                                 float* const* sino, hipStream_t s);
+hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* const* sino,
+                                 float* vol, hipStream_t s);
+
+// Positive-length segments walked by the launch's rays; adds into *count (device, zeroed by
+// the caller).
+hipError_t launch_count(const GenericLaunch& a, unsigned long long* count, hipStream_t s);
+hipError_t launch_column_count(const ColumnLaunch& a, unsigned long long* count, hipStream_t s);
+
+// Layout conversion for the column walk. to_native: nb members of a DHW volume (member
+// stride vox) -> interleaved z-fastest ws. from_native: the reverse, optionally adding into
+// the destination.
+hipError_t launch_to_native(const float* in, int64_t member_stride, int nb, int32_t D,
+                            int32_t H, int32_t W, int whd_in, float* ws, hipStream_t s);
+hipError_t launch_from_native(const float* ws, int nb, int32_t D, int32_t H, int32_t W,
+                              int whd_out, float* out, int64_t member_stride, int accumulate,
+                              hipStream_t s);
+// Plain DHW <-> WHD conversion of one member.
+hipError_t launch_convert(const float* in, int32_t D, int32_t H, int32_t W, int to_whd,
+                          float* out, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+}  // namespace mbp

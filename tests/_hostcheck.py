@@ -1,0 +1,127 @@
+"""ctypes wrapper of the CPU replay of the GPU walks (``csrc/hostcheck.cpp``).
+
+The replay compiles the same traversal header as the HIP kernels for the host. Tests use it to
+prove that every cell a launch configuration visits lies inside the volume before the
+configuration runs on a GPU, and to check the walk logic against the oracle on the CPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_LIB = os.path.join(ROOT, "matched_backprojection_amd", "csrc", "_build", "libmbp_hostcheck.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            import importlib.util
+            spec = importlib.util.spec_from_file_location(
+                "mbp_build", os.path.join(ROOT, "matched_backprojection_amd", "csrc", "build.py"))
+            mod = importlib.util.module_from_spec(spec)
+            spec.loader.exec_module(mod)
+            mod.build_hostcheck()
+        lib = ctypes.CDLL(_LIB)
+        P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P]
+        lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
+        lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
+        lib.mbph_check_rays.restype = I64
+        _lib = lib
+    return _lib
+
+
+def frames(geom: dict, traj: dict) -> np.ndarray:
+    """Per-view (s, c, u, v) in 3-D, as the plan stages them (2-D: rays in the plane z = 0)."""
+    views = int(geom["views"])
+    f = np.zeros((views, 12), dtype=np.float64)
+    rank = 3 if geom["beam"] == "cone" else 2
+    f[:, 0:rank] = traj["src"]
+    f[:, 3:3 + rank] = traj["det"]
+    f[:, 6:6 + rank] = traj["eu"]
+    if rank == 3:
+        f[:, 9:12] = traj["ev"]
+    return f
+
+
+def box(geom: dict):
+    shape = tuple(int(s) for s in geom["shape"])
+    spacing = tuple(float(s) for s in geom["spacing"])
+    if geom["beam"] == "cone":
+        n = (shape[2], shape[1], shape[0])
+        p = (spacing[2], spacing[1], spacing[0])
+    else:
+        n = (shape[1], shape[0], 1)
+        p = (spacing[1], spacing[0], 1.0)
+    c = tuple(geom.get("center", (0.0, 0.0, 0.0))) + (0.0,) * 3
+    lo = np.array([c[a] - 0.5 * n[a] * p[a] for a in range(3)])
+    return lo, np.array(p, dtype=np.float64), np.array(n, dtype=np.int32)
+
+
+_BEAM = {"parallel": 0, "fan": 1, "cone": 2}
+_PATH = {"generic": 1, "column": 2}
+
+
+def _common(geom, traj):
+    f = frames(geom, traj)
+    lo, p, n = box(geom)
+    hi = lo + n * p
+    return f, lo, hi, p, n
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def project(path: str, geom: dict, traj: dict, vol: np.ndarray):
+    """Replay the forward walk on a (D, H, W) / (H, W) float32 volume."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    rows = int(geom.get("rows", 1))
+    vol = np.ascontiguousarray(vol, dtype=np.float32)
+    views, cols = int(geom["views"]), int(geom["cols"])
+    sino = np.zeros((views, rows, cols), dtype=np.float32)
+    counts = np.zeros((views, rows, cols), dtype=np.int64)
+    viol = ctypes.c_longlong(0)
+    sx, sy, sz = 1, int(n[0]), int(n[0] * n[1])
+    lib.mbph_project(_PATH[path], _ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(hi), _ptr(p),
+                     _ptr(n), views, rows, cols, float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)),
+                     _ptr(vol), sx, sy, sz, _ptr(sino), _ptr(counts), ctypes.byref(viol))
+    if geom["beam"] != "cone":
+        sino, counts = sino[:, 0], counts[:, 0]
+    return sino, counts, int(viol.value)
+
+
+def backproject(path: str, geom: dict, traj: dict, sino: np.ndarray):
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    rows = int(geom.get("rows", 1))
+    views, cols = int(geom["views"]), int(geom["cols"])
+    s = np.ascontiguousarray(sino, dtype=np.float32).reshape(views, rows, cols)
+    vol = np.zeros(int(n[0]) * int(n[1]) * int(n[2]), dtype=np.float64)
+    viol = ctypes.c_longlong(0)
+    sx, sy, sz = 1, int(n[0]), int(n[0] * n[1])
+    lib.mbph_backproject(_PATH[path], _ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(hi), _ptr(p),
+                         _ptr(n), views, rows, cols, float(geom.get("du", 1.0)),
+                         float(geom.get("dv", 1.0)), _ptr(s), _ptr(vol), sx, sy, sz,
+                         ctypes.byref(viol))
+    return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value)
+
+
+def check_rays(path: str, geom: dict, traj: dict, ray_ids) -> tuple:
+    """Walk selected rays with bounds checks only; returns (visits, violations)."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    ids = np.ascontiguousarray(ray_ids, dtype=np.int64)
+    viol = ctypes.c_longlong(0)
+    visits = lib.mbph_check_rays(_PATH[path], _ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p),
+                                 _ptr(n), int(geom["views"]), int(geom.get("rows", 1)),
+                                 int(geom["cols"]), float(geom.get("du", 1.0)),
+                                 float(geom.get("dv", 1.0)), _ptr(ids), ids.size, ctypes.byref(viol))
+    return int(visits), int(viol.value)

@@ -1,0 +1,220 @@
+"""The C ABI on the CPU: symbols, validation, plans and batch-0 calls (no device work).
+
+Every check here runs in the host code of ``libmbp.so`` before any HIP call, so it needs no
+GPU: validation happens at plan creation, and plan creation stages nothing.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from matched_backprojection_amd import _capi
+from workloads import CONFIGS, SMALL_CONFIGS, config_trajectory, random_cone_trajectory
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _capi.load()
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mbp.h")).read()
+    return sorted(set(re.findall(r"\b(mbp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    declared = _declared_symbols()
+    assert len(declared) >= 14
+    assert set(declared) == set(_capi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.mbp_abi_version() == 1
+    assert lib.mbp_status_string(_capi.MBP_ERANGE) == b"geometry out of range"
+
+
+def _geometry(cfg, layout=None):
+    g = _capi.Geometry()
+    g.beam = _capi.BEAMS[cfg.beam]
+    g.layout = _capi.LAYOUTS[layout or cfg.layout]
+    if cfg.beam == "cone":
+        g.D, g.H, g.W = cfg.shape
+        g.spacing[0], g.spacing[1], g.spacing[2] = cfg.spacing
+    else:
+        g.D, (g.H, g.W) = 1, cfg.shape
+        g.spacing[0], g.spacing[1], g.spacing[2] = 1.0, cfg.spacing[0], cfg.spacing[1]
+    g.views, g.rows, g.cols = cfg.views, cfg.rows, cfg.cols
+    g.du, g.dv = cfg.du, cfg.dv
+    return g
+
+
+def _create(lib, g, traj):
+    arrs = [np.ascontiguousarray(traj[k], dtype=np.float64) if traj.get(k) is not None else None
+            for k in ("src", "det", "eu", "ev")]
+    ptrs = [None if a is None else a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
+    h = ctypes.c_void_p()
+    rc = lib.mbp_plan_create(ctypes.byref(g), *ptrs, ctypes.byref(h))
+    return rc, h
+
+
+def _info(lib, h):
+    inf = _capi.PlanInfo()
+    assert lib.mbp_plan_get_info(h, ctypes.byref(inf)) == 0
+    return inf
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_configs_plan_and_pick_walks(lib, name):
+    cfg = CONFIGS[name]
+    rc, h = _create(lib, _geometry(cfg), config_trajectory(cfg))
+    assert rc == 0, lib.mbp_last_error()
+    inf = _info(lib, h)
+    assert inf.rays == cfg.n_rays and inf.voxels == cfg.n_voxels
+    if cfg.beam == "cone":
+        assert inf.column_capable == 1 and inf.path == 2
+    else:
+        assert inf.column_capable == 0 and inf.path == 1
+    assert inf.views_per_launch == cfg.views and inf.launches == 1
+    ws = ctypes.c_size_t()
+    assert lib.mbp_workspace_size(h, cfg.members, ctypes.byref(ws)) == 0
+    if cfg.beam != "cone" or (cfg.layout == "WHD" and cfg.members == 1):
+        assert ws.value == 0
+    else:
+        assert ws.value == min(4, cfg.members) * cfg.n_voxels * 4
+    # view batching: a ragged split into launches of 7 views
+    assert lib.mbp_plan_set_view_batch(h, 7) == 0
+    inf = _info(lib, h)
+    assert inf.views_per_launch == 7 and inf.launches == -(-cfg.views // 7)
+    assert lib.mbp_plan_set_view_batch(h, -1) == _capi.MBP_EINVAL
+    # forcing walks
+    assert lib.mbp_plan_set_path(h, 1) == 0 and _info(lib, h).path == 1
+    want = 0 if cfg.beam == "cone" else _capi.MBP_EINVAL
+    assert lib.mbp_plan_set_path(h, 2) == want
+    assert lib.mbp_plan_set_path(h, 7) == _capi.MBP_EINVAL
+    lib.mbp_plan_destroy(h)
+
+
+def test_tilted_detector_uses_generic_walk(lib):
+    cfg = SMALL_CONFIGS["c3_cone256"]
+    rc, h = _create(lib, _geometry(cfg), random_cone_trajectory(cfg.views, seed=1, radius=200.0,
+                                                                  sdd=350.0))
+    assert rc == 0
+    inf = _info(lib, h)
+    assert inf.column_capable == 0 and inf.path == 1
+    lib.mbp_plan_destroy(h)
+
+
+def test_batch_zero_and_bad_calls_do_no_device_work(lib):
+    cfg = SMALL_CONFIGS["c3_cone256"]
+    rc, h = _create(lib, _geometry(cfg), config_trajectory(cfg))
+    assert rc == 0
+    # batch 0: nothing to do, NULL buffers allowed, no HIP call made
+    assert lib.mbp_project(h, None, 0, None, None) == 0
+    assert lib.mbp_backproject(h, None, 0, None, 0, None) == 0
+    assert lib.mbp_convert_layout(None, 0, 4, 5, 6, 1, None, None) == 0
+    # invalid arguments are rejected before any device work
+    assert lib.mbp_project(h, None, -1, None, None) == _capi.MBP_EINVAL
+    assert lib.mbp_project(h, None, 1, None, None) == _capi.MBP_EINVAL
+    assert lib.mbp_project(None, None, 1, None, None) == _capi.MBP_EINVAL
+    assert lib.mbp_backproject(h, ctypes.c_void_p(16), 1, ctypes.c_void_p(32), 2, None) == _capi.MBP_EINVAL
+    assert lib.mbp_project(h, ctypes.c_void_p(18), 1, ctypes.c_void_p(32), None) == _capi.MBP_EINVAL
+    assert b"aligned" in lib.mbp_last_error()
+    assert lib.mbp_convert_layout(ctypes.c_void_p(64), 2, 4, 5, 6, 1, ctypes.c_void_p(64 + 4 * 100), None) == _capi.MBP_EINVAL
+    assert b"overlap" in lib.mbp_last_error()
+    assert lib.mbp_set_workspace(h, ctypes.c_void_p(8), 64) == _capi.MBP_EINVAL
+    assert lib.mbp_set_workspace(h, None, 64) == _capi.MBP_EINVAL
+    assert lib.mbp_set_workspace(h, None, 0) == 0
+    lib.mbp_plan_destroy(h)
+    lib.mbp_plan_destroy(None)
+
+
+def _bad(lib, mutate_geom=None, mutate_traj=None, cfg=None):
+    cfg = cfg or SMALL_CONFIGS["c3_cone256"]
+    g = _geometry(cfg)
+    traj = {k: (None if v is None else v.copy()) for k, v in config_trajectory(cfg).items()}
+    if mutate_geom:
+        mutate_geom(g)
+    if mutate_traj:
+        mutate_traj(traj)
+    rc, h = _create(lib, g, traj)
+    if rc == 0:
+        lib.mbp_plan_destroy(h)
+    return rc, lib.mbp_last_error().decode()
+
+
+def test_validation_error_codes(lib):
+    E = _capi
+    # enums and shapes
+    assert _bad(lib, lambda g: setattr(g, "beam", 5))[0] == E.MBP_EINVAL
+    assert _bad(lib, lambda g: setattr(g, "layout", 3))[0] == E.MBP_EINVAL
+    assert _bad(lib, lambda g: setattr(g, "D", 0))[0] == E.MBP_EINVAL
+    assert _bad(lib, lambda g: setattr(g, "views", 0))[0] == E.MBP_EINVAL
+    assert _bad(lib, lambda g: setattr(g, "du", -1.0))[0] == E.MBP_EINVAL
+    c1 = CONFIGS["c1_parallel2d"]
+    assert _bad(lib, lambda g: setattr(g, "rows", 2), cfg=c1)[0] == E.MBP_EINVAL
+    assert _bad(lib, lambda g: setattr(g, "layout", 1), cfg=c1)[0] == E.MBP_EINVAL
+    # non-finite geometry
+    rc, msg = _bad(lib, mutate_traj=lambda t: t["src"].__setitem__((3, 1), np.nan))
+    assert rc == E.MBP_ENONFINITE and "finite" in msg
+    assert _bad(lib, mutate_traj=lambda t: t["ev"].__setitem__((0, 2), np.inf))[0] == E.MBP_ENONFINITE
+    assert _bad(lib, lambda g: g.spacing.__setitem__(1, float("nan")))[0] == E.MBP_ENONFINITE
+    assert _bad(lib, lambda g: g.center.__setitem__(0, float("inf")))[0] == E.MBP_ENONFINITE
+    # pitch range and ratio
+    rc, msg = _bad(lib, lambda g: g.spacing.__setitem__(0, 1e-7))
+    assert rc == E.MBP_ERANGE and "1e-6" in msg
+    assert _bad(lib, lambda g: g.spacing.__setitem__(2, 2e6))[0] == E.MBP_ERANGE
+    rc, msg = _bad(lib, lambda g: (g.spacing.__setitem__(0, 1e-3), g.spacing.__setitem__(1, 20.0)))
+    assert rc == E.MBP_ERANGE and "1e4" in msg
+    # source on a pixel, zero axes, parallel axes
+    def on_pixel(t):
+        t["src"][2] = t["det"][2]
+    rc, msg = _bad(lib, mutate_traj=on_pixel)
+    assert rc == E.MBP_ECOINCIDENT and "must differ" in msg
+    assert _bad(lib, mutate_traj=lambda t: t["eu"].__setitem__(1, 0.0))[0] == E.MBP_ECOINCIDENT
+    assert _bad(lib, mutate_traj=lambda t: t["ev"].__setitem__(1, t["eu"][1]))[0] == E.MBP_ECOINCIDENT
+    assert _bad(lib, mutate_traj=lambda t: t["src"].__setitem__(0, 0.0), cfg=c1)[0] == E.MBP_ECOINCIDENT
+    # near and far geometry
+    def near(t):
+        t["src"][4] = t["det"][4] + 1e-9 * np.cross(t["eu"][4], t["ev"][4])
+    rc, msg = _bad(lib, mutate_traj=near)
+    assert rc == E.MBP_ERANGE and "1e6" in msg
+    rc, msg = _bad(lib, mutate_traj=lambda t: t["src"].__setitem__((5, 0), 2e15))
+    assert rc == E.MBP_ERANGE and "1e15" in msg
+    # a source in the detector plane but off the pixel array is fine
+    def in_plane_off_array(t):
+        t["src"][6] = t["det"][6] + 1e4 * t["eu"][6]
+    assert _bad(lib, mutate_traj=in_plane_off_array)[0] == 0
+    # 2^31-element arrays
+    assert _bad(lib, lambda g: (setattr(g, "D", 2048), setattr(g, "H", 1024), setattr(g, "W", 1024)))[0] == E.MBP_ETOOLARGE
+    assert _bad(lib, lambda g: (setattr(g, "rows", 1 << 16), setattr(g, "cols", 1 << 16)))[0] == E.MBP_ETOOLARGE
+    # missing trajectory arrays
+    g = _geometry(SMALL_CONFIGS["c3_cone256"])
+    h = ctypes.c_void_p()
+    assert lib.mbp_plan_create(ctypes.byref(g), None, None, None, None, ctypes.byref(h)) == E.MBP_EINVAL
+    assert lib.mbp_plan_create(None, None, None, None, None, ctypes.byref(h)) == E.MBP_EINVAL
+
+
+def test_python_plan_maps_errors_and_shapes():
+    import matched_backprojection_amd as mbp
+    cfg = SMALL_CONFIGS["c4_cone512_aniso"]
+    traj = config_trajectory(cfg)
+    plan = mbp.Plan("cone", cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols), (cfg.dv, cfg.du),
+                    layout="WHD")
+    assert plan.sino_shape == (cfg.views, cfg.rows, cfg.cols)
+    assert plan.info["path"] == "column" and plan.workspace_size(1) == 0
+    assert plan.workspace_size(3) == 2 * cfg.n_voxels * 4
+    bad = dict(traj)
+    bad["src"] = traj["src"].copy()
+    bad["src"][0, 0] = np.nan
+    with pytest.raises(ValueError, match="finite"):
+        mbp.Plan("cone", cfg.shape, cfg.spacing, bad, (cfg.rows, cfg.cols), (cfg.dv, cfg.du))
+    with pytest.raises(ValueError):
+        mbp.Plan("cone", cfg.shape, (1.0, 1e-9, 1.0), traj, (cfg.rows, cfg.cols))
+    p2 = mbp.Plan("parallel", (64, 64), 1.0, config_trajectory(CONFIGS["c1_parallel2d"]), 96, 1.0)
+    assert p2.sino_shape == (90, 96) and p2.info["path"] == "generic"
+    plan.close()
+    p2.close()

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path against the fp64 oracle, through the C ABI (runs on the GPU machine).
+
+Bar (per configuration and batch member): relative L2 error <= 1e-5; max relative error
+<= 1e-4 per ray / voxel, where the relative error of element i is
+|g_i - o_i| / max(|o_i|, 1e-6 * max|o|); adjoint identity |<Ax, y> - <x, A^T y>| / |<Ax, y>|
+<= 1e-5 with fp64 dot products of the GPU's fp32 outputs. Rays the oracle gives exactly 0
+(misses) must be exactly 0.
+
+Reduced twins of the five configurations are compared element by element in full; the
+full-size configurations are compared on sampled rays and voxels that the oracle computes
+one by one (forward: Siddon on the chosen rays; adjoint: the chord definition at the chosen
+voxels), plus the adjoint identity over the whole arrays.
+"""
+
+import numpy as np
+import pytest
+
+from workloads import (CONFIGS, SMALL_CONFIGS, add_noise, config_phantom, config_trajectory,
+                       random_cone_trajectory, sinogram_field)
+
+pytestmark = pytest.mark.gpu
+
+RTOL_L2 = 1e-5
+RTOL_MAX = 1e-4
+RTOL_ADJ = 1e-5
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    return torch, torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def mbp():
+    import matched_backprojection_amd as m
+    return m
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def rel_l2(g, o):
+    return float(np.linalg.norm((g - o).ravel()) / np.linalg.norm(o.ravel()))
+
+
+def max_rel(g, o):
+    floor = 1e-6 * float(np.abs(o).max())
+    return float((np.abs(g - o) / np.maximum(np.abs(o), floor)).max())
+
+
+def check(g, o, what):
+    e2, em = rel_l2(g, o), max_rel(g, o)
+    say(f"  {what}: rel-L2 {e2:.2e}  max-rel {em:.2e}")
+    assert e2 <= RTOL_L2, (what, e2)
+    assert em <= RTOL_MAX, (what, em)
+
+
+def geom_of(cfg):
+    return {"beam": cfg.beam, "shape": cfg.shape, "spacing": cfg.spacing, "views": cfg.views,
+            "rows": cfg.rows, "cols": cfg.cols, "du": cfg.du, "dv": cfg.dv}
+
+
+def make_plan(mbp, cfg, traj=None, layout=None):
+    traj = config_trajectory(cfg) if traj is None else traj
+    if cfg.beam == "cone":
+        return mbp.Plan("cone", cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols),
+                        (cfg.dv, cfg.du), layout=layout or cfg.layout)
+    return mbp.Plan(cfg.beam, cfg.shape, cfg.spacing, traj, cfg.cols, cfg.du)
+
+
+def to_device_volume(torch, dev, x, layout):
+    """numpy (B?, D, H, W) -> device tensor of the same shape in the given layout."""
+    if layout == "DHW" or x.ndim == 2:
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    perm = (2, 1, 0) if x.ndim == 3 else (0, 3, 2, 1)
+    t = torch.from_numpy(np.ascontiguousarray(x.transpose(perm))).to(dev)
+    return t.permute(perm)
+
+
+def paths_of(cfg):
+    return ["column", "generic"] if cfg.beam == "cone" else ["generic"]
+
+
+# ------------------------------------------------------------------------------------------
+# Reduced configurations: full element-by-element comparison
+
+
+@pytest.mark.parametrize("name", list(SMALL_CONFIGS))
+def test_small_config_parity(torch_dev, mbp, oracle, name):
+    torch, dev = torch_dev
+    cfg = SMALL_CONFIGS[name]
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    x = config_phantom(cfg)
+    ref = oracle.project(geom, traj, x)
+    y = ref.astype(np.float32)
+    if cfg.noise_sigma:
+        y = add_noise(y, cfg.noise_sigma, cfg.noise_seed)
+    bref = oracle.backproject(geom, traj, y)
+    for path in paths_of(cfg):
+        say(f"case {cfg.name} path={path} layout={cfg.layout} batch={cfg.batch}")
+        plan = make_plan(mbp, cfg)
+        plan.set_path(path)
+        xd = to_device_volume(torch, dev, x, cfg.layout)
+        p = plan.project(xd).cpu().numpy().astype(np.float64)
+        torch.cuda.synchronize()
+        members = range(cfg.batch) if cfg.batch else [None]
+        for m in members:
+            g, o = (p, ref) if m is None else (p[m], ref[m])
+            check(g, o, f"forward member {m}")
+            assert np.all(g[o == 0.0] == 0.0), "missed rays must be exactly 0"
+        yd = torch.from_numpy(y).to(dev)
+        b = plan.backproject(yd)
+        torch.cuda.synchronize()
+        bn = b.cpu().numpy().astype(np.float64)
+        for m in members:
+            g, o = (bn, bref) if m is None else (bn[m], bref[m])
+            check(g, o, f"adjoint member {m}")
+        # adjoint identity on the GPU pair
+        lhs = float(np.dot(p.ravel(), y.astype(np.float64).ravel()))
+        rhs = float(np.dot(x.astype(np.float64).ravel(), bn.ravel()))
+        say(f"  adjoint identity {abs(lhs - rhs) / abs(lhs):.2e}")
+        assert abs(lhs - rhs) <= RTOL_ADJ * abs(lhs)
+        plan.close()
+
+
+def test_general_trajectory_parity(torch_dev, mbp, oracle):
+    """Tilted detectors (row axis not parallel to z): the generic walk, anisotropic grid."""
+    torch, dev = torch_dev
+    cfg = SMALL_CONFIGS["c4_cone512_aniso"]
+    traj = random_cone_trajectory(30, seed=12, radius=150.0, sdd=260.0, tilt=0.5)
+    from dataclasses import replace
+    cfg = replace(cfg, views=30)
+    geom = geom_of(cfg)
+    x = config_phantom(cfg)
+    ref = oracle.project(geom, traj, x)
+    y = np.random.default_rng(3).random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    say("case random tilted cone trajectory (generic walk)")
+    plan = make_plan(mbp, cfg, traj=traj)
+    assert plan.info["path"] == "generic"
+    p = plan.project(to_device_volume(torch, dev, x, cfg.layout)).cpu().numpy().astype(np.float64)
+    check(p, ref, "forward")
+    b = plan.backproject(torch.from_numpy(y).to(dev)).cpu().numpy().astype(np.float64)
+    check(b, bref, "adjoint")
+    plan.close()
+
+
+def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
+    """Ragged view batches, both layouts, batch sizes 0..5, accumulation, caller workspace."""
+    torch, dev = torch_dev
+    cfg = SMALL_CONFIGS["c3_cone256"]
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(8)
+    xs = rng.random((5,) + cfg.shape).astype(np.float32)
+    ref = oracle.project(geom, traj, xs)
+    ys = rng.random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    for layout in ("DHW", "WHD"):
+        for path in ("column", "generic"):
+            plan = make_plan(mbp, cfg, layout=layout)
+            plan.set_path(path)
+            plan.set_view_batch(7)            # 36 views -> launches of 7 + ragged 1
+            for B in (0, 1, 3, 5):
+                say(f"case view-batch 7 layout={layout} path={path} B={B}")
+                xd = to_device_volume(torch, dev, xs[:B], layout)
+                p = plan.project(xd).cpu().numpy().astype(np.float64)
+                assert p.shape == (B, cfg.views, cfg.rows, cfg.cols)
+                for m in range(B):
+                    check(p[m], ref[m], f"forward member {m}")
+                b = plan.backproject(torch.from_numpy(ys[:B]).to(dev)).cpu().numpy().astype(np.float64)
+                assert b.shape == (B,) + cfg.shape
+                for m in range(B):
+                    check(b[m], bref[m], f"adjoint member {m}")
+            # accumulate into a prefilled volume, unbatched
+            pre = rng.random(cfg.shape).astype(np.float32)
+            out = to_device_volume(torch, dev, pre, layout)
+            plan.backproject(torch.from_numpy(ys[0]).to(dev), out=out, accumulate=True)
+            check(out.cpu().numpy().astype(np.float64), bref[0] + pre.astype(np.float64), "accumulate")
+            plan.close()
+    # a caller-owned workspace gives the same result; a too-small one is refused
+    plan = make_plan(mbp, cfg)
+    need = plan.workspace_size(5)
+    assert need == 4 * cfg.n_voxels * 4
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    plan.set_workspace(ws)
+    p = plan.project(torch.from_numpy(xs).to(dev)).cpu().numpy().astype(np.float64)
+    for m in range(5):
+        check(p[m], ref[m], f"caller workspace member {m}")
+    plan.set_workspace(torch.empty(16, dtype=torch.float32, device=dev))
+    with pytest.raises(mbp.MbpError):
+        plan.project(torch.from_numpy(xs).to(dev))
+    plan.close()
+
+
+def test_layout_conversion_roundtrip(torch_dev, mbp):
+    torch, dev = torch_dev
+    x = torch.rand((3, 37, 41, 29), device=dev)
+    w = mbp.convert_layout(x, to_whd=True)
+    assert w.stride()[1:] == (1, 37, 37 * 41)
+    assert torch.equal(w, x)                       # same logical tensor
+    back = mbp.convert_layout(w, to_whd=False)
+    assert back.is_contiguous() and torch.equal(back, x)
+
+
+def test_segment_counts_match_oracle(torch_dev, mbp, oracle):
+    torch, dev = torch_dev
+    for name in ("c2_fan2d", "c3_cone256", "c5_helical_b4"):
+        cfg = SMALL_CONFIGS[name]
+        geom, traj = geom_of(cfg), config_trajectory(cfg)
+        x = np.zeros(cfg.shape, np.float32)
+        _, cnt = oracle.project(geom, traj, x, counts=True)
+        for path in paths_of(cfg):
+            say(f"case segment count {cfg.name} path={path}")
+            plan = make_plan(mbp, cfg)
+            plan.set_path(path)
+            n = plan.segment_count()
+            say(f"  gpu {n} oracle {int(cnt.sum())}")
+            assert abs(n - int(cnt.sum())) <= 1e-3 * cnt.sum()
+            plan.close()
+
+
+# ------------------------------------------------------------------------------------------
+# Full-size configurations: sampled rays and voxels, adjoint identity
+
+
+def _sample_rays(cfg, n, rng):
+    per_view = cfg.rows * cfg.cols
+    ids = [rng.integers(0, cfg.n_rays, n)]
+    v = int(rng.integers(cfg.views))
+    ids.append(v * per_view + (cfg.rows - 1) * cfg.cols + np.arange(0, cfg.cols, 7))   # last row
+    ids.append(v * per_view + np.arange(0, cfg.rows, 5) * cfg.cols)                   # first column
+    return np.unique(np.concatenate(ids))
+
+
+def _sample_voxels(cfg, n, rng):
+    ids = [rng.integers(0, cfg.n_voxels, n)]
+    shape = cfg.shape
+    corners = np.array(np.meshgrid(*[[0, s - 1] for s in shape], indexing="ij")).reshape(len(shape), -1)
+    ids.append(np.ravel_multi_index(corners, shape))
+    return np.unique(np.concatenate(ids))
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_full_size_parity(torch_dev, mbp, oracle, name):
+    torch, dev = torch_dev
+    cfg = CONFIGS[name]
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(100 + len(name))
+    x = config_phantom(cfg)
+    small = cfg.n_rays * 1000 < 5e8         # c1, c2: the oracle runs the whole operator
+    plan = make_plan(mbp, cfg)
+    say(f"case full-size {cfg.name} path={plan.info['path']} layout={cfg.layout} batch={cfg.batch}")
+    xd = to_device_volume(torch, dev, x, cfg.layout)
+    p_dev = plan.project(xd)
+    torch.cuda.synchronize()
+    members = list(range(cfg.batch)) if cfg.batch else [None]
+    if small:
+        ref = oracle.project(geom, traj, x)
+        check(p_dev.cpu().numpy().astype(np.float64), ref, "forward (all rays)")
+        y = ref.astype(np.float32)
+        if cfg.noise_sigma:
+            y = add_noise(y, cfg.noise_sigma, cfg.noise_seed)
+    else:
+        ids = _sample_rays(cfg, 3000, rng)
+        ref = oracle.project_rays(geom, traj, x, ids)
+        flat = p_dev.reshape((cfg.batch or 1), -1)[:, torch.from_numpy(ids).to(dev)].cpu().numpy()
+        for m in members:
+            g = flat[0 if m is None else m].astype(np.float64)
+            o = ref if m is None else ref[m]
+            check(g, o, f"forward member {m} ({ids.size} sampled rays)")
+        y = sinogram_field(tuple(p_dev.shape), seed=7)
+    yd = torch.from_numpy(y).to(dev)
+    b_dev = plan.backproject(yd)
+    torch.cuda.synchronize()
+    if small:
+        bref = oracle.backproject(geom, traj, y)
+        check(b_dev.cpu().numpy().astype(np.float64), bref, "adjoint (all voxels)")
+    else:
+        vids = _sample_voxels(cfg, 400, rng)
+        bref = oracle.backproject_voxels(geom, traj, y, vids)
+        bflat = b_dev.reshape((cfg.batch or 1), -1) if cfg.layout == "DHW" else \
+            b_dev.contiguous().reshape((cfg.batch or 1), -1)
+        g_all = bflat[:, torch.from_numpy(vids).to(dev)].cpu().numpy().astype(np.float64)
+        for m in members:
+            check(g_all[0 if m is None else m], bref if m is None else bref[m],
+                  f"adjoint member {m} ({vids.size} sampled voxels)")
+    # adjoint identity over the whole arrays (fp64 dot products of fp32 outputs)
+    pv = p_dev.double()
+    lhs = torch.dot(pv.reshape(-1), yd.double().reshape(-1)).item()
+    rhs = torch.dot(xd.double().contiguous().reshape(-1), b_dev.double().contiguous().reshape(-1)).item()
+    say(f"  adjoint identity {abs(lhs - rhs) / abs(lhs):.2e}")
+    assert abs(lhs - rhs) <= RTOL_ADJ * abs(lhs)
+    plan.close()
+    del p_dev, b_dev, xd, yd
+    torch.cuda.empty_cache()

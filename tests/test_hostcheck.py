@@ -1,0 +1,85 @@
+"""CPU replay of the GPU walks: bounds on every launch shape, and the walk logic (no GPU).
+
+The replay compiles the kernels' traversal header for the host. It is not parity (it shares
+the GPU path's code); it shows, before anything runs on a GPU, that every cell the walks visit
+at the parity and benchmark shapes lies inside the volume, and that the walk logic reproduces
+the oracle's line integrals at fp32 rounding level.
+"""
+
+import numpy as np
+import pytest
+
+from tests import _hostcheck as HC
+from workloads import (CONFIGS, SMALL_CONFIGS, config_phantom, config_trajectory,
+                       random_cone_trajectory)
+
+
+def _geom(cfg):
+    return {"beam": cfg.beam, "shape": cfg.shape, "spacing": cfg.spacing, "views": cfg.views,
+            "rows": cfg.rows, "cols": cfg.cols, "du": cfg.du, "dv": cfg.dv}
+
+
+def _paths(cfg):
+    return ["generic", "column"] if cfg.beam == "cone" else ["generic"]
+
+
+@pytest.mark.parametrize("name", list(SMALL_CONFIGS))
+def test_walks_reproduce_oracle_on_small_configs(oracle, name):
+    cfg = SMALL_CONFIGS[name]
+    geom, traj = _geom(cfg), config_trajectory(cfg)
+    x = config_phantom(cfg)
+    if cfg.batch:
+        x = x[0]
+    ref, cnt = oracle.project(geom, traj, x, counts=True)
+    y = np.random.default_rng(1).random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    for path in _paths(cfg):
+        s, k, viol = HC.project(path, geom, traj, x)
+        assert viol == 0
+        assert np.linalg.norm(s - ref) / np.linalg.norm(ref) < 1e-6
+        assert np.abs(s - ref).max() / np.abs(ref).max() < 1e-5
+        # counts differ only where planes cross at one point (a zero-length pair in the oracle
+        # may round to a tiny positive length in fp32, or the reverse)
+        assert abs(int(k.sum()) - int(cnt.sum())) <= 1e-3 * cnt.sum()
+        assert (k == cnt).mean() > 0.95
+        b, viol = HC.backproject(path, geom, traj, y)
+        assert viol == 0
+        assert np.linalg.norm(b - bref) / np.linalg.norm(bref) < 1e-6
+
+
+def test_generic_walk_on_tilted_detectors_and_inside_sources(oracle):
+    """Sources inside the volume, tilted detectors, anisotropic off-centre grid."""
+    traj = random_cone_trajectory(12, seed=4, radius=9.0, sdd=40.0, tilt=0.6)
+    geom = {"beam": "cone", "shape": (14, 17, 19), "spacing": (1.5, 1.0, 0.75),
+            "center": (0.375, -0.25, 0.5), "views": 12, "rows": 23, "cols": 21,
+            "du": 1.1, "dv": 0.9}
+    x = np.random.default_rng(3).random(geom["shape"]).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    s, _, viol = HC.project("generic", geom, traj, x)
+    assert viol == 0
+    assert np.linalg.norm(s - ref) / np.linalg.norm(ref) < 1e-6
+
+
+def _edge_and_random_rays(cfg, n_random, seed):
+    rng = np.random.default_rng(seed)
+    per_view = cfg.rows * cfg.cols
+    ids = [rng.integers(0, cfg.n_rays, n_random)]
+    for v in (0, cfg.views // 4, cfg.views // 2, cfg.views - 1):
+        k = np.arange(cfg.rows)
+        j = np.arange(cfg.cols)
+        for kk in (0, cfg.rows - 1):                       # first and last detector rows
+            ids.append(v * per_view + kk * cfg.cols + j)
+        for jj in (0, cfg.cols // 2, cfg.cols - 1):        # first, middle and last columns
+            ids.append(v * per_view + k * cfg.cols + jj)
+    return np.concatenate(ids)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_walks_stay_in_bounds_at_full_size(name):
+    cfg = CONFIGS[name]
+    geom, traj = _geom(cfg), config_trajectory(cfg)
+    ids = _edge_and_random_rays(cfg, 20000, seed=len(name))
+    for path in _paths(cfg):
+        visits, viol = HC.check_rays(path, geom, traj, ids)
+        assert viol == 0, (name, path)
+        assert visits > ids.size        # rays really cross the volume

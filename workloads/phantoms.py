@@ -76,11 +76,21 @@ def voxelise(shape, spacing, ellipsoids) -> np.ndarray:
             sl.append((lo, hi))
         if any(hi <= lo for lo, hi in sl):
             continue
-        grids = np.meshgrid(*[coords[a][sl[a][0]:sl[a][1]] - centre[a] for a in range(ndim)],
-                            indexing="ij")          # world-axis order (x, y[, z])
-        pts = np.stack(grids, axis=-1)              # [..., ndim] world offsets
-        body = pts @ R                              # body coordinates (R^T p)
-        inside = ((body / axes) ** 2).sum(axis=-1) <= 1.0
+        # quadratic form (p - c)^T M (p - c) <= 1 with M = R diag(1/a^2) R^T, evaluated by
+        # broadcasting the per-axis offsets (world-axis order x, y[, z])
+        M = (R / axes[None, :] ** 2) @ R.T
+        offs = []
+        for a in range(ndim):
+            o = coords[a][sl[a][0]:sl[a][1]] - centre[a]
+            shp = [1] * ndim
+            shp[a] = o.size
+            offs.append(o.reshape(shp))
+        q = None
+        for a in range(ndim):
+            for b in range(a, ndim):
+                term = (M[a, a] if a == b else 2.0 * M[a, b]) * (offs[a] * offs[b])
+                q = term if q is None else q + term
+        inside = q <= 1.0
         # world-axis order -> tensor order (reverse axes)
         inside_t = np.transpose(inside, tuple(range(ndim - 1, -1, -1)))
         tsl = tuple(slice(*sl[ndim - 1 - t]) for t in range(ndim))
