@@ -67,6 +67,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--adjoint", choices=("gather", "scatter"), default="gather",
+                    help="adjoint kernel of the column walk")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is "
@@ -88,6 +90,7 @@ def main() -> int:
     log(f"phantom {cfg.shape} built in {time.perf_counter() - t:.1f} s")
     plan = mbp.Plan("cone", cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols), (cfg.dv, cfg.du),
                     layout="WHD")
+    plan.set_adjoint(args.adjoint)
     info = plan.info
     # the z-fastest volume: a (D, H, W) tensor with strides (1, D, D*H)
     xd = torch.from_numpy(np.ascontiguousarray(x.transpose(2, 1, 0))).to(dev).permute(2, 1, 0)
@@ -126,7 +129,8 @@ def main() -> int:
 
     io_bytes = 4.0 * (cfg.n_voxels + cfg.n_rays) + 96.0 * cfg.views
     alg_bytes = 4.0 * segs + io_bytes
-    dominant = "column_adjoint_kernel" if b_avg >= f_avg else "column_forward_kernel"
+    adj_kernel = "column_gather_kernel" if args.adjoint == "gather" else "column_adjoint_kernel"
+    dominant = adj_kernel if b_avg >= f_avg else "column_forward_kernel"
     dom_ms = max(b_avg, f_avg)
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
     pair_gbs = 2 * alg_bytes / ((f_avg + b_avg) * 1e-3) / 1e9
@@ -154,6 +158,7 @@ def main() -> int:
             "segments_per_op": segs,
             "rays_per_op": cfg.n_rays,
             "path": info["path"],
+            "adjoint_kernel": adj_kernel,
             "forward_ms": f_avg,
             "adjoint_ms": b_avg,
             "rays_per_s": 2.0 * cfg.n_rays * args.steps / wall,

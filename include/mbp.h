@@ -80,6 +80,16 @@ typedef enum mbp_path {
                               a detector column share their xy walk                          */
 } mbp_path;
 
+typedef enum mbp_adjoint {
+    MBP_ADJOINT_AUTO = 0,     /* the gather for the column walk                               */
+    MBP_ADJOINT_GATHER = 1,   /* column walk: each wave owns one xy cell's z column in LDS and
+                                 sums, over views, crossing columns and rows, the exact chord
+                                 of every ray through each of its voxels; no global atomics   */
+    MBP_ADJOINT_SCATTER = 2   /* column walk: each ray scatters its value along its segments
+                                 with global float atomics (64 adjacent rows per wave, z-inner
+                                 stepping); always used by the generic walk                   */
+} mbp_adjoint;
+
 typedef struct mbp_geometry {
     int32_t beam;          /* mbp_beam                                                       */
     int32_t layout;        /* mbp_layout of the caller's volumes                            */
@@ -123,6 +133,10 @@ int mbp_plan_get_info(const mbp_plan* plan, mbp_plan_info* info);
    geometry that cannot use it returns MBP_EINVAL. Both walks visit the same segments. */
 int mbp_plan_set_path(mbp_plan* plan, int32_t path);
 
+/* Choose the adjoint kernel of the column walk. Both compute the same sums (the chord of
+   every ray through every voxel times the ray's value); they differ in summation order. */
+int mbp_plan_set_adjoint(mbp_plan* plan, int32_t kind);
+
 /* Limit the views of one kernel launch (0 = automatic: as many as index and grid limits
    allow). Results do not depend on it (page "diffct 2.1.0 -> 2.2.1", CHANGELOG 2.2.0,
    "Changed": backprojection accumulators span all contributing view batches). */
@@ -140,12 +154,15 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
 int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
                     int32_t accumulate, void* stream);
 
-/* Number of positive-length ray/voxel segments one projection of one member walks (the
-   work unit of the throughput metric). Runs a counting kernel on `stream`, then waits. */
+/* Number of ray/voxel segments one projection of one member walks, counting those longer
+   than 1e-6 of the smallest voxel pitch (shorter ones are rounding residue where a ray
+   crosses several grid planes at one point). This is the work unit of the throughput
+   metric. Runs a counting kernel on `stream`, then waits. */
 int mbp_segment_count(mbp_plan* plan, int64_t* count, void* stream);
 
-/* Device workspace the plan needs for `batch` members (layout conversion for the column
-   walk). 0 when none is needed. */
+/* Device workspace the plan needs for `batch` members on the column walk: a z-fastest copy of
+   up to four interleaved volumes (not needed for one z-fastest volume) plus, for the gather
+   adjoint, a reordered copy of their sinograms. 0 when none is needed. */
 int mbp_workspace_size(const mbp_plan* plan, int64_t batch, size_t* bytes);
 
 /* Hand the plan a caller-owned device workspace (NULL, 0 = let the library allocate its

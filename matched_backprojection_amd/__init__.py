@@ -133,6 +133,10 @@ class Plan:
     def set_path(self, path: str) -> None:
         _capi.check(self._lib.mbp_plan_set_path(self._handle, _capi.PATHS[path]), "mbp_plan_set_path")
 
+    def set_adjoint(self, kind: str) -> None:
+        """Adjoint kernel of the column walk: "gather" (default), "scatter" or "auto"."""
+        _capi.check(self._lib.mbp_plan_set_adjoint(self._handle, _capi.ADJOINTS[kind]), "mbp_plan_set_adjoint")
+
     def set_view_batch(self, views: int) -> None:
         _capi.check(self._lib.mbp_plan_set_view_batch(self._handle, int(views)), "mbp_plan_set_view_batch")
 

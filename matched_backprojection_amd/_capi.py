@@ -24,11 +24,12 @@ BEAMS = {"parallel": 0, "fan": 1, "cone": 2}
 LAYOUTS = {"DHW": 0, "WHD": 1}
 PATHS = {"auto": 0, "generic": 1, "column": 2}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
+ADJOINTS = {"auto": 0, "gather": 1, "scatter": 2}
 
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = (
     "mbp_plan_create", "mbp_plan_destroy", "mbp_plan_get_info", "mbp_plan_set_path",
-    "mbp_plan_set_view_batch", "mbp_project", "mbp_backproject", "mbp_segment_count",
+    "mbp_plan_set_view_batch", "mbp_plan_set_adjoint", "mbp_project", "mbp_backproject", "mbp_segment_count",
     "mbp_workspace_size", "mbp_set_workspace", "mbp_convert_layout", "mbp_status_string",
     "mbp_last_error", "mbp_abi_version",
 )
@@ -85,6 +86,7 @@ def load():
     lib.mbp_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.mbp_plan_set_path.argtypes = [P, I32]
     lib.mbp_plan_set_view_batch.argtypes = [P, I64]
+    lib.mbp_plan_set_adjoint.argtypes = [P, I32]
     lib.mbp_project.argtypes = [P, P, I64, P, P]
     lib.mbp_backproject.argtypes = [P, P, I64, P, I32, P]
     lib.mbp_segment_count.argtypes = [P, ctypes.POINTER(I64), P]

@@ -57,7 +57,7 @@ extern "C" {
 
 // Forward projection with the generic (path 1) or column (path 2) walk. frames: views x 12
 // doubles (s, c, u, v); volume element (x, y, z) at x*sx + y*sy + z*sz. Outputs the fp32
-// sinogram [views][rows][cols], per-ray counts of positive-length segments, and the number of bound violations.
+// sinogram [views][rows][cols], per-ray counts of segments longer than 1e-6 min pitch, and the number of bound violations.
 int mbph_project(int path, const double* frames, int beam, const double* lo, const double* hi,
                  const double* pitch, const int32_t* n, int views, int rows, int cols,
                  double du, double dv, const float* vol, int64_t sx, int64_t sy, int64_t sz,
@@ -68,6 +68,7 @@ int mbph_project(int path, const double* frames, int beam, const double* lo, con
     const Box B = box_from(lo, pitch, n);
     *violations = 0;
     Checked chk{&B, violations};
+    const float eps = (float)(1e-6 * std::fmin(B.pitch[0], std::fmin(B.pitch[1], B.pitch[2])));
     for (int i = 0; i < views; ++i) {
         for (int j = 0; j < cols; ++j) {
             ColumnWalk c;
@@ -76,7 +77,7 @@ int mbph_project(int path, const double* frames, int beam, const double* lo, con
                 float acc = 0.0f;
                 int64_t cnt = 0;
                 auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
-                    if (len > 0.0f) ++cnt;
+                    if (len > eps) ++cnt;
                     if (!chk.ok(cx, cy, cz, len)) return;
                     acc = fmaf(len, vol[cx * sx + cy * sy + cz * sz], acc);
                 };
@@ -131,6 +132,51 @@ int mbph_backproject(int path, const double* frames, int beam, const double* lo,
                     RayWalk r;
                     ray_setup(F[i], B, beam, centred(j, cols, du), centred(k, rows, dv), r);
                     walk_ray(r, visit);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+// Adjoint by the cell gather (voxel side), accumulated in fp64: every xy cell, every view,
+// every crossing column and every row, exactly as the gather kernel enumerates them.
+int mbph_gather(const double* frames, int beam, const double* lo, const double* pitch,
+                const int32_t* n, int views, int rows, int cols, double du, double dv,
+                const float* sino, double* vol, long long* violations) {
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *violations = 0;
+    const double roff = 0.5 * (double)(rows - 1);
+    for (int ix = 0; ix < n[0]; ++ix) {
+        for (int iy = 0; iy < n[1]; ++iy) {
+            const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
+            const double y0 = B.lo[1] + iy * B.pitch[1], y1 = y0 + B.pitch[1];
+            for (int v = 0; v < views; ++v) {
+                int32_t j0, j1;
+                if (!cell_column_range(F[v], beam, cols, du, x0, x1, y0, y1, j0, j1)) continue;
+                if (j0 < 0 || j1 >= cols) ++*violations;
+                for (int32_t j = j0; j <= j1; ++j) {
+                    CellCrossing x;
+                    if (!cell_crossing(F[v], beam, j, cols, du, x0, x1, y0, y1, x)) continue;
+                    for (int k = 0; k < rows; ++k) {
+                        double len;
+                        if (beam == BEAM_PARALLEL) {
+                            len = std::sqrt(F[v].s[0] * F[v].s[0] + F[v].s[1] * F[v].s[1] + F[v].s[2] * F[v].s[2]);
+                        } else {
+                            double p[3];
+                            pixel_point(F[v], centred(j, cols, du), centred(k, rows, dv), p);
+                            const double a = p[0] - F[v].s[0], b = p[1] - F[v].s[1], c = p[2] - F[v].s[2];
+                            len = std::sqrt(a * a + b * b + c * c);
+                        }
+                        const double w = (double)sino[((int64_t)v * rows + k) * cols + j] * len;
+                        auto piece = [&](int32_t iz, double share) {
+                            if (iz < 0 || iz >= n[2] || !(share >= 0.0)) { ++*violations; return; }
+                            vol[((int64_t)iz * n[1] + iy) * n[0] + ix] += share * w;
+                        };
+                        row_pieces(x, ((double)k - roff) * F[v].v[2] * dv, B, 0, n[2], piece);
+                    }
                 }
             }
         }

@@ -112,8 +112,13 @@ __global__ void __launch_bounds__(256) generic_adjoint_kernel(const GenericLaunc
     walk_ray(r, visit);
 }
 
-// Segment counts: positive-length segments of the generic walk, grid-stride over rays, one
-// 64-bit atomic per block.
+// Segment counts: segments of the generic walk longer than 1e-6 of the smallest voxel pitch
+// (shorter ones are the rounding residue of planes crossed at one point), grid-stride over
+// rays, one 64-bit atomic per block.
+__device__ __forceinline__ float count_eps(const Box& b) {
+    return (float)(1e-6 * fmin(b.pitch[0], fmin(b.pitch[1], b.pitch[2])));
+}
+
 __device__ __forceinline__ void block_count_add(unsigned long long local, unsigned long long* count) {
     __shared__ unsigned long long part[256];
     part[threadIdx.x] = local;
@@ -139,7 +144,8 @@ __global__ void __launch_bounds__(256) generic_count_kernel(const GenericLaunch 
         RayWalk r;
         ray_setup(F, A.box, A.beam, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), r);
         uint32_t c = 0;
-        auto visit = [&](int32_t, int32_t, int32_t, float len) { c += len > 0.0f ? 1u : 0u; };
+        const float eps = count_eps(A.box);
+        auto visit = [&](int32_t, int32_t, int32_t, float len) { c += len > eps ? 1u : 0u; };
         walk_ray(r, visit);
         local += c;
     }
@@ -261,10 +267,136 @@ __global__ void __launch_bounds__(256) column_count_kernel(const ColumnLaunch A,
         RowWalk r;
         row_setup(cw, A.box, centred(t.row, A.rows, A.dv), F.v[2], r);
         if (!t.valid) { r.t_lo = 0.0f; r.t_hi = 0.0f; }
-        auto visit = [&](int32_t, int32_t, int32_t, float len) { c += len > 0.0f ? 1u : 0u; };
+        const float eps = count_eps(A.box);
+        auto visit = [&](int32_t, int32_t, int32_t, float len) { c += len > eps ? 1u : 0u; };
         walk_column_row(cw, r, visit);
     }
     block_count_add(c, count);
+}
+
+// ------------------------------------------------------------------------------------------
+// Column gather: the matched adjoint without global atomics.
+//
+// The adjoint value of voxel v is the sum over rays of len(ray, v) * y[ray]. For the column
+// geometry the rays of detector column j (all rows) share one line in the xy plane, and a ray
+// parameter alpha (0 at the source, 1 at the pixel) is the same for all of them at a given xy
+// point. So for one xy cell and one view:
+//  * the columns whose xy line crosses the cell are the pixels whose centre lies inside the
+//    detector interval that the cell's four corners project to;
+//  * for such a column the xy cell is crossed for alpha in [a0, a1] (fp64 slab clip), by
+//    every row alike;
+//  * along that piece row k's z runs linearly from z_k(a0) to z_k(a1); the part inside z cell
+//    iz has length (a1 - a0) * |d_k| * (z overlap / z extent), which is exactly the chord of
+//    the ray through the voxel.
+// A wave owns one xy cell (all of its z cells, held in LDS) and loops over every view, every
+// crossing column and all rows (lanes = 64 adjacent rows), adding each piece into LDS; the
+// column is written once at the end. The sinogram is read through a pre-pass copy in
+// [view][col][row] order (rows contiguous, so a wave's 64 lanes load 256 contiguous bytes),
+// already multiplied by |d_k|, the ray's length per unit of alpha.
+
+template <int NB>
+__global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A, const Ptrs4 sino,
+                                                           float* __restrict__ ysc) {
+    __shared__ float tile[NB][32][33];
+    const int32_t j0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+    const int32_t view = A.view0 + (int32_t)blockIdx.z;
+    const int32_t tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const int64_t vbase = (int64_t)view * A.rows * A.cols;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t k = k0 + ty + 8 * i, j = j0 + tx;
+        if (k < A.rows && j < A.cols) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+                tile[m][ty + 8 * i][tx] = sino.p[m][vbase + (int64_t)k * A.cols + j];
+        }
+    }
+    __syncthreads();
+    const Frame F = A.frames[view];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t j = j0 + ty + 8 * i, k = k0 + tx;
+        if (k < A.rows && j < A.cols) {
+            double len;
+            if (A.beam == BEAM_PARALLEL) {
+                len = sqrt(F.s[0] * F.s[0] + F.s[1] * F.s[1] + F.s[2] * F.s[2]);
+            } else {
+                double p[3];
+                pixel_point(F, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), p);
+                const double dx = p[0] - F.s[0], dy = p[1] - F.s[1], dz = p[2] - F.s[2];
+                len = sqrt(dx * dx + dy * dy + dz * dz);
+            }
+            const float scale = (float)len;
+            const int64_t o = ((vbase + (int64_t)j * A.rows + k)) * NB;
+#pragma unroll
+            for (int m = 0; m < NB; ++m) ysc[o + m] = tile[m][tx][ty + 8 * i] * scale;
+        }
+    }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A,
+                                                            const float* __restrict__ ysc,
+                                                            float* __restrict__ vol,
+                                                            int32_t zchunk, int32_t nchunks,
+                                                            int32_t accumulate) {
+    extern __shared__ float lds[];
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    const int32_t lane = (int32_t)(threadIdx.x & 63u);
+    const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
+    const uint32_t task = blk * 4u + wave;
+    const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
+    const bool live = task < (uint32_t)W * (uint32_t)H * (uint32_t)nchunks;
+    const int32_t zc = (int32_t)(task % (uint32_t)nchunks);
+    const uint32_t xy = task / (uint32_t)nchunks;
+    const int32_t iy = (int32_t)(xy % (uint32_t)H), ix = (int32_t)(xy / (uint32_t)H);
+    const int32_t z0 = zc * zchunk;
+    const int32_t z1 = live ? (z0 + zchunk < D ? z0 + zchunk : D) : z0;
+    float* col = lds + wave * zchunk * NB;
+    for (int32_t i = lane; i < (z1 - z0) * NB; i += 64) col[i] = 0.0f;
+    __syncthreads();
+    if (live) {
+        const double x0 = A.box.lo[0] + ix * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
+        const double y0 = A.box.lo[1] + iy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
+        const double roff = 0.5 * (double)(A.rows - 1);
+        for (int32_t view = A.view0; view < A.view0 + A.nviews; ++view) {
+            const Frame F = A.frames[view];
+            int32_t j0, j1;
+            if (!cell_column_range(F, A.beam, A.cols, A.du, x0, x1, y0, y1, j0, j1)) continue;
+            const double evz = F.v[2] * A.dv;
+            for (int32_t j = j0; j <= j1; ++j) {
+                CellCrossing x;
+                if (!cell_crossing(F, A.beam, j, A.cols, A.du, x0, x1, y0, y1, x)) continue;
+                const int64_t ybase = ((int64_t)view * A.cols + j) * A.rows;
+                for (int32_t k0 = 0; k0 < A.rows; k0 += 64) {
+                    const int32_t k = k0 + lane;
+                    if (k >= A.rows) continue;
+                    float w[NB];
+                    if constexpr (NB == 1) {
+                        w[0] = ysc[ybase + k];
+                    } else if constexpr (NB == 2) {
+                        const float2 t = *reinterpret_cast<const float2*>(ysc + (ybase + k) * 2);
+                        w[0] = t.x; w[1] = t.y;
+                    } else {
+                        const float4 t = *reinterpret_cast<const float4*>(ysc + (ybase + k) * 4);
+                        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+                    }
+                    auto piece = [&](int32_t iz, double share) {
+                        const float f = (float)share;
+#pragma unroll
+                        for (int m = 0; m < NB; ++m) atomicAdd(col + (iz - z0) * NB + m, f * w[m]);
+                    };
+                    row_pieces(x, ((double)k - roff) * evz, A.box, z0, z1, piece);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (live) {
+        const int64_t base = (((int64_t)ix * H + iy) * D + z0) * NB;
+        for (int32_t i = lane; i < (z1 - z0) * NB; i += 64)
+            vol[base + i] = accumulate ? vol[base + i] + col[i] : col[i];
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -462,6 +594,49 @@ hipError_t launch_count(const GenericLaunch& a, unsigned long long* count, hipSt
 hipError_t launch_column_count(const ColumnLaunch& a, unsigned long long* count, hipStream_t s) {
     if (a.tasks == 0) return hipSuccess;
     column_count_kernel<<<dim3((a.tasks + 3) / 4), dim3(256), 0, s>>>(a, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const* sino, float* ysc,
+                               hipStream_t s) {
+    if (a.nviews == 0) return hipSuccess;
+    Ptrs4 y{};
+    for (int m = 0; m < nb; ++m) y.p[m] = sino[m];
+    for (int32_t v0 = 0; v0 < a.nviews; v0 += 65535) {
+        ColumnLaunch b = a;
+        b.view0 = a.view0 + v0;
+        b.nviews = a.nviews - v0 < 65535 ? a.nviews - v0 : 65535;
+        const dim3 grid((a.cols + 31) / 32, (a.rows + 31) / 32, b.nviews);
+        switch (nb) {
+            case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, ysc); break;
+            case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, ysc); break;
+            case 4: sino_prepass_kernel<4><<<grid, dim3(256), 0, s>>>(b, y, ysc); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
+}
+
+int32_t gather_zchunk(int32_t D, int nb) {
+    const int32_t cap = 2048 / nb;           // floats of LDS per wave: at most 8 KiB
+    return D < cap ? D : cap;
+}
+
+hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol,
+                                int accumulate, hipStream_t s) {
+    const int32_t D = a.box.n[2];
+    const int32_t zchunk = gather_zchunk(D, nb);
+    const int32_t nchunks = (D + zchunk - 1) / zchunk;
+    const uint64_t tasks = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)nchunks;
+    if (tasks == 0) return hipSuccess;
+    const dim3 grid((unsigned)((tasks + 3) / 4));
+    const size_t lds = (size_t)4 * zchunk * nb * sizeof(float);
+    switch (nb) {
+        case 1: column_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, accumulate); break;
+        case 2: column_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, accumulate); break;
+        case 4: column_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, accumulate); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

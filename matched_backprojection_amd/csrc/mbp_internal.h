@@ -49,6 +49,16 @@ hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol
 hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* const* sino,
                                  float* vol, hipStream_t s);
 
+// Matched adjoint of the column geometry without global atomics: a pre-pass copies the
+// sinogram to [view][col][row] order (nb members interleaved innermost) scaled by each ray's
+// length per unit of its parameter; the gather then writes every voxel of the z-fastest
+// interleaved volume once (optionally adding into it). ysc holds nb * views * rows * cols
+// floats; the launch covers views [view0, view0 + nviews).
+hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const* sino, float* ysc,
+                               hipStream_t s);
+hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol,
+                                int accumulate, hipStream_t s);
+
 // Positive-length segments walked by the launch's rays; adds into *count (device, zeroed by
 // the caller).
 hipError_t launch_count(const GenericLaunch& a, unsigned long long* count, hipStream_t s);

@@ -78,6 +78,7 @@ struct mbp_plan {
     std::vector<Frame> frames;
     bool column_capable = false;
     int32_t forced_path = MBP_PATH_AUTO;
+    int32_t adjoint_kind = MBP_ADJOINT_AUTO;
     int64_t view_batch = 0;           // 0: automatic
     void* user_ws = nullptr;
     size_t user_ws_bytes = 0;
@@ -281,6 +282,22 @@ float* get_workspace(mbp_plan* p, DeviceState* d, size_t need, bool* fits, int* 
     if (e != hipSuccess) { *rc = hip_fail(e, "hipMalloc(workspace)"); return nullptr; }
     d->ws_bytes = need;
     return d->ws;
+}
+
+// Adjoint kernel of the column walk: the atomic-free gather unless the scatter is forced.
+int32_t adjoint_kind(const mbp_plan* p) {
+    return p->adjoint_kind == MBP_ADJOINT_SCATTER ? MBP_ADJOINT_SCATTER : MBP_ADJOINT_GATHER;
+}
+
+// Workspace of one column-walk pass over nb members: the interleaved z-fastest volume (not
+// needed when the caller's own z-fastest buffer is used directly) and, for the gather
+// adjoint, the reordered sinogram.
+size_t column_ws_bytes(const mbp_plan* p, int nb, bool direct, bool gather) {
+    const mbp_geometry& g = p->g;
+    size_t n = 0;
+    if (!direct) n += (size_t)nb * (size_t)(g.D * g.H * g.W);
+    if (gather) n += (size_t)nb * (size_t)(g.views * g.rows * g.cols);
+    return n * sizeof(float);
 }
 
 int check_call(const mbp_plan* p, const void* a, const void* b, int64_t batch) {
@@ -498,9 +515,17 @@ int mbp_workspace_size(const mbp_plan* plan, int64_t batch, size_t* bytes) {
     if (batch < 0) return fail(MBP_EINVAL, "batch must be >= 0");
     *bytes = 0;
     if (batch == 0 || active_path(plan) != MBP_PATH_COLUMN) return MBP_OK;
-    if (plan->g.layout == MBP_LAYOUT_WHD && batch == 1) return MBP_OK;
-    const int nb = interleave_for(plan, batch);
-    *bytes = (size_t)nb * (size_t)(plan->g.D * plan->g.H * plan->g.W) * sizeof(float);
+    const bool direct = plan->g.layout == MBP_LAYOUT_WHD && batch == 1;
+    const int nb = direct ? 1 : interleave_for(plan, batch);
+    *bytes = column_ws_bytes(plan, nb, direct, adjoint_kind(plan) == MBP_ADJOINT_GATHER);
+    return MBP_OK;
+}
+
+int mbp_plan_set_adjoint(mbp_plan* plan, int32_t kind) {
+    if (!plan) return fail(MBP_EINVAL, "plan is NULL");
+    if (kind != MBP_ADJOINT_AUTO && kind != MBP_ADJOINT_GATHER && kind != MBP_ADJOINT_SCATTER)
+        return fail(MBP_EINVAL, "unknown adjoint kernel %d", kind);
+    plan->adjoint_kind = kind;
     return MBP_OK;
 }
 
@@ -537,7 +562,7 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
             bool fits = false;
             float* ws = nullptr;
             for (;;) {
-                ws = get_workspace(plan, d, (size_t)nb * (size_t)vox * sizeof(float), &fits, &rc);
+                ws = get_workspace(plan, d, column_ws_bytes(plan, nb, false, false), &fits, &rc);
                 if (rc != MBP_OK) return rc;
                 if (fits || nb == 1) break;
                 nb /= 2;
@@ -576,37 +601,51 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
     int64_t m0 = 0;
     if (active_path(plan) == MBP_PATH_COLUMN) {
         const bool whd = g.layout == MBP_LAYOUT_WHD;
+        const bool direct = whd && batch == 1;
+        bool gather = adjoint_kind(plan) == MBP_ADJOINT_GATHER;
         while (m0 < batch) {
-            if (whd && batch == 1) {
-                if (!accumulate) {
-                    hipError_t e = mbp::launch_fill_zero(volume, vox, s);
-                    if (e != hipSuccess) return hip_fail(e, "zero fill launch");
-                }
-                const float* si[4] = {sinogram, nullptr, nullptr, nullptr};
-                rc = run_column(plan, d, true, nullptr, volume, si, nullptr, 1, s);
-                if (rc != MBP_OK) return rc;
-                m0 = 1;
-                break;
-            }
-            int nb = interleave_for(plan, batch - m0);
+            int nb = direct ? 1 : interleave_for(plan, batch - m0);
             bool fits = false;
             float* ws = nullptr;
             for (;;) {
-                ws = get_workspace(plan, d, (size_t)nb * (size_t)vox * sizeof(float), &fits, &rc);
+                ws = get_workspace(plan, d, column_ws_bytes(plan, nb, direct, gather), &fits, &rc);
                 if (rc != MBP_OK) return rc;
-                if (fits || nb == 1) break;
-                nb /= 2;
+                if (fits) break;
+                if (nb > 1) { nb /= 2; continue; }
+                if (gather) { gather = false; continue; }   // no room for the sinogram copy
+                break;
             }
-            if (!fits) break;
-            hipError_t e = mbp::launch_fill_zero(ws, (int64_t)nb * vox, s);
-            if (e != hipSuccess) return hip_fail(e, "zero fill launch");
+            if (!fits) break;   // not even the volume copy fits: generic walk for the rest
+            float* target = direct ? volume : ws;
+            float* ysc = direct ? ws : ws + (size_t)nb * (size_t)vox;
+            const int acc_target = direct ? accumulate : 0;
+            hipError_t e;
+            if (!gather && !acc_target) {
+                e = mbp::launch_fill_zero(target, (int64_t)nb * vox, s);
+                if (e != hipSuccess) return hip_fail(e, "zero fill launch");
+            }
             const float* si[4] = {nullptr, nullptr, nullptr, nullptr};
             for (int m = 0; m < nb; ++m) si[m] = sinogram + (m0 + m) * rays;
-            rc = run_column(plan, d, true, nullptr, ws, si, nullptr, nb, s);
-            if (rc != MBP_OK) return rc;
-            e = mbp::launch_from_native(ws, nb, (int32_t)g.D, (int32_t)g.H, (int32_t)g.W, whd ? 1 : 0,
-                                        volume + m0 * vox, vox, accumulate, s);
-            if (e != hipSuccess) return hip_fail(e, "layout conversion launch");
+            if (gather) {
+                mbp::ColumnLaunch a = column_args(plan, d);
+                const int64_t vb = views_per_launch(plan);
+                for (int64_t v0 = 0; v0 < g.views; v0 += vb) {
+                    a.view0 = (int32_t)v0;
+                    a.nviews = (int32_t)std::min(vb, g.views - v0);
+                    e = mbp::launch_sino_prepass(a, nb, si, ysc, s);
+                    if (e != hipSuccess) return hip_fail(e, "sinogram pre-pass launch");
+                    e = mbp::launch_column_gather(a, nb, ysc, target, v0 == 0 ? acc_target : 1, s);
+                    if (e != hipSuccess) return hip_fail(e, "column gather launch");
+                }
+            } else {
+                rc = run_column(plan, d, true, nullptr, target, si, nullptr, nb, s);
+                if (rc != MBP_OK) return rc;
+            }
+            if (!direct) {
+                e = mbp::launch_from_native(ws, nb, (int32_t)g.D, (int32_t)g.H, (int32_t)g.W, whd ? 1 : 0,
+                                            volume + m0 * vox, vox, accumulate, s);
+                if (e != hipSuccess) return hip_fail(e, "layout conversion launch");
+            }
             m0 += nb;
         }
     }

@@ -5,12 +5,15 @@
 // sum over voxels of (physical length inside the voxel) x (voxel value); the backprojector is
 // its exact transpose and so walks exactly the same segments.
 //
-// Precision scheme (diffct pages, "diffct 2.2.1 -> 2.3.0", CHANGELOG 2.3.0, "Added": rays are
-// clipped and their entries located in FP64, and the FP32 traversal measures distances from
-// each entry): everything up to the entry point, the entry cell and the per-axis crossing
-// counts is fp64; the walk itself is fp32, with every crossing distance taken as
-// first + k * step by one fma from fp64-rounded constants (never a running sum), measured
-// from the fp64 entry point, so distant endpoints keep voxel-sized resolution.
+// Precision scheme. The diffct pages ("diffct 2.2.1 -> 2.3.0", CHANGELOG 2.3.0, "Added") clip
+// rays and locate their entries in FP64 and let an FP32 walk measure distances from each
+// entry. Here the entry point, entry cell and per-axis crossing counts are fp64 as there, and
+// every crossing distance is first + k * step (one fma from the fp64 constants, never a
+// running sum) measured from the fp64 entry point; the distances themselves are also kept in
+// fp64, because an fp32 distance carries an absolute error of about ulp(box chord), which is
+// large against the short chords of grazing rays (it broke the 1e-4 per-ray bound). On
+// gfx950 an fp64 fma issues at the same rate as an unpacked fp32 one, so this costs
+// registers, not throughput. Voxel values, sinogram values and sums stay fp32.
 //
 // Two walks share the per-axis setup:
 //  * the generic walk, one ray at a time, in 3-D (2-D beams run with a single z cell);
@@ -63,8 +66,9 @@ struct AxisWalk {
     int32_t c0;
     int32_t step;
     int32_t steps;
-    float t_first;
-    float t_step;
+    int32_t pad_;
+    double t_first;
+    double t_step;
 };
 
 MBP_HD MBP_INLINE int32_t clamp_cell(double s, int32_t n) {
@@ -92,12 +96,12 @@ MBP_HD MBP_INLINE int32_t cell_before(double s, double w, int32_t n) {
 // Walk of one axis from world coordinate `e` (the entry point) to `x` (the exit point);
 // `w` is the world displacement along this axis per unit of walk distance; `t0` is the walk
 // distance of `e` (added to every crossing distance).
-// Crossing constants are kept finite (|value| <= 1e28, so first + k * step with k < 2^31
+// Crossing constants are kept finite (|value| <= 1e280, so first + k * step with k < 2^31
 // cannot overflow): an axis with crossings left then always has a finite next distance and is
 // chosen before any exhausted axis (whose next distance is +inf). That is what keeps every
 // visited cell between the clamped entry and exit cells, whatever the rounding.
-MBP_HD MBP_INLINE float finite_distance(double t) {
-    return (float)(t > 1e28 ? 1e28 : (t < -1e28 ? -1e28 : t));
+MBP_HD MBP_INLINE double finite_distance(double t) {
+    return t > 1e280 ? 1e280 : (t < -1e280 ? -1e280 : t);
 }
 
 MBP_HD MBP_INLINE AxisWalk axis_walk(double e, double x, double w, double t0, double lo,
@@ -124,8 +128,9 @@ MBP_HD MBP_INLINE AxisWalk axis_walk(double e, double x, double w, double t0, do
         a.step = 0;
         a.steps = 0;
         a.t_first = INFINITY;
-        a.t_step = 0.0f;
+        a.t_step = 0.0;
     }
+    a.pad_ = 0;
     return a;
 }
 
@@ -162,7 +167,7 @@ MBP_HD MBP_INLINE double centred(int32_t i, int32_t n, double pitch) {
 
 struct RayWalk {
     AxisWalk ax[3];
-    float T;        // physical length inside the box
+    double T;       // physical length inside the box
     int32_t hit;
 };
 
@@ -181,9 +186,10 @@ MBP_HD MBP_INLINE void ray_setup(const Frame& F, const Box& B, int beam, double 
     }
     r.hit = clip_slab(a, d, B.lo, B.hi, 3, t0, t1) ? 1 : 0;
     if (!r.hit) {
-        r.T = 0.0f;
+        r.T = 0.0;
         for (int k = 0; k < 3; ++k) { r.ax[k].c0 = 0; r.ax[k].step = 0; r.ax[k].steps = 0;
-                                      r.ax[k].t_first = INFINITY; r.ax[k].t_step = 0.0f; }
+                                      r.ax[k].pad_ = 0; r.ax[k].t_first = INFINITY;
+                                      r.ax[k].t_step = 0.0; }
         return;
     }
     const double dn = sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
@@ -192,7 +198,7 @@ MBP_HD MBP_INLINE void ray_setup(const Frame& F, const Box& B, int beam, double 
         const double x = a[k] + t1 * d[k];
         r.ax[k] = axis_walk(e, x, d[k] / dn, 0.0, B.lo[k], B.pitch[k], B.n[k]);
     }
-    r.T = (float)((t1 - t0) * dn);
+    r.T = (t1 - t0) * dn;
 }
 
 // Visit the segments of a generic walk. `visit(cx, cy, cz, length)` once per segment, in
@@ -202,29 +208,29 @@ MBP_HD MBP_INLINE void walk_ray(const RayWalk& r, Visit& visit) {
     if (!r.hit) return;
     int32_t cx = r.ax[0].c0, cy = r.ax[1].c0, cz = r.ax[2].c0;
     int32_t kx = 0, ky = 0, kz = 0;
-    float nx = r.ax[0].steps > 0 ? r.ax[0].t_first : INFINITY;
-    float ny = r.ax[1].steps > 0 ? r.ax[1].t_first : INFINITY;
-    float nz = r.ax[2].steps > 0 ? r.ax[2].t_first : INFINITY;
+    double nx = r.ax[0].steps > 0 ? r.ax[0].t_first : INFINITY;
+    double ny = r.ax[1].steps > 0 ? r.ax[1].t_first : INFINITY;
+    double nz = r.ax[2].steps > 0 ? r.ax[2].t_first : INFINITY;
     const int32_t total = r.ax[0].steps + r.ax[1].steps + r.ax[2].steps;
-    float t = 0.0f;
+    double t = 0.0;
     for (int32_t m = 0; m < total; ++m) {
         const bool bx = nx <= ny && nx <= nz;
         const bool by = !bx && ny <= nz;
-        const float tb = bx ? nx : (by ? ny : nz);
-        visit(cx, cy, cz, fmaxf(tb - t, 0.0f));
-        t = fmaxf(t, tb);
+        const double tb = bx ? nx : (by ? ny : nz);
+        visit(cx, cy, cz, (float)fmax(tb - t, 0.0));
+        t = fmax(t, tb);
         if (bx) {
             cx += r.ax[0].step; ++kx;
-            nx = kx < r.ax[0].steps ? fmaf((float)kx, r.ax[0].t_step, r.ax[0].t_first) : INFINITY;
+            nx = kx < r.ax[0].steps ? fma((double)kx, r.ax[0].t_step, r.ax[0].t_first) : INFINITY;
         } else if (by) {
             cy += r.ax[1].step; ++ky;
-            ny = ky < r.ax[1].steps ? fmaf((float)ky, r.ax[1].t_step, r.ax[1].t_first) : INFINITY;
+            ny = ky < r.ax[1].steps ? fma((double)ky, r.ax[1].t_step, r.ax[1].t_first) : INFINITY;
         } else {
             cz += r.ax[2].step; ++kz;
-            nz = kz < r.ax[2].steps ? fmaf((float)kz, r.ax[2].t_step, r.ax[2].t_first) : INFINITY;
+            nz = kz < r.ax[2].steps ? fma((double)kz, r.ax[2].t_step, r.ax[2].t_first) : INFINITY;
         }
     }
-    visit(cx, cy, cz, fmaxf(r.T - t, 0.0f));
+    visit(cx, cy, cz, (float)fmax(r.T - t, 0.0));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -237,9 +243,8 @@ MBP_HD MBP_INLINE void walk_ray(const RayWalk& r, Visit& visit) {
 
 struct ColumnWalk {                  // shared by all rows of a column
     AxisWalk x, y;
-    float T;                         // xy length inside the box's xy rectangle
+    double T;                        // xy length inside the box's xy rectangle
     int32_t hit;
-    double Txy;                      // the same length in fp64
     // kept for the row setup (fp64)
     double t_in;                     // ray parameter of the xy entry
     double dxy;                      // |d_xy|
@@ -250,7 +255,7 @@ struct ColumnWalk {                  // shared by all rows of a column
 
 struct RowWalk {                     // one row of the column
     AxisWalk z;
-    float t_lo, t_hi;                // active tau range of this row (empty if t_hi <= t_lo)
+    double t_lo, t_hi;               // active tau range of this row (empty if t_hi <= t_lo)
     float kappa;
 };
 
@@ -281,32 +286,32 @@ MBP_HD MBP_INLINE void column_setup(const Frame& F, const Box& B, int beam, doub
     c.hit = (c.dxy > 0.0 && clip_slab(a, d, B.lo, B.hi, 2, t0, t1)) ? 1 : 0;
     c.t_in = t0;
     if (!c.hit) {
-        c.T = 0.0f;
-        c.Txy = 0.0;
+        c.T = 0.0;
         c.x.c0 = c.y.c0 = 0; c.x.step = c.y.step = 0; c.x.steps = c.y.steps = 0;
-        c.x.t_first = c.y.t_first = INFINITY; c.x.t_step = c.y.t_step = 0.0f;
+        c.x.pad_ = c.y.pad_ = 0;
+        c.x.t_first = c.y.t_first = INFINITY; c.x.t_step = c.y.t_step = 0.0;
         return;
     }
     const double ex = a[0] + t0 * d[0], ey = a[1] + t0 * d[1];
     const double xx = a[0] + t1 * d[0], xy = a[1] + t1 * d[1];
     c.x = axis_walk(ex, xx, d[0] / c.dxy, 0.0, B.lo[0], B.pitch[0], B.n[0]);
     c.y = axis_walk(ey, xy, d[1] / c.dxy, 0.0, B.lo[1], B.pitch[1], B.n[1]);
-    c.Txy = (t1 - t0) * c.dxy;
-    c.T = (float)c.Txy;
+    c.T = (t1 - t0) * c.dxy;
 }
 
 // Row setup: `v` is the row's detector coordinate, `evz` the z component of the row axis.
 MBP_HD MBP_INLINE void row_setup(const ColumnWalk& c, const Box& B, double v, double evz,
                                  RowWalk& r) {
-    r.t_lo = 0.0f; r.t_hi = 0.0f; r.kappa = 0.0f;
-    r.z.c0 = 0; r.z.step = 0; r.z.steps = 0; r.z.t_first = INFINITY; r.z.t_step = 0.0f;
+    r.t_lo = 0.0; r.t_hi = 0.0; r.kappa = 0.0f;
+    r.z.c0 = 0; r.z.step = 0; r.z.steps = 0; r.z.pad_ = 0; r.z.t_first = INFINITY;
+    r.z.t_step = 0.0;
     if (!c.hit) return;
     const double dz = c.line ? c.dz_col : c.dz_col + v * evz;   // z change per unit parameter
     const double z0 = c.line ? c.sz + v * evz : c.sz;           // z at parameter 0
     const double wz = dz / c.dxy;                                // z change per unit tau
     const double z_in = z0 + c.t_in * dz;                        // z at tau = 0
     // tau range where lo_z <= z < hi_z, intersected with the column's xy range [0, Txy]
-    double tlo = 0.0, thi = c.Txy;
+    double tlo = 0.0, thi = c.T;
     if (wz != 0.0) {
         const double s1 = (B.lo[2] - z_in) / wz;
         const double s2 = (B.hi[2] - z_in) / wz;
@@ -318,8 +323,8 @@ MBP_HD MBP_INLINE void row_setup(const ColumnWalk& c, const Box& B, double v, do
     }
     if (!(thi > tlo)) return;
     r.z = axis_walk(z_in + tlo * wz, z_in + thi * wz, wz, tlo, B.lo[2], B.pitch[2], B.n[2]);
-    r.t_lo = (float)tlo;
-    r.t_hi = (float)thi;
+    r.t_lo = tlo;
+    r.t_hi = thi;
     r.kappa = (float)(sqrt(c.dxy * c.dxy + dz * dz) / c.dxy);
 }
 
@@ -331,36 +336,158 @@ MBP_HD MBP_INLINE void walk_column_row(const ColumnWalk& c, const RowWalk& r, Vi
     if (!c.hit) return;
     int32_t cx = c.x.c0, cy = c.y.c0;
     int32_t kx = 0, ky = 0;
-    float nx = c.x.steps > 0 ? c.x.t_first : INFINITY;
-    float ny = c.y.steps > 0 ? c.y.t_first : INFINITY;
+    double nx = c.x.steps > 0 ? c.x.t_first : INFINITY;
+    double ny = c.y.steps > 0 ? c.y.t_first : INFINITY;
     const int32_t total = c.x.steps + c.y.steps;
     int32_t cz = r.z.c0, kz = 0;
-    float nz = r.z.steps > 0 ? r.z.t_first : INFINITY;
-    float ta = 0.0f;
+    double nz = r.z.steps > 0 ? r.z.t_first : INFINITY;
+    double ta = 0.0;
     for (int32_t m = 0; m <= total; ++m) {
         const bool last = m == total;
         const bool bx = !last && nx <= ny;
-        const float tb = last ? c.T : (bx ? nx : ny);
-        float lo = fmaxf(ta, r.t_lo);
-        const float hi = fminf(tb, r.t_hi);
+        const double tb = last ? c.T : (bx ? nx : ny);
+        double lo = fmax(ta, r.t_lo);
+        const double hi = fmin(tb, r.t_hi);
         if (lo < hi) {
             while (nz < hi) {
-                visit(cx, cy, cz, fmaxf(nz - lo, 0.0f));
-                lo = fmaxf(lo, nz);
+                visit(cx, cy, cz, (float)fmax(nz - lo, 0.0));
+                lo = fmax(lo, nz);
                 cz += r.z.step; ++kz;
-                nz = kz < r.z.steps ? fmaf((float)kz, r.z.t_step, r.z.t_first) : INFINITY;
+                nz = kz < r.z.steps ? fma((double)kz, r.z.t_step, r.z.t_first) : INFINITY;
             }
-            visit(cx, cy, cz, hi - lo);
+            visit(cx, cy, cz, (float)(hi - lo));
         }
-        ta = fmaxf(ta, tb);
+        ta = fmax(ta, tb);
         if (last) break;
         if (bx) {
             cx += c.x.step; ++kx;
-            nx = kx < c.x.steps ? fmaf((float)kx, c.x.t_step, c.x.t_first) : INFINITY;
+            nx = kx < c.x.steps ? fma((double)kx, c.x.t_step, c.x.t_first) : INFINITY;
         } else {
             cy += c.y.step; ++ky;
-            ny = ky < c.y.steps ? fmaf((float)ky, c.y.t_step, c.y.t_first) : INFINITY;
+            ny = ky < c.y.steps ? fma((double)ky, c.y.t_step, c.y.t_first) : INFINITY;
         }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Cell gather (matched adjoint of the column geometry, voxel side).
+//
+// For one xy cell and one view: the detector columns whose xy line crosses the cell, each
+// with the ray-parameter interval [t0, t1] of the crossing (common to all rows of the
+// column); then, for one row, the pieces of that crossing inside each z cell. A piece is
+// returned as its share of (t1 - t0); times the ray's length per unit parameter it is the
+// chord of the ray through the voxel.
+
+struct CellCrossing {
+    int32_t j;          // detector column
+    int32_t line;       // 1: parallel line, 0: segment from the source
+    double t0, t1;      // ray-parameter interval inside the xy cell
+    double zs, dz0;     // z(t) of row k: line: zs + v_k evz + t dz0; segment: zs + t (dz0 + v_k evz)
+};
+
+MBP_HD MBP_INLINE double cross2d(double ax, double ay, double bx, double by) {
+    return ax * by - ay * bx;
+}
+
+// Column range [j0, j1] whose xy line can cross the cell [x0,x1) x [y0,y1) in view F;
+// returns false when none can.
+MBP_HD MBP_INLINE bool cell_column_range(const Frame& F, int beam, int32_t cols, double du,
+                                         double x0, double x1, double y0, double y1,
+                                         int32_t& j0, int32_t& j1) {
+    double umin = INFINITY, umax = -INFINITY, sign = 0.0;
+    bool bounded = true;
+    for (int c = 0; c < 4; ++c) {
+        const double qx = (c & 1) ? x1 : x0, qy = (c & 2) ? y1 : y0;
+        double num, den;
+        if (beam == BEAM_PARALLEL) {    // q + l r = det + u e: u = cross(q - det, r) / cross(e, r)
+            num = cross2d(qx - F.c[0], qy - F.c[1], F.s[0], F.s[1]);
+            den = cross2d(F.u[0], F.u[1], F.s[0], F.s[1]);
+        } else {                        // s + l (q - s) = det + u e: u = cross(det - s, a) / cross(a, e)
+            const double ax = qx - F.s[0], ay = qy - F.s[1];
+            num = cross2d(F.c[0] - F.s[0], F.c[1] - F.s[1], ax, ay);
+            den = cross2d(ax, ay, F.u[0], F.u[1]);
+        }
+        if (den == 0.0 || (c > 0 && (den > 0.0) != (sign > 0.0))) bounded = false;
+        sign = den;
+        const double u = num / den;
+        umin = fmin(umin, u);
+        umax = fmax(umax, u);
+    }
+    j0 = 0;
+    j1 = cols - 1;
+    if (!bounded) return true;
+    const double coff = 0.5 * (double)(cols - 1);
+    const double f0 = ceil(umin / du + coff - 1e-7), f1 = floor(umax / du + coff + 1e-7);
+    if (!(f1 >= 0.0) || !(f0 <= (double)(cols - 1))) return false;
+    j0 = f0 < 0.0 ? 0 : (int32_t)f0;
+    j1 = f1 > (double)(cols - 1) ? cols - 1 : (int32_t)f1;
+    return j0 <= j1;
+}
+
+// The crossing of column j's xy line with the cell; false when it has no positive length.
+MBP_HD MBP_INLINE bool cell_crossing(const Frame& F, int beam, int32_t j, int32_t cols, double du,
+                                     double x0, double x1, double y0, double y1, CellCrossing& x) {
+    const double u = centred(j, cols, du);
+    const double pxj = F.c[0] + u * F.u[0], pyj = F.c[1] + u * F.u[1], pzj = F.c[2] + u * F.u[2];
+    double a[2], d[2];
+    double t0, t1;
+    if (beam == BEAM_PARALLEL) {
+        a[0] = pxj; a[1] = pyj; d[0] = F.s[0]; d[1] = F.s[1];
+        t0 = -INFINITY; t1 = INFINITY;
+        x.line = 1; x.zs = pzj; x.dz0 = F.s[2];
+    } else {
+        a[0] = F.s[0]; a[1] = F.s[1]; d[0] = pxj - F.s[0]; d[1] = pyj - F.s[1];
+        t0 = 0.0; t1 = 1.0;
+        x.line = 0; x.zs = F.s[2]; x.dz0 = pzj - F.s[2];
+    }
+    const double lo[2] = {x0, y0}, hi[2] = {x1, y1};
+    if (!clip_slab(a, d, lo, hi, 2, t0, t1)) return false;
+    x.j = j;
+    x.t0 = t0;
+    x.t1 = t1;
+    return true;
+}
+
+// Pieces of row k (detector coordinate vk_evz = v_k * evz) inside the z cells [z0, z1) of
+// the box: piece(iz, share) with share = the part of (t1 - t0) spent in z cell iz.
+template <class Piece>
+MBP_HD MBP_INLINE void row_pieces(const CellCrossing& x, double vk_evz, const Box& B, int32_t z0,
+                                  int32_t z1, Piece& piece) {
+    double za, zb;
+    if (x.line) {
+        const double zk = x.zs + vk_evz;
+        za = zk + x.t0 * x.dz0;
+        zb = zk + x.t1 * x.dz0;
+    } else {
+        const double dzk = x.dz0 + vk_evz;
+        za = x.zs + x.t0 * dzk;
+        zb = x.zs + x.t1 * dzk;
+    }
+    const double pz = B.pitch[2];
+    const double zlo = B.lo[2] + z0 * pz, zhi = B.lo[2] + z1 * pz;
+    const double zmin = fmin(za, zb), zmax = fmax(za, zb);
+    if (zmax < zlo || zmin >= zhi) return;
+    const double dt = x.t1 - x.t0;
+    const double ext = zmax - zmin;
+    const double inv = 1.0 / pz;
+    int32_t ia = (int32_t)floor((fmax(zmin, zlo) - B.lo[2]) * inv);
+    int32_t ib = (int32_t)floor((fmin(zmax, zhi) - B.lo[2]) * inv);
+    ia = ia < z0 ? z0 : (ia > z1 - 1 ? z1 - 1 : ia);
+    ib = ib < z0 ? z0 : (ib > z1 - 1 ? z1 - 1 : ib);
+    if (ext == 0.0) {                       // in a z plane: the half-open cell containing it
+        if (zmin >= zlo && zmin < zhi) piece(ia, dt);
+        return;
+    }
+    if (ia == ib) {
+        const double ov = fmin(zmax, zhi) - fmax(zmin, zlo);
+        if (ov > 0.0) piece(ia, ov >= ext ? dt : dt * (ov / ext));
+        return;
+    }
+    const double scale = dt / ext;
+    for (int32_t iz = ia; iz <= ib; ++iz) {
+        const double c0 = B.lo[2] + iz * pz, c1 = c0 + pz;
+        const double ov = fmin(zmax, c1) - fmax(zmin, c0);
+        if (ov > 0.0) piece(iz, ov * scale);
     }
 }
 

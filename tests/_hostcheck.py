@@ -32,6 +32,7 @@ def _load():
         lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P]
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
+        lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
         lib.mbph_check_rays.restype = I64
         _lib = lib
     return _lib
@@ -125,3 +126,18 @@ def check_rays(path: str, geom: dict, traj: dict, ray_ids) -> tuple:
                                  int(geom["cols"]), float(geom.get("du", 1.0)),
                                  float(geom.get("dv", 1.0)), _ptr(ids), ids.size, ctypes.byref(viol))
     return int(visits), int(viol.value)
+
+
+def gather(geom: dict, traj: dict, sino: np.ndarray):
+    """Replay the cell-gather adjoint (fp64 accumulation) on a (views, rows, cols) sinogram."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    rows = int(geom.get("rows", 1))
+    views, cols = int(geom["views"]), int(geom["cols"])
+    s = np.ascontiguousarray(sino, dtype=np.float32).reshape(views, rows, cols)
+    vol = np.zeros(int(n[0]) * int(n[1]) * int(n[2]), dtype=np.float64)
+    viol = ctypes.c_longlong(0)
+    lib.mbph_gather(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n), views, rows, cols,
+                    float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)), _ptr(s), _ptr(vol),
+                    ctypes.byref(viol))
+    return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value)

@@ -81,10 +81,12 @@ def test_configs_plan_and_pick_walks(lib, name):
     assert inf.views_per_launch == cfg.views and inf.launches == 1
     ws = ctypes.c_size_t()
     assert lib.mbp_workspace_size(h, cfg.members, ctypes.byref(ws)) == 0
-    if cfg.beam != "cone" or (cfg.layout == "WHD" and cfg.members == 1):
+    if cfg.beam != "cone":
         assert ws.value == 0
-    else:
-        assert ws.value == min(4, cfg.members) * cfg.n_voxels * 4
+    else:   # z-fastest volume copy (unless used in place) + reordered sinogram for the gather
+        nb = min(4, cfg.members)
+        direct = cfg.layout == "WHD" and cfg.members == 1
+        assert ws.value == 4 * nb * ((0 if direct else cfg.n_voxels) + cfg.n_rays)
     # view batching: a ragged split into launches of 7 views
     assert lib.mbp_plan_set_view_batch(h, 7) == 0
     inf = _info(lib, h)
@@ -205,8 +207,12 @@ def test_python_plan_maps_errors_and_shapes():
     plan = mbp.Plan("cone", cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols), (cfg.dv, cfg.du),
                     layout="WHD")
     assert plan.sino_shape == (cfg.views, cfg.rows, cfg.cols)
-    assert plan.info["path"] == "column" and plan.workspace_size(1) == 0
-    assert plan.workspace_size(3) == 2 * cfg.n_voxels * 4
+    assert plan.info["path"] == "column"
+    assert plan.workspace_size(1) == 4 * cfg.n_rays
+    assert plan.workspace_size(3) == 2 * (cfg.n_voxels + cfg.n_rays) * 4
+    plan.set_adjoint("scatter")
+    assert plan.workspace_size(1) == 0 and plan.workspace_size(3) == 2 * cfg.n_voxels * 4
+    plan.set_adjoint("auto")
     bad = dict(traj)
     bad["src"] = traj["src"].copy()
     bad["src"][0, 0] = np.nan

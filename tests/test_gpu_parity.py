@@ -184,7 +184,7 @@ def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
     # a caller-owned workspace gives the same result; a too-small one is refused
     plan = make_plan(mbp, cfg)
     need = plan.workspace_size(5)
-    assert need == 4 * cfg.n_voxels * 4
+    assert need == 4 * (cfg.n_voxels + cfg.n_rays) * 4
     ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
     plan.set_workspace(ws)
     p = plan.project(torch.from_numpy(xs).to(dev)).cpu().numpy().astype(np.float64)
