@@ -7,6 +7,7 @@
 // traversal code with the HIP kernels, so agreement here is a logic check, not parity.
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -140,7 +141,7 @@ int mbph_backproject(int path, const double* frames, int beam, const double* lo,
 }
 
 // Adjoint by the cell gather (voxel side), accumulated in fp64: every xy cell, every view,
-// every crossing column and every row, exactly as the gather kernel enumerates them.
+// every candidate column and every row, exactly as the gather kernel enumerates them.
 int mbph_gather(const double* frames, int beam, const double* lo, const double* pitch,
                 const int32_t* n, int views, int rows, int cols, double du, double dv,
                 const float* sino, double* vol, long long* violations) {
@@ -148,7 +149,10 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
     frames_from(frames, views, F);
     const Box B = box_from(lo, pitch, n);
     *violations = 0;
-    const double roff = 0.5 * (double)(rows - 1);
+    std::vector<ColLine> lines((size_t)views * cols);
+    for (int v = 0; v < views; ++v)
+        for (int j = 0; j < cols; ++j) column_line(F[v], B, beam, j, cols, rows, du, dv, lines[(size_t)v * cols + j]);
+    const bool line = beam == BEAM_PARALLEL;
     for (int ix = 0; ix < n[0]; ++ix) {
         for (int iy = 0; iy < n[1]; ++iy) {
             const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
@@ -158,11 +162,15 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                 if (!cell_column_range(F[v], beam, cols, du, x0, x1, y0, y1, j0, j1)) continue;
                 if (j0 < 0 || j1 >= cols) ++*violations;
                 for (int32_t j = j0; j <= j1; ++j) {
-                    CellCrossing x;
-                    if (!cell_crossing(F[v], beam, j, cols, du, x0, x1, y0, y1, x)) continue;
+                    const ColLine& L = lines[(size_t)v * cols + j];
+                    double t0, t1;
+                    if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) continue;
+                    const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
+                    const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
+                    const double dt = t1 - t0;
                     for (int k = 0; k < rows; ++k) {
                         double len;
-                        if (beam == BEAM_PARALLEL) {
+                        if (line) {
                             len = std::sqrt(F[v].s[0] * F[v].s[0] + F[v].s[1] * F[v].s[1] + F[v].s[2] * F[v].s[2]);
                         } else {
                             double p[3];
@@ -175,13 +183,89 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                             if (iz < 0 || iz >= n[2] || !(share >= 0.0)) { ++*violations; return; }
                             vol[((int64_t)iz * n[1] + iy) * n[0] + ix] += share * w;
                         };
-                        row_pieces(x, ((double)k - roff) * F[v].v[2] * dv, B, 0, n[2], piece);
+                        const double za = std::fma((double)k, za1, za0);
+                        const double zb = std::fma((double)k, zb1, zb0);
+                        const double fa = std::floor(std::fmin(za, zb)), fb = std::floor(std::fmax(za, zb));
+                        if (fa == fb && fa >= 0.0 && fa < (double)n[2]) piece((int32_t)fa, dt);
+                        else row_pieces_split(za, zb, dt, 0, n[2], false, piece);
                     }
                 }
             }
         }
     }
     return 0;
+}
+
+// Emulates the gather's instruction grouping and checks its race-freedom claim: for every
+// column crossing that the kernel treats as exclusive, every chunk of 64 lanes (rows S
+// apart) and every step (the single-piece add, then step i of the aligned piece walk), the
+// z cells the active lanes add into must be distinct. Returns the number of exclusive
+// crossings checked; *conflicts counts steps with a repeated cell. aligned = 0 replays the
+// walk that starts at the first in-range cell instead (rows entering from below the box
+// then meet in its bottom cell), which the tests use to show the check can fail.
+int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, const double* pitch,
+                              const int32_t* n, int views, int rows, int cols, double du, double dv,
+                              int aligned, long long* conflicts) {
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *conflicts = 0;
+    const bool line = beam == BEAM_PARALLEL;
+    const int32_t S = gather_stride(rows);
+    int64_t checked = 0;
+    std::vector<int32_t> first(64), seen;
+    for (int ix = 0; ix < n[0]; ++ix) {
+        for (int iy = 0; iy < n[1]; ++iy) {
+            const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
+            const double y0 = B.lo[1] + iy * B.pitch[1], y1 = y0 + B.pitch[1];
+            for (int v = 0; v < views; ++v) {
+                int32_t j0, j1;
+                if (!cell_column_range(F[v], beam, cols, du, x0, x1, y0, y1, j0, j1)) continue;
+                for (int32_t j = j0; j <= j1; ++j) {
+                    ColLine L;
+                    column_line(F[v], B, beam, j, cols, rows, du, dv, L);
+                    double t0, t1;
+                    if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) continue;
+                    const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
+                    const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
+                    if (!gather_exclusive(S, rows, za0, za1, zb0, zb1)) continue;
+                    ++checked;
+                    for (int32_t g0 = 0; g0 < rows; g0 += 64 * S) {
+                        for (int32_t c = 0; c < S; ++c) {
+                            // step "single piece" and steps of the aligned walk
+                            std::vector<std::vector<int32_t>> steps(1);
+                            for (int lane = 0; lane < 64; ++lane) {
+                                const int32_t k = g0 + c + S * lane;
+                                if (k >= rows) continue;
+                                const double za = std::fma((double)k, za1, za0);
+                                const double zb = std::fma((double)k, zb1, zb0);
+                                const double fa = std::floor(std::fmin(za, zb)), fb = std::floor(std::fmax(za, zb));
+                                if (fa == fb && fa >= 0.0 && fa < (double)n[2]) {
+                                    steps[0].push_back((int32_t)fa);
+                                    continue;
+                                }
+                                // step index of each piece: its position in this row's walk
+                                const int32_t start = aligned ? (int32_t)std::floor(std::fmin(za, zb))
+                                                              : (int32_t)std::floor(std::fmax(std::fmin(za, zb), 0.0));
+                                auto piece = [&](int32_t iz, double) {
+                                    const int step = iz - start + 1;
+                                    if ((int)steps.size() <= step) steps.resize(step + 1);
+                                    steps[step].push_back(iz);
+                                };
+                                row_pieces_split(za, zb, t1 - t0, 0, n[2], aligned != 0, piece);
+                            }
+                            for (auto& st : steps) {
+                                seen = st;
+                                std::sort(seen.begin(), seen.end());
+                                if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+    return checked;
 }
 
 // Bounds-only sweep of selected rays (flat ids) with either walk; returns visits.

@@ -334,8 +334,26 @@ __global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A,
     }
 }
 
+__global__ void __launch_bounds__(256) column_line_kernel(const ColumnLaunch A, int32_t views,
+                                                          ColLine* __restrict__ out) {
+    const int64_t n = (int64_t)views * A.cols;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int32_t view = (int32_t)(i / A.cols), j = (int32_t)(i % A.cols);
+        column_line(A.frames[view], A.box, A.beam, j, A.cols, A.rows, A.du, A.dv, out[i]);
+    }
+}
+
+// Rows are taken in groups of S * 64 (S = min(kGroup, ceil(rows / 64)) chunks of 64 lanes):
+// the sinogram values of a whole group are loaded before any is used, so a wave has S loads
+// in flight, and chunk c of a group holds rows c, c + S, c + 2S, ... A lane's neighbours are
+// then S rows away, which on these geometries is more than one z cell, so the 64 LDS
+// additions of one instruction go to different addresses (adjacent rows would share a z cell
+// and serialise).
+constexpr int kGroup = 8;
+
 template <int NB>
 __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A,
+                                                            const ColLine* __restrict__ lines,
                                                             const float* __restrict__ ysc,
                                                             float* __restrict__ vol,
                                                             int32_t zchunk, int32_t nchunks,
@@ -358,35 +376,70 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
     if (live) {
         const double x0 = A.box.lo[0] + ix * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
         const double y0 = A.box.lo[1] + iy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
-        const double roff = 0.5 * (double)(A.rows - 1);
+        const bool line = A.beam == BEAM_PARALLEL;
+        const int32_t S = gather_stride(A.rows);
+        const int32_t group_rows = 64 * S;
         for (int32_t view = A.view0; view < A.view0 + A.nviews; ++view) {
-            const Frame F = A.frames[view];
             int32_t j0, j1;
-            if (!cell_column_range(F, A.beam, A.cols, A.du, x0, x1, y0, y1, j0, j1)) continue;
-            const double evz = F.v[2] * A.dv;
+            if (!cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, j0, j1))
+                continue;
             for (int32_t j = j0; j <= j1; ++j) {
-                CellCrossing x;
-                if (!cell_crossing(F, A.beam, j, A.cols, A.du, x0, x1, y0, y1, x)) continue;
-                const int64_t ybase = ((int64_t)view * A.cols + j) * A.rows;
-                for (int32_t k0 = 0; k0 < A.rows; k0 += 64) {
-                    const int32_t k = k0 + lane;
-                    if (k >= A.rows) continue;
-                    float w[NB];
-                    if constexpr (NB == 1) {
-                        w[0] = ysc[ybase + k];
-                    } else if constexpr (NB == 2) {
-                        const float2 t = *reinterpret_cast<const float2*>(ysc + (ybase + k) * 2);
-                        w[0] = t.x; w[1] = t.y;
-                    } else {
-                        const float4 t = *reinterpret_cast<const float4*>(ysc + (ybase + k) * 4);
-                        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
-                    }
-                    auto piece = [&](int32_t iz, double share) {
-                        const float f = (float)share;
+                const ColLine L = lines[(int64_t)view * A.cols + j];
+                double t0, t1;
+                if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) continue;
+                const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
+                const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
+                const double dt = t1 - t0;
+                const float fdt = (float)dt;
+                const float* yrow = ysc + ((int64_t)view * A.cols + j) * A.rows * NB;
+                // Lanes of one instruction are S rows apart; when gather_exclusive holds they
+                // add into different z cells at every step, and this wave alone owns `col`, so
+                // a plain read-add-write is race free. Otherwise: LDS atomics.
+                const bool exclusive = gather_exclusive(S, A.rows, za0, za1, zb0, zb1);
+                for (int32_t g0 = 0; g0 < A.rows; g0 += group_rows) {
+                    float w[kGroup][NB];
 #pragma unroll
-                        for (int m = 0; m < NB; ++m) atomicAdd(col + (iz - z0) * NB + m, f * w[m]);
-                    };
-                    row_pieces(x, ((double)k - roff) * evz, A.box, z0, z1, piece);
+                    for (int c = 0; c < kGroup; ++c) {
+                        const int32_t k = g0 + c + S * lane;
+                        if (c < S && k < A.rows) {
+                            if constexpr (NB == 1) {
+                                w[c][0] = yrow[k];
+                            } else if constexpr (NB == 2) {
+                                const float2 t = *reinterpret_cast<const float2*>(yrow + k * 2);
+                                w[c][0] = t.x; w[c][1] = t.y;
+                            } else {
+                                const float4 t = *reinterpret_cast<const float4*>(yrow + k * 4);
+                                w[c][0] = t.x; w[c][1] = t.y; w[c][2] = t.z; w[c][3] = t.w;
+                            }
+                        } else {
+#pragma unroll
+                            for (int m = 0; m < NB; ++m) w[c][m] = 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int c = 0; c < kGroup; ++c) {
+                        const int32_t k = g0 + c + S * lane;
+                        if (c >= S || k >= A.rows) continue;
+                        const double za = fma((double)k, za1, za0);
+                        const double zb = fma((double)k, zb1, zb0);
+                        const double fa = floor(fmin(za, zb)), fb = floor(fmax(za, zb));
+                        auto add = [&](int32_t iz, float f) {
+                            float* dst = col + (iz - z0) * NB;
+                            if (exclusive) {
+#pragma unroll
+                                for (int m = 0; m < NB; ++m) dst[m] += f * w[c][m];
+                            } else {
+#pragma unroll
+                                for (int m = 0; m < NB; ++m) atomicAdd(dst + m, f * w[c][m]);
+                            }
+                        };
+                        if (fa == fb && fa >= (double)z0 && fa < (double)z1) {
+                            add((int32_t)fa, fdt);
+                        } else {
+                            auto piece = [&](int32_t iz, double share) { add(iz, (float)share); };
+                            row_pieces_split(za, zb, dt, z0, z1, exclusive, piece);
+                        }
+                    }
                 }
             }
         }
@@ -622,8 +675,16 @@ int32_t gather_zchunk(int32_t D, int nb) {
     return D < cap ? D : cap;
 }
 
-hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol,
-                                int accumulate, hipStream_t s) {
+hipError_t launch_column_lines(const ColumnLaunch& a, int32_t views, ColLine* lines, hipStream_t s) {
+    const int64_t n = (int64_t)views * a.cols;
+    if (n == 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    column_line_kernel<<<dim3((unsigned)(want < 65536 ? want : 65536)), dim3(256), 0, s>>>(a, views, lines);
+    return hipGetLastError();
+}
+
+hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* lines, const float* ysc,
+                                float* vol, int accumulate, hipStream_t s) {
     const int32_t D = a.box.n[2];
     const int32_t zchunk = gather_zchunk(D, nb);
     const int32_t nchunks = (D + zchunk - 1) / zchunk;
@@ -632,9 +693,9 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const float* ysc,
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * zchunk * nb * sizeof(float);
     switch (nb) {
-        case 1: column_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, accumulate); break;
-        case 2: column_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, accumulate); break;
-        case 4: column_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, accumulate); break;
+        case 1: column_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;
+        case 2: column_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;
+        case 4: column_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -56,8 +56,11 @@ hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* con
 // floats; the launch covers views [view0, view0 + nviews).
 hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const* sino, float* ysc,
                                hipStream_t s);
-hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol,
-                                int accumulate, hipStream_t s);
+hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* lines, const float* ysc,
+                                float* vol, int accumulate, hipStream_t s);
+// Per-(view, column) line constants of the gather, for views [0, views) (lines holds
+// views * cols entries); computed once per plan and device.
+hipError_t launch_column_lines(const ColumnLaunch& a, int32_t views, ColLine* lines, hipStream_t s);
 
 // Positive-length segments walked by the launch's rays; adds into *count (device, zeroed by
 // the caller).

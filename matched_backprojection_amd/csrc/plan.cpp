@@ -61,6 +61,7 @@ struct DeviceState {
     float* ws = nullptr;              // library-owned workspace
     size_t ws_bytes = 0;
     unsigned long long* counter = nullptr;
+    mbp::ColLine* lines = nullptr;    // gather constants per (view, column)
 };
 
 bool finite3(const double* p, int n) {
@@ -473,6 +474,7 @@ void mbp_plan_destroy(mbp_plan* plan) {
         if (d.frames) (void)hipFree(d.frames);
         if (d.ws) (void)hipFree(d.ws);
         if (d.counter) (void)hipFree(d.counter);
+        if (d.lines) (void)hipFree(d.lines);
     }
     if (have_cur && !plan->devs.empty()) (void)hipSetDevice(cur);
     delete plan;
@@ -626,6 +628,14 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
             }
             const float* si[4] = {nullptr, nullptr, nullptr, nullptr};
             for (int m = 0; m < nb; ++m) si[m] = sinogram + (m0 + m) * rays;
+            if (gather && !d->lines) {
+                const size_t bytes = (size_t)g.views * (size_t)g.cols * sizeof(mbp::ColLine);
+                e = hipMalloc(reinterpret_cast<void**>(&d->lines), bytes);
+                if (e != hipSuccess) { d->lines = nullptr; return hip_fail(e, "hipMalloc(column lines)"); }
+                mbp::ColumnLaunch a = column_args(plan, d);
+                e = mbp::launch_column_lines(a, (int32_t)g.views, d->lines, s);
+                if (e != hipSuccess) return hip_fail(e, "column line launch");
+            }
             if (gather) {
                 mbp::ColumnLaunch a = column_args(plan, d);
                 const int64_t vb = views_per_launch(plan);
@@ -634,7 +644,7 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
                     a.nviews = (int32_t)std::min(vb, g.views - v0);
                     e = mbp::launch_sino_prepass(a, nb, si, ysc, s);
                     if (e != hipSuccess) return hip_fail(e, "sinogram pre-pass launch");
-                    e = mbp::launch_column_gather(a, nb, ysc, target, v0 == 0 ? acc_target : 1, s);
+                    e = mbp::launch_column_gather(a, nb, d->lines, ysc, target, v0 == 0 ? acc_target : 1, s);
                     if (e != hipSuccess) return hip_fail(e, "column gather launch");
                 }
             } else {

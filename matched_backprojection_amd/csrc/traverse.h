@@ -372,123 +372,155 @@ MBP_HD MBP_INLINE void walk_column_row(const ColumnWalk& c, const RowWalk& r, Vi
 // ------------------------------------------------------------------------------------------
 // Cell gather (matched adjoint of the column geometry, voxel side).
 //
-// For one xy cell and one view: the detector columns whose xy line crosses the cell, each
-// with the ray-parameter interval [t0, t1] of the crossing (common to all rows of the
-// column); then, for one row, the pieces of that crossing inside each z cell. A piece is
-// returned as its share of (t1 - t0); times the ray's length per unit parameter it is the
-// chord of the ray through the voxel.
+// All rows of detector column j share the column's line in the xy plane, and the ray
+// parameter t (0 at the source, 1 at the pixel; any real for parallel lines) is the same for
+// all of them at a given xy point. For one xy cell and one view:
+//  * the columns whose xy line can cross the cell are found from the detector interval that
+//    the cell's corners project to (fp32, widened by a pixel; the fp64 clip decides);
+//  * the crossing is t in [t0, t1], a slab clip of the column's line against the cell;
+//  * row k is at z cell coordinate zeta(t) = c0 + t c1 + k (c2 + t c3) (the z cell index is
+//    floor(zeta)); along the crossing it runs from zeta_a to zeta_b, and its chord through z
+//    cell iz is (t1 - t0) * |d_k| * (overlap of [zeta_a, zeta_b] with [iz, iz + 1]) / |zeta_b -
+//    zeta_a|, or (t1 - t0) * |d_k| when the piece lies in one z cell.
+// |d_k| (the ray's length per unit t) is folded into the sinogram by a pre-pass, so the
+// gather adds share * y'.
 
-struct CellCrossing {
-    int32_t j;          // detector column
-    int32_t line;       // 1: parallel line, 0: segment from the source
-    double t0, t1;      // ray-parameter interval inside the xy cell
-    double zs, dz0;     // z(t) of row k: line: zs + v_k evz + t dz0; segment: zs + t (dz0 + v_k evz)
+// Per (view, column) constants of the column's line: t(x) = x * ax + bx when ax != 0, else
+// the line keeps x == bx (likewise for y); zeta coefficients c0..c3 as above.
+struct ColLine {
+    double ax, bx, ay, by;
+    double c0, c1, c2, c3;
 };
 
-MBP_HD MBP_INLINE double cross2d(double ax, double ay, double bx, double by) {
-    return ax * by - ay * bx;
+MBP_HD MBP_INLINE void column_line(const Frame& F, const Box& B, int beam, int32_t j, int32_t cols,
+                                   int32_t rows, double du, double dv, ColLine& L) {
+    const double u = centred(j, cols, du);
+    const double px = F.c[0] + u * F.u[0], py = F.c[1] + u * F.u[1], pz = F.c[2] + u * F.u[2];
+    double ax, ay, dx, dy, zs, dz0;
+    if (beam == BEAM_PARALLEL) {
+        ax = px; ay = py; dx = F.s[0]; dy = F.s[1]; zs = pz; dz0 = F.s[2];
+    } else {
+        ax = F.s[0]; ay = F.s[1]; dx = px - F.s[0]; dy = py - F.s[1]; zs = F.s[2]; dz0 = pz - F.s[2];
+    }
+    if (dx != 0.0) { L.ax = 1.0 / dx; L.bx = -ax / dx; } else { L.ax = 0.0; L.bx = ax; }
+    if (dy != 0.0) { L.ay = 1.0 / dy; L.by = -ay / dy; } else { L.ay = 0.0; L.by = ay; }
+    const double inv = 1.0 / B.pitch[2];
+    const double roff = 0.5 * (double)(rows - 1);
+    const double evz = F.v[2] * dv;                 // z change per row at unit parameter
+    if (beam == BEAM_PARALLEL) {                    // z = zs + v_k evz + t dz0
+        L.c0 = (zs - roff * evz - B.lo[2]) * inv;
+        L.c1 = dz0 * inv;
+        L.c2 = evz * inv;
+        L.c3 = 0.0;
+    } else {                                        // z = zs + t (dz0 + v_k evz)
+        L.c0 = (zs - B.lo[2]) * inv;
+        L.c1 = (dz0 - roff * evz) * inv;
+        L.c2 = 0.0;
+        L.c3 = evz * inv;
+    }
 }
 
-// Column range [j0, j1] whose xy line can cross the cell [x0,x1) x [y0,y1) in view F;
-// returns false when none can.
+// Detector columns whose xy line can cross the cell [x0,x1) x [y0,y1): corner projections in
+// fp32, widened by one pixel on each side (the fp64 clip of each column decides).
 MBP_HD MBP_INLINE bool cell_column_range(const Frame& F, int beam, int32_t cols, double du,
                                          double x0, double x1, double y0, double y1,
                                          int32_t& j0, int32_t& j1) {
-    double umin = INFINITY, umax = -INFINITY, sign = 0.0;
-    bool bounded = true;
+    float umin = INFINITY, umax = -INFINITY;
+    bool bounded = true, neg = false;
+    const float sx = (float)F.s[0], sy = (float)F.s[1];
+    const float bx = (float)(F.c[0] - F.s[0]), by = (float)(F.c[1] - F.s[1]);
+    const float ex = (float)F.u[0], ey = (float)F.u[1];
+    const float cx = (float)F.c[0], cy = (float)F.c[1];
     for (int c = 0; c < 4; ++c) {
-        const double qx = (c & 1) ? x1 : x0, qy = (c & 2) ? y1 : y0;
-        double num, den;
+        const float qx = (float)((c & 1) ? x1 : x0), qy = (float)((c & 2) ? y1 : y0);
+        float num, den;
         if (beam == BEAM_PARALLEL) {    // q + l r = det + u e: u = cross(q - det, r) / cross(e, r)
-            num = cross2d(qx - F.c[0], qy - F.c[1], F.s[0], F.s[1]);
-            den = cross2d(F.u[0], F.u[1], F.s[0], F.s[1]);
+            num = (qx - cx) * sy - (qy - cy) * sx;
+            den = ex * sy - ey * sx;
         } else {                        // s + l (q - s) = det + u e: u = cross(det - s, a) / cross(a, e)
-            const double ax = qx - F.s[0], ay = qy - F.s[1];
-            num = cross2d(F.c[0] - F.s[0], F.c[1] - F.s[1], ax, ay);
-            den = cross2d(ax, ay, F.u[0], F.u[1]);
+            const float ax = qx - sx, ay = qy - sy;
+            num = bx * ay - by * ax;
+            den = ax * ey - ay * ex;
         }
-        if (den == 0.0 || (c > 0 && (den > 0.0) != (sign > 0.0))) bounded = false;
-        sign = den;
-        const double u = num / den;
-        umin = fmin(umin, u);
-        umax = fmax(umax, u);
+        if (den == 0.0f || (c > 0 && (den < 0.0f) != neg)) bounded = false;
+        neg = den < 0.0f;
+        const float u = num / den;
+        umin = fminf(umin, u);
+        umax = fmaxf(umax, u);
     }
     j0 = 0;
     j1 = cols - 1;
-    if (!bounded) return true;
-    const double coff = 0.5 * (double)(cols - 1);
-    const double f0 = ceil(umin / du + coff - 1e-7), f1 = floor(umax / du + coff + 1e-7);
-    if (!(f1 >= 0.0) || !(f0 <= (double)(cols - 1))) return false;
-    j0 = f0 < 0.0 ? 0 : (int32_t)f0;
-    j1 = f1 > (double)(cols - 1) ? cols - 1 : (int32_t)f1;
+    if (!bounded || !(umin == umin) || !(umax == umax)) return true;
+    const float coff = 0.5f * (float)(cols - 1);
+    const float inv = (float)(1.0 / du);
+    const float f0 = ceilf(umin * inv + coff) - 1.0f, f1 = floorf(umax * inv + coff) + 1.0f;
+    if (!(f1 >= 0.0f) || !(f0 <= (float)(cols - 1))) return false;
+    j0 = f0 < 0.0f ? 0 : (int32_t)f0;
+    j1 = f1 > (float)(cols - 1) ? cols - 1 : (int32_t)f1;
     return j0 <= j1;
 }
 
-// The crossing of column j's xy line with the cell; false when it has no positive length.
-MBP_HD MBP_INLINE bool cell_crossing(const Frame& F, int beam, int32_t j, int32_t cols, double du,
-                                     double x0, double x1, double y0, double y1, CellCrossing& x) {
-    const double u = centred(j, cols, du);
-    const double pxj = F.c[0] + u * F.u[0], pyj = F.c[1] + u * F.u[1], pzj = F.c[2] + u * F.u[2];
-    double a[2], d[2];
-    double t0, t1;
-    if (beam == BEAM_PARALLEL) {
-        a[0] = pxj; a[1] = pyj; d[0] = F.s[0]; d[1] = F.s[1];
-        t0 = -INFINITY; t1 = INFINITY;
-        x.line = 1; x.zs = pzj; x.dz0 = F.s[2];
-    } else {
-        a[0] = F.s[0]; a[1] = F.s[1]; d[0] = pxj - F.s[0]; d[1] = pyj - F.s[1];
-        t0 = 0.0; t1 = 1.0;
-        x.line = 0; x.zs = F.s[2]; x.dz0 = pzj - F.s[2];
+// Clip column line L to the cell: t in [t0, t1] (segments start from [0, 1]).
+MBP_HD MBP_INLINE bool cell_clip(const ColLine& L, bool line, double x0, double x1, double y0,
+                                 double y1, double& t0, double& t1) {
+    t0 = line ? -INFINITY : 0.0;
+    t1 = line ? INFINITY : 1.0;
+    if (L.ax != 0.0) {
+        const double p = x0 * L.ax + L.bx, q = x1 * L.ax + L.bx;
+        t0 = fmax(t0, fmin(p, q));
+        t1 = fmin(t1, fmax(p, q));
+    } else if (!(L.bx >= x0 && L.bx < x1)) {
+        return false;
     }
-    const double lo[2] = {x0, y0}, hi[2] = {x1, y1};
-    if (!clip_slab(a, d, lo, hi, 2, t0, t1)) return false;
-    x.j = j;
-    x.t0 = t0;
-    x.t1 = t1;
-    return true;
+    if (L.ay != 0.0) {
+        const double p = y0 * L.ay + L.by, q = y1 * L.ay + L.by;
+        t0 = fmax(t0, fmin(p, q));
+        t1 = fmin(t1, fmax(p, q));
+    } else if (!(L.by >= y0 && L.by < y1)) {
+        return false;
+    }
+    return t1 > t0;
 }
 
-// Pieces of row k (detector coordinate vk_evz = v_k * evz) inside the z cells [z0, z1) of
-// the box: piece(iz, share) with share = the part of (t1 - t0) spent in z cell iz.
+// Pieces of the row whose z cell coordinate runs from za to zb, restricted to z cells
+// [z0, z1), when they are not a single piece in one cell: piece(iz, share of (t1 - t0)).
+// With `aligned`, the walk starts at floor(min(za, zb)) even below z0 (cells outside
+// [z0, z1) are stepped over, not visited), so step i of every row is cell floor(zmin) + i:
+// rows whose zmin differ by more than one cell then never meet in the same cell at the same
+// step. The caller only asks for it when min(za, zb) lies at most a few cells below z0.
 template <class Piece>
-MBP_HD MBP_INLINE void row_pieces(const CellCrossing& x, double vk_evz, const Box& B, int32_t z0,
-                                  int32_t z1, Piece& piece) {
-    double za, zb;
-    if (x.line) {
-        const double zk = x.zs + vk_evz;
-        za = zk + x.t0 * x.dz0;
-        zb = zk + x.t1 * x.dz0;
-    } else {
-        const double dzk = x.dz0 + vk_evz;
-        za = x.zs + x.t0 * dzk;
-        zb = x.zs + x.t1 * dzk;
-    }
-    const double pz = B.pitch[2];
-    const double zlo = B.lo[2] + z0 * pz, zhi = B.lo[2] + z1 * pz;
+MBP_HD MBP_INLINE void row_pieces_split(double za, double zb, double dt, int32_t z0, int32_t z1,
+                                        bool aligned, Piece& piece) {
     const double zmin = fmin(za, zb), zmax = fmax(za, zb);
-    if (zmax < zlo || zmin >= zhi) return;
-    const double dt = x.t1 - x.t0;
     const double ext = zmax - zmin;
-    const double inv = 1.0 / pz;
-    int32_t ia = (int32_t)floor((fmax(zmin, zlo) - B.lo[2]) * inv);
-    int32_t ib = (int32_t)floor((fmin(zmax, zhi) - B.lo[2]) * inv);
-    ia = ia < z0 ? z0 : (ia > z1 - 1 ? z1 - 1 : ia);
-    ib = ib < z0 ? z0 : (ib > z1 - 1 ? z1 - 1 : ib);
-    if (ext == 0.0) {                       // in a z plane: the half-open cell containing it
-        if (zmin >= zlo && zmin < zhi) piece(ia, dt);
-        return;
-    }
-    if (ia == ib) {
-        const double ov = fmin(zmax, zhi) - fmax(zmin, zlo);
-        if (ov > 0.0) piece(ia, ov >= ext ? dt : dt * (ov / ext));
-        return;
-    }
+    if (!(ext > 0.0)) return;              // a point piece outside [z0, z1)
+    if (!(zmax > (double)z0) || !(zmin < (double)z1)) return;
     const double scale = dt / ext;
+    const int32_t ia = (int32_t)floor(aligned ? zmin : fmax(zmin, (double)z0));
+    const int32_t ib = (int32_t)fmin(floor(zmax), (double)(z1 - 1));
     for (int32_t iz = ia; iz <= ib; ++iz) {
-        const double c0 = B.lo[2] + iz * pz, c1 = c0 + pz;
-        const double ov = fmin(zmax, c1) - fmax(zmin, c0);
+        if (iz < z0) continue;
+        const double ov = fmin(zmax, (double)(iz + 1)) - fmax(zmin, (double)iz);
         if (ov > 0.0) piece(iz, ov * scale);
     }
+}
+
+// Row grouping of the gather: groups of S * 64 rows (S = min(8, ceil(rows / 64))) in which
+// chunk c (one instruction's 64 lanes) holds rows c, c + S, c + 2S, ...
+MBP_HD MBP_INLINE int32_t gather_stride(int32_t rows) {
+    const int32_t s = (rows + 63) / 64;
+    return s < 8 ? s : 8;
+}
+
+// Whether the lanes of one gather instruction (rows S apart, z cell coordinate at row k
+// za0 + k za1 at the crossing's start and zb0 + k zb1 at its end) always add into different
+// z cells when pieces are walked aligned: S rows move z by more than one cell at both ends,
+// and no row spans more than 64 z cells inside the xy cell.
+MBP_HD MBP_INLINE bool gather_exclusive(int32_t S, int32_t rows, double za0, double za1, double zb0,
+                                        double zb1) {
+    const double span0 = fabs(zb0 - za0);
+    const double span1 = fabs(zb0 - za0 + (double)(rows - 1) * (zb1 - za1));
+    return (double)S * fmin(fabs(za1), fabs(zb1)) > 1.0 + 1e-6 && fmax(span0, span1) <= 64.0;
 }
 
 }  // namespace mbp

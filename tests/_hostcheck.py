@@ -33,6 +33,8 @@ def _load():
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
         lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
+        lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P]
+        lib.mbph_gather_conflicts.restype = I64
         lib.mbph_check_rays.restype = I64
         _lib = lib
     return _lib
@@ -141,3 +143,15 @@ def gather(geom: dict, traj: dict, sino: np.ndarray):
                     float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)), _ptr(s), _ptr(vol),
                     ctypes.byref(viol))
     return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value)
+
+
+def gather_conflicts(geom: dict, traj: dict, aligned: bool = True):
+    """(exclusive crossings checked, steps whose lanes would add into one z cell twice)."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    viol = ctypes.c_longlong(0)
+    checked = lib.mbph_gather_conflicts(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n),
+                                        int(geom["views"]), int(geom.get("rows", 1)),
+                                        int(geom["cols"]), float(geom.get("du", 1.0)),
+                                        float(geom.get("dv", 1.0)), int(aligned), ctypes.byref(viol))
+    return int(checked), int(viol.value)

@@ -98,3 +98,27 @@ def test_cell_gather_reproduces_oracle_adjoint(oracle, name):
     assert np.linalg.norm(b - bref) / np.linalg.norm(bref) < 1e-12
     floor = 1e-6 * np.abs(bref).max()
     assert (np.abs(b - bref) / np.maximum(np.abs(bref), floor)).max() < 1e-9
+
+
+@pytest.mark.parametrize("name", ["c3_cone256", "c4_cone512_aniso"])
+def test_gather_plain_lds_adds_never_collide(name):
+    """Where the gather adds into LDS without atomics, the 64 lanes of every instruction hit
+    distinct z cells (emulated instruction by instruction). The same emulation of a walk that
+    starts at the first in-range cell does collide, so the check has teeth."""
+    cfg = SMALL_CONFIGS[name]
+    geom, traj = _geom(cfg), config_trajectory(cfg)
+    checked, conflicts = HC.gather_conflicts(geom, traj, aligned=True)
+    assert checked > 10000 and conflicts == 0
+    if name == "c3_cone256":      # rays leave through the top and bottom faces in this twin
+        _, bad = HC.gather_conflicts(geom, traj, aligned=False)
+        assert bad > 0
+
+
+@pytest.mark.parametrize("name", ["c3_cone256", "c4_cone512_aniso"])
+def test_gather_plain_lds_adds_never_collide_full_size(name):
+    cfg = CONFIGS[name]
+    sel = [0, cfg.views // 3, (2 * cfg.views) // 3]
+    traj = {k: (None if v is None else v[sel]) for k, v in config_trajectory(cfg).items()}
+    geom = dict(_geom(cfg), views=len(sel))
+    checked, conflicts = HC.gather_conflicts(geom, traj)
+    assert checked > 100000 and conflicts == 0
