@@ -31,6 +31,32 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c4_cone512_hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources (the key the traffic measurements are stored under)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "traverse.h", "mbp_internal.h"):
+        with open(os.path.join(ROOT, "matched_backprojection_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            line = next(l for l in f if l.startswith("traffic-json:"))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line.split(":", 1)[1])
+    if rec.get("source_sha256") != kernel_source_hash() or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return float(k["read_bytes"] + k["write_bytes"])
 
 
 def log(msg: str) -> None:
@@ -69,6 +95,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adjoint", choices=("gather", "scatter"), default="gather",
                     help="adjoint kernel of the column walk")
+    ap.add_argument("--probe", action="store_true",
+                    help="for hardware-counter runs: one forward, one adjoint and a 1 GiB "
+                         "device-to-device copy (the counters' calibration), no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is "
@@ -96,6 +125,16 @@ def main() -> int:
     xd = torch.from_numpy(np.ascontiguousarray(x.transpose(2, 1, 0))).to(dev).permute(2, 1, 0)
     sino = torch.empty((cfg.views, cfg.rows, cfg.cols), dtype=torch.float32, device=dev)
     vol = plan.empty_volume(device=dev)
+    if args.probe:
+        plan.project(xd, out=sino)
+        plan.backproject(sino, out=vol)
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)                        # 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        log("probe: forward, adjoint and a 1 GiB copy done")
+        plan.close()
+        return 0
     segs = plan.segment_count()
     log(f"plan: {info}; {segs} positive-length segments per op")
 
@@ -133,6 +172,7 @@ def main() -> int:
     dominant = adj_kernel if b_avg >= f_avg else "column_forward_kernel"
     dom_ms = max(b_avg, f_avg)
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(dominant)
     pair_gbs = 2 * alg_bytes / ((f_avg + b_avg) * 1e-3) / 1e9
     log(f"algorithmic bytes per launch {alg_bytes / 1e9:.1f} GB; dominant {dominant}: "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak; pair {pair_gbs:.0f} GB/s")
@@ -171,7 +211,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic,
         },
     }
     if not args.no_cpu_baseline:
