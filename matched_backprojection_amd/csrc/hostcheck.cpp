@@ -200,12 +200,14 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
 // column crossing that the kernel treats as exclusive, every chunk of 64 lanes (rows S
 // apart) and every step (the single-piece add, then step i of the aligned piece walk), the
 // z cells the active lanes add into must be distinct. Returns the number of exclusive
-// crossings checked; *conflicts counts steps with a repeated cell. aligned = 0 replays the
-// walk that starts at the first in-range cell instead (rows entering from below the box
-// then meet in its bottom cell), which the tests use to show the check can fail.
+// crossings checked; *conflicts counts steps with a repeated cell. mode 0 replays the
+// kernel; two planted mistakes show the check can fail: mode 1 starts the walk of rows that
+// span several cells at the first in-range cell (rows entering from below the box then meet
+// in its bottom cell), mode 2 deals adjacent rows to the lanes of one instruction.
 int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, const double* pitch,
                               const int32_t* n, int views, int rows, int cols, double du, double dv,
-                              int aligned, long long* conflicts) {
+                              int mode, long long* conflicts) {
+    const bool aligned = mode != 1;
     std::vector<Frame> F;
     frames_from(frames, views, F);
     const Box B = box_from(lo, pitch, n);
@@ -230,25 +232,29 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                     const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
                     if (!gather_exclusive(S, rows, za0, za1, zb0, zb1)) continue;
                     ++checked;
-                    for (int32_t g0 = 0; g0 < rows; g0 += 64 * S) {
+                    const int32_t rows_pad = gather_rows_padded(rows);
+                    for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S) {
                         for (int32_t c = 0; c < S; ++c) {
-                            // step "single piece" and steps of the aligned walk
-                            std::vector<std::vector<int32_t>> steps(1);
+                            // steps: the two-piece adds (cell fa, then cell fb), then the
+                            // steps of the aligned walk of rows spanning a cell or more
+                            std::vector<std::vector<int32_t>> steps(2);
                             for (int lane = 0; lane < 64; ++lane) {
-                                const int32_t k = g0 + c + S * lane;
-                                if (k >= rows) continue;
+                                // padded rows too; mode 2 puts adjacent rows in one instruction
+                                const int32_t k = mode == 2 ? g0 + 64 * c + lane : g0 + c + S * lane;
                                 const double za = std::fma((double)k, za1, za0);
                                 const double zb = std::fma((double)k, zb1, zb0);
-                                const double fa = std::floor(std::fmin(za, zb)), fb = std::floor(std::fmax(za, zb));
-                                if (fa == fb && fa >= 0.0 && fa < (double)n[2]) {
-                                    steps[0].push_back((int32_t)fa);
+                                const double zmin = std::fmin(za, zb), zmax = std::fmax(za, zb);
+                                if (zmax - zmin < 1.0) {
+                                    const double fa = std::floor(zmin), fb = std::floor(zmax);
+                                    if (fa >= 0.0 && fa < (double)n[2]) steps[0].push_back((int32_t)fa);
+                                    if (fb != fa && fb >= 0.0 && fb < (double)n[2]) steps[1].push_back((int32_t)fb);
                                     continue;
                                 }
                                 // step index of each piece: its position in this row's walk
-                                const int32_t start = aligned ? (int32_t)std::floor(std::fmin(za, zb))
-                                                              : (int32_t)std::floor(std::fmax(std::fmin(za, zb), 0.0));
+                                const int32_t start = aligned ? (int32_t)std::floor(zmin)
+                                                              : (int32_t)std::floor(std::fmax(zmin, 0.0));
                                 auto piece = [&](int32_t iz, double) {
-                                    const int step = iz - start + 1;
+                                    const int step = iz - start + 2;
                                     if ((int)steps.size() <= step) steps.resize(step + 1);
                                     steps[step].push_back(iz);
                                 };

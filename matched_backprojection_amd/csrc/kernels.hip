@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(256) column_count_kernel(const ColumnLaunch A,
 
 template <int NB>
 __global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A, const Ptrs4 sino,
-                                                           float* __restrict__ ysc) {
+                                                           int32_t rows_pad, float* __restrict__ ysc) {
     __shared__ float tile[NB][32][33];
     const int32_t j0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int32_t view = A.view0 + (int32_t)blockIdx.z;
@@ -305,18 +305,17 @@ __global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int32_t k = k0 + ty + 8 * i, j = j0 + tx;
-        if (k < A.rows && j < A.cols) {
 #pragma unroll
-            for (int m = 0; m < NB; ++m)
-                tile[m][ty + 8 * i][tx] = sino.p[m][vbase + (int64_t)k * A.cols + j];
-        }
+        for (int m = 0; m < NB; ++m)
+            tile[m][ty + 8 * i][tx] = (k < A.rows && j < A.cols)
+                                          ? sino.p[m][vbase + (int64_t)k * A.cols + j] : 0.0f;
     }
     __syncthreads();
     const Frame F = A.frames[view];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int32_t j = j0 + ty + 8 * i, k = k0 + tx;
-        if (k < A.rows && j < A.cols) {
+        if (k < rows_pad && j < A.cols) {
             double len;
             if (A.beam == BEAM_PARALLEL) {
                 len = sqrt(F.s[0] * F.s[0] + F.s[1] * F.s[1] + F.s[2] * F.s[2]);
@@ -327,7 +326,7 @@ __global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A,
                 len = sqrt(dx * dx + dy * dy + dz * dz);
             }
             const float scale = (float)len;
-            const int64_t o = ((vbase + (int64_t)j * A.rows + k)) * NB;
+            const int64_t o = (((int64_t)view * A.cols + j) * rows_pad + k) * NB;
 #pragma unroll
             for (int m = 0; m < NB; ++m) ysc[o + m] = tile[m][tx][ty + 8 * i] * scale;
         }
@@ -378,7 +377,8 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
         const double y0 = A.box.lo[1] + iy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
         const bool line = A.beam == BEAM_PARALLEL;
         const int32_t S = gather_stride(A.rows);
-        const int32_t group_rows = 64 * S;
+        const int32_t rows_pad = gather_rows_padded(A.rows);
+        const double lane_k = (double)(S * lane);
         for (int32_t view = A.view0; view < A.view0 + A.nviews; ++view) {
             int32_t j0, j1;
             if (!cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, j0, j1))
@@ -391,17 +391,28 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
                 const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
                 const double dt = t1 - t0;
                 const float fdt = (float)dt;
-                const float* yrow = ysc + ((int64_t)view * A.cols + j) * A.rows * NB;
+                const float* yrow = ysc + ((int64_t)view * A.cols + j) * rows_pad * NB;
                 // Lanes of one instruction are S rows apart; when gather_exclusive holds they
                 // add into different z cells at every step, and this wave alone owns `col`, so
                 // a plain read-add-write is race free. Otherwise: LDS atomics.
                 const bool exclusive = gather_exclusive(S, A.rows, za0, za1, zb0, zb1);
-                for (int32_t g0 = 0; g0 < A.rows; g0 += group_rows) {
+                auto add = [&](int32_t iz, float f, const float* wv) {
+                    float* dst = col + (iz - z0) * NB;
+                    if (exclusive) {
+#pragma unroll
+                        for (int m = 0; m < NB; ++m) dst[m] += f * wv[m];
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < NB; ++m) atomicAdd(dst + m, f * wv[m]);
+                    }
+                };
+                for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S) {
+                    // all loads of the group first (the copy is zero-padded to whole groups)
                     float w[kGroup][NB];
 #pragma unroll
                     for (int c = 0; c < kGroup; ++c) {
-                        const int32_t k = g0 + c + S * lane;
-                        if (c < S && k < A.rows) {
+                        if (c < S) {
+                            const int32_t k = g0 + c + S * lane;
                             if constexpr (NB == 1) {
                                 w[c][0] = yrow[k];
                             } else if constexpr (NB == 2) {
@@ -411,32 +422,26 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
                                 const float4 t = *reinterpret_cast<const float4*>(yrow + k * 4);
                                 w[c][0] = t.x; w[c][1] = t.y; w[c][2] = t.z; w[c][3] = t.w;
                             }
-                        } else {
-#pragma unroll
-                            for (int m = 0; m < NB; ++m) w[c][m] = 0.0f;
                         }
                     }
 #pragma unroll
                     for (int c = 0; c < kGroup; ++c) {
-                        const int32_t k = g0 + c + S * lane;
-                        if (c >= S || k >= A.rows) continue;
-                        const double za = fma((double)k, za1, za0);
-                        const double zb = fma((double)k, zb1, zb0);
-                        const double fa = floor(fmin(za, zb)), fb = floor(fmax(za, zb));
-                        auto add = [&](int32_t iz, float f) {
-                            float* dst = col + (iz - z0) * NB;
-                            if (exclusive) {
-#pragma unroll
-                                for (int m = 0; m < NB; ++m) dst[m] += f * w[c][m];
-                            } else {
-#pragma unroll
-                                for (int m = 0; m < NB; ++m) atomicAdd(dst + m, f * w[c][m]);
-                            }
-                        };
-                        if (fa == fb && fa >= (double)z0 && fa < (double)z1) {
-                            add((int32_t)fa, fdt);
+                        if (c >= S) continue;
+                        const double kd = lane_k + (double)(g0 + c);
+                        const double za = fma(kd, za1, za0);
+                        const double zb = fma(kd, zb1, zb0);
+                        const double zmin = fmin(za, zb), zmax = fmax(za, zb);
+                        const double ext = zmax - zmin;
+                        if (ext < 1.0) {
+                            // at most two z cells: fa gets the share f of dt, fb the rest
+                            const double fa = floor(zmin), fb = floor(zmax);
+                            const float f = fa == fb ? 1.0f
+                                : (float)(fa + 1.0 - zmin) * __builtin_amdgcn_rcpf((float)ext);
+                            const float p1 = f * fdt, p2 = fdt - p1;
+                            if (fa >= (double)z0 && fa < (double)z1) add((int32_t)fa, p1, w[c]);
+                            if (fb != fa && fb >= (double)z0 && fb < (double)z1) add((int32_t)fb, p2, w[c]);
                         } else {
-                            auto piece = [&](int32_t iz, double share) { add(iz, (float)share); };
+                            auto piece = [&](int32_t iz, double share) { add(iz, (float)share, w[c]); };
                             row_pieces_split(za, zb, dt, z0, z1, exclusive, piece);
                         }
                     }
@@ -655,15 +660,16 @@ hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const
     if (a.nviews == 0) return hipSuccess;
     Ptrs4 y{};
     for (int m = 0; m < nb; ++m) y.p[m] = sino[m];
+    const int32_t rows_pad = gather_rows_padded(a.rows);
     for (int32_t v0 = 0; v0 < a.nviews; v0 += 65535) {
         ColumnLaunch b = a;
         b.view0 = a.view0 + v0;
         b.nviews = a.nviews - v0 < 65535 ? a.nviews - v0 : 65535;
-        const dim3 grid((a.cols + 31) / 32, (a.rows + 31) / 32, b.nviews);
+        const dim3 grid((a.cols + 31) / 32, (rows_pad + 31) / 32, b.nviews);
         switch (nb) {
-            case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, ysc); break;
-            case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, ysc); break;
-            case 4: sino_prepass_kernel<4><<<grid, dim3(256), 0, s>>>(b, y, ysc); break;
+            case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, ysc); break;
+            case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, ysc); break;
+            case 4: sino_prepass_kernel<4><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, ysc); break;
             default: return hipErrorInvalidValue;
         }
     }

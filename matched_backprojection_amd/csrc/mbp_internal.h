@@ -51,9 +51,10 @@ hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* con
 
 // Matched adjoint of the column geometry without global atomics: a pre-pass copies the
 // sinogram to [view][col][row] order (nb members interleaved innermost) scaled by each ray's
-// length per unit of its parameter; the gather then writes every voxel of the z-fastest
-// interleaved volume once (optionally adding into it). ysc holds nb * views * rows * cols
-// floats; the launch covers views [view0, view0 + nviews).
+// length per unit of its parameter, rows zero-padded to gather_rows_padded(rows); the gather
+// then writes every voxel of the z-fastest interleaved volume once (optionally adding into
+// it). ysc holds nb * views * cols * gather_rows_padded(rows) floats; the launch covers
+// views [view0, view0 + nviews).
 hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const* sino, float* ysc,
                                hipStream_t s);
 hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* lines, const float* ysc,

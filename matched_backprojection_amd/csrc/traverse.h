@@ -512,6 +512,12 @@ MBP_HD MBP_INLINE int32_t gather_stride(int32_t rows) {
     return s < 8 ? s : 8;
 }
 
+// Rows of the reordered sinogram, padded with zeros to whole groups of S * 64.
+MBP_HD MBP_INLINE int32_t gather_rows_padded(int32_t rows) {
+    const int32_t g = 64 * gather_stride(rows);
+    return (rows + g - 1) / g * g;
+}
+
 // Whether the lanes of one gather instruction (rows S apart, z cell coordinate at row k
 // za0 + k za1 at the crossing's start and zb0 + k zb1 at its end) always add into different
 // z cells when pieces are walked aligned: S rows move z by more than one cell at both ends,

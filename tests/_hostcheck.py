@@ -145,13 +145,14 @@ def gather(geom: dict, traj: dict, sino: np.ndarray):
     return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value)
 
 
-def gather_conflicts(geom: dict, traj: dict, aligned: bool = True):
-    """(exclusive crossings checked, steps whose lanes would add into one z cell twice)."""
+def gather_conflicts(geom: dict, traj: dict, mode: int = 0):
+    """(exclusive crossings checked, steps whose lanes would add into one z cell twice).
+    mode 0: the kernel's grouping; 1 and 2: planted mistakes (see hostcheck.cpp)."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
     viol = ctypes.c_longlong(0)
     checked = lib.mbph_gather_conflicts(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n),
                                         int(geom["views"]), int(geom.get("rows", 1)),
                                         int(geom["cols"]), float(geom.get("du", 1.0)),
-                                        float(geom.get("dv", 1.0)), int(aligned), ctypes.byref(viol))
+                                        float(geom.get("dv", 1.0)), int(mode), ctypes.byref(viol))
     return int(checked), int(viol.value)

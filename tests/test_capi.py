@@ -22,6 +22,13 @@ def lib():
     return _capi.load()
 
 
+def rows_padded(rows):
+    """Rows of the gather's reordered sinogram: zero-padded to whole groups of S * 64 rows,
+    S = min(8, ceil(rows / 64))."""
+    g = 64 * min(8, -(-rows // 64))
+    return -(-rows // g) * g
+
+
 def _declared_symbols():
     text = open(os.path.join(ROOT, "include", "mbp.h")).read()
     return sorted(set(re.findall(r"\b(mbp_[a-z_]+)\s*\(", text)))
@@ -86,7 +93,8 @@ def test_configs_plan_and_pick_walks(lib, name):
     else:   # z-fastest volume copy (unless used in place) + reordered sinogram for the gather
         nb = min(4, cfg.members)
         direct = cfg.layout == "WHD" and cfg.members == 1
-        assert ws.value == 4 * nb * ((0 if direct else cfg.n_voxels) + cfg.n_rays)
+        sino = cfg.views * cfg.cols * rows_padded(cfg.rows)
+        assert ws.value == 4 * nb * ((0 if direct else cfg.n_voxels) + sino)
     # view batching: a ragged split into launches of 7 views
     assert lib.mbp_plan_set_view_batch(h, 7) == 0
     inf = _info(lib, h)
@@ -208,8 +216,9 @@ def test_python_plan_maps_errors_and_shapes():
                     layout="WHD")
     assert plan.sino_shape == (cfg.views, cfg.rows, cfg.cols)
     assert plan.info["path"] == "column"
-    assert plan.workspace_size(1) == 4 * cfg.n_rays
-    assert plan.workspace_size(3) == 2 * (cfg.n_voxels + cfg.n_rays) * 4
+    sino = cfg.views * cfg.cols * rows_padded(cfg.rows)
+    assert plan.workspace_size(1) == 4 * sino
+    assert plan.workspace_size(3) == 2 * (cfg.n_voxels + sino) * 4
     plan.set_adjoint("scatter")
     assert plan.workspace_size(1) == 0 and plan.workspace_size(3) == 2 * cfg.n_voxels * 4
     plan.set_adjoint("auto")

@@ -128,6 +128,29 @@ def test_small_config_parity(torch_dev, mbp, oracle, name):
         plan.close()
 
 
+def test_steep_cone_parity(torch_dev, mbp, oracle):
+    """Rows crossing several z cells per xy cell and leaving through the box's z faces: the
+    gather's general piece walk, in both its plain-LDS and its atomic mode."""
+    from tests.test_hostcheck import steep_cone_config
+    torch, dev = torch_dev
+    cfg = steep_cone_config()
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(21)
+    x = rng.random(cfg.shape).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    y = rng.random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    for adjoint in ("gather", "scatter"):
+        say(f"case steep cone, adjoint={adjoint}")
+        plan = make_plan(mbp, cfg)
+        plan.set_adjoint(adjoint)
+        p = plan.project(to_device_volume(torch, dev, x, cfg.layout)).cpu().numpy().astype(np.float64)
+        check(p, ref, "forward")
+        b = plan.backproject(torch.from_numpy(y).to(dev)).cpu().numpy().astype(np.float64)
+        check(b, bref, "adjoint")
+        plan.close()
+
+
 def test_general_trajectory_parity(torch_dev, mbp, oracle):
     """Tilted detectors (row axis not parallel to z): the generic walk, anisotropic grid."""
     torch, dev = torch_dev
@@ -185,7 +208,8 @@ def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
     # a caller-owned workspace gives the same result; a too-small one is refused
     plan = make_plan(mbp, cfg)
     need = plan.workspace_size(5)
-    assert need == 4 * (cfg.n_voxels + cfg.n_rays) * 4
+    from tests.test_capi import rows_padded
+    assert need == 4 * (cfg.n_voxels + cfg.views * cfg.cols * rows_padded(cfg.rows)) * 4
     ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
     plan.set_workspace(ws)
     p = plan.project(torch.from_numpy(xs).to(dev)).cpu().numpy().astype(np.float64)

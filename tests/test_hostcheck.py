@@ -103,15 +103,32 @@ def test_cell_gather_reproduces_oracle_adjoint(oracle, name):
 @pytest.mark.parametrize("name", ["c3_cone256", "c4_cone512_aniso"])
 def test_gather_plain_lds_adds_never_collide(name):
     """Where the gather adds into LDS without atomics, the 64 lanes of every instruction hit
-    distinct z cells (emulated instruction by instruction). The same emulation of a walk that
-    starts at the first in-range cell does collide, so the check has teeth."""
+    distinct z cells (emulated instruction by instruction). Dealing adjacent rows to one
+    instruction instead does collide, so the check has teeth."""
     cfg = SMALL_CONFIGS[name]
     geom, traj = _geom(cfg), config_trajectory(cfg)
-    checked, conflicts = HC.gather_conflicts(geom, traj, aligned=True)
+    checked, conflicts = HC.gather_conflicts(geom, traj, mode=0)
     assert checked > 10000 and conflicts == 0
-    if name == "c3_cone256":      # rays leave through the top and bottom faces in this twin
-        _, bad = HC.gather_conflicts(geom, traj, aligned=False)
-        assert bad > 0
+    assert HC.gather_conflicts(geom, traj, mode=2)[1] > 0
+
+
+def steep_cone_config():
+    """A tall, narrow volume next to the source: rows cross several z cells inside one xy cell
+    and leave through the bottom and top faces (the gather's general piece walk)."""
+    from dataclasses import replace
+    return replace(SMALL_CONFIGS["c3_cone256"], name="steep_cone", shape=(100, 20, 20), rows=128,
+                   cols=40, dv=3.0, sid=18.0, sdd=40.0, views=6)
+
+
+def test_gather_steep_rows_walk_aligned():
+    """On the steep cone the aligned piece walk stays collision free; the walk that starts at
+    the first in-range cell collides."""
+    cfg = steep_cone_config()
+    geom, traj = _geom(cfg), config_trajectory(cfg)
+    checked, conflicts = HC.gather_conflicts(geom, traj, mode=0)
+    assert checked > 1000 and conflicts == 0
+    assert HC.gather_conflicts(geom, traj, mode=1)[1] > 0
+    assert HC.gather_conflicts(geom, traj, mode=2)[1] > 0
 
 
 @pytest.mark.parametrize("name", ["c3_cone256", "c4_cone512_aniso"])
