@@ -102,6 +102,83 @@ int mbph_project(int path, const double* frames, int beam, const double* lo, con
     return 0;
 }
 
+// Forward projection with the chunked column walk of the forward kernel: per column, the
+// 64 lanes' entries of each chunk of merged xy crossings are filled one lane after another,
+// then every row consumes them (the kernel does the same with one wave per 64 rows).
+int mbph_project_chunked(const double* frames, int beam, const double* lo, const double* pitch,
+                         const int32_t* n, int views, int rows, int cols, double du, double dv,
+                         const float* vol, float* sino, long long* violations) {
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *violations = 0;
+    const int32_t H = n[1], D = n[2];
+    std::vector<XYEvent> E(kXYChunk);
+    std::vector<std::vector<XYEvent>> chunks;
+    for (int i = 0; i < views; ++i) {
+        for (int j = 0; j < cols; ++j) {
+            ColumnWalk c;
+            column_setup(F[i], B, beam, centred(j, cols, du), c);
+            // the column's chunks, as one wave builds them
+            chunks.clear();
+            std::vector<int32_t> counts;
+            int32_t final_cxy = 0;
+            if (c.hit) {
+                const int32_t total = c.x.steps + c.y.steps;
+                int32_t done = 0, kx0 = 0, ky0 = 0;
+                while (done < total) {
+                    const int32_t count = total - done < kXYChunk ? total - done : kXYChunk;
+                    for (auto& e : E) { e.tb = NAN; e.cxy = -1; }
+                    int32_t a = 0;
+                    for (int lane = 0; lane < 64; ++lane) a += xy_chunk_fill(c, H, kx0, ky0, count, lane, E.data());
+                    for (int32_t p = 0; p < count; ++p)   // every position filled exactly once
+                        if (E[p].cxy < 0 || E[p].cxy >= n[0] * H || !(E[p].tb == E[p].tb)) ++*violations;
+                    chunks.push_back(std::vector<XYEvent>(E.begin(), E.begin() + count));
+                    kx0 += a; ky0 += count - a; done += count;
+                }
+                if (kx0 != c.x.steps || ky0 != c.y.steps) ++*violations;
+                final_cxy = (c.x.c0 + c.x.step * c.x.steps) * H + (c.y.c0 + c.y.step * c.y.steps);
+            }
+            for (int k = 0; k < rows; ++k) {
+                RowWalk r;
+                row_setup(c, B, centred(k, rows, dv), F[i].v[2], r);
+                float acc = 0.0f;
+                auto visit = [&](int32_t cxy, int32_t cz, float len) {
+                    if (cxy < 0 || cxy >= n[0] * H || cz < 0 || cz >= D || !(len >= 0.0f)) { ++*violations; return; }
+                    const int32_t cx = cxy / H, cy = cxy % H;
+                    acc = fmaf(len, vol[((int64_t)cz * H + cy) * n[0] + cx], acc);
+                };
+                if (c.hit) {
+                    int32_t cz = r.z.c0, kz = 0;
+                    double nz = r.z.steps > 0 ? r.z.t_first : INFINITY;
+                    double ta = 0.0;
+                    // rows meeting at most one z plane per xy cell take the grouped two-piece
+                    // form for whole groups of a chunk, the general one for the rest
+                    const bool two = row_single_crossing(r, B);
+                    for (const auto& ch : chunks) {
+                        const size_t grouped = two ? ch.size() / kCellGroup * kCellGroup : 0;
+                        size_t p = 0;
+                        for (; p < grouped; ++p) {
+                            const double hi = fmin(ch[p].tb, r.t_hi);
+                            int32_t z0, z1;
+                            float l0, l1;
+                            row_cell_two(r, ta, ch[p].tb, cz, kz, nz, z0, l0, z1, l1);
+                            if (nz < hi && fmax(ta, r.t_lo) < hi) ++*violations;   // a second crossing
+                            if (l0 != 0.0f) visit(ch[p].cxy, z0, l0);
+                            if (l1 != 0.0f) visit(ch[p].cxy, z1, l1);
+                            ta = ch[p].tb;
+                        }
+                        for (; p < ch.size(); ++p) { row_cell(r, ta, ch[p].tb, ch[p].cxy, cz, kz, nz, visit); ta = ch[p].tb; }
+                    }
+                    row_cell(r, ta, c.T, final_cxy, cz, kz, nz, visit);
+                }
+                sino[((int64_t)i * rows + k) * cols + j] = acc * r.kappa;
+            }
+        }
+    }
+    return 0;
+}
+
 // Adjoint with the same walks, accumulated in fp64 on the host (order is deterministic).
 int mbph_backproject(int path, const double* frames, int beam, const double* lo,
                      const double* hi, const double* pitch, const int32_t* n, int views,

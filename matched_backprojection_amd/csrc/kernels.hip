@@ -177,6 +177,19 @@ __device__ __forceinline__ void load_acc(const float* __restrict__ p, float len,
     }
 }
 
+template <int NB>
+__device__ __forceinline__ void load_vals(const float* __restrict__ p, float* v) {
+    if constexpr (NB == 1) {
+        v[0] = p[0];
+    } else if constexpr (NB == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        v[0] = t.x; v[1] = t.y;
+    } else {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    }
+}
+
 struct ColumnTask {
     int32_t view, col, row;
     bool valid;
@@ -199,27 +212,107 @@ __device__ __forceinline__ ColumnTask column_task(const ColumnLaunch& A) {
     return t;
 }
 
+// Sum over the wave of a lane value in {0, 1, 2}.
+__device__ __forceinline__ int32_t wave_sum012(int32_t v) {
+    return (int32_t)(__popcll(__ballot(v & 1)) + 2 * __popcll(__ballot((v >> 1) & 1)));
+}
+
+// Makes one lane's LDS writes visible to the other lanes of its wave (and keeps the compiler
+// from moving LDS accesses across this point).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int NB>
 __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch A,
                                                              const float* __restrict__ vol,
                                                              const MPtrs4 sino) {
+    __shared__ XYEvent events[4][kXYChunk];
     const ColumnTask t = column_task(A);
     if (!t.live) return;
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    const int32_t lane = (int32_t)(threadIdx.x & 63u);
+    XYEvent* E = events[wave];
     const Frame F = A.frames[t.view];
     ColumnWalk c;
     column_setup(F, A.box, A.beam, centred(t.col, A.cols, A.du), c);
     RowWalk r;
     row_setup(c, A.box, centred(t.row, A.rows, A.dv), F.v[2], r);
-    if (!t.valid) { r.t_lo = 0.0f; r.t_hi = 0.0f; }
+    if (!t.valid) { r.t_lo = 0.0; r.t_hi = 0.0; }
     float acc[NB];
 #pragma unroll
     for (int m = 0; m < NB; ++m) acc[m] = 0.0f;
-    const uint32_t H = (uint32_t)A.H, D = (uint32_t)A.D;
-    auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
-        const uint32_t base = (((uint32_t)cx * H + (uint32_t)cy) * D + (uint32_t)cz) * NB;
-        load_acc<NB>(vol + base, len, acc);
-    };
-    walk_column_row(c, r, visit);
+    if (c.hit) {
+        const uint32_t D = (uint32_t)A.D;
+        auto visit = [&](int32_t cxy, int32_t cz, float len) {
+            load_acc<NB>(vol + ((uint32_t)cxy * D + (uint32_t)cz) * NB, len, acc);
+        };
+        int32_t cz = r.z.c0, kz = 0;
+        double nz = r.z.steps > 0 ? r.z.t_first : INFINITY;
+        const int32_t total = c.x.steps + c.y.steps;
+        int32_t done = 0, kx0 = 0, ky0 = 0;
+        double ta = 0.0;
+        // when every lane meets at most one z plane per xy cell, cells are handled in fixed
+        // groups with all their loads issued before the sums
+        const bool two_pieces = __all(row_single_crossing(r, A.box));
+        for (;;) {
+            const int32_t count = total - done < kXYChunk ? total - done : kXYChunk;
+            int32_t a = 0;
+            if (count > 0) {
+                a = wave_sum012(xy_chunk_fill(c, A.H, kx0, ky0, count, lane, E));
+                wave_lds_sync();
+            }
+            int32_t p = 0;
+            if (two_pieces) {
+                // groups of kCellGroup cells: every lane's pieces (at most two per cell: before and
+                // after its single z crossing) first, then all their loads, then the sums
+                for (; p + kCellGroup <= count; p += kCellGroup) {
+                    uint32_t off[2 * kCellGroup];
+                    float len[2 * kCellGroup];
+#pragma unroll
+                    for (int q = 0; q < kCellGroup; ++q) {
+                        const double tb = E[p + q].tb;
+                        const uint32_t base = (uint32_t)E[p + q].cxy * D;
+                        int32_t z0, z1;
+                        row_cell_two(r, ta, tb, cz, kz, nz, z0, len[2 * q], z1, len[2 * q + 1]);
+                        off[2 * q] = (base + (uint32_t)z0) * NB;
+                        off[2 * q + 1] = (base + (uint32_t)z1) * NB;
+                        ta = tb;
+                    }
+                    float val[2 * kCellGroup][NB];
+#pragma unroll
+                    for (int q = 0; q < 2 * kCellGroup; ++q) {
+                        if (len[q] != 0.0f) {
+                            load_vals<NB>(vol + off[q], val[q]);
+                        } else {
+#pragma unroll
+                            for (int m = 0; m < NB; ++m) val[q][m] = 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < 2 * kCellGroup; ++q)
+#pragma unroll
+                        for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
+                }
+            }
+            for (; p < count; ++p) {
+                const double tb = E[p].tb;
+                row_cell(r, ta, tb, E[p].cxy, cz, kz, nz, visit);
+                ta = tb;
+            }
+            kx0 += a;
+            ky0 += count - a;
+            done += count;
+            if (done >= total) {
+                const int32_t cxy = (c.x.c0 + c.x.step * c.x.steps) * A.H + (c.y.c0 + c.y.step * c.y.steps);
+                row_cell(r, ta, c.T, cxy, cz, kz, nz, visit);
+                break;
+            }
+            wave_lds_sync();
+        }
+    }
     if (t.valid) {
         const int64_t ray = ((int64_t)t.view * A.rows + t.row) * A.cols + t.col;
 #pragma unroll

@@ -529,4 +529,125 @@ MBP_HD MBP_INLINE bool gather_exclusive(int32_t S, int32_t rows, double za0, dou
     return (double)S * fmin(fabs(za1), fabs(zb1)) > 1.0 + 1e-6 && fmax(span0, span1) <= 64.0;
 }
 
+// ------------------------------------------------------------------------------------------
+// Column walk in chunks: the xy crossings of a column, merged in order, built in parallel.
+//
+// The xy cells a column's line visits do not depend on the row, so a wave can lay them out
+// once for all of its rows: the crossings are the x sequence x_i = first_x + i step_x and the
+// y sequence y_j = first_y + j step_y (one fma each, as in walk_column_row), and their merged
+// order, x first on ties, gives the cells. For a chunk of up to kXYChunk crossings that start
+// after kx0 x and ky0 y crossings, x_i lands at position i + #{y in the chunk's y window
+// strictly before x_i} and y_j at j + #{x in the x window at or before y_j}; the counts come
+// from branch-free binary searches over the same fma'd values (both sequences are
+// non-decreasing), so every position of the chunk is filled exactly once. Each entry holds
+// the distance at which a cell ends and the cell's xy index, the cell before that crossing.
+
+constexpr int32_t kXYChunk = 128;
+// Cells per group when a row's pieces are computed ahead of their loads.
+constexpr int32_t kCellGroup = 4;
+
+struct XYEvent {
+    double tb;          // distance at which the cell ends
+    int32_t cxy;        // cx * H + cy
+    int32_t pad_;
+};
+
+MBP_HD MBP_INLINE double crossing(const AxisWalk& a, int32_t k) {
+    return fma((double)k, a.t_step, a.t_first);
+}
+
+// Number of crossings of `a` with index in [k0, k0 + n) at or before `t` (strict = false) or
+// strictly before it (strict = true); n <= 255.
+MBP_HD MBP_INLINE int32_t count_before(const AxisWalk& a, int32_t k0, int32_t n, double t, bool strict) {
+    int32_t lo = 0;
+    for (int32_t step = 128; step > 0; step >>= 1) {
+        if (lo + step <= n) {
+            const double v = crossing(a, k0 + lo + step - 1);
+            if (strict ? v < t : v <= t) lo += step;
+        }
+    }
+    return lo;
+}
+
+// Fill the entries of one lane's candidates (window indices lane and lane + 64 of each axis)
+// for the chunk of `count` crossings after kx0 x and ky0 y crossings. Returns how many of
+// this lane's x candidates fall inside the chunk (their sum over lanes is the number of x
+// crossings the chunk consumes).
+MBP_HD MBP_INLINE int32_t xy_chunk_fill(const ColumnWalk& c, int32_t H, int32_t kx0, int32_t ky0,
+                                        int32_t count, int32_t lane, XYEvent* E) {
+    const int32_t nxw = c.x.steps - kx0 < kXYChunk ? c.x.steps - kx0 : kXYChunk;
+    const int32_t nyw = c.y.steps - ky0 < kXYChunk ? c.y.steps - ky0 : kXYChunk;
+    int32_t xin = 0;
+    for (int32_t q = 0; q < 2; ++q) {
+        const int32_t i = lane + 64 * q;
+        if (i < nxw) {
+            const double tx = crossing(c.x, kx0 + i);
+            const int32_t jy = count_before(c.y, ky0, nyw, tx, true);
+            const int32_t pos = i + jy;
+            if (pos < count) {
+                E[pos].tb = tx;
+                E[pos].cxy = (c.x.c0 + c.x.step * (kx0 + i)) * H + (c.y.c0 + c.y.step * (ky0 + jy));
+                ++xin;
+            }
+        }
+        if (i < nyw) {
+            const double ty = crossing(c.y, ky0 + i);
+            const int32_t ix = count_before(c.x, kx0, nxw, ty, false);
+            const int32_t pos = i + ix;
+            if (pos < count) {
+                E[pos].tb = ty;
+                E[pos].cxy = (c.x.c0 + c.x.step * (kx0 + ix)) * H + (c.y.c0 + c.y.step * (ky0 + i));
+            }
+        }
+    }
+    return xin;
+}
+
+// One row's share of one xy cell [ta, tb] with column-base index `cxy`: visit(cxy, cz, len)
+// for the row's pieces inside the cell (lengths in units of tau). The row's z state (cz, kz,
+// nz) carries over from cell to cell.
+template <class Visit>
+MBP_HD MBP_INLINE void row_cell(const RowWalk& r, double ta, double tb, int32_t cxy, int32_t& cz,
+                                int32_t& kz, double& nz, Visit& visit) {
+    double lo = fmax(ta, r.t_lo);
+    const double hi = fmin(tb, r.t_hi);
+    if (!(lo < hi)) return;
+    while (nz < hi) {
+        visit(cxy, cz, (float)fmax(nz - lo, 0.0));
+        lo = fmax(lo, nz);
+        cz += r.z.step; ++kz;
+        nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
+    }
+    visit(cxy, cz, (float)(hi - lo));
+}
+
+// A row meets at most one z plane inside any xy cell when its z crossings lie farther apart
+// than the longest chord of an xy cell (the cell's diagonal); the margin is far above the
+// rounding of the crossing distances.
+MBP_HD MBP_INLINE bool row_single_crossing(const RowWalk& r, const Box& B) {
+    const double diag = sqrt(B.pitch[0] * B.pitch[0] + B.pitch[1] * B.pitch[1]);
+    return r.z.steps == 0 || r.z.t_step > 1.001 * diag;
+}
+
+// row_cell for a row with row_single_crossing(): the piece before the cell's z crossing
+// (z cell cz0, length len0) and the piece after it (cz1, len1; len1 = 0 when the row meets
+// no z plane in the cell). Lengths are 0 where the row is outside the slab.
+MBP_HD MBP_INLINE void row_cell_two(const RowWalk& r, double ta, double tb, int32_t& cz,
+                                    int32_t& kz, double& nz, int32_t& cz0, float& len0,
+                                    int32_t& cz1, float& len1) {
+    const double lo = fmax(ta, r.t_lo), hi = fmin(tb, r.t_hi);
+    const bool in = lo < hi;
+    const bool cross = in && nz < hi;
+    cz0 = cz;
+    len0 = in ? (float)(cross ? fmax(nz - lo, 0.0) : hi - lo) : 0.0f;
+    len1 = 0.0f;
+    if (cross) {
+        len1 = (float)(hi - fmax(lo, nz));
+        cz += r.z.step;
+        ++kz;
+        nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
+    }
+    cz1 = cz;
+}
+
 }  // namespace mbp

@@ -33,6 +33,7 @@ def _load():
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
         lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
+        lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
         lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P]
         lib.mbph_gather_conflicts.restype = I64
         lib.mbph_check_rays.restype = I64
@@ -156,3 +157,18 @@ def gather_conflicts(geom: dict, traj: dict, mode: int = 0):
                                         int(geom["cols"]), float(geom.get("du", 1.0)),
                                         float(geom.get("dv", 1.0)), int(mode), ctypes.byref(viol))
     return int(checked), int(viol.value)
+
+
+def project_chunked(geom: dict, traj: dict, vol: np.ndarray):
+    """Replay the forward kernel's chunked column walk on a (D, H, W) float32 volume."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    rows = int(geom.get("rows", 1))
+    views, cols = int(geom["views"]), int(geom["cols"])
+    vol = np.ascontiguousarray(vol, dtype=np.float32)
+    sino = np.zeros((views, rows, cols), dtype=np.float32)
+    viol = ctypes.c_longlong(0)
+    lib.mbph_project_chunked(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n), views, rows,
+                             cols, float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)),
+                             _ptr(vol), _ptr(sino), ctypes.byref(viol))
+    return sino, int(viol.value)
