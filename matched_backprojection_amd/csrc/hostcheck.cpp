@@ -217,35 +217,47 @@ int mbph_backproject(int path, const double* frames, int beam, const double* lo,
     return 0;
 }
 
-// Adjoint by the cell gather (voxel side), accumulated in fp64: every xy cell, every view,
-// every candidate column and every row, exactly as the gather kernel enumerates them.
+// Replays the gather adjoint item by item as the kernel forms items: per cell, view and
+// crossing column one item, taken in the fast fixed-point form where the kernel takes it
+// (rows of a lane relative to the lane's origin cell, shares num / ext in fp32 when
+// `kernel_shares`, else in fp64 from the same integers) and in the fp64 general form
+// otherwise. Sums in fp64. *fast counts items taken in the fast form.
 int mbph_gather(const double* frames, int beam, const double* lo, const double* pitch,
                 const int32_t* n, int views, int rows, int cols, double du, double dv,
-                const float* sino, double* vol, long long* violations) {
+                const float* sino, int kernel_shares, double* vol, long long* violations,
+                long long* fast) {
     std::vector<Frame> F;
     frames_from(frames, views, F);
     const Box B = box_from(lo, pitch, n);
     *violations = 0;
+    *fast = 0;
     std::vector<ColLine> lines((size_t)views * cols);
     for (int v = 0; v < views; ++v)
         for (int j = 0; j < cols; ++j) column_line(F[v], B, beam, j, cols, rows, du, dv, lines[(size_t)v * cols + j]);
     const bool line = beam == BEAM_PARALLEL;
+    const int32_t S = gather_stride(rows), rows_pad = gather_rows_padded(rows), D = n[2];
+    std::vector<double> w(rows_pad);
     for (int ix = 0; ix < n[0]; ++ix) {
         for (int iy = 0; iy < n[1]; ++iy) {
             const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
             const double y0 = B.lo[1] + iy * B.pitch[1], y1 = y0 + B.pitch[1];
+            double* colv = vol;
+            auto add = [&](int32_t iz, double share, double wk) {
+                if (iz < 0 || iz >= D || !(share >= 0.0)) { ++*violations; return; }
+                colv[((int64_t)iz * n[1] + iy) * n[0] + ix] += share * wk;
+            };
             for (int v = 0; v < views; ++v) {
                 int32_t j0, j1;
                 if (!cell_column_range(F[v], beam, cols, du, x0, x1, y0, y1, j0, j1)) continue;
                 if (j0 < 0 || j1 >= cols) ++*violations;
                 for (int32_t j = j0; j <= j1; ++j) {
-                    const ColLine& L = lines[(size_t)v * cols + j];
-                    double t0, t1;
-                    if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) continue;
-                    const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
-                    const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
-                    const double dt = t1 - t0;
-                    for (int k = 0; k < rows; ++k) {
+                    GatherItem it;
+                    if (!gather_item(lines[(size_t)v * cols + j], line, x0, x1, y0, y1, S, rows,
+                                     rows_pad, v * cols + j, it))
+                        continue;
+                    // the reordered sinogram line: values times the ray length, zero padded
+                    for (int k = 0; k < rows_pad; ++k) {
+                        if (k >= rows) { w[k] = 0.0; continue; }
                         double len;
                         if (line) {
                             len = std::sqrt(F[v].s[0] * F[v].s[0] + F[v].s[1] * F[v].s[1] + F[v].s[2] * F[v].s[2]);
@@ -255,16 +267,47 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                             const double a = p[0] - F[v].s[0], b = p[1] - F[v].s[1], c = p[2] - F[v].s[2];
                             len = std::sqrt(a * a + b * b + c * c);
                         }
-                        const double w = (double)sino[((int64_t)v * rows + k) * cols + j] * len;
-                        auto piece = [&](int32_t iz, double share) {
-                            if (iz < 0 || iz >= n[2] || !(share >= 0.0)) { ++*violations; return; }
-                            vol[((int64_t)iz * n[1] + iy) * n[0] + ix] += share * w;
-                        };
-                        const double za = std::fma((double)k, za1, za0);
-                        const double zb = std::fma((double)k, zb1, zb0);
+                        w[k] = (double)sino[((int64_t)v * rows + k) * cols + j] * len;
+                    }
+                    // the kernel carries the crossing length in fp32; the fp64 replay takes it
+                    // from the clip again
+                    double dt = (double)it.dt;
+                    if (!kernel_shares) {
+                        double t0, t1;
+                        cell_clip(lines[(size_t)v * cols + j], line, x0, x1, y0, y1, t0, t1);
+                        dt = t1 - t0;
+                    }
+                    if (it.a1fx != kNotFast) {
+                        ++*fast;
+                        for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S)
+                            for (int lane = 0; lane < 64; ++lane) {
+                                const int32_t k0 = g0 + S * lane;
+                                int32_t la, lb, base;
+                                fast_origin(it, (double)k0, -1, la, lb, base);
+                                for (int32_t c = 0; c < S; ++c) {
+                                    int32_t fa, num, ext;
+                                    bool split;
+                                    fast_row(la + c * it.a1fx, lb + c * it.b1fx, fa, num, ext, split);
+                                    double f = 1.0;
+                                    if (split) f = kernel_shares ? (double)((float)num * (1.0f / (float)ext))
+                                                                 : (double)num / (double)ext;
+                                    const int32_t i0 = base + fa;
+                                    if ((uint32_t)i0 > (uint32_t)D) continue;     // outside: discarded
+                                    const int32_t z = i0 - 1;                      // cell of index i0
+                                    const double wk = w[k0 + c];
+                                    if (z >= 0) add(z, f * dt, wk);
+                                    if (z + 1 < D) add(z + 1, (1.0 - f) * dt, wk);
+                                }
+                            }
+                        continue;
+                    }
+                    for (int k = 0; k < rows; ++k) {
+                        auto piece = [&](int32_t iz, double share) { add(iz, share, w[k]); };
+                        const double za = std::fma((double)k, it.za1, it.za0);
+                        const double zb = std::fma((double)k, it.zb1, it.zb0);
                         const double fa = std::floor(std::fmin(za, zb)), fb = std::floor(std::fmax(za, zb));
-                        if (fa == fb && fa >= 0.0 && fa < (double)n[2]) piece((int32_t)fa, dt);
-                        else row_pieces_split(za, zb, dt, 0, n[2], false, piece);
+                        if (fa == fb && fa >= 0.0 && fa < (double)D) piece((int32_t)fa, dt);
+                        else row_pieces_split(za, zb, dt, 0, D, false, piece);
                     }
                 }
             }
@@ -273,26 +316,29 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
     return 0;
 }
 
-// Emulates the gather's instruction grouping and checks its race-freedom claim: for every
-// column crossing that the kernel treats as exclusive, every chunk of 64 lanes (rows S
-// apart) and every step (the single-piece add, then step i of the aligned piece walk), the
-// z cells the active lanes add into must be distinct. Returns the number of exclusive
-// crossings checked; *conflicts counts steps with a repeated cell. mode 0 replays the
-// kernel; two planted mistakes show the check can fail: mode 1 starts the walk of rows that
-// span several cells at the first in-range cell (rows entering from below the box then meet
-// in its bottom cell), mode 2 deals adjacent rows to the lanes of one instruction.
+// Emulates the gather's instruction grouping and checks its race-freedom claims. Fast items:
+// for every instruction (row c of each lane), the cell pairs {fa, fa + 1} that in-range lanes
+// read and write must be disjoint. General items that the kernel treats as exclusive: for
+// every instruction and every step (the single-piece add, then step i of the aligned piece
+// walk), the z cells the active lanes add into must be distinct. Returns the number of items
+// checked; *conflicts counts instructions or steps with a repeated cell, *fast the fast items.
+// mode 0 replays the kernel; two planted mistakes show the check can fail: mode 1 starts the
+// walk of rows that span several cells at the first in-range cell (rows entering from below
+// the box then meet in its bottom cell), mode 2 deals adjacent rows to the lanes of one
+// instruction.
 int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, const double* pitch,
                               const int32_t* n, int views, int rows, int cols, double du, double dv,
-                              int mode, long long* conflicts) {
+                              int mode, long long* conflicts, long long* fast) {
     const bool aligned = mode != 1;
     std::vector<Frame> F;
     frames_from(frames, views, F);
     const Box B = box_from(lo, pitch, n);
     *conflicts = 0;
+    *fast = 0;
     const bool line = beam == BEAM_PARALLEL;
-    const int32_t S = gather_stride(rows);
+    const int32_t S = gather_stride(rows), rows_pad = gather_rows_padded(rows), D = n[2];
     int64_t checked = 0;
-    std::vector<int32_t> first(64), seen;
+    std::vector<int32_t> seen;
     for (int ix = 0; ix < n[0]; ++ix) {
         for (int iy = 0; iy < n[1]; ++iy) {
             const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
@@ -303,28 +349,46 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                 for (int32_t j = j0; j <= j1; ++j) {
                     ColLine L;
                     column_line(F[v], B, beam, j, cols, rows, du, dv, L);
-                    double t0, t1;
-                    if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) continue;
-                    const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
-                    const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
-                    if (!gather_exclusive(S, rows, za0, za1, zb0, zb1)) continue;
+                    GatherItem it;
+                    if (!gather_item(L, line, x0, x1, y0, y1, S, rows, rows_pad, v * cols + j, it)) continue;
+                    const bool is_fast = it.a1fx != kNotFast;
+                    if (!is_fast && it.b1fx == 0) continue;       // LDS atomics: nothing to check
                     ++checked;
-                    const int32_t rows_pad = gather_rows_padded(rows);
+                    if (is_fast) ++*fast;
                     for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S) {
                         for (int32_t c = 0; c < S; ++c) {
+                            if (is_fast) {
+                                seen.clear();
+                                for (int lane = 0; lane < 64; ++lane) {
+                                    // mode 2: adjacent rows in one instruction
+                                    const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
+                                    int32_t la, lb, base;
+                                    fast_origin(it, (double)k0, -1, la, lb, base);
+                                    int32_t fa, num, ext;
+                                    bool split;
+                                    fast_row(la + c * it.a1fx, lb + c * it.b1fx, fa, num, ext, split);
+                                    const int32_t i0 = base + fa;
+                                    if ((uint32_t)i0 > (uint32_t)D) continue;   // discard pair
+                                    seen.push_back(i0);
+                                    seen.push_back(i0 + 1);
+                                }
+                                std::sort(seen.begin(), seen.end());
+                                if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
+                                continue;
+                            }
                             // steps: the two-piece adds (cell fa, then cell fb), then the
                             // steps of the aligned walk of rows spanning a cell or more
                             std::vector<std::vector<int32_t>> steps(2);
                             for (int lane = 0; lane < 64; ++lane) {
                                 // padded rows too; mode 2 puts adjacent rows in one instruction
                                 const int32_t k = mode == 2 ? g0 + 64 * c + lane : g0 + c + S * lane;
-                                const double za = std::fma((double)k, za1, za0);
-                                const double zb = std::fma((double)k, zb1, zb0);
+                                const double za = std::fma((double)k, it.za1, it.za0);
+                                const double zb = std::fma((double)k, it.zb1, it.zb0);
                                 const double zmin = std::fmin(za, zb), zmax = std::fmax(za, zb);
                                 if (zmax - zmin < 1.0) {
                                     const double fa = std::floor(zmin), fb = std::floor(zmax);
-                                    if (fa >= 0.0 && fa < (double)n[2]) steps[0].push_back((int32_t)fa);
-                                    if (fb != fa && fb >= 0.0 && fb < (double)n[2]) steps[1].push_back((int32_t)fb);
+                                    if (fa >= 0.0 && fa < (double)D) steps[0].push_back((int32_t)fa);
+                                    if (fb != fa && fb >= 0.0 && fb < (double)D) steps[1].push_back((int32_t)fb);
                                     continue;
                                 }
                                 // step index of each piece: its position in this row's walk
@@ -335,7 +399,7 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                                     if ((int)steps.size() <= step) steps.resize(step + 1);
                                     steps[step].push_back(iz);
                                 };
-                                row_pieces_split(za, zb, t1 - t0, 0, n[2], aligned != 0, piece);
+                                row_pieces_split(za, zb, (double)it.dt, 0, D, aligned, piece);
                             }
                             for (auto& st : steps) {
                                 seen = st;

@@ -435,13 +435,106 @@ __global__ void __launch_bounds__(256) column_line_kernel(const ColumnLaunch A, 
     }
 }
 
-// Rows are taken in groups of S * 64 (S = min(kGroup, ceil(rows / 64)) chunks of 64 lanes):
-// the sinogram values of a whole group are loaded before any is used, so a wave has S loads
-// in flight, and chunk c of a group holds rows c, c + S, c + 2S, ... A lane's neighbours are
-// then S rows away, which on these geometries is more than one z cell, so the 64 LDS
-// additions of one instruction go to different addresses (adjacent rows would share a z cell
-// and serialise).
-constexpr int kGroup = 8;
+// Rows are taken in groups of S * 64 (S = min(kGroup, ceil(rows / 64))): lane l holds rows
+// g0 + S l .. g0 + S l + S - 1 of a group, and one instruction handles row g0 + S l + c of every
+// lane. A lane's neighbours in an instruction are S rows away, which on these geometries is
+// more than one z cell, so the 64 LDS additions of one instruction go to different addresses.
+constexpr int kGroup = kGatherGroup;
+// Items a wave queues before it processes them (the queue is drained once it holds more
+// than kQueue - 64, so one more round of 64 always fits).
+constexpr int kQueue = 96;
+
+// The column of one wave in LDS: index i holds z cell z0 - 1 + i for i in [0, n + 1]
+// (n = z1 - z0; indices 0 and n + 1 are guard cells just outside the chunk, never written
+// out), and indices n + 2, n + 3 are a discard pair for pieces outside the chunk.
+__host__ __device__ constexpr int32_t gather_column_floats(int32_t zchunk, int nb) {
+    return (zchunk + 4) * nb;
+}
+
+// A lane's kGroup consecutive rows starting at row k0 of one sinogram line (rows past the
+// lane's S are loaded and ignored: a fixed count keeps the loads unconditional, so the next
+// unit's loads can be in flight while the current one is summed).
+template <int NB>
+__device__ __forceinline__ void gather_load_rows(const float* __restrict__ p, float (&w)[kGroup][NB]) {
+#pragma unroll
+    for (int c = 0; c < kGroup; ++c) load_vals<NB>(p + c * NB, w[c]);
+}
+
+// Fast form of one item for one group of rows (see gather_fast): every row adds its two
+// pieces to the disjoint cell pair {fa, fa + 1} with one paired read and write.
+template <int NB>
+__device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
+                                                  float dt, const float (&w)[kGroup][NB],
+                                                  int32_t k0, int32_t S, int32_t z0, int32_t n,
+                                                  float* col) {
+    int32_t la, lb, base;
+    fast_origin(it, (double)k0, z0 - 1, la, lb, base);
+#pragma unroll
+    for (int c = 0; c < kGroup; ++c) {
+        if (c >= S) continue;
+        int32_t fa, num, ext;
+        bool split;
+        fast_row(la + c * a1, lb + c * b1, fa, num, ext, split);
+        const float f = split ? (float)num * __builtin_amdgcn_rcpf((float)ext) : 1.0f;
+        const int32_t i0 = base + fa;
+        const int32_t idx = (uint32_t)i0 <= (uint32_t)n ? i0 : n + 2;
+        float* dst = col + idx * NB;
+        float v[2 * NB];
+#pragma unroll
+        for (int m = 0; m < 2 * NB; ++m) v[m] = dst[m];
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            const float q = dt * w[c][m];
+            const float pa = f * q;
+            v[m] += pa;
+            v[NB + m] += q - pa;
+        }
+#pragma unroll
+        for (int m = 0; m < 2 * NB; ++m) dst[m] = v[m];
+    }
+}
+
+// General form of one item for one group of rows: rows of any z extent, pieces walked in
+// fp64; plain LDS read-add-write when the item's lanes add exclusively, else LDS atomics.
+template <int NB>
+__device__ __forceinline__ void gather_general_group(const GatherItem& it, bool exclusive,
+                                                     const float (&w)[kGroup][NB], int32_t k0,
+                                                     int32_t S, int32_t z0, int32_t z1,
+                                                     float* col) {
+    const double dt = (double)it.dt;
+    const float fdt = it.dt;
+    auto add = [&](int32_t iz, float f, const float* wv) {
+        float* dst = col + (iz - z0 + 1) * NB;
+        if (exclusive) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m) dst[m] += f * wv[m];
+        } else {
+#pragma unroll
+            for (int m = 0; m < NB; ++m) atomicAdd(dst + m, f * wv[m]);
+        }
+    };
+#pragma unroll
+    for (int c = 0; c < kGroup; ++c) {
+        if (c >= S) continue;
+        const double kd = (double)(k0 + c);
+        const double za = fma(kd, it.za1, it.za0);
+        const double zb = fma(kd, it.zb1, it.zb0);
+        const double zmin = fmin(za, zb), zmax = fmax(za, zb);
+        const double ext = zmax - zmin;
+        if (ext < 1.0) {
+            // at most two z cells: fa gets the share f of dt, fb the rest
+            const double fa = floor(zmin), fb = floor(zmax);
+            const float f = fa == fb ? 1.0f
+                : (float)(fa + 1.0 - zmin) * __builtin_amdgcn_rcpf((float)ext);
+            const float p1 = f * fdt, p2 = fdt - p1;
+            if (fa >= (double)z0 && fa < (double)z1) add((int32_t)fa, p1, w[c]);
+            if (fb != fa && fb >= (double)z0 && fb < (double)z1) add((int32_t)fb, p2, w[c]);
+        } else {
+            auto piece = [&](int32_t iz, double share) { add(iz, (float)share, w[c]); };
+            row_pieces_split(za, zb, dt, z0, z1, exclusive, piece);
+        }
+    }
+}
 
 template <int NB>
 __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A,
@@ -450,7 +543,7 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
                                                             float* __restrict__ vol,
                                                             int32_t zchunk, int32_t nchunks,
                                                             int32_t accumulate) {
-    extern __shared__ float lds[];
+    extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
     const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
@@ -462,8 +555,11 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
     const int32_t iy = (int32_t)(xy % (uint32_t)H), ix = (int32_t)(xy / (uint32_t)H);
     const int32_t z0 = zc * zchunk;
     const int32_t z1 = live ? (z0 + zchunk < D ? z0 + zchunk : D) : z0;
-    float* col = lds + wave * zchunk * NB;
-    for (int32_t i = lane; i < (z1 - z0) * NB; i += 64) col[i] = 0.0f;
+    const int32_t n = z1 - z0;
+    const int32_t colf = gather_column_floats(zchunk, NB);
+    GatherItem* Q = reinterpret_cast<GatherItem*>(lds_raw) + wave * kQueue;
+    float* col = reinterpret_cast<float*>(lds_raw + 4 * kQueue * sizeof(GatherItem)) + wave * colf;
+    for (int32_t i = lane; i < colf; i += 64) col[i] = 0.0f;
     __syncthreads();
     if (live) {
         const double x0 = A.box.lo[0] + ix * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
@@ -471,82 +567,84 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
         const bool line = A.beam == BEAM_PARALLEL;
         const int32_t S = gather_stride(A.rows);
         const int32_t rows_pad = gather_rows_padded(A.rows);
-        const double lane_k = (double)(S * lane);
-        for (int32_t view = A.view0; view < A.view0 + A.nviews; ++view) {
-            int32_t j0, j1;
-            if (!cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, j0, j1))
-                continue;
-            for (int32_t j = j0; j <= j1; ++j) {
-                const ColLine L = lines[(int64_t)view * A.cols + j];
-                double t0, t1;
-                if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) continue;
-                const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
-                const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
-                const double dt = t1 - t0;
-                const float fdt = (float)dt;
-                const float* yrow = ysc + ((int64_t)view * A.cols + j) * rows_pad * NB;
-                // Lanes of one instruction are S rows apart; when gather_exclusive holds they
-                // add into different z cells at every step, and this wave alone owns `col`, so
-                // a plain read-add-write is race free. Otherwise: LDS atomics.
-                const bool exclusive = gather_exclusive(S, A.rows, za0, za1, zb0, zb1);
-                auto add = [&](int32_t iz, float f, const float* wv) {
-                    float* dst = col + (iz - z0) * NB;
-                    if (exclusive) {
+        const int32_t vend = A.view0 + A.nviews;
+
+        // Units of work: (item, row group) in queue order. The rows of the next unit are
+        // loaded while the current one is summed.
+        const int32_t ngroups = rows_pad / (64 * S);
+        auto unit_rows = [&](int32_t u) {
+            const int32_t i = u / ngroups, g0 = (u - i * ngroups) * 64 * S;
+            const int32_t yoff = (int32_t)uniform((uint32_t)Q[i].yoff);
+            return ysc + ((int64_t)yoff * rows_pad + g0 + S * lane) * NB;
+        };
+        auto drain = [&](int32_t count) {
+            const int32_t units = count * ngroups;
+            if (units == 0) return;
+            float w[kGroup][NB], wn[kGroup][NB];
+            gather_load_rows<NB>(unit_rows(0), w);
+            for (int32_t u = 0; u < units; ++u) {
+                gather_load_rows<NB>(unit_rows(u + 1 < units ? u + 1 : u), wn);
+                const int32_t i = u / ngroups;
+                const int32_t k0 = (u - i * ngroups) * 64 * S + S * lane;
+                const GatherItem it = Q[i];
+                const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
+                const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
+                if (a1 != kNotFast) {
+                    const float dt = __uint_as_float(uniform(__float_as_uint(it.dt)));
+                    gather_fast_group<NB>(it, a1, b1, dt, w, k0, S, z0, n, col);
+                } else {
+                    gather_general_group<NB>(it, b1 != 0, w, k0, S, z0, z1, col);
+                }
 #pragma unroll
-                        for (int m = 0; m < NB; ++m) dst[m] += f * wv[m];
-                    } else {
+                for (int c = 0; c < kGroup; ++c)
 #pragma unroll
-                        for (int m = 0; m < NB; ++m) atomicAdd(dst + m, f * wv[m]);
-                    }
-                };
-                for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S) {
-                    // all loads of the group first (the copy is zero-padded to whole groups)
-                    float w[kGroup][NB];
-#pragma unroll
-                    for (int c = 0; c < kGroup; ++c) {
-                        if (c < S) {
-                            const int32_t k = g0 + c + S * lane;
-                            if constexpr (NB == 1) {
-                                w[c][0] = yrow[k];
-                            } else if constexpr (NB == 2) {
-                                const float2 t = *reinterpret_cast<const float2*>(yrow + k * 2);
-                                w[c][0] = t.x; w[c][1] = t.y;
-                            } else {
-                                const float4 t = *reinterpret_cast<const float4*>(yrow + k * 4);
-                                w[c][0] = t.x; w[c][1] = t.y; w[c][2] = t.z; w[c][3] = t.w;
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int c = 0; c < kGroup; ++c) {
-                        if (c >= S) continue;
-                        const double kd = lane_k + (double)(g0 + c);
-                        const double za = fma(kd, za1, za0);
-                        const double zb = fma(kd, zb1, zb0);
-                        const double zmin = fmin(za, zb), zmax = fmax(za, zb);
-                        const double ext = zmax - zmin;
-                        if (ext < 1.0) {
-                            // at most two z cells: fa gets the share f of dt, fb the rest
-                            const double fa = floor(zmin), fb = floor(zmax);
-                            const float f = fa == fb ? 1.0f
-                                : (float)(fa + 1.0 - zmin) * __builtin_amdgcn_rcpf((float)ext);
-                            const float p1 = f * fdt, p2 = fdt - p1;
-                            if (fa >= (double)z0 && fa < (double)z1) add((int32_t)fa, p1, w[c]);
-                            if (fb != fa && fb >= (double)z0 && fb < (double)z1) add((int32_t)fb, p2, w[c]);
-                        } else {
-                            auto piece = [&](int32_t iz, double share) { add(iz, (float)share, w[c]); };
-                            row_pieces_split(za, zb, dt, z0, z1, exclusive, piece);
-                        }
-                    }
+                    for (int m = 0; m < NB; ++m) w[c][m] = wn[c][m];
+            }
+        };
+
+        // Items: each lane takes one view of a round of 64 and walks its candidate columns;
+        // the crossings found are appended to the queue in lane order.
+        int32_t count = 0;
+        for (int32_t vb = A.view0; vb < vend; vb += 64) {
+            const int32_t view = vb + lane;
+            int32_t jn = 0, j1 = -1;
+            if (view < vend &&
+                !cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, jn, j1)) {
+                jn = 0;
+                j1 = -1;
+            }
+            if (view >= vend) j1 = -1;
+            while (__ballot(jn <= j1) != 0) {
+                GatherItem it;
+                bool hit = false;
+                if (jn <= j1) {
+                    const int32_t yoff = view * A.cols + jn;
+                    hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff, it);
+                    ++jn;
+                }
+                const uint64_t m = __ballot(hit);
+                if (hit) {
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    Q[count + (int32_t)below] = it;
+                }
+                count += (int32_t)__popcll(m);
+                if (count > kQueue - 64) {
+                    wave_lds_sync();
+                    drain(count);
+                    count = 0;
+                    wave_lds_sync();
                 }
             }
         }
+        wave_lds_sync();
+        drain(count);
     }
     __syncthreads();
     if (live) {
         const int64_t base = (((int64_t)ix * H + iy) * D + z0) * NB;
-        for (int32_t i = lane; i < (z1 - z0) * NB; i += 64)
-            vol[base + i] = accumulate ? vol[base + i] + col[i] : col[i];
+        for (int32_t i = lane; i < n * NB; i += 64)
+            vol[base + i] = accumulate ? vol[base + i] + col[NB + i] : col[NB + i];
     }
 }
 
@@ -790,7 +888,8 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     const uint64_t tasks = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)nchunks;
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
-    const size_t lds = (size_t)4 * zchunk * nb * sizeof(float);
+    const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
+                                    (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
     switch (nb) {
         case 1: column_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;
         case 2: column_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;

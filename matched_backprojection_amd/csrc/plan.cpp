@@ -297,7 +297,7 @@ size_t column_ws_bytes(const mbp_plan* p, int nb, bool direct, bool gather) {
     const mbp_geometry& g = p->g;
     size_t n = 0;
     if (!direct) n += (size_t)nb * (size_t)(g.D * g.H * g.W);
-    if (gather) n += (size_t)nb * (size_t)(g.views * g.cols) * (size_t)mbp::gather_rows_padded((int32_t)g.rows);
+    if (gather) n += (size_t)mbp::gather_sino_floats((int32_t)g.views, (int32_t)g.cols, (int32_t)g.rows, nb);
     return n * sizeof(float);
 }
 

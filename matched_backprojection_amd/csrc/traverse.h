@@ -505,17 +505,25 @@ MBP_HD MBP_INLINE void row_pieces_split(double za, double zb, double dt, int32_t
     }
 }
 
-// Row grouping of the gather: groups of S * 64 rows (S = min(8, ceil(rows / 64))) in which
-// chunk c (one instruction's 64 lanes) holds rows c, c + S, c + 2S, ...
+// Row grouping of the gather: groups of S * 64 rows (S = min(kGatherGroup, ceil(rows / 64)))
+// in which chunk c (one instruction's 64 lanes) holds rows c, c + S, c + 2S, ...
+constexpr int32_t kGatherGroup = 8;
+
 MBP_HD MBP_INLINE int32_t gather_stride(int32_t rows) {
     const int32_t s = (rows + 63) / 64;
-    return s < 8 ? s : 8;
+    return s < kGatherGroup ? s : kGatherGroup;
 }
 
 // Rows of the reordered sinogram, padded with zeros to whole groups of S * 64.
 MBP_HD MBP_INLINE int32_t gather_rows_padded(int32_t rows) {
     const int32_t g = 64 * gather_stride(rows);
     return (rows + g - 1) / g * g;
+}
+
+// Floats of the reordered sinogram of nb members: [view][column][padded row][member], plus a
+// tail of kGatherGroup rows that a lane's fixed-width row loads may reach past the last line.
+MBP_HD MBP_INLINE int64_t gather_sino_floats(int32_t views, int32_t cols, int32_t rows, int nb) {
+    return (int64_t)nb * ((int64_t)views * cols * gather_rows_padded(rows) + kGatherGroup);
 }
 
 // Whether the lanes of one gather instruction (rows S apart, z cell coordinate at row k
@@ -527,6 +535,94 @@ MBP_HD MBP_INLINE bool gather_exclusive(int32_t S, int32_t rows, double za0, dou
     const double span0 = fabs(zb0 - za0);
     const double span1 = fabs(zb0 - za0 + (double)(rows - 1) * (zb1 - za1));
     return (double)S * fmin(fabs(za1), fabs(zb1)) > 1.0 + 1e-6 && fmax(span0, span1) <= 64.0;
+}
+
+// ------------------------------------------------------------------------------------------
+// Gather work items and the fixed-point row form.
+//
+// One item is one detector column crossing one xy cell in one view: row k's z cell
+// coordinate is za0 + k za1 where it enters the cell and zb0 + k zb1 where it leaves, over a
+// parameter length dt. Items are built by all lanes at once (one view per lane) and then
+// processed one at a time by the whole wave (lanes = rows).
+//
+// The fast form applies when each row's z extent inside the cell is below one cell, so a
+// row has at most two pieces (cells fa and fa + 1), and the rows of one instruction (S
+// apart) are more than two cells apart, so the cell pairs {fa, fa + 1} of different lanes
+// are disjoint. A lane then takes its S consecutive rows relative to an integer origin cell
+// in signed fixed point with kZFrac fraction bits: differences of positions are exact
+// integers, so the share of the lower cell, (distance to the plane above) / extent, keeps
+// full relative precision however flat the row is.
+
+constexpr int kZFrac = 27;
+constexpr int32_t kZOne = 1 << kZFrac;
+constexpr double kZScale = 134217728.0;          // 2^kZFrac
+constexpr int32_t kNotFast = INT32_MIN;
+
+struct GatherItem {
+    double za0, za1;    // z cell coordinate where row k enters the cell: za0 + k za1
+    double zb0, zb1;    // ... and where it leaves: zb0 + k zb1
+    float dt;           // parameter length of the crossing
+    int32_t yoff;       // view * cols + column: the line of the reordered sinogram
+    int32_t a1fx;       // fast form: za1 in fixed point; kNotFast selects the general form
+    int32_t b1fx;       // fast form: zb1 in fixed point; general form: 1 if lanes add exclusively
+};
+
+// Whether an item takes the fast form (rows 0 .. rows_pad - 1, lanes S rows apart, each
+// lane's rows within twelve cells of its first).
+MBP_HD MBP_INLINE bool gather_fast(int32_t S, int32_t rows_pad, double za0, double za1,
+                                   double zb0, double zb1) {
+    const double a = fabs(za1), b = fabs(zb1);
+    const double e0 = fabs(zb0 - za0), e1 = fabs(zb0 - za0 + (double)(rows_pad - 1) * (zb1 - za1));
+    return za1 * zb1 > 0.0 && (double)S * fmin(a, b) > 2.0 + 1e-6 &&
+           (double)(S - 1) * fmax(a, b) <= 12.0 && fmax(e0, e1) < 1.0 - 1e-6;
+}
+
+// The item of column line L crossing the cell, or false when it misses.
+MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, double x1, double y0,
+                                   double y1, int32_t S, int32_t rows, int32_t rows_pad,
+                                   int32_t yoff, GatherItem& it) {
+    double t0, t1;
+    if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) return false;
+    it.za0 = L.c0 + t0 * L.c1;
+    it.za1 = L.c2 + t0 * L.c3;
+    it.zb0 = L.c0 + t1 * L.c1;
+    it.zb1 = L.c2 + t1 * L.c3;
+    it.dt = (float)(t1 - t0);
+    it.yoff = yoff;
+    if (gather_fast(S, rows_pad, it.za0, it.za1, it.zb0, it.zb1)) {
+        it.a1fx = (int32_t)rint(it.za1 * kZScale);
+        it.b1fx = (int32_t)rint(it.zb1 * kZScale);
+    } else {
+        it.a1fx = kNotFast;
+        it.b1fx = gather_exclusive(S, rows, it.za0, it.za1, it.zb0, it.zb1) ? 1 : 0;
+    }
+    return true;
+}
+
+// A lane's origin for the fast form: its first row k (as a double), the integer cell I below
+// that row's lower end and the row's ends relative to I in fixed point. `base` is I minus
+// `cell0` (the cell held at index 0); lanes whose rows are far outside (|I| >= 2^30) get a
+// base that puts every pair out of range.
+MBP_HD MBP_INLINE void fast_origin(const GatherItem& it, double k, int32_t cell0, int32_t& la,
+                                   int32_t& lb, int32_t& base) {
+    const double za = fma(k, it.za1, it.za0), zb = fma(k, it.zb1, it.zb0);
+    const double I = floor(fmin(za, zb));
+    const bool far = !(fabs(I) < 1073741824.0);
+    la = far ? 0 : (int32_t)((za - I) * kZScale);
+    lb = far ? 0 : (int32_t)((zb - I) * kZScale);
+    base = far ? 1073741824 : (int32_t)I - cell0;
+}
+
+// One row of the fast form with ends za, zb (fixed point, relative to the lane origin): the
+// lower cell fa (relative to the origin), and the lower cell's share num / ext of the row when
+// it crosses the plane above fa (split), else the whole row.
+MBP_HD MBP_INLINE void fast_row(int32_t za, int32_t zb, int32_t& fa, int32_t& num, int32_t& ext,
+                                bool& split) {
+    const int32_t lo = za < zb ? za : zb, hi = za < zb ? zb : za;
+    fa = lo >> kZFrac;                              // arithmetic shift: floor
+    num = kZOne - (lo & (kZOne - 1));               // distance from lo to the plane above
+    ext = hi - lo;
+    split = num < ext;
 }
 
 // ------------------------------------------------------------------------------------------

@@ -32,9 +32,9 @@ def _load():
         lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P]
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
-        lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
+        lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, P, P, P]
         lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
-        lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P]
+        lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_gather_conflicts.restype = I64
         lib.mbph_check_rays.restype = I64
         _lib = lib
@@ -131,32 +131,36 @@ def check_rays(path: str, geom: dict, traj: dict, ray_ids) -> tuple:
     return int(visits), int(viol.value)
 
 
-def gather(geom: dict, traj: dict, sino: np.ndarray):
-    """Replay the cell-gather adjoint (fp64 accumulation) on a (views, rows, cols) sinogram."""
+def gather(geom: dict, traj: dict, sino: np.ndarray, kernel_shares: bool = True):
+    """Replay the cell-gather adjoint item by item (fast fixed-point items with fp32 shares as
+    the kernel computes them, or fp64 shares from the same integers; fp64 sums) on a
+    (views, rows, cols) sinogram. Returns (volume, violations, items in the fast form)."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
     rows = int(geom.get("rows", 1))
     views, cols = int(geom["views"]), int(geom["cols"])
     s = np.ascontiguousarray(sino, dtype=np.float32).reshape(views, rows, cols)
     vol = np.zeros(int(n[0]) * int(n[1]) * int(n[2]), dtype=np.float64)
-    viol = ctypes.c_longlong(0)
+    viol, fast = ctypes.c_longlong(0), ctypes.c_longlong(0)
     lib.mbph_gather(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n), views, rows, cols,
-                    float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)), _ptr(s), _ptr(vol),
-                    ctypes.byref(viol))
-    return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value)
+                    float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)), _ptr(s),
+                    int(kernel_shares), _ptr(vol), ctypes.byref(viol), ctypes.byref(fast))
+    return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value), int(fast.value)
 
 
 def gather_conflicts(geom: dict, traj: dict, mode: int = 0):
-    """(exclusive crossings checked, steps whose lanes would add into one z cell twice).
-    mode 0: the kernel's grouping; 1 and 2: planted mistakes (see hostcheck.cpp)."""
+    """(items checked, instructions or steps whose lanes would touch one z cell twice, fast
+    items checked). mode 0: the kernel's grouping; 1 and 2: planted mistakes (see
+    hostcheck.cpp)."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
-    viol = ctypes.c_longlong(0)
+    viol, fast = ctypes.c_longlong(0), ctypes.c_longlong(0)
     checked = lib.mbph_gather_conflicts(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n),
                                         int(geom["views"]), int(geom.get("rows", 1)),
                                         int(geom["cols"]), float(geom.get("du", 1.0)),
-                                        float(geom.get("dv", 1.0)), int(mode), ctypes.byref(viol))
-    return int(checked), int(viol.value)
+                                        float(geom.get("dv", 1.0)), int(mode), ctypes.byref(viol),
+                                        ctypes.byref(fast))
+    return int(checked), int(viol.value), int(fast.value)
 
 
 def project_chunked(geom: dict, traj: dict, vol: np.ndarray):

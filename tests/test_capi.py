@@ -29,6 +29,12 @@ def rows_padded(rows):
     return -(-rows // g) * g
 
 
+def gather_sino_floats(cfg):
+    """Floats per member of the reordered sinogram: every padded line, plus a tail of eight
+    rows that fixed-width row loads may reach past the last line."""
+    return cfg.views * cfg.cols * rows_padded(cfg.rows) + 8
+
+
 def _declared_symbols():
     text = open(os.path.join(ROOT, "include", "mbp.h")).read()
     return sorted(set(re.findall(r"\b(mbp_[a-z_]+)\s*\(", text)))
@@ -93,7 +99,7 @@ def test_configs_plan_and_pick_walks(lib, name):
     else:   # z-fastest volume copy (unless used in place) + reordered sinogram for the gather
         nb = min(4, cfg.members)
         direct = cfg.layout == "WHD" and cfg.members == 1
-        sino = cfg.views * cfg.cols * rows_padded(cfg.rows)
+        sino = gather_sino_floats(cfg)
         assert ws.value == 4 * nb * ((0 if direct else cfg.n_voxels) + sino)
     # view batching: a ragged split into launches of 7 views
     assert lib.mbp_plan_set_view_batch(h, 7) == 0
@@ -216,7 +222,7 @@ def test_python_plan_maps_errors_and_shapes():
                     layout="WHD")
     assert plan.sino_shape == (cfg.views, cfg.rows, cfg.cols)
     assert plan.info["path"] == "column"
-    sino = cfg.views * cfg.cols * rows_padded(cfg.rows)
+    sino = gather_sino_floats(cfg)
     assert plan.workspace_size(1) == 4 * sino
     assert plan.workspace_size(3) == 2 * (cfg.n_voxels + sino) * 4
     plan.set_adjoint("scatter")

@@ -151,6 +151,38 @@ def test_steep_cone_parity(torch_dev, mbp, oracle):
         plan.close()
 
 
+@pytest.mark.parametrize("flip", [False, True])
+def test_tall_detector_parity(torch_dev, mbp, oracle, flip):
+    """Eight rows per lane: the gather's fast fixed-point form (pairs of z cells per row,
+    rows far above and below the volume discarded), for one volume and batches of two and
+    four interleaved members, with detector rows running up or down."""
+    from tests.test_hostcheck import flipped, tall_detector_config
+    torch, dev = torch_dev
+    cfg = tall_detector_config()
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    if flip:
+        traj = flipped(traj)
+    rng = np.random.default_rng(31)
+    x = rng.random(cfg.shape).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    ys = rng.random((4,) + ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    plan = make_plan(mbp, cfg, traj=traj)
+    assert plan.info["path"] == "column"
+    say(f"case tall detector flip={flip} forward")
+    p = plan.project(to_device_volume(torch, dev, x, cfg.layout)).cpu().numpy().astype(np.float64)
+    check(p, ref, "forward")
+    for B in (0, 2, 4):
+        say(f"case tall detector flip={flip} adjoint B={B}")
+        yd = torch.from_numpy(ys[0] if B == 0 else ys[:B]).to(dev)
+        b = plan.backproject(yd).cpu().numpy().astype(np.float64)
+        if B == 0:
+            check(b, bref[0], "adjoint")
+        for m in range(B):
+            check(b[m], bref[m], f"adjoint member {m}")
+    plan.close()
+
+
 def test_general_trajectory_parity(torch_dev, mbp, oracle):
     """Tilted detectors (row axis not parallel to z): the generic walk, anisotropic grid."""
     torch, dev = torch_dev
@@ -208,8 +240,8 @@ def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
     # a caller-owned workspace gives the same result; a too-small one is refused
     plan = make_plan(mbp, cfg)
     need = plan.workspace_size(5)
-    from tests.test_capi import rows_padded
-    assert need == 4 * (cfg.n_voxels + cfg.views * cfg.cols * rows_padded(cfg.rows)) * 4
+    from tests.test_capi import gather_sino_floats
+    assert need == 4 * (cfg.n_voxels + gather_sino_floats(cfg)) * 4
     ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
     plan.set_workspace(ws)
     p = plan.project(torch.from_numpy(xs).to(dev)).cpu().numpy().astype(np.float64)

@@ -93,11 +93,59 @@ def test_cell_gather_reproduces_oracle_adjoint(oracle, name):
     geom, traj = _geom(cfg), config_trajectory(cfg)
     y = np.random.default_rng(2).random((cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
     bref = oracle.backproject(geom, traj, y)
-    b, viol = HC.gather(geom, traj, y)
+    b, viol, _ = HC.gather(geom, traj, y, kernel_shares=False)
     assert viol == 0
     assert np.linalg.norm(b - bref) / np.linalg.norm(bref) < 1e-12
     floor = 1e-6 * np.abs(bref).max()
     assert (np.abs(b - bref) / np.maximum(np.abs(bref), floor)).max() < 1e-9
+
+
+def tall_detector_config():
+    """The small anisotropic cone with a tall detector (460 rows, so eight rows per lane): the
+    gather takes its fast fixed-point form. Most rows pass above or below the volume."""
+    from dataclasses import replace
+    return replace(SMALL_CONFIGS["c4_cone512_aniso"], name="c4t_tall_detector", rows=460, cols=40,
+                   views=12)
+
+
+def flipped(traj):
+    """The same trajectory with detector rows running downwards (z falls as the row grows)."""
+    return dict(traj, ev=-traj["ev"])
+
+
+@pytest.mark.parametrize("flip", [False, True])
+def test_fast_gather_reproduces_oracle_adjoint(oracle, flip):
+    """The fast form (each lane's rows in fixed point relative to an origin cell, the lower
+    cell's share num / ext from exact integer differences) gives the chord lengths to the
+    fixed point's resolution: positions are within ~4e-8 cells (2^-27 steps, the per-row
+    increment rounded, at most seven increments), which moves a split by at most that much;
+    the kernel's fp32 shares add fp32 rounding. Both stay far inside the 1e-4 per-voxel bar."""
+    cfg = tall_detector_config()
+    geom, traj = _geom(cfg), config_trajectory(cfg)
+    if flip:
+        traj = flipped(traj)
+    y = np.random.default_rng(5).random((cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    floor = 1e-6 * np.abs(bref).max()
+    for kernel_shares, tol_l2, tol_max in ((False, 3e-8, 5e-6), (True, 5e-8, 5e-6)):
+        b, viol, fast = HC.gather(geom, traj, y, kernel_shares=kernel_shares)
+        assert viol == 0 and fast > 1000
+        assert np.linalg.norm(b - bref) / np.linalg.norm(bref) < tol_l2
+        assert (np.abs(b - bref) / np.maximum(np.abs(bref), floor)).max() < tol_max
+
+
+@pytest.mark.parametrize("flip", [False, True])
+def test_fast_gather_cell_pairs_never_collide(flip):
+    """In the fast form every instruction reads and writes each lane's cell pair {fa, fa + 1}
+    without atomics: the pairs of the 64 lanes are disjoint. Adjacent rows in one instruction
+    would overlap."""
+    cfg = tall_detector_config()
+    geom, traj = _geom(cfg), config_trajectory(cfg)
+    if flip:
+        traj = flipped(traj)
+    checked, conflicts, fast = HC.gather_conflicts(geom, traj, mode=0)
+    assert fast > 1000 and conflicts == 0
+    assert HC.gather_conflicts(geom, traj, mode=2)[1] > 0
 
 
 @pytest.mark.parametrize("name", ["c3_cone256", "c4_cone512_aniso"])
@@ -107,7 +155,7 @@ def test_gather_plain_lds_adds_never_collide(name):
     instruction instead does collide, so the check has teeth."""
     cfg = SMALL_CONFIGS[name]
     geom, traj = _geom(cfg), config_trajectory(cfg)
-    checked, conflicts = HC.gather_conflicts(geom, traj, mode=0)
+    checked, conflicts, _ = HC.gather_conflicts(geom, traj, mode=0)
     assert checked > 10000 and conflicts == 0
     assert HC.gather_conflicts(geom, traj, mode=2)[1] > 0
 
@@ -125,7 +173,7 @@ def test_gather_steep_rows_walk_aligned():
     the first in-range cell collides."""
     cfg = steep_cone_config()
     geom, traj = _geom(cfg), config_trajectory(cfg)
-    checked, conflicts = HC.gather_conflicts(geom, traj, mode=0)
+    checked, conflicts, _ = HC.gather_conflicts(geom, traj, mode=0)
     assert checked > 1000 and conflicts == 0
     assert HC.gather_conflicts(geom, traj, mode=1)[1] > 0
     assert HC.gather_conflicts(geom, traj, mode=2)[1] > 0
@@ -137,8 +185,10 @@ def test_gather_plain_lds_adds_never_collide_full_size(name):
     sel = [0, cfg.views // 3, (2 * cfg.views) // 3]
     traj = {k: (None if v is None else v[sel]) for k, v in config_trajectory(cfg).items()}
     geom = dict(_geom(cfg), views=len(sel))
-    checked, conflicts = HC.gather_conflicts(geom, traj)
+    checked, conflicts, fast = HC.gather_conflicts(geom, traj)
     assert checked > 100000 and conflicts == 0
+    if name == "c4_cone512_aniso":
+        assert fast == checked          # every crossing of this geometry takes the fast form
 
 
 @pytest.mark.parametrize("which", ["c3_cone256", "c4_cone512_aniso", "c5_helical_b4", "steep"])
