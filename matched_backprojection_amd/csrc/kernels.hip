@@ -451,6 +451,20 @@ __host__ __device__ constexpr int32_t gather_column_floats(int32_t zchunk, int n
     return (zchunk + 4) * nb;
 }
 
+// Cells are dealt in tiles of tx x ty (y fastest inside a tile): the tasks that run at the
+// same time on one XCD then cover a compact patch of the grid, whose shadow on the detector
+// is a few dozen columns in every view, so its waves share sinogram lines in L2 (a line of
+// cells along y would cover the whole detector width in views along x). The launcher picks
+// 16 x 32 when the grid is a whole number of such tiles, else 1 x H (plain y-fastest order).
+__device__ __forceinline__ void gather_tile_cell(uint32_t xy, int32_t H, int32_t tx, int32_t ty,
+                                                 int32_t& ix, int32_t& iy) {
+    const uint32_t per = (uint32_t)(tx * ty);
+    const uint32_t tile = xy / per, within = xy % per;
+    const uint32_t tiles_y = (uint32_t)(H / ty);
+    ix = (int32_t)((tile / tiles_y) * (uint32_t)tx + within / (uint32_t)ty);
+    iy = (int32_t)((tile % tiles_y) * (uint32_t)ty + within % (uint32_t)ty);
+}
+
 // A lane's kGroup consecutive rows starting at row k0 of one sinogram line (rows past the
 // lane's S are loaded and ignored: a fixed count keeps the loads unconditional, so the next
 // unit's loads can be in flight while the current one is summed).
@@ -542,6 +556,7 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
                                                             const float* __restrict__ ysc,
                                                             float* __restrict__ vol,
                                                             int32_t zchunk, int32_t nchunks,
+                                                            int32_t tx, int32_t ty,
                                                             int32_t accumulate) {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -549,10 +564,10 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
     const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
     const uint32_t task = blk * 4u + wave;
     const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
-    const bool live = task < (uint32_t)W * (uint32_t)H * (uint32_t)nchunks;
     const int32_t zc = (int32_t)(task % (uint32_t)nchunks);
-    const uint32_t xy = task / (uint32_t)nchunks;
-    const int32_t iy = (int32_t)(xy % (uint32_t)H), ix = (int32_t)(xy / (uint32_t)H);
+    const bool live = task < (uint32_t)W * (uint32_t)H * (uint32_t)nchunks;
+    int32_t ix, iy;
+    gather_tile_cell(task / (uint32_t)nchunks, H, tx, ty, ix, iy);
     const int32_t z0 = zc * zchunk;
     const int32_t z1 = live ? (z0 + zchunk < D ? z0 + zchunk : D) : z0;
     const int32_t n = z1 - z0;
@@ -886,14 +901,16 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     const int32_t zchunk = gather_zchunk(D, nb);
     const int32_t nchunks = (D + zchunk - 1) / zchunk;
     const uint64_t tasks = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)nchunks;
+    const bool tiled = a.box.n[0] % 16 == 0 && a.box.n[1] % 32 == 0;
+    const int32_t tx = tiled ? 16 : 1, ty = tiled ? 32 : a.box.n[1];
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
                                     (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
     switch (nb) {
-        case 1: column_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;
-        case 2: column_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;
-        case 4: column_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, accumulate); break;
+        case 1: column_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
+        case 2: column_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
+        case 4: column_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
