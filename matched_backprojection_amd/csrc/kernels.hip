@@ -267,34 +267,48 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
             int32_t p = 0;
             if (two_pieces) {
                 // groups of kCellGroup cells: every lane's pieces (at most two per cell: before and
-                // after its single z crossing) first, then all their loads, then the sums
-                for (; p + kCellGroup <= count; p += kCellGroup) {
-                    uint32_t off[2 * kCellGroup];
-                    float len[2 * kCellGroup];
+                // after its single z crossing) first, then all their loads, then the sums. When
+                // the chunk lies inside every lane's slab, the pieces need no clip.
+                const double t_end = count > 0 ? E[count - 1].tb : ta;
+                const bool inside = __all(r.t_lo <= ta && r.t_hi >= t_end);
+                auto groups = [&](auto pieces) {
+                    for (; p + kCellGroup <= count; p += kCellGroup) {
+                        uint32_t off[2 * kCellGroup];
+                        float len[2 * kCellGroup];
 #pragma unroll
-                    for (int q = 0; q < kCellGroup; ++q) {
-                        const double tb = E[p + q].tb;
-                        const uint32_t base = (uint32_t)E[p + q].cxy * D;
-                        int32_t z0, z1;
-                        row_cell_two(r, ta, tb, cz, kz, nz, z0, len[2 * q], z1, len[2 * q + 1]);
-                        off[2 * q] = (base + (uint32_t)z0) * NB;
-                        off[2 * q + 1] = (base + (uint32_t)z1) * NB;
-                        ta = tb;
-                    }
-                    float val[2 * kCellGroup][NB];
-#pragma unroll
-                    for (int q = 0; q < 2 * kCellGroup; ++q) {
-                        if (len[q] != 0.0f) {
-                            load_vals<NB>(vol + off[q], val[q]);
-                        } else {
-#pragma unroll
-                            for (int m = 0; m < NB; ++m) val[q][m] = 0.0f;
+                        for (int q = 0; q < kCellGroup; ++q) {
+                            const double tb = E[p + q].tb;
+                            const uint32_t base = uniform((uint32_t)E[p + q].cxy) * D;
+                            int32_t z0, z1;
+                            pieces(tb, z0, len[2 * q], z1, len[2 * q + 1]);
+                            off[2 * q] = (base + (uint32_t)z0) * NB;
+                            off[2 * q + 1] = (base + (uint32_t)z1) * NB;
+                            ta = tb;
                         }
+                        float val[2 * kCellGroup][NB];
+#pragma unroll
+                        for (int q = 0; q < 2 * kCellGroup; ++q) {
+                            if (len[q] != 0.0f) {
+                                load_vals<NB>(vol + off[q], val[q]);
+                            } else {
+#pragma unroll
+                                for (int m = 0; m < NB; ++m) val[q][m] = 0.0f;
+                            }
+                        }
+#pragma unroll
+                        for (int q = 0; q < 2 * kCellGroup; ++q)
+#pragma unroll
+                            for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
                     }
-#pragma unroll
-                    for (int q = 0; q < 2 * kCellGroup; ++q)
-#pragma unroll
-                        for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
+                };
+                if (inside) {
+                    groups([&](double tb, int32_t& z0, float& l0, int32_t& z1, float& l1) {
+                        row_cell_two_inside(r, ta, tb, cz, kz, nz, z0, l0, z1, l1);
+                    });
+                } else {
+                    groups([&](double tb, int32_t& z0, float& l0, int32_t& z1, float& l1) {
+                        row_cell_two(r, ta, tb, cz, kz, nz, z0, l0, z1, l1);
+                    });
                 }
             }
             for (; p < count; ++p) {
