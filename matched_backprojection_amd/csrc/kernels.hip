@@ -457,12 +457,16 @@ constexpr int kGroup = kGatherGroup;
 // Items a wave queues before it processes them (the queue is drained once it holds more
 // than kQueue - 64, so one more round of 64 always fits).
 constexpr int kQueue = 96;
+// Lanes per view when items are built.
+constexpr int kViewLanes = 4;
 
-// The column of one wave in LDS: index i holds z cell z0 - 1 + i for i in [0, n + 1]
-// (n = z1 - z0; indices 0 and n + 1 are guard cells just outside the chunk, never written
-// out), and indices n + 2, n + 3 are a discard pair for pieces outside the chunk.
+// The column of one wave in LDS, indexed from its guard cell below: index i holds z cell
+// z0 - 1 + i for i in [0, n + 1] (n = z1 - z0; indices 0 and n + 1 are guard cells just
+// outside the chunk, never written out); indices -2, -1 and n + 2 take pieces that fall
+// outside the chunk, so a clamp of the pair index to [-2, n + 1] keeps every pair that
+// touches a chunk cell and parks the rest on cells that are never written out.
 __host__ __device__ constexpr int32_t gather_column_floats(int32_t zchunk, int nb) {
-    return (zchunk + 4) * nb;
+    return (zchunk + 5) * nb;
 }
 
 // Cells are dealt in tiles of tx x ty (y fastest inside a tile): the tasks that run at the
@@ -489,23 +493,26 @@ __device__ __forceinline__ void gather_load_rows(const float* __restrict__ p, fl
 }
 
 // Fast form of one item for one group of rows (see gather_fast): every row adds its two
-// pieces to the disjoint cell pair {fa, fa + 1} with one paired read and write.
-template <int NB>
+// pieces to the disjoint cell pair {fa, fa + 1} with one paired read and write. FULL: the
+// lane takes all kGroup rows (S == kGroup), so the unrolled rows need no guard.
+template <int NB, bool FULL>
 __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
                                                   float dt, const float (&w)[kGroup][NB],
                                                   int32_t k0, int32_t S, int32_t z0, int32_t n,
                                                   float* col) {
-    int32_t la, lb, base;
-    fast_origin(it, (double)k0, z0 - 1, la, lb, base);
+    int32_t za, zb, base;
+    fast_origin(it, (double)k0, z0 - 1, za, zb, base);
 #pragma unroll
     for (int c = 0; c < kGroup; ++c) {
-        if (c >= S) continue;
+        if (!FULL && c >= S) continue;
         int32_t fa, num, ext;
         bool split;
-        fast_row(la + c * a1, lb + c * b1, fa, num, ext, split);
+        fast_row(za, zb, fa, num, ext, split);
+        za += a1;
+        zb += b1;
         const float f = split ? (float)num * __builtin_amdgcn_rcpf((float)ext) : 1.0f;
         const int32_t i0 = base + fa;
-        const int32_t idx = (uint32_t)i0 <= (uint32_t)n ? i0 : n + 2;
+        const int32_t idx = max(min(i0, n + 1), -2);
         float* dst = col + idx * NB;
         float v[2 * NB];
 #pragma unroll
@@ -586,9 +593,10 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
     const int32_t z1 = live ? (z0 + zchunk < D ? z0 + zchunk : D) : z0;
     const int32_t n = z1 - z0;
     const int32_t colf = gather_column_floats(zchunk, NB);
-    GatherItem* Q = reinterpret_cast<GatherItem*>(lds_raw) + wave * kQueue;
-    float* col = reinterpret_cast<float*>(lds_raw + 4 * kQueue * sizeof(GatherItem)) + wave * colf;
-    for (int32_t i = lane; i < colf; i += 64) col[i] = 0.0f;
+    float* const cols = reinterpret_cast<float*>(lds_raw) + wave * colf;
+    float* const col = cols + 2 * NB;                   // the guard cell below the chunk
+    GatherItem* Q = reinterpret_cast<GatherItem*>(lds_raw + 4 * (size_t)colf * sizeof(float)) + wave * kQueue;
+    for (int32_t i = lane; i < colf; i += 64) cols[i] = 0.0f;
     __syncthreads();
     if (live) {
         const double x0 = A.box.lo[0] + ix * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
@@ -620,7 +628,10 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
                 const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
                 if (a1 != kNotFast) {
                     const float dt = __uint_as_float(uniform(__float_as_uint(it.dt)));
-                    gather_fast_group<NB>(it, a1, b1, dt, w, k0, S, z0, n, col);
+                    if (S == kGroup)
+                        gather_fast_group<NB, true>(it, a1, b1, dt, w, k0, S, z0, n, col);
+                    else
+                        gather_fast_group<NB, false>(it, a1, b1, dt, w, k0, S, z0, n, col);
                 } else {
                     gather_general_group<NB>(it, b1 != 0, w, k0, S, z0, z1, col);
                 }
@@ -631,11 +642,14 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
             }
         };
 
-        // Items: each lane takes one view of a round of 64 and walks its candidate columns;
-        // the crossings found are appended to the queue in lane order.
+        // Items: kViewLanes lanes take one view of a round of 64 / kViewLanes and walk its
+        // candidate columns, lane r of a view taking candidates j0 + r, j0 + r + kViewLanes, ...;
+        // the crossings found are appended to the queue in lane order. A round spans few
+        // views, so the sinogram lines the concurrently running waves of a tile read stay few
+        // enough to share L2.
         int32_t count = 0;
-        for (int32_t vb = A.view0; vb < vend; vb += 64) {
-            const int32_t view = vb + lane;
+        for (int32_t vb = A.view0; vb < vend; vb += 64 / kViewLanes) {
+            const int32_t view = vb + lane / kViewLanes;
             int32_t jn = 0, j1 = -1;
             if (view < vend &&
                 !cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, jn, j1)) {
@@ -643,13 +657,14 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
                 j1 = -1;
             }
             if (view >= vend) j1 = -1;
+            jn += lane % kViewLanes;
             while (__ballot(jn <= j1) != 0) {
                 GatherItem it;
                 bool hit = false;
                 if (jn <= j1) {
                     const int32_t yoff = view * A.cols + jn;
                     hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff, it);
-                    ++jn;
+                    jn += kViewLanes;
                 }
                 const uint64_t m = __ballot(hit);
                 if (hit) {
