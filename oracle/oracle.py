@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-bas
 import this module; the library under test never does, and this module never imports it.
 
 All functions take plain numpy arrays:
-- ``geom``: a dict with ``beam`` ("parallel" | "fan" | "cone"), ``shape`` (tensor order,
+- ``geom``: a dict with ``beam`` ("parallel" | "fan" | "cone" | "parallel3d"), ``shape`` (tensor order,
   ``(H, W)`` or ``(D, H, W)``), ``spacing`` (tensor order), optional ``center`` (world x, y, z),
   ``views``, ``rows``, ``cols``, ``du``, ``dv``;
 - ``traj``: a dict of float64 arrays ``src``, ``det``, ``eu`` and ``ev`` (``None`` for 2-D),
@@ -24,7 +24,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "siddon_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
-_BEAMS = {"parallel": 0, "fan": 1, "cone": 2}
+_BEAMS = {"parallel": 0, "fan": 1, "cone": 2, "parallel3d": 3}
+_BEAMS_3D = ("cone", "parallel3d")
 
 
 class _Geom(ctypes.Structure):
@@ -82,7 +83,7 @@ def _geom(geom: dict) -> _Geom:
     beam = geom["beam"]
     shape = tuple(int(s) for s in geom["shape"])
     spacing = tuple(float(s) for s in geom["spacing"])
-    if beam == "cone":
+    if beam in _BEAMS_3D:
         D, H, W = shape
         dz, dy, dx = spacing
     else:
@@ -97,7 +98,7 @@ def _geom(geom: dict) -> _Geom:
 
 
 def _traj(traj: dict, beam: str):
-    rank = 3 if beam == "cone" else 2
+    rank = 3 if beam in _BEAMS_3D else 2
     arrs = []
     for key in ("src", "det", "eu", "ev"):
         a = traj.get(key)
@@ -127,7 +128,7 @@ def _vol_batch(vol: np.ndarray, ndim: int):
 
 
 def _sino_shape(g: _Geom, beam: str):
-    return (g.views, g.rows, g.cols) if beam == "cone" else (g.views, g.cols)
+    return (g.views, g.rows, g.cols) if beam in _BEAMS_3D else (g.views, g.cols)
 
 
 def _check(rc: int, what: str):
@@ -140,7 +141,7 @@ def project(geom: dict, traj: dict, vol: np.ndarray, threads: int = 0, counts: b
     lib = _load()
     g = _geom(geom)
     beam = geom["beam"]
-    ndim = 3 if beam == "cone" else 2
+    ndim = 3 if beam in _BEAMS_3D else 2
     vol, B, batched = _vol_batch(vol, ndim)
     src, det, eu, ev = _traj(traj, beam)
     sshape = _sino_shape(g, beam)
@@ -158,7 +159,7 @@ def project_rays(geom: dict, traj: dict, vol: np.ndarray, ray_ids, threads: int 
     lib = _load()
     g = _geom(geom)
     beam = geom["beam"]
-    ndim = 3 if beam == "cone" else 2
+    ndim = 3 if beam in _BEAMS_3D else 2
     vol, B, batched = _vol_batch(vol, ndim)
     src, det, eu, ev = _traj(traj, beam)
     ids = np.ascontiguousarray(ray_ids, dtype=np.int64)

@@ -31,7 +31,9 @@
  *    tuples are on page "diffct 2.1.0 -> 2.2.1", diffct/analytical.py);
  *  - fan/cone rays are the segments source -> pixel (parameter in [0, 1]); parallel rays are
  *    infinite lines through the pixel along the per-view ray direction (page
- *    "diffct 2.2.1 -> 2.4.0", CHANGELOG 2.4.0: infinite parallel rays);
+ *    "diffct 2.2.1 -> 2.4.0", CHANGELOG 2.4.0: infinite parallel rays; the same page adds a
+ *    3-D parallel beam, "parallel3d", whose rays are such lines through the pixels of a flat
+ *    2-D detector);
  *  - cells are half-open [lo, hi): a ray lying exactly in a grid plane belongs to the cell
  *    above it; a ray with a zero direction component outside [lo, hi) on that axis misses.
  */
@@ -43,12 +45,12 @@
 #include <omp.h>
 #endif
 
-enum { ORC_PARALLEL = 0, ORC_FAN = 1, ORC_CONE = 2 };
+enum { ORC_PARALLEL = 0, ORC_FAN = 1, ORC_CONE = 2, ORC_PARALLEL3D = 3 };
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ENOMEM = -2, ORC_ECAP = -3 };
 
 /* Geometry, in tensor order as the caller holds it. Mirrored by oracle/oracle.py. */
 typedef struct {
-    int32_t beam;          /* ORC_PARALLEL, ORC_FAN (2-D) or ORC_CONE (3-D)      */
+    int32_t beam;          /* ORC_PARALLEL, ORC_FAN (2-D), ORC_CONE, ORC_PARALLEL3D (3-D) */
     int32_t pad_;
     int64_t D, H, W;       /* volume shape; 2-D beams: D == 1                     */
     double dz, dy, dx;     /* voxel pitch; 2-D beams ignore dz                    */
@@ -77,7 +79,14 @@ typedef struct {
     double tmin, tmax;     /* parameter range before clipping                         */
 } ray_t;
 
-static int rank_of(const orc_geom *g) { return g->beam == ORC_CONE ? 3 : 2; }
+static int rank_of(const orc_geom *g) {
+    return g->beam == ORC_CONE || g->beam == ORC_PARALLEL3D ? 3 : 2;
+}
+
+/* Parallel beams (2-D and 3-D) have infinite lines for rays; fan and cone have segments. */
+static int is_line(const orc_geom *g) {
+    return g->beam == ORC_PARALLEL || g->beam == ORC_PARALLEL3D;
+}
 
 static void make_box(const orc_geom *g, box_t *b) {
     b->rank = rank_of(g);
@@ -101,7 +110,7 @@ static void make_ray(const orc_geom *g, const orc_traj *t, int64_t view, int64_t
         if (R == 3) p[a] += v * t->ev[view * R + a];
     }
     for (int a = 0; a < 3; ++a) { r->a[a] = 0.0; r->d[a] = 0.0; }
-    if (g->beam == ORC_PARALLEL) {
+    if (is_line(g)) {
         for (int a = 0; a < R; ++a) { r->a[a] = p[a]; r->d[a] = t->src[view * R + a]; }
         r->tmin = -INFINITY; r->tmax = INFINITY;
     } else {
@@ -231,9 +240,11 @@ static int64_t siddon(const box_t *b, const ray_t *r, seg_visit visit, void *ctx
 
 static int check(const orc_geom *g, const orc_traj *t) {
     if (!g || !t || !t->src || !t->det || !t->eu) return ORC_EINVAL;
-    if (g->beam != ORC_PARALLEL && g->beam != ORC_FAN && g->beam != ORC_CONE) return ORC_EINVAL;
-    if (g->beam == ORC_CONE && !t->ev) return ORC_EINVAL;
-    if (g->beam != ORC_CONE && (g->D != 1 || g->rows != 1)) return ORC_EINVAL;
+    if (g->beam != ORC_PARALLEL && g->beam != ORC_FAN && g->beam != ORC_CONE &&
+        g->beam != ORC_PARALLEL3D)
+        return ORC_EINVAL;
+    if (rank_of(g) == 3 && !t->ev) return ORC_EINVAL;
+    if (rank_of(g) == 2 && (g->D != 1 || g->rows != 1)) return ORC_EINVAL;
     if (g->D < 1 || g->H < 1 || g->W < 1 || g->views < 0 || g->rows < 1 || g->cols < 1)
         return ORC_EINVAL;
     if (!(g->dx > 0) || !(g->dy > 0) || !(g->dz > 0)) return ORC_EINVAL;
@@ -452,12 +463,16 @@ static int project_point(const orc_geom *g, const orc_traj *t, int64_t view, con
         *v = 0.0;
         return 1;
     }
+    /* det + u*eu + v*ev = base + s*w, with (w, base) = (r, c) for a parallel beam (the line
+       through c along the ray direction r) or (c - src, src) for a cone (the ray from the
+       source through c) */
     const double *ev = t->ev + view * 3;
     double A[3][3], rhs[3], x[3];
     for (int a = 0; a < 3; ++a) {
-        double w = c[a] - src[a];
+        const double w = is_line(g) ? src[a] : c[a] - src[a];
+        const double base = is_line(g) ? c[a] : src[a];
         A[a][0] = eu[a]; A[a][1] = ev[a]; A[a][2] = -w;
-        rhs[a] = src[a] - det[a];
+        rhs[a] = base - det[a];
     }
     if (!solve3(A, rhs, x)) return 0;
     *u = x[0]; *v = x[1]; *s = x[2];
@@ -472,7 +487,6 @@ int orc_backproject_voxels(const orc_geom *g, const double *src, const double *d
     int rc = check(g, &t);
     if (rc) return rc;
     if (batch < 0 || (n > 0 && (!vox_ids || !out)) || (batch > 0 && !sino)) return ORC_EINVAL;
-    if (g->beam == ORC_PARALLEL && rank_of(g) == 3) return ORC_EINVAL;
     box_t b;
     make_box(g, &b);
     const int R = b.rank;
@@ -501,7 +515,7 @@ int orc_backproject_voxels(const orc_geom *g, const double *src, const double *d
                                 (m & 4) ? vhi[2] : vlo[2] };
                 double u, v, s;
                 if (!project_point(g, &t, view, c, &u, &v, &s)) { ok = 0; break; }
-                if (g->beam != ORC_PARALLEL && !(s > 0.0)) { ok = 0; break; }
+                if (!is_line(g) && !(s > 0.0)) { ok = 0; break; }
                 double jj = u / g->du + 0.5 * (double)(g->cols - 1);
                 double kk = R == 3 ? v / g->dv + 0.5 * (double)(g->rows - 1) : 0.0;
                 if (jj < jlo) jlo = jj;

@@ -7,7 +7,8 @@ len(r, v) = |ray r  intersected with  voxel v|.
 
 Conventions follow the shared reading of the diffct pages: world x <-> W, y <-> H, z <-> D;
 volume box centred on ``center``; pixel (k, j) at det + u_j*eu + v_k*ev with centred u_j, v_k;
-fan/cone rays are segments source -> pixel, parallel rays are full lines; cells are half-open.
+fan/cone rays are segments source -> pixel, parallel rays (2-D and 3-D) are full lines; cells
+are half-open.
 """
 
 from __future__ import annotations
@@ -18,7 +19,7 @@ import numpy as np
 def rays_of(geom: dict, traj: dict):
     """List of (start, direction, tmin, tmax) in world coordinates, ray order view, row, col."""
     beam = geom["beam"]
-    rank = 3 if beam == "cone" else 2
+    rank = 3 if beam in ("cone", "parallel3d") else 2
     rows = int(geom.get("rows", 1))
     cols = int(geom["cols"])
     du = float(geom.get("du", 1.0))
@@ -34,7 +35,7 @@ def rays_of(geom: dict, traj: dict):
             for j in range(cols):
                 u = (j - (cols - 1) / 2.0) * du
                 p = det + u * eu + (v * ev if ev is not None else 0.0)
-                if beam == "parallel":
+                if beam in ("parallel", "parallel3d"):
                     out.append((p, src.copy(), -np.inf, np.inf))
                 else:
                     out.append((src.copy(), p - src, 0.0, 1.0))
@@ -59,7 +60,7 @@ def voxel_boxes(geom: dict):
         ia = idx[rank - 1 - a]
         lo[:, a] = lo0[a] + ia * pitch[a]
         hi[:, a] = lo0[a] + (ia + 1) * pitch[a]
-    assert beam in ("parallel", "fan", "cone")
+    assert beam in ("parallel", "fan", "cone", "parallel3d")
     return lo, hi
 
 

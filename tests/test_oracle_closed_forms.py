@@ -6,6 +6,8 @@ O4  2-D parallel beam at 0 and 90 degrees gives exact row and column sums;
 O5  parallel sinogram symmetries (90-degree rotation, mirror, half-turn reversal);
 O8  a single-voxel phantom lights exactly the pixels whose rays cross the voxel, around the
     central projection of the voxel centre;
+O10 3-D parallel beam: horizontal rays with the row axis along z stay inside one z slice and
+    reduce to the 2-D parallel transform of that slice; rays along z give column sums;
 golden hand-derived cases in tests/golden/hand_cases.json.
 """
 
@@ -16,7 +18,8 @@ import numpy as np
 import pytest
 
 from tests._brute import box_chords, ray_arrays
-from workloads import (CONFIGS, SMALL_CONFIGS, config_trajectory, parallel_2d_trajectory)
+from workloads import (CONFIGS, SMALL_CONFIGS, config_trajectory, parallel_2d_trajectory,
+                       parallel_3d_trajectory)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
 
@@ -165,3 +168,45 @@ def test_single_voxel_phantom(oracle):
         assert p[view, k, j] > 0.5 * p[view].max()
         nz = np.argwhere(p[view] > 0)
         assert np.abs(nz[:, 0] - k).max() <= 2 and np.abs(nz[:, 1] - j).max() <= 2
+
+
+def test_parallel3d_reduces_to_2d_slices(oracle):
+    """O10: with ev = z and horizontal ray directions, detector row k at height v_k (mid-slice
+    by construction) sees exactly z slice k, so its sinogram row is the 2-D parallel
+    projection of that slice with the same angles, columns and pitches. Checked both ways
+    (forward and adjoint)."""
+    rng = np.random.default_rng(13)
+    D, H, W = 6, 10, 12
+    spacing = (1.5, 1.0, 0.75)
+    x = rng.random((D, H, W)).astype(np.float32)
+    views, cols, du = 9, 17, 0.8
+    g3 = {"beam": "parallel3d", "shape": (D, H, W), "spacing": spacing, "views": views,
+          "rows": D, "cols": cols, "du": du, "dv": spacing[0]}
+    g2 = {"beam": "parallel", "shape": (H, W), "spacing": spacing[1:], "views": views,
+          "rows": 1, "cols": cols, "du": du}
+    t3 = parallel_3d_trajectory(views)
+    t2 = parallel_2d_trajectory(views)
+    np.testing.assert_array_equal(t3["src"][:, :2], t2["src"])
+    p3 = oracle.project(g3, t3, x)
+    for k in range(D):
+        np.testing.assert_allclose(p3[:, k, :], oracle.project(g2, t2, x[k]), rtol=0, atol=1e-12)
+    y = rng.random((views, D, cols)).astype(np.float32)
+    b3 = oracle.backproject(g3, t3, y)
+    for k in range(D):
+        np.testing.assert_allclose(b3[k], oracle.backproject(g2, t2, y[:, k, :]), rtol=0, atol=1e-12)
+    assert np.abs(p3).max() > 1.0
+
+
+def test_parallel3d_axial_rays_give_column_sums(oracle):
+    """O10: rays along +z through voxel centres (eu = x, ev = y, pitches equal to the voxel
+    pitches) integrate each (y, x) column: P[row iy, col ix] = dz * sum_z x[z, iy, ix]."""
+    rng = np.random.default_rng(14)
+    D, H, W = 5, 4, 6
+    spacing = (1.25, 0.5, 0.75)
+    x = rng.random((D, H, W)).astype(np.float32)
+    g = {"beam": "parallel3d", "shape": (D, H, W), "spacing": spacing, "views": 1,
+         "rows": H, "cols": W, "du": spacing[2], "dv": spacing[1]}
+    t = {"src": np.array([[0.0, 0.0, 1.0]]), "det": np.array([[0.0, 0.0, -7.0]]),
+         "eu": np.array([[1.0, 0.0, 0.0]]), "ev": np.array([[0.0, 1.0, 0.0]])}
+    p = oracle.project(g, t, x)
+    np.testing.assert_allclose(p[0], spacing[0] * x.astype(np.float64).sum(axis=0), rtol=1e-14)

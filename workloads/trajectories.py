@@ -107,6 +107,47 @@ def random_cone_trajectory(views: int, seed: int, radius: float = 150.0,
     return {"src": src, "det": det, "eu": eu, "ev": ev}
 
 
+def parallel_3d_trajectory(views: int, tilt: float = 0.0) -> dict:
+    """3-D parallel beam on a circle: view k looks along (cos t, sin t, 0), t = k*pi/views, at
+    a detector through the origin with eu = (-sin t, cos t, 0) and ev = z; with tilt != 0 the
+    detector axes are rotated by `tilt` radians about the viewing direction (ev no longer
+    parallel to z)."""
+    theta = np.arange(views, dtype=np.float64) * (np.pi / views)
+    c, s = np.cos(theta), np.sin(theta)
+    zero = np.zeros(views)
+    a = np.stack([-s, c, zero], axis=1)
+    b = np.tile([0.0, 0.0, 1.0], (views, 1))
+    return {
+        "src": np.stack([c, s, zero], axis=1),           # ray direction
+        "det": np.zeros((views, 3), dtype=np.float64),
+        "eu": np.cos(tilt) * a + np.sin(tilt) * b,
+        "ev": -np.sin(tilt) * a + np.cos(tilt) * b,
+    }
+
+
+def random_parallel_3d_trajectory(views: int, seed: int, tilt: float = 0.35,
+                                  offset: float = 2.0) -> dict:
+    """General 3-D parallel beam: per view (draw order) a ray direction from 3 normals
+    (normalised), a detector-u axis from 3 normals (orthogonalised against it), one in-plane
+    tilt U[-tilt, tilt] rotating (u, v) about the direction, and a detector centre offset from
+    3 normals times `offset`."""
+    rng = np.random.default_rng(seed)
+    out = {k: np.empty((views, 3)) for k in ("src", "det", "eu", "ev")}
+    for i in range(views):
+        w = rng.standard_normal(3)
+        w /= np.linalg.norm(w)
+        a = rng.standard_normal(3)
+        a -= a.dot(w) * w
+        a /= np.linalg.norm(a)
+        b = np.cross(w, a)
+        phi = rng.uniform(-tilt, tilt)
+        out["src"][i] = w
+        out["eu"][i] = np.cos(phi) * a + np.sin(phi) * b
+        out["ev"][i] = -np.sin(phi) * a + np.cos(phi) * b
+        out["det"][i] = offset * rng.standard_normal(3)
+    return out
+
+
 def config_trajectory(cfg: Config) -> dict:
     if cfg.beam == "parallel":
         return parallel_2d_trajectory(cfg.views)
