@@ -65,18 +65,21 @@ typedef enum mbp_status {
 typedef enum mbp_beam {
     MBP_PARALLEL = 0,      /* 2-D parallel beam: volume (H, W), D = 1, rows = 1             */
     MBP_FAN = 1,           /* 2-D fan beam, flat (line) detector: D = 1, rows = 1           */
-    MBP_CONE = 2           /* 3-D cone beam, flat detector                                   */
+    MBP_CONE = 2,          /* 3-D cone beam, flat detector                                   */
+    MBP_PARALLEL3D = 3     /* 3-D parallel beam, flat detector: infinite parallel rays, one
+                              direction per view (page "diffct 2.2.1 -> 2.4.0", CHANGELOG
+                              2.4.0, "Added")                                                */
 } mbp_beam;
 
 typedef enum mbp_layout {
     MBP_LAYOUT_DHW = 0,    /* W fastest (C order of (D, H, W))                               */
-    MBP_LAYOUT_WHD = 1     /* D fastest; cone beams only                                     */
+    MBP_LAYOUT_WHD = 1     /* D fastest; 3-D beams only                                      */
 } mbp_layout;
 
 typedef enum mbp_path {
     MBP_PATH_AUTO = 0,     /* pick the column walk when the geometry allows it               */
     MBP_PATH_GENERIC = 1,  /* one lane per ray, full 3-D walk, any flat-detector geometry    */
-    MBP_PATH_COLUMN = 2    /* cone beam whose detector row axis is parallel to z: the rows of
+    MBP_PATH_COLUMN = 2    /* 3-D beam whose detector row axis is parallel to z: the rows of
                               a detector column share their xy walk                          */
 } mbp_path;
 
@@ -115,9 +118,9 @@ typedef struct mbp_plan_info {
 } mbp_plan_info;
 
 /* Validate the geometry and trajectory and build a plan. Trajectory arrays are host fp64,
-   row-major [views][rank] with rank 3 for cone and 2 for 2-D beams: src = source position
-   (fan/cone) or ray direction (parallel); det = detector centre; eu, ev = detector axes
-   (ev NULL for 2-D beams). The arrays are copied; no device call is made here (frames are
+   row-major [views][rank] with rank 3 for 3-D beams (cone, parallel3d) and 2 for 2-D beams:
+   src = source position (fan/cone) or ray direction (parallel, parallel3d; any nonzero
+   length); det = detector centre; eu, ev = detector axes (ev NULL for 2-D beams). The arrays are copied; no device call is made here (frames are
    staged to device memory on first use on each device). On success *out owns the plan. */
 int mbp_plan_create(const mbp_geometry* geometry, const double* src, const double* det,
                     const double* eu, const double* ev, mbp_plan** out);

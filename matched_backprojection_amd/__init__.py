@@ -47,14 +47,15 @@ class Plan:
 
     Parameters
     ----------
-    beam: "parallel" | "fan" (2-D) or "cone" (3-D).
+    beam: "parallel" | "fan" (2-D) or "cone" | "parallel3d" (3-D).
     volume_shape: ``(H, W)`` or ``(D, H, W)``.
     voxel_spacing: scalar or per axis in tensor order, ``(dy, dx)`` / ``(dz, dy, dx)``.
-    trajectory: dict with ``src`` (source, or ray direction for "parallel"), ``det``
-        (detector centre), ``eu`` and, for cones, ``ev`` (detector axes), each ``(views, rank)``.
+    trajectory: dict with ``src`` (source, or ray direction for the parallel beams), ``det``
+        (detector centre), ``eu`` and, for 3-D beams, ``ev`` (detector axes), each
+        ``(views, rank)``.
     detector_shape: ``cols`` (2-D) or ``(rows, cols)``.
     detector_spacing: ``du`` (2-D) or ``(dv, du)``.
-    layout: "DHW" (C order) or "WHD" (z fastest, cone only) for the caller's volumes.
+    layout: "DHW" (C order) or "WHD" (z fastest, 3-D beams only) for the caller's volumes.
     center: world position of the volume centre.
     """
 
@@ -66,7 +67,7 @@ class Plan:
             raise ValueError(f"beam must be one of {sorted(_capi.BEAMS)}")
         if layout not in _capi.LAYOUTS:
             raise ValueError(f"layout must be one of {sorted(_capi.LAYOUTS)}")
-        cone = beam == "cone"
+        cone = beam in _capi.BEAMS_3D        # a 3-D beam: (D, H, W) volume, (rows, cols) detector
         rank = 3 if cone else 2
         shape = tuple(int(s) for s in volume_shape)
         if len(shape) != rank:
@@ -256,7 +257,7 @@ def project(volume, voxel_spacing, trajectory: dict, detector, beam: str = "cone
     """One-shot ``project(volume[D,H,W], voxel_spacing, trajectory[views], detector)``.
 
     ``detector`` is ``(detector_shape, detector_spacing)`` as in :class:`Plan`."""
-    nd = 3 if beam == "cone" else 2
+    nd = 3 if beam in _capi.BEAMS_3D else 2
     plan = _plan_from(tuple(volume.shape[-nd:]), voxel_spacing, trajectory, detector, beam, layout, center)
     return plan.project(volume)
 

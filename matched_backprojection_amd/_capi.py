@@ -20,7 +20,8 @@ MBP_ETOOLARGE = -5
 MBP_EHIP = -6
 MBP_ENOMEM = -7
 
-BEAMS = {"parallel": 0, "fan": 1, "cone": 2}
+BEAMS = {"parallel": 0, "fan": 1, "cone": 2, "parallel3d": 3}
+BEAMS_3D = ("cone", "parallel3d")
 LAYOUTS = {"DHW": 0, "WHD": 1}
 PATHS = {"auto": 0, "generic": 1, "column": 2}
 PATH_NAMES = {v: k for k, v in PATHS.items()}

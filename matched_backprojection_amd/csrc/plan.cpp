@@ -108,16 +108,17 @@ int64_t views_per_launch(const mbp_plan* p) {
 // Geometry checks of one plan; `frames` already hold the 3-D frames.
 int validate_frames(const mbp_plan& P) {
     const mbp_geometry& g = P.g;
+    const bool three_d = g.beam == MBP_CONE || g.beam == MBP_PARALLEL3D;
     const bool cone = g.beam == MBP_CONE;
     double minp = std::min(g.spacing[1], g.spacing[2]);
-    if (cone) minp = std::min(minp, g.spacing[0]);
-    const double ctr[3] = {g.center[0], g.center[1], cone ? g.center[2] : 0.0};
+    if (three_d) minp = std::min(minp, g.spacing[0]);
+    const double ctr[3] = {g.center[0], g.center[1], three_d ? g.center[2] : 0.0};
     for (int64_t i = 0; i < g.views; ++i) {
         const Frame& F = P.frames[(size_t)i];
         double un = 0, vn = 0, sn = 0;
         for (int a = 0; a < 3; ++a) { un += F.u[a] * F.u[a]; vn += F.v[a] * F.v[a]; sn += F.s[a] * F.s[a]; }
         if (un == 0.0) return fail(MBP_ECOINCIDENT, "view %lld: detector u axis must be nonzero (axes must differ from zero)", (long long)i);
-        if (cone) {
+        if (three_d) {
             if (vn == 0.0) return fail(MBP_ECOINCIDENT, "view %lld: detector v axis must be nonzero", (long long)i);
             const double cx = F.u[1] * F.v[2] - F.u[2] * F.v[1];
             const double cy = F.u[2] * F.v[0] - F.u[0] * F.v[2];
@@ -129,7 +130,7 @@ int validate_frames(const mbp_plan& P) {
             if (std::fabs(F.c[a] - ctr[a]) > kFar * minp)
                 return fail(MBP_ERANGE, "view %lld: detector centre is farther than 1e15 voxel pitches (far geometry)", (long long)i);
         }
-        if (g.beam == MBP_PARALLEL) {
+        if (g.beam == MBP_PARALLEL || g.beam == MBP_PARALLEL3D) {
             if (sn == 0.0) return fail(MBP_ECOINCIDENT, "view %lld: ray direction must differ from zero", (long long)i);
             continue;
         }
@@ -181,11 +182,18 @@ int validate_frames(const mbp_plan& P) {
 
 bool column_ok(const mbp_plan& P) {
     const mbp_geometry& g = P.g;
-    if (g.beam != MBP_CONE) return false;
+    if (g.beam != MBP_CONE && g.beam != MBP_PARALLEL3D) return false;
     const double minp = std::min(g.spacing[0], std::min(g.spacing[1], g.spacing[2]));
     for (int64_t i = 0; i < g.views; ++i) {
         const Frame& F = P.frames[(size_t)i];
         if (F.v[0] != 0.0 || F.v[1] != 0.0) return false;
+        if (g.beam == MBP_PARALLEL3D) {
+            // the rays' common xy direction must not vanish against their length
+            const double sxy = std::sqrt(F.s[0] * F.s[0] + F.s[1] * F.s[1]);
+            const double sn = std::sqrt(sxy * sxy + F.s[2] * F.s[2]);
+            if (!(sxy > 1e-6 * sn)) return false;
+            continue;
+        }
         for (int64_t j = 0; j < g.cols; ++j) {
             const double u = mbp::centred((int32_t)j, (int32_t)g.cols, g.du);
             const double px = F.c[0] + u * F.u[0], py = F.c[1] + u * F.u[1];
@@ -214,6 +222,13 @@ DeviceState* device_state(mbp_plan* p, int* rc) {
     return &p->devs.back();
 }
 
+// Ray kind the kernels take: lines for both parallel beams, segments from the source for
+// fan and cone.
+int32_t kernel_beam(const mbp_geometry& g) {
+    if (g.beam == MBP_PARALLEL || g.beam == MBP_PARALLEL3D) return mbp::BEAM_PARALLEL;
+    return g.beam == MBP_FAN ? mbp::BEAM_FAN : mbp::BEAM_CONE;
+}
+
 mbp::GenericLaunch generic_args(const mbp_plan* p, const DeviceState* d, int32_t whd) {
     const mbp_geometry& g = p->g;
     mbp::GenericLaunch a{};
@@ -222,7 +237,7 @@ mbp::GenericLaunch generic_args(const mbp_plan* p, const DeviceState* d, int32_t
     a.cols = (int32_t)g.cols;
     a.du = g.du;
     a.dv = g.dv;
-    a.beam = g.beam;
+    a.beam = kernel_beam(g);
     a.box = p->box;
     const int32_t D = (int32_t)g.D, H = (int32_t)g.H, W = (int32_t)g.W;
     if (whd) { a.sz = 1; a.sy = D; a.sx = D * H; }
@@ -237,7 +252,7 @@ mbp::ColumnLaunch column_args(const mbp_plan* p, const DeviceState* d) {
     a.rows = (int32_t)g.rows;
     a.cols = (int32_t)g.cols;
     a.row_blocks = (int32_t)((g.rows + 63) / 64);
-    a.beam = g.beam;
+    a.beam = kernel_beam(g);
     a.du = g.du;
     a.dv = g.dv;
     a.box = p->box;
@@ -385,11 +400,11 @@ int mbp_plan_create(const mbp_geometry* geometry, const double* src, const doubl
     *out = nullptr;
     if (!geometry) return fail(MBP_EINVAL, "geometry must be non-NULL");
     const mbp_geometry g = *geometry;
-    if (g.beam != MBP_PARALLEL && g.beam != MBP_FAN && g.beam != MBP_CONE)
-        return fail(MBP_EINVAL, "beam must be MBP_PARALLEL, MBP_FAN or MBP_CONE (got %d)", g.beam);
+    if (g.beam != MBP_PARALLEL && g.beam != MBP_FAN && g.beam != MBP_CONE && g.beam != MBP_PARALLEL3D)
+        return fail(MBP_EINVAL, "beam must be MBP_PARALLEL, MBP_FAN, MBP_CONE or MBP_PARALLEL3D (got %d)", g.beam);
     if (g.layout != MBP_LAYOUT_DHW && g.layout != MBP_LAYOUT_WHD)
         return fail(MBP_EINVAL, "layout must be MBP_LAYOUT_DHW or MBP_LAYOUT_WHD (got %d)", g.layout);
-    const bool cone = g.beam == MBP_CONE;
+    const bool cone = g.beam == MBP_CONE || g.beam == MBP_PARALLEL3D;   // a 3-D beam
     if (!cone && (g.D != 1 || g.rows != 1))
         return fail(MBP_EINVAL, "2-D beams need D == 1 and rows == 1");
     if (!cone && g.layout != MBP_LAYOUT_DHW)
@@ -442,7 +457,7 @@ int mbp_plan_create(const mbp_geometry* geometry, const double* src, const doubl
                 F.u[a] = eu[i * R + a];
                 F.v[a] = cone ? ev[i * R + a] : 0.0;
             } else {   // 2-D beams: rays in the plane z = centre z of a one-cell-thick slab
-                F.s[a] = g.beam == MBP_PARALLEL ? 0.0 : cz;
+                F.s[a] = g.beam == MBP_PARALLEL ? 0.0 : cz;   // (2-D beams only reach here)
                 F.c[a] = cz;
                 F.u[a] = 0.0;
                 F.v[a] = 0.0;
@@ -500,7 +515,7 @@ int mbp_plan_set_path(mbp_plan* plan, int32_t path) {
     if (path != MBP_PATH_AUTO && path != MBP_PATH_GENERIC && path != MBP_PATH_COLUMN)
         return fail(MBP_EINVAL, "unknown path %d", path);
     if (path == MBP_PATH_COLUMN && !plan->column_capable)
-        return fail(MBP_EINVAL, "the column walk needs a cone beam whose detector row axis is parallel to z");
+        return fail(MBP_EINVAL, "the column walk needs a 3-D beam whose detector row axis is parallel to z");
     plan->forced_path = path;
     return MBP_OK;
 }

@@ -41,11 +41,14 @@ def _load():
     return _lib
 
 
+_BEAMS_3D = ("cone", "parallel3d")
+
+
 def frames(geom: dict, traj: dict) -> np.ndarray:
     """Per-view (s, c, u, v) in 3-D, as the plan stages them (2-D: rays in the plane z = 0)."""
     views = int(geom["views"])
     f = np.zeros((views, 12), dtype=np.float64)
-    rank = 3 if geom["beam"] == "cone" else 2
+    rank = 3 if geom["beam"] in _BEAMS_3D else 2
     f[:, 0:rank] = traj["src"]
     f[:, 3:3 + rank] = traj["det"]
     f[:, 6:6 + rank] = traj["eu"]
@@ -57,7 +60,7 @@ def frames(geom: dict, traj: dict) -> np.ndarray:
 def box(geom: dict):
     shape = tuple(int(s) for s in geom["shape"])
     spacing = tuple(float(s) for s in geom["spacing"])
-    if geom["beam"] == "cone":
+    if geom["beam"] in _BEAMS_3D:
         n = (shape[2], shape[1], shape[0])
         p = (spacing[2], spacing[1], spacing[0])
     else:
@@ -68,7 +71,8 @@ def box(geom: dict):
     return lo, np.array(p, dtype=np.float64), np.array(n, dtype=np.int32)
 
 
-_BEAM = {"parallel": 0, "fan": 1, "cone": 2}
+# the kernels' ray kinds: lines (both parallel beams), fan and cone segments
+_BEAM = {"parallel": 0, "fan": 1, "cone": 2, "parallel3d": 0}
 _PATH = {"generic": 1, "column": 2}
 
 
@@ -97,7 +101,7 @@ def project(path: str, geom: dict, traj: dict, vol: np.ndarray):
     lib.mbph_project(_PATH[path], _ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(hi), _ptr(p),
                      _ptr(n), views, rows, cols, float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)),
                      _ptr(vol), sx, sy, sz, _ptr(sino), _ptr(counts), ctypes.byref(viol))
-    if geom["beam"] != "cone":
+    if geom["beam"] not in _BEAMS_3D:
         sino, counts = sino[:, 0], counts[:, 0]
     return sino, counts, int(viol.value)
 

@@ -54,7 +54,7 @@ def _geometry(cfg, layout=None):
     g = _capi.Geometry()
     g.beam = _capi.BEAMS[cfg.beam]
     g.layout = _capi.LAYOUTS[layout or cfg.layout]
-    if cfg.beam == "cone":
+    if cfg.beam in _capi.BEAMS_3D:
         g.D, g.H, g.W = cfg.shape
         g.spacing[0], g.spacing[1], g.spacing[2] = cfg.spacing
     else:
@@ -212,6 +212,39 @@ def test_validation_error_codes(lib):
     h = ctypes.c_void_p()
     assert lib.mbp_plan_create(ctypes.byref(g), None, None, None, None, ctypes.byref(h)) == E.MBP_EINVAL
     assert lib.mbp_plan_create(None, None, None, None, None, ctypes.byref(h)) == E.MBP_EINVAL
+
+
+def test_parallel3d_plans_and_errors(lib):
+    """The 3-D parallel beam: a circular trajectory with rows along z takes the column walk in
+    either layout, a tilted one the generic walk; a missing row axis, a zero ray direction and
+    a non-finite direction are refused."""
+    from tests.test_hostcheck import parallel3d_config
+    from workloads import random_parallel_3d_trajectory
+    E = _capi
+    cfg = parallel3d_config()
+    for layout in ("DHW", "WHD"):
+        rc, h = _create(lib, _geometry(cfg, layout), config_trajectory(cfg))
+        assert rc == 0
+        inf = _info(lib, h)
+        assert inf.column_capable == 1 and inf.path == 2
+        lib.mbp_plan_destroy(h)
+    rc, h = _create(lib, _geometry(cfg), random_parallel_3d_trajectory(cfg.views, seed=2))
+    assert rc == 0 and _info(lib, h).column_capable == 0
+    lib.mbp_plan_destroy(h)
+    # rays along z: the column walk has no xy line to share
+    t = config_trajectory(cfg)
+    t["src"][3] = (0.0, 0.0, 1.0)
+    t["eu"][3] = (1.0, 0.0, 0.0)
+    t["ev"][3] = (0.0, 1.0, 0.0)
+    rc, h = _create(lib, _geometry(cfg), t)
+    assert rc == 0 and _info(lib, h).column_capable == 0
+    lib.mbp_plan_destroy(h)
+    assert _bad(lib, mutate_traj=lambda t: t.__setitem__("ev", None), cfg=cfg)[0] == E.MBP_EINVAL
+    rc, msg = _bad(lib, mutate_traj=lambda t: t["src"].__setitem__(2, 0.0), cfg=cfg)
+    assert rc == E.MBP_ECOINCIDENT and "must differ" in msg
+    assert _bad(lib, mutate_traj=lambda t: t["src"].__setitem__((1, 2), np.nan), cfg=cfg)[0] == E.MBP_ENONFINITE
+    # no source: no near-geometry refusal for a detector anywhere along the rays
+    assert _bad(lib, mutate_traj=lambda t: t["det"].__setitem__(0, (1e3, 0.0, 0.0)), cfg=cfg)[0] == 0
 
 
 def test_python_plan_maps_errors_and_shapes():

@@ -66,8 +66,8 @@ def geom_of(cfg):
 
 def make_plan(mbp, cfg, traj=None, layout=None):
     traj = config_trajectory(cfg) if traj is None else traj
-    if cfg.beam == "cone":
-        return mbp.Plan("cone", cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols),
+    if cfg.beam in ("cone", "parallel3d"):
+        return mbp.Plan(cfg.beam, cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols),
                         (cfg.dv, cfg.du), layout=layout or cfg.layout)
     return mbp.Plan(cfg.beam, cfg.shape, cfg.spacing, traj, cfg.cols, cfg.du)
 
@@ -181,6 +181,40 @@ def test_tall_detector_parity(torch_dev, mbp, oracle, flip):
         for m in range(B):
             check(b[m], bref[m], f"adjoint member {m}")
     plan.close()
+
+
+def test_parallel3d_parity(torch_dev, mbp, oracle):
+    """3-D parallel beam (infinite lines): circular with detector rows along z (column walk
+    with the gather adjoint, and the generic walk), random directions with tilted detectors
+    (generic walk), in both layouts, unbatched and with a batch of three."""
+    from tests.test_hostcheck import parallel3d_config
+    from workloads import random_parallel_3d_trajectory
+    torch, dev = torch_dev
+    cfg = parallel3d_config()
+    geom = geom_of(cfg)
+    rng = np.random.default_rng(41)
+    xs = rng.random((3,) + cfg.shape).astype(np.float32)
+    cases = ((config_trajectory(cfg), ("column", "generic"), "circular"),
+             (random_parallel_3d_trajectory(cfg.views, seed=6, offset=3.0), ("generic",), "random"))
+    for traj, paths, label in cases:
+        ref = oracle.project(geom, traj, xs)
+        ys = rng.random(ref.shape).astype(np.float32)
+        bref = oracle.backproject(geom, traj, ys)
+        for layout in ("DHW", "WHD"):
+            plan = make_plan(mbp, cfg, traj=traj, layout=layout)
+            for path in paths:
+                plan.set_path(path)
+                for B in (0, 3):
+                    say(f"case parallel3d {label} layout={layout} path={path} B={B}")
+                    x_in = xs[0] if B == 0 else xs
+                    p = plan.project(to_device_volume(torch, dev, x_in, layout)).cpu().numpy().astype(np.float64)
+                    y_in = ys[0] if B == 0 else ys
+                    b = plan.backproject(torch.from_numpy(y_in).to(dev)).cpu().numpy().astype(np.float64)
+                    for m in range(max(B, 1)):
+                        g_p, g_b = (p, b) if B == 0 else (p[m], b[m])
+                        check(g_p, ref[m], f"forward member {m}")
+                        check(g_b, bref[m], f"adjoint member {m}")
+            plan.close()
 
 
 def test_general_trajectory_parity(torch_dev, mbp, oracle):

@@ -27,7 +27,7 @@ from typing import Optional, Tuple
 @dataclass(frozen=True)
 class Config:
     name: str
-    beam: str                      # "parallel" | "fan" | "cone"
+    beam: str                      # "parallel" | "fan" | "cone" | "parallel3d"
     trajectory: str                # "parallel_half" | "circular" | "helical"
     shape: Tuple[int, ...]         # (H, W) or (D, H, W)
     spacing: Tuple[float, ...]     # tensor order

@@ -151,6 +151,8 @@ def random_parallel_3d_trajectory(views: int, seed: int, tilt: float = 0.35,
 def config_trajectory(cfg: Config) -> dict:
     if cfg.beam == "parallel":
         return parallel_2d_trajectory(cfg.views)
+    if cfg.beam == "parallel3d":
+        return parallel_3d_trajectory(cfg.views)
     if cfg.beam == "fan":
         return fan_2d_trajectory(cfg.views, cfg.sid, cfg.sdd)
     if cfg.trajectory == "helical":
