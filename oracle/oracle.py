@@ -248,3 +248,85 @@ def geom_from_config(cfg) -> dict:
     """Geometry dict of a :class:`workloads.Config`."""
     return {"beam": cfg.beam, "shape": cfg.shape, "spacing": cfg.spacing, "views": cfg.views,
             "rows": cfg.rows, "cols": cfg.cols, "du": cfg.du, "dv": cfg.dv}
+
+
+# -- Normal operator and CGLS (fp64) -----------------------------------------------------------
+#
+# The C oracle reads fp32 volumes and sinograms. An fp64 vector a is passed as two fp32 parts,
+# hi = fp32(a) and lo = fp32(a - hi), so a = hi + lo to about 2^-48 relative; by linearity
+# A a = A hi + A lo, which keeps the operator products at fp64 accuracy.
+
+def _split(a: np.ndarray):
+    a = np.asarray(a, dtype=np.float64)
+    hi = a.astype(np.float32)
+    lo = (a - hi.astype(np.float64)).astype(np.float32)
+    return hi, lo
+
+
+def project64(geom: dict, traj: dict, vol: np.ndarray, threads: int = 0) -> np.ndarray:
+    """A vol for an fp64 volume (optionally batched), fp64 result."""
+    hi, lo = _split(vol)
+    return project(geom, traj, hi, threads) + project(geom, traj, lo, threads)
+
+
+def backproject64(geom: dict, traj: dict, sino: np.ndarray, threads: int = 0) -> np.ndarray:
+    """A^T sino for an fp64 sinogram (optionally batched), fp64 result."""
+    hi, lo = _split(sino)
+    return backproject(geom, traj, hi, threads) + backproject(geom, traj, lo, threads)
+
+
+def normal(geom: dict, traj: dict, vol: np.ndarray, threads: int = 0) -> np.ndarray:
+    """The normal operator A^T A vol in fp64."""
+    return backproject64(geom, traj, project64(geom, traj, vol, threads), threads)
+
+
+def cgls(geom: dict, traj: dict, y: np.ndarray, iters: int, x0=None, rtol: float = 0.0,
+         threads: int = 0):
+    """CGLS for min ||A x - y|| (one unbatched problem), in fp64.
+
+    Conjugate gradients applied to the normal equations A^T A x = A^T y in the form that keeps
+    the residual r = y - A x (the "CGLS" variant in A. Bjorck, Numerical Methods for Least
+    Squares Problems, SIAM 1996, section 7.4): from x0 (zeros if None),
+        r = y - A x,  s = A^T r,  p = s,  gamma = ||s||^2
+        per iteration: q = A p,  alpha = gamma / ||q||^2,  x += alpha p,  r -= alpha q,
+                       s = A^T r,  beta = ||s||^2 / gamma,  gamma = ||s||^2,  p = s + beta p.
+    Once ||r|| <= rtol ||y|| (or A^T r = 0, or ||q|| = 0) the iterate stays as it is. Returns
+    (x, norms) with norms[k] = ||r_k|| for k = 0..iters (the recursively updated residual).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    ndim = 3 if geom["beam"] in _BEAMS_3D else 2
+    shape = tuple(int(s) for s in geom["shape"])
+    if len(shape) != ndim:
+        raise ValueError("geometry shape does not match the beam")
+    x = np.zeros(shape) if x0 is None else np.array(x0, dtype=np.float64)
+    r = y - project64(geom, traj, x, threads)
+    y_norm = float(np.linalg.norm(y))
+    norms = [float(np.linalg.norm(r))]
+    active = norms[0] > rtol * y_norm
+    s = backproject64(geom, traj, r, threads)
+    gamma = float(np.vdot(s, s))
+    if not gamma > 0.0:
+        active = False
+    p = s.copy()
+    for _ in range(int(iters)):
+        if active:
+            q = project64(geom, traj, p, threads)
+            delta = float(np.vdot(q, q))
+            if delta > 0.0:
+                alpha = gamma / delta
+                x += alpha * p
+                r -= alpha * q
+            else:
+                active = False
+        norms.append(float(np.linalg.norm(r)))
+        if active and not norms[-1] > rtol * y_norm:
+            active = False
+        if active:
+            s = backproject64(geom, traj, r, threads)
+            gamma_new = float(np.vdot(s, s))
+            beta = gamma_new / gamma
+            gamma = gamma_new
+            p = s + beta * p
+            if not gamma > 0.0:
+                active = False
+    return x, np.array(norms)
