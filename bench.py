@@ -95,6 +95,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adjoint", choices=("gather", "scatter"), default="gather",
                     help="adjoint kernel of the column walk")
+    ap.add_argument("--cgls", type=int, default=10,
+                    help="iterations of the CGLS solve timed for context (0: skip)")
     ap.add_argument("--probe", action="store_true",
                     help="for hardware-counter runs: one forward, one adjoint and a 1 GiB "
                          "device-to-device copy (the counters' calibration), no timing")
@@ -214,6 +216,25 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if args.cgls > 0:
+        # context, not the headline: one CGLS solve of args.cgls iterations on the same
+        # workload after a two-iteration warm-up solve (the pages time ten-iteration solves
+        # and divide by ten), volumes kept z-fastest, sinogram = the forward projection above
+        ws = torch.empty(plan.cgls_workspace_size(1, args.cgls), dtype=torch.uint8, device=dev)
+        xc = plan.empty_volume(device=dev)
+        xc.zero_()
+        plan.cgls(sino, 2, x0=xc, workspace=ws)
+        xc.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, hist = plan.cgls(sino, args.cgls, x0=xc, workspace=ws)
+        torch.cuda.synchronize()
+        cg_ms = (time.perf_counter() - t0) * 1e3 / args.cgls
+        log(f"CGLS: {args.cgls} iterations, {cg_ms:.1f} ms per iteration (including the start), "
+            f"residual {hist[0]:.4g} -> {hist[-1]:.4g}")
+        result["config"]["cgls_iter_ms"] = cg_ms
+        result["config"]["cgls_iters"] = args.cgls
+        del ws, xc
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, traj, x)
     print(json.dumps(result), flush=True)

@@ -120,8 +120,9 @@ typedef struct mbp_plan_info {
 /* Validate the geometry and trajectory and build a plan. Trajectory arrays are host fp64,
    row-major [views][rank] with rank 3 for 3-D beams (cone, parallel3d) and 2 for 2-D beams:
    src = source position (fan/cone) or ray direction (parallel, parallel3d; any nonzero
-   length); det = detector centre; eu, ev = detector axes (ev NULL for 2-D beams). The arrays are copied; no device call is made here (frames are
-   staged to device memory on first use on each device). On success *out owns the plan. */
+   length); det = detector centre; eu, ev = detector axes (ev NULL for 2-D beams). The arrays
+   are copied; no device call is made here (frames are staged to device memory on first use
+   on each device). On success *out owns the plan. */
 int mbp_plan_create(const mbp_geometry* geometry, const double* src, const double* det,
                     const double* eu, const double* ev, mbp_plan** out);
 
@@ -180,6 +181,35 @@ int mbp_set_workspace(mbp_plan* plan, void* device_ptr, size_t bytes);
    application). */
 int mbp_convert_layout(const float* in, int64_t batch, int64_t D, int64_t H, int64_t W,
                        int32_t to_whd, float* out, void* stream);
+
+/* Normal operator of the pair: out = A^T (A volume) for `batch` members, in the plan's
+   layout; `sinogram` ([batch][views][rows][cols], caller-owned) receives A volume on the way.
+   `out` must not alias `volume`. A caller that keeps its volumes in MBP_LAYOUT_WHD pays no
+   layout copy per application (page "diffct 2.2.1 -> 2.4.0", CHANGELOG 2.4.0,
+   native_volume_layout). */
+int mbp_normal(mbp_plan* plan, const float* volume, int64_t batch, float* sinogram, float* out,
+               void* stream);
+
+/* Device workspace bytes mbp_cgls needs for `batch` members and `iters` iterations: per
+   member two sinograms (the residual r and q = A p) and two volumes (s = A^T r and the search
+   direction p), plus fp64 scalars, the residual history and reduction partials. */
+int mbp_cgls_workspace_size(const mbp_plan* plan, int64_t batch, int32_t iters, size_t* bytes);
+
+/* CGLS (conjugate gradients on the normal equations, keeping the residual r = y - A x) for
+   min_x ||A x - y||, one independent problem per batch member, started from the caller's
+   `volume` (x0; zeros for a cold start), which holds the iterate after the call. `iters`
+   iterations are enqueued; a member whose residual norm falls to rtol * ||y|| stays
+   unchanged from then on (rtol = 0: never). Norms are accumulated in fp64 blocks and the
+   step sizes formed in fp64 on the device (page "diffct 2.1.0 -> 2.2.1", CHANGELOG 2.2.0;
+   solver with residual history, optional x0 and residual thresholds: page "diffct 2.2.1 ->
+   2.3.0", CHANGELOG 2.3.0). `workspace` is caller-owned device memory of at least
+   mbp_cgls_workspace_size bytes, 256-byte aligned, not overlapping `sinogram` or `volume`.
+   residual_norms (host, may be NULL): [batch][iters + 1] values of ||r_k|| (the recursively
+   updated residual), k = 0..iters; when it is non-NULL the call waits for `stream` to finish,
+   otherwise nothing synchronises the host. */
+int mbp_cgls(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume, int32_t iters,
+             double rtol, void* workspace, size_t workspace_bytes, double* residual_norms,
+             void* stream);
 
 const char* mbp_status_string(int status);
 const char* mbp_last_error(void);

@@ -247,6 +247,69 @@ class Plan:
         return out
 
 
+    def normal(self, volume, out=None, sinogram=None):
+        """Normal operator ``A^T A volume`` in the plan's layout; ``sinogram`` (optional)
+        receives ``A volume``. Returns ``out``."""
+        torch = _torch()
+        batch = self._check_volume(volume)
+        lead = () if batch is None else (batch,)
+        if sinogram is None:
+            sinogram = torch.empty(lead + self.sino_shape, dtype=torch.float32, device=volume.device)
+        elif self._check_sino(sinogram) != batch or sinogram.device != volume.device:
+            raise ValueError("sinogram does not match the volume's batch or device")
+        if out is None:
+            out = self.empty_volume(batch, device=volume.device)
+        elif self._check_volume(out) != batch or out.device != volume.device:
+            raise ValueError("out does not match the volume's batch or device")
+        with torch.cuda.device(volume.device):
+            stream = torch.cuda.current_stream(volume.device).cuda_stream
+            _capi.check(self._lib.mbp_normal(self._handle, ctypes.c_void_p(volume.data_ptr()),
+                                             1 if batch is None else batch,
+                                             ctypes.c_void_p(sinogram.data_ptr()),
+                                             ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream)),
+                        "mbp_normal")
+        return out
+
+    def cgls_workspace_size(self, batch: Optional[int], iters: int) -> int:
+        n = ctypes.c_size_t()
+        _capi.check(self._lib.mbp_cgls_workspace_size(self._handle, 1 if batch is None else int(batch),
+                                                      int(iters), ctypes.byref(n)),
+                    "mbp_cgls_workspace_size")
+        return int(n.value)
+
+    def cgls(self, sinogram, iters: int, x0=None, rtol: float = 0.0, workspace=None):
+        """CGLS for ``min ||A x - y||`` from ``x0`` (zeros if None), ``iters`` iterations.
+
+        Returns ``(x, residual_norms)``: the iterate in the plan's layout (``x0`` itself is
+        updated in place when given) and a numpy array ``[B?, iters + 1]`` of residual norms."""
+        torch = _torch()
+        batch = self._check_sino(sinogram)
+        if x0 is None:
+            x = self.empty_volume(batch, device=sinogram.device)
+            x.zero_()
+        else:
+            if self._check_volume(x0) != batch or x0.device != sinogram.device:
+                raise ValueError("x0 does not match the sinogram's batch or device")
+            x = x0
+        nb = 1 if batch is None else batch
+        need = self.cgls_workspace_size(nb, iters)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=sinogram.device)
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+        hist = np.zeros((nb, int(iters) + 1), dtype=np.float64)
+        with torch.cuda.device(sinogram.device):
+            stream = torch.cuda.current_stream(sinogram.device).cuda_stream
+            _capi.check(self._lib.mbp_cgls(self._handle, ctypes.c_void_p(sinogram.data_ptr()), nb,
+                                           ctypes.c_void_p(x.data_ptr()), int(iters), float(rtol),
+                                           ctypes.c_void_p(workspace.data_ptr()),
+                                           workspace.numel() * workspace.element_size(),
+                                           hist.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                           ctypes.c_void_p(stream)),
+                        "mbp_cgls")
+        return x, (hist[0] if batch is None else hist)
+
+
 def _plan_from(volume_shape, voxel_spacing, trajectory, detector, beam, layout, center):
     shape, spacing = detector
     return Plan(beam, volume_shape, voxel_spacing, trajectory, shape, spacing, layout, center)

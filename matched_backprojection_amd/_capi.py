@@ -31,8 +31,9 @@ ADJOINTS = {"auto": 0, "gather": 1, "scatter": 2}
 EXPORTS = (
     "mbp_plan_create", "mbp_plan_destroy", "mbp_plan_get_info", "mbp_plan_set_path",
     "mbp_plan_set_view_batch", "mbp_plan_set_adjoint", "mbp_project", "mbp_backproject", "mbp_segment_count",
-    "mbp_workspace_size", "mbp_set_workspace", "mbp_convert_layout", "mbp_status_string",
-    "mbp_last_error", "mbp_abi_version",
+    "mbp_workspace_size", "mbp_set_workspace", "mbp_convert_layout", "mbp_normal",
+    "mbp_cgls_workspace_size", "mbp_cgls", "mbp_status_string", "mbp_last_error",
+    "mbp_abi_version",
 )
 
 
@@ -94,6 +95,10 @@ def load():
     lib.mbp_workspace_size.argtypes = [P, I64, ctypes.POINTER(ctypes.c_size_t)]
     lib.mbp_set_workspace.argtypes = [P, P, ctypes.c_size_t]
     lib.mbp_convert_layout.argtypes = [P, I64, I64, I64, I64, I32, P, P]
+    lib.mbp_normal.argtypes = [P, P, I64, P, P, P]
+    lib.mbp_cgls_workspace_size.argtypes = [P, I64, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mbp_cgls.argtypes = [P, P, I64, P, I32, ctypes.c_double, P, ctypes.c_size_t,
+                             ctypes.POINTER(ctypes.c_double), P]
     lib.mbp_status_string.argtypes = [ctypes.c_int]
     lib.mbp_status_string.restype = ctypes.c_char_p
     lib.mbp_last_error.argtypes = []

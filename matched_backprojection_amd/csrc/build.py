@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmbp.so")
-SOURCES = [os.path.join(HERE, "kernels.hip"), os.path.join(HERE, "plan.cpp")]
+SOURCES = [os.path.join(HERE, "kernels.hip"), os.path.join(HERE, "plan.cpp"),
+           os.path.join(HERE, "solver.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("MBP_OFFLOAD_ARCH", "gfx950")
 

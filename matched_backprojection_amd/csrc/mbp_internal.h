@@ -81,4 +81,7 @@ hipError_t launch_convert(const float* in, int32_t D, int32_t H, int32_t W, int 
                           float* out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
+// Record the calling thread's error message (mbp_last_error) and return `code`.
+int set_error(int code, const char* fmt, ...);
+
 }  // namespace mbp

@@ -72,6 +72,18 @@ bool finite3(const double* p, int n) {
 
 }  // namespace
 
+namespace mbp {
+int set_error(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+}  // namespace mbp
+
 struct mbp_plan {
     mbp_geometry g{};
     int rank = 3;

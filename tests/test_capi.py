@@ -247,6 +247,46 @@ def test_parallel3d_plans_and_errors(lib):
     assert _bad(lib, mutate_traj=lambda t: t["det"].__setitem__(0, (1e3, 0.0, 0.0)), cfg=cfg)[0] == 0
 
 
+def test_solver_workspace_and_argument_checks(lib):
+    """mbp_cgls_workspace_size follows its stated layout; mbp_normal and mbp_cgls refuse bad
+    arguments with their status before any device work; batch 0 does nothing."""
+    E = _capi
+    cfg = SMALL_CONFIGS["c3_cone256"]
+    rc, h = _create(lib, _geometry(cfg), config_trajectory(cfg))
+    assert rc == 0
+    n = ctypes.c_size_t()
+    P = ctypes.c_void_p
+
+    def up(b):
+        return (b + 255) // 256 * 256
+    for batch, iters in ((1, 0), (2, 10), (3, 7)):
+        assert lib.mbp_cgls_workspace_size(h, batch, iters, ctypes.byref(n)) == 0
+        want = (2 * up(batch * cfg.n_rays * 4) + 2 * up(batch * cfg.n_voxels * 4)
+                + up(batch * 8 * 8) + up(batch * (iters + 1) * 8) + up(batch * 512 * 8))
+        assert n.value == want
+    assert lib.mbp_cgls_workspace_size(h, 0, 5, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.mbp_cgls_workspace_size(h, -1, 5, ctypes.byref(n)) == E.MBP_EINVAL
+    assert lib.mbp_cgls_workspace_size(h, 1, -1, ctypes.byref(n)) == E.MBP_EINVAL
+    assert lib.mbp_cgls_workspace_size(None, 1, 1, ctypes.byref(n)) == E.MBP_EINVAL
+    fake = P(1 << 20)            # never dereferenced: every call below fails validation
+    hist = (ctypes.c_double * 4)()
+    assert lib.mbp_cgls(None, fake, 1, fake, 3, 0.0, fake, 1 << 40, hist, None) == E.MBP_EINVAL
+    assert lib.mbp_cgls(h, fake, -1, fake, 3, 0.0, fake, 1 << 40, hist, None) == E.MBP_EINVAL
+    assert lib.mbp_cgls(h, fake, 1, fake, -2, 0.0, fake, 1 << 40, hist, None) == E.MBP_EINVAL
+    assert lib.mbp_cgls(h, fake, 1, fake, 3, -1.0, fake, 1 << 40, hist, None) == E.MBP_EINVAL
+    assert lib.mbp_cgls(h, fake, 1, fake, 3, float("nan"), fake, 1 << 40, hist, None) == E.MBP_EINVAL
+    assert lib.mbp_cgls(h, None, 1, fake, 3, 0.0, fake, 1 << 40, hist, None) == E.MBP_EINVAL
+    assert lib.mbp_cgls(h, fake, 1, fake, 3, 0.0, P(1 << 20 | 8), 1 << 40, hist, None) == E.MBP_EINVAL
+    rc = lib.mbp_cgls(h, fake, 1, fake, 3, 0.0, fake, 1024, hist, None)
+    assert rc == E.MBP_ENOMEM and "workspace" in lib.mbp_last_error().decode()
+    assert lib.mbp_cgls(h, None, 0, None, 3, 0.0, None, 0, None, None) == 0
+    assert lib.mbp_normal(h, None, 1, fake, fake, None) == E.MBP_EINVAL
+    assert lib.mbp_normal(h, fake, 1, fake, fake, None) == E.MBP_EINVAL     # out aliases volume
+    assert lib.mbp_normal(h, fake, -1, fake, P(1 << 21), None) == E.MBP_EINVAL
+    assert lib.mbp_normal(h, None, 0, None, None, None) == 0
+    lib.mbp_plan_destroy(h)
+
+
 def test_python_plan_maps_errors_and_shapes():
     import matched_backprojection_amd as mbp
     cfg = SMALL_CONFIGS["c4_cone512_aniso"]
