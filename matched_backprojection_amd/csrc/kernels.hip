@@ -492,6 +492,13 @@ __device__ __forceinline__ void gather_load_rows(const float* __restrict__ p, fl
     for (int c = 0; c < kGroup; ++c) load_vals<NB>(p + c * NB, w[c]);
 }
 
+// Pair index clamped to [-2, hi]: one v_med3_i32 (the compiler emits a max and a min).
+__device__ __forceinline__ int32_t clamp_pair(int32_t i, int32_t hi) {
+    int32_t r;
+    asm("v_med3_i32 %0, %1, -2, %2" : "=v"(r) : "v"(i), "s"(hi));
+    return r;
+}
+
 // Fast form of one item for one group of rows (see gather_fast): every row adds its two
 // pieces to the disjoint cell pair {fa, fa + 1} with one paired read and write. FULL: the
 // lane takes all kGroup rows (S == kGroup), so the unrolled rows need no guard.
@@ -510,9 +517,13 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         fast_row(za, zb, fa, num, ext, split);
         za += a1;
         zb += b1;
-        const float f = split ? (float)num * __builtin_amdgcn_rcpf((float)ext) : 1.0f;
+        // the lower cell's share: num / ext when the row crosses the plane above fa, else 1;
+        // num >= ext exactly when it does not (ext = 0 gives an infinite ratio), so a min
+        // with 1 selects both cases
+        const float f = fminf((float)num * __builtin_amdgcn_rcpf((float)ext), 1.0f);
+        (void)split;
         const int32_t i0 = base + fa;
-        const int32_t idx = max(min(i0, n + 1), -2);
+        const int32_t idx = clamp_pair(i0, n + 1);
         float* dst = col + idx * NB;
         float v[2 * NB];
 #pragma unroll
