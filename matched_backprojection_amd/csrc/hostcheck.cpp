@@ -157,23 +157,19 @@ int mbph_project_chunked(const double* frames, int beam, const double* lo, const
                     const bool two = row_single_crossing(r, B);
                     for (const auto& ch : chunks) {
                         const size_t grouped = two ? ch.size() / kCellGroup * kCellGroup : 0;
-                        // chunks inside the row's slab take the clip-free form; it must agree
-                        // with the clipped one cell by cell
+                        // chunks inside the row's slab (for this row; the kernel requires it of
+                        // all 64 rows of a wave) take the clip-free form, with the next z
+                        // crossing re-anchored at the chunk start and then stepped
                         const bool inside = !ch.empty() && r.t_lo <= ta && r.t_hi >= ch.back().tb;
+                        if (inside && grouped > 0) nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
                         size_t p = 0;
                         for (; p < grouped; ++p) {
                             const double hi = fmin(ch[p].tb, r.t_hi);
                             int32_t z0, z1;
                             float l0, l1;
                             if (inside) {
-                                int32_t czi = cz, kzi = kz, zi0, zi1;
-                                double nzi = nz;
-                                float li0, li1;
-                                row_cell_two_inside(r, ta, ch[p].tb, czi, kzi, nzi, zi0, li0, zi1, li1);
-                                row_cell_two(r, ta, ch[p].tb, cz, kz, nz, z0, l0, z1, l1);
-                                if (czi != cz || kzi != kz || !(nzi == nz || (nzi != nzi && nz != nz)) ||
-                                    zi0 != z0 || zi1 != z1 || li0 != l0 || li1 != l1)
-                                    ++*violations;
+                                if (nz < ta && kz < r.z.steps) ++*violations;   // a crossing left behind
+                                row_cell_two_inside(r, ta, ch[p].tb, cz, kz, nz, z0, l0, z1, l1);
                             } else {
                                 row_cell_two(r, ta, ch[p].tb, cz, kz, nz, z0, l0, z1, l1);
                             }

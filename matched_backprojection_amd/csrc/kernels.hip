@@ -190,6 +190,23 @@ __device__ __forceinline__ void load_vals(const float* __restrict__ p, float* v)
     }
 }
 
+// Third dword of a raw buffer resource (32-bit elements, unformatted access).
+constexpr int kBufferFlags = 0x00020000;
+
+template <int NB>
+__device__ __forceinline__ void buffer_vals(__amdgpu_buffer_rsrc_t r, uint32_t off, float* v) {
+    if constexpr (NB == 1) {
+        v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    } else if constexpr (NB == 2) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+        v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
+    } else {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
+        v[2] = __uint_as_float(t[2]); v[3] = __uint_as_float(t[3]);
+    }
+}
+
 struct ColumnTask {
     int32_t view, col, row;
     bool valid;
@@ -302,9 +319,45 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                     }
                 };
                 if (inside) {
-                    groups([&](double tb, int32_t& z0, float& l0, int32_t& z1, float& l1) {
-                        row_cell_two_inside(r, ta, tb, cz, kz, nz, z0, l0, z1, l1);
-                    });
+                    // re-anchor the next z crossing exactly (row_cell_two_inside steps it by
+                    // the spacing); voxels are read through a buffer resource per cell based
+                    // at the cell's z column, so each load takes a 32-bit offset
+                    nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
+                    const int32_t colbytes = (int32_t)(D * NB * sizeof(float));
+                    for (; p + kCellGroup <= count; p += kCellGroup) {
+                        uint32_t zoff[2 * kCellGroup];
+                        float len[2 * kCellGroup];
+                        uint32_t cell[kCellGroup];
+#pragma unroll
+                        for (int q = 0; q < kCellGroup; ++q) {
+                            const double tb = E[p + q].tb;
+                            cell[q] = uniform((uint32_t)E[p + q].cxy);
+                            int32_t z0, z1;
+                            row_cell_two_inside(r, ta, tb, cz, kz, nz, z0, len[2 * q], z1, len[2 * q + 1]);
+                            zoff[2 * q] = (uint32_t)z0 * (NB * sizeof(float));
+                            zoff[2 * q + 1] = (uint32_t)z1 * (NB * sizeof(float));
+                            ta = tb;
+                        }
+                        float val[2 * kCellGroup][NB];
+#pragma unroll
+                        for (int q = 0; q < kCellGroup; ++q) {
+                            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                                const_cast<float*>(vol + (size_t)cell[q] * D * NB), (short)0, colbytes, kBufferFlags);
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                if (len[2 * q + h] != 0.0f) {
+                                    buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h]);
+                                } else {
+#pragma unroll
+                                    for (int m = 0; m < NB; ++m) val[2 * q + h][m] = 0.0f;
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int q = 0; q < 2 * kCellGroup; ++q)
+#pragma unroll
+                            for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
+                    }
                 } else {
                     groups([&](double tb, int32_t& z0, float& l0, int32_t& z1, float& l1) {
                         row_cell_two(r, ta, tb, cz, kz, nz, z0, l0, z1, l1);

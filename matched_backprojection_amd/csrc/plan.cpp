@@ -195,6 +195,8 @@ int validate_frames(const mbp_plan& P) {
 bool column_ok(const mbp_plan& P) {
     const mbp_geometry& g = P.g;
     if (g.beam != MBP_CONE && g.beam != MBP_PARALLEL3D) return false;
+    // a z column of up to four interleaved members must fit a 32-bit byte offset
+    if (g.D >= ((int64_t)1 << 26)) return false;
     const double minp = std::min(g.spacing[0], std::min(g.spacing[1], g.spacing[2]));
     for (int64_t i = 0; i < g.views; ++i) {
         const Frame& F = P.frames[(size_t)i];

@@ -749,7 +749,9 @@ MBP_HD MBP_INLINE void row_cell_two(const RowWalk& r, double ta, double tb, int3
 // row_cell_two for a cell inside the row's slab (t_lo <= ta and tb <= t_hi) of a row with
 // row_single_crossing(): no clip is needed, and the row's next z crossing is not before ta
 // (the previous one lies inside an earlier cell, more than a cell diagonal back), so the
-// pieces are (cross ? nz : tb) - ta and tb - nz. Equal to row_cell_two under those conditions.
+// pieces are (cross ? nz : tb) - ta and tb - nz. The next crossing is the previous one plus
+// the spacing: the caller re-anchors nz = crossing(kz) exactly at every chunk of at most
+// kXYChunk cells, so the running sum drifts by at most ~kXYChunk rounding steps.
 MBP_HD MBP_INLINE void row_cell_two_inside(const RowWalk& r, double ta, double tb, int32_t& cz,
                                            int32_t& kz, double& nz, int32_t& cz0, float& len0,
                                            int32_t& cz1, float& len1) {
@@ -761,7 +763,7 @@ MBP_HD MBP_INLINE void row_cell_two_inside(const RowWalk& r, double ta, double t
         len1 = (float)(tb - nz);
         cz += r.z.step;
         ++kz;
-        nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
+        nz = kz < r.z.steps ? nz + r.z.t_step : INFINITY;
     }
     cz1 = cz;
 }
