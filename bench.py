@@ -87,6 +87,58 @@ def cpu_baseline(cfg, traj, x_dhw, views=(0, 180, 360, 540)):
                        f"{t2 - t0:.1f} s total")}
 
 
+def measure_pair(mbp, torch, cfg, steps: int, warmup: int) -> dict:
+    """Forward + matched backprojection of one configuration (its own layout and batch), timed
+    like the headline pair; for the secondary workloads reported next to it."""
+    import numpy as np
+    from workloads import config_phantom, config_trajectory
+    dev = torch.device("cuda:0")
+    traj = config_trajectory(cfg)
+    x = config_phantom(cfg)
+    plan = mbp.Plan(cfg.beam, cfg.shape, cfg.spacing, traj, (cfg.rows, cfg.cols), (cfg.dv, cfg.du),
+                    layout=cfg.layout)
+    batch = cfg.batch or None
+    xs = x if batch else x[None]
+    if cfg.layout == "WHD":
+        xd = torch.from_numpy(np.ascontiguousarray(xs.transpose(0, 3, 2, 1))).to(dev).permute(0, 3, 2, 1)
+    else:
+        xd = torch.from_numpy(np.ascontiguousarray(xs)).to(dev)
+    if not batch:
+        xd = xd[0]
+    sino = torch.empty(((batch,) if batch else ()) + plan.sino_shape, dtype=torch.float32, device=dev)
+    vol = plan.empty_volume(batch, device=dev)
+    segs = plan.segment_count() * (batch or 1)
+    for _ in range(warmup):
+        plan.project(xd, out=sino)
+        plan.backproject(sino, out=vol)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        plan.project(xd, out=sino)
+        ev[1].record()
+        plan.backproject(sino, out=vol)
+        ev[2].record()
+        events.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    io = 4.0 * (cfg.n_voxels + cfg.n_rays) * (batch or 1) + 96.0 * cfg.views
+    alg = 4.0 * segs + io
+    out = {"workload": cfg.name, "batch": cfg.batch, "layout": cfg.layout, "path": plan.info["path"],
+           "segments_per_op": segs, "forward_ms": f_ms, "adjoint_ms": b_ms,
+           "gsegments_per_s": 2.0 * segs * steps / wall / 1e9,
+           "rays_per_s": 2.0 * cfg.n_rays * (batch or 1) * steps / wall,
+           "pct_hbm_peak_pair": 100.0 * 2 * alg / ((f_ms + b_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    log(f"{cfg.name}: forward {f_ms:.2f} ms, adjoint {b_ms:.2f} ms, "
+        f"{out['gsegments_per_s']:.0f} G segments/s, {out['pct_hbm_peak_pair']:.1f}% of HBM peak")
+    plan.close()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +149,8 @@ def main() -> int:
                     help="adjoint kernel of the column walk")
     ap.add_argument("--cgls", type=int, default=10,
                     help="iterations of the CGLS solve timed for context (0: skip)")
+    ap.add_argument("--no-others", dest="others", action="store_false",
+                    help="skip timing the 256^3 cone and the batched helical cone")
     ap.add_argument("--probe", action="store_true",
                     help="for hardware-counter runs: one forward, one adjoint and a 1 GiB "
                          "device-to-device copy (the counters' calibration), no timing")
@@ -235,6 +289,11 @@ def main() -> int:
         result["config"]["cgls_iter_ms"] = cg_ms
         result["config"]["cgls_iters"] = args.cgls
         del ws, xc
+    if args.others:
+        # the 256^3 cone of the metric and the batched helical cone, timed the same way
+        result["config"]["other_workloads"] = [
+            measure_pair(mbp, torch, CONFIGS[name], steps=5, warmup=2)
+            for name in ("c3_cone256", "c5_helical_b4")]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, traj, x)
     print(json.dumps(result), flush=True)

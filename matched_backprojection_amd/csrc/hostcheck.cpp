@@ -229,13 +229,14 @@ int mbph_backproject(int path, const double* frames, int beam, const double* lo,
 
 // Replays the gather adjoint item by item as the kernel forms items: per cell, view and
 // crossing column one item, taken in the fast fixed-point form where the kernel takes it
-// (rows of a lane relative to the lane's origin cell, shares num / ext in fp32 when
-// `kernel_shares`, else in fp64 from the same integers) and in the fp64 general form
-// otherwise. Sums in fp64. *fast counts items taken in the fast form.
+// (rows of a lane relative to the lane's origin cell, shares in fp32 when `kernel_shares`,
+// else in fp64 from the same integers) and in the fp64 general form otherwise; `general_only`
+// takes every item in the general form. Sums in fp64. *violations counts pieces out of range
+// and fast-form positions outside the fixed point's range; *fast counts fast items.
 int mbph_gather(const double* frames, int beam, const double* lo, const double* pitch,
                 const int32_t* n, int views, int rows, int cols, double du, double dv,
-                const float* sino, int kernel_shares, double* vol, long long* violations,
-                long long* fast) {
+                const float* sino, int kernel_shares, int general_only, double* vol,
+                long long* violations, long long* fast) {
     std::vector<Frame> F;
     frames_from(frames, views, F);
     const Box B = box_from(lo, pitch, n);
@@ -287,26 +288,41 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                         cell_clip(lines[(size_t)v * cols + j], line, x0, x1, y0, y1, t0, t1);
                         dt = t1 - t0;
                     }
-                    if (it.a1fx != kNotFast) {
+                    if (it.form > 0 && !general_only) {
                         ++*fast;
                         for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S)
                             for (int lane = 0; lane < 64; ++lane) {
                                 const int32_t k0 = g0 + S * lane;
+                                const int32_t c0 = fast_origin_row(S);
                                 int32_t la, lb, base;
-                                fast_origin(it, (double)k0, -1, la, lb, base);
+                                fast_origin(it, (double)(k0 + c0), -1, la, lb, base);
                                 for (int32_t c = 0; c < S; ++c) {
-                                    int32_t fa, num, ext;
-                                    bool split;
-                                    fast_row(la + c * it.a1fx, lb + c * it.b1fx, fa, num, ext, split);
-                                    double f = 1.0;
-                                    if (split) f = kernel_shares ? (double)((float)num * (1.0f / (float)ext))
-                                                                 : (double)num / (double)ext;
+                                    // the row's ends must stay inside the fixed point's range
+                                    const int64_t pa = (int64_t)la + (int64_t)(c - c0) * it.a1fx;
+                                    const int64_t pb = (int64_t)lb + (int64_t)(c - c0) * it.b1fx;
+                                    if (pa != (int32_t)pa || pb != (int32_t)pb) ++*violations;
+                                    int32_t fa;
+                                    uint32_t num, ext;
+                                    fast_row((int32_t)pa, (int32_t)pb, fa, num, ext);
+                                    // both shares from integers: the lower cell's num / ext and
+                                    // the upper one's (ext - num) / ext
+                                    double f = 1.0, g = 0.0;
+                                    if (num < ext) {
+                                        if (kernel_shares) {
+                                            const float r = 1.0f / (float)ext;
+                                            f = (double)((float)num * r);
+                                            g = (double)((float)(ext - num) * r);
+                                        } else {
+                                            f = (double)num / (double)ext;
+                                            g = (double)(ext - num) / (double)ext;
+                                        }
+                                    }
                                     const int32_t i0 = base + fa;
                                     if ((uint32_t)i0 > (uint32_t)D) continue;     // outside: discarded
                                     const int32_t z = i0 - 1;                      // cell of index i0
                                     const double wk = w[k0 + c];
                                     if (z >= 0) add(z, f * dt, wk);
-                                    if (z + 1 < D) add(z + 1, (1.0 - f) * dt, wk);
+                                    if (z + 1 < D) add(z + 1, g * dt, wk);
                                 }
                             }
                         continue;
@@ -332,10 +348,10 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
 // every instruction and every step (the single-piece add, then step i of the aligned piece
 // walk), the z cells the active lanes add into must be distinct. Returns the number of items
 // checked; *conflicts counts instructions or steps with a repeated cell, *fast the fast items.
-// mode 0 replays the kernel; two planted mistakes show the check can fail: mode 1 starts the
-// walk of rows that span several cells at the first in-range cell (rows entering from below
-// the box then meet in its bottom cell), mode 2 deals adjacent rows to the lanes of one
-// instruction.
+// mode 0 replays the kernel; three planted mistakes show the check can fail: mode 1 starts
+// the walk of rows that span several cells at the first in-range cell (rows entering from
+// below the box then meet in its bottom cell), mode 2 deals adjacent rows to the lanes of one
+// instruction, mode 3 lets all lanes of a fast item write in one phase.
 int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, const double* pitch,
                               const int32_t* n, int views, int rows, int cols, double du, double dv,
                               int mode, long long* conflicts, long long* fast) {
@@ -361,29 +377,34 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                     column_line(F[v], B, beam, j, cols, rows, du, dv, L);
                     GatherItem it;
                     if (!gather_item(L, line, x0, x1, y0, y1, S, rows, rows_pad, v * cols + j, it)) continue;
-                    const bool is_fast = it.a1fx != kNotFast;
-                    if (!is_fast && it.b1fx == 0) continue;       // LDS atomics: nothing to check
+                    const bool is_fast = it.form > 0;
+                    if (it.form == kGeneralAtomic) continue;      // LDS atomics: nothing to check
                     ++checked;
                     if (is_fast) ++*fast;
                     for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S) {
                         for (int32_t c = 0; c < S; ++c) {
                             if (is_fast) {
-                                seen.clear();
-                                for (int lane = 0; lane < 64; ++lane) {
-                                    // mode 2: adjacent rows in one instruction
-                                    const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
-                                    int32_t la, lb, base;
-                                    fast_origin(it, (double)k0, -1, la, lb, base);
-                                    int32_t fa, num, ext;
-                                    bool split;
-                                    fast_row(la + c * it.a1fx, lb + c * it.b1fx, fa, num, ext, split);
-                                    const int32_t i0 = base + fa;
-                                    if ((uint32_t)i0 > (uint32_t)D) continue;   // discard pair
-                                    seen.push_back(i0);
-                                    seen.push_back(i0 + 1);
+                                // lane l writes in phase l mod G; modes 2 and 3 ignore the phases
+                                const int32_t G = mode >= 2 ? 1 : it.form;
+                                if (G < 1) ++*conflicts;
+                                for (int32_t q = 0; q < std::max(G, 1); ++q) {
+                                    seen.clear();
+                                    for (int lane = q; lane < 64; lane += std::max(G, 1)) {
+                                        // mode 2: adjacent rows in one instruction
+                                        const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
+                                        const int32_t c0 = fast_origin_row(S);
+                                        int32_t la, lb, base, fa;
+                                        uint32_t num, ext;
+                                        fast_origin(it, (double)(k0 + c0), -1, la, lb, base);
+                                        fast_row(la + (c - c0) * it.a1fx, lb + (c - c0) * it.b1fx, fa, num, ext);
+                                        const int32_t i0 = base + fa;
+                                        if ((uint32_t)i0 > (uint32_t)D) continue;   // discard pair
+                                        seen.push_back(i0);
+                                        seen.push_back(i0 + 1);
+                                    }
+                                    std::sort(seen.begin(), seen.end());
+                                    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
                                 }
-                                std::sort(seen.begin(), seen.end());
-                                if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
                                 continue;
                             }
                             // steps: the two-piece adds (cell fa, then cell fb), then the

@@ -552,44 +552,90 @@ __device__ __forceinline__ int32_t clamp_pair(int32_t i, int32_t hi) {
     return r;
 }
 
+// a * b with 0 * anything = 0 (also 0 * inf): one v_mul_legacy_f32.
+__device__ __forceinline__ float mul_legacy(float a, float b) {
+    float r;
+    asm("v_mul_legacy_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Fast form of one item for one group of rows (see gather_fast): every row adds its two
-// pieces to the disjoint cell pair {fa, fa + 1} with one paired read and write. FULL: the
-// lane takes all kGroup rows (S == kGroup), so the unrolled rows need no guard.
-template <int NB, bool FULL>
+// pieces to the cell pair {fa, fa + 1} with one paired read and write. The lane's rows are
+// placed relative to its origin row c0 (fast_origin_row): row c lies (c - c0) per-row
+// advances a1, b1 from it, an exact integer step. PHASED: the lanes write in G phases (lane l
+// in phase l mod G); lanes of one phase are S * G rows apart and so hold disjoint pairs;
+// otherwise all lanes write at once. FULL: the lane takes all kGroup rows (S == kGroup), so
+// the unrolled rows need no guard.
+template <int NB, bool FULL, bool PHASED>
 __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
                                                   float dt, const float (&w)[kGroup][NB],
                                                   int32_t k0, int32_t S, int32_t z0, int32_t n,
-                                                  float* col) {
-    int32_t za, zb, base;
-    fast_origin(it, (double)k0, z0 - 1, za, zb, base);
+                                                  float* col, int32_t G, int32_t lane) {
+    int32_t phase = 0;
+    if constexpr (PHASED) {
+        // lane mod G from a float quotient: (lane + 1/2) / G stays at least 1/32 away from an
+        // integer, so the rounding of the reciprocal cannot move it
+        const uint32_t qt = (uint32_t)(((float)lane + 0.5f) * __builtin_amdgcn_rcpf((float)G));
+        phase = lane - (int32_t)qt * G;
+    }
+    constexpr int c0 = FULL ? kGroup / 2 : 0;
+    int32_t la, lb, base;
+    fast_origin(it, (double)(k0 + c0), z0 - 1, la, lb, base);
+    int32_t za[kGroup], zb[kGroup];
+    za[c0] = la;
+    zb[c0] = lb;
+#pragma unroll
+    for (int c = c0 + 1; c < kGroup; ++c) {
+        za[c] = za[c - 1] + a1;
+        zb[c] = zb[c - 1] + b1;
+    }
+#pragma unroll
+    for (int c = c0 - 1; c >= 0; --c) {
+        za[c] = za[c + 1] - a1;
+        zb[c] = zb[c + 1] - b1;
+    }
 #pragma unroll
     for (int c = 0; c < kGroup; ++c) {
         if (!FULL && c >= S) continue;
-        int32_t fa, num, ext;
-        bool split;
-        fast_row(za, zb, fa, num, ext, split);
-        za += a1;
-        zb += b1;
-        // the lower cell's share: num / ext when the row crosses the plane above fa, else 1;
-        // num >= ext exactly when it does not (ext = 0 gives an infinite ratio), so a min
-        // with 1 selects both cases
-        const float f = fminf((float)num * __builtin_amdgcn_rcpf((float)ext), 1.0f);
-        (void)split;
-        const int32_t i0 = base + fa;
-        const int32_t idx = clamp_pair(i0, n + 1);
+        int32_t fa;
+        uint32_t num, ext;
+        fast_row(za[c], zb[c], fa, num, ext);
+        // the shares of the lower and upper cells, num / ext and (ext - num) / ext, when the
+        // row crosses the plane above fa, else 1 and 0: num >= ext exactly when it does not,
+        // so a min with 1 and a saturating difference select both cases; a row of zero extent
+        // has an infinite reciprocal, which the min turns into 1 (num >= 1) and the legacy
+        // multiply (0 times anything is 0) into 0. Each share comes from its own integer, so
+        // a thin piece keeps its relative precision.
+        const float r = __builtin_amdgcn_rcpf((float)ext);
+        const float f = fminf((float)num * r, 1.0f);
+        const float g = mul_legacy((float)__builtin_elementwise_sub_sat(ext, num), r);
+        const int32_t idx = clamp_pair(base + fa, n + 1);
         float* dst = col + idx * NB;
-        float v[2 * NB];
-#pragma unroll
-        for (int m = 0; m < 2 * NB; ++m) v[m] = dst[m];
+        float qa[NB], qb[NB];
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
             const float q = dt * w[c][m];
-            const float pa = f * q;
-            v[m] += pa;
-            v[NB + m] += q - pa;
+            qa[m] = f * q;
+            qb[m] = g * q;
         }
+        auto rmw = [&]() {
+            float v[2 * NB];
 #pragma unroll
-        for (int m = 0; m < 2 * NB; ++m) dst[m] = v[m];
+            for (int m = 0; m < 2 * NB; ++m) v[m] = dst[m];
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                v[m] += qa[m];
+                v[NB + m] += qb[m];
+            }
+#pragma unroll
+            for (int m = 0; m < 2 * NB; ++m) dst[m] = v[m];
+        };
+        if constexpr (PHASED) {
+            for (int32_t q = 0; q < G; ++q)
+                if (phase == q) rmw();
+        } else {
+            rmw();
+        }
     }
 }
 
@@ -688,16 +734,24 @@ __global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A
                 const int32_t i = u / ngroups;
                 const int32_t k0 = (u - i * ngroups) * 64 * S + S * lane;
                 const GatherItem it = Q[i];
-                const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
-                const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
-                if (a1 != kNotFast) {
+                const int32_t form = (int32_t)uniform((uint32_t)it.form);
+                if (form > 0) {
                     const float dt = __uint_as_float(uniform(__float_as_uint(it.dt)));
-                    if (S == kGroup)
-                        gather_fast_group<NB, true>(it, a1, b1, dt, w, k0, S, z0, n, col);
-                    else
-                        gather_fast_group<NB, false>(it, a1, b1, dt, w, k0, S, z0, n, col);
+                    const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
+                    const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
+                    if (form == 1) {
+                        if (S == kGroup)
+                            gather_fast_group<NB, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
+                        else
+                            gather_fast_group<NB, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
+                    } else {
+                        if (S == kGroup)
+                            gather_fast_group<NB, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, form, lane);
+                        else
+                            gather_fast_group<NB, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, form, lane);
+                    }
                 } else {
-                    gather_general_group<NB>(it, b1 != 0, w, k0, S, z0, z1, col);
+                    gather_general_group<NB>(it, form == kGeneralExclusive, w, k0, S, z0, z1, col);
                 }
 #pragma unroll
                 for (int c = 0; c < kGroup; ++c)

@@ -546,35 +546,75 @@ MBP_HD MBP_INLINE bool gather_exclusive(int32_t S, int32_t rows, double za0, dou
 // processed one at a time by the whole wave (lanes = rows).
 //
 // The fast form applies when each row's z extent inside the cell is below one cell, so a
-// row has at most two pieces (cells fa and fa + 1), and the rows of one instruction (S
-// apart) are more than two cells apart, so the cell pairs {fa, fa + 1} of different lanes
-// are disjoint. A lane then takes its S consecutive rows relative to an integer origin cell
-// in signed fixed point with kZFrac fraction bits: differences of positions are exact
-// integers, so the share of the lower cell, (distance to the plane above) / extent, keeps
-// full relative precision however flat the row is.
+// row has at most two pieces (cells fa and fa + 1), and lanes that write together are more
+// than two cells apart, so their cell pairs {fa, fa + 1} are disjoint. A lane takes S
+// consecutive rows. Its origin row (the middle one when the lane holds kGatherGroup rows,
+// else the first) is placed in fp64: the integer cell I below that row's lower end, and the
+// row's two ends relative to I in signed fixed point with kZFrac fraction bits, rounded to
+// nearest. The other rows move from it by whole multiples of the per-row advance (rounded to
+// the same resolution), which keeps every row of the lane within kFastSpan cells of it and so
+// inside the fixed point's range. Differences of positions are exact integers: the share of
+// each cell, (distance to the plane between them) / extent, keeps full relative precision
+// however flat the row is.
 
-constexpr int kZFrac = 27;
+constexpr int kZFrac = 28;
 constexpr int32_t kZOne = 1 << kZFrac;
-constexpr double kZScale = 134217728.0;          // 2^kZFrac
-constexpr int32_t kNotFast = INT32_MIN;
+constexpr double kZScale = 268435456.0;            // 2^kZFrac
+// Most cells a lane's rows move from its origin row: positions stay below 1 + 1 + kFastSpan
+// cells in magnitude, inside the 8 cells of the fixed point.
+constexpr double kFastSpan = 5.5;
+// GatherItem::form of items in the general form: lanes add exclusively, or need atomics.
+constexpr int32_t kGeneralExclusive = 0;
+constexpr int32_t kGeneralAtomic = -1;
 
 struct GatherItem {
     double za0, za1;    // z cell coordinate where row k enters the cell: za0 + k za1
     double zb0, zb1;    // ... and where it leaves: zb0 + k zb1
     float dt;           // parameter length of the crossing
     int32_t yoff;       // view * cols + column: the line of the reordered sinogram
-    int32_t a1fx;       // fast form: za1 in fixed point; kNotFast selects the general form
-    int32_t b1fx;       // fast form: zb1 in fixed point; general form: 1 if lanes add exclusively
+    int32_t a1fx;       // fast form: za1 in fixed point
+    int32_t b1fx;       // fast form: zb1 in fixed point
+    int32_t form;       // fast form: its write phases (>= 1); else kGeneralExclusive/kGeneralAtomic
+    int32_t pad_[3];    // 64 bytes: the wave reads an item with four aligned 16-byte loads
 };
 
-// Whether an item takes the fast form (rows 0 .. rows_pad - 1, lanes S rows apart, each
-// lane's rows within twelve cells of its first).
+// The row of a lane (0 .. S - 1) that holds the lane's origin, and the most rows any other row
+// of the lane lies from it.
+MBP_HD MBP_INLINE int32_t fast_origin_row(int32_t S) {
+    return S == kGatherGroup ? kGatherGroup / 2 : 0;
+}
+MBP_HD MBP_INLINE int32_t fast_span_rows(int32_t S) {
+    return S == kGatherGroup ? kGatherGroup / 2 : S - 1;
+}
+
+// Most write phases of the fast form.
+constexpr int32_t kMaxPhases = 16;
+
+// Write phases of a fast item whose rows advance by a1 and b1 per row (fixed point): lanes
+// that write in the same phase are S * G rows apart, which must move z by more than two cells
+// (plus a margin of 2^-10 cell, far above the fixed point's rounding) so that their cell pairs
+// are disjoint. G = floor(need / step) + 1 from an fp64 quotient of integers below 2^53:
+// should the quotient round up to an integer, G comes out one larger, which still separates
+// the pairs. 0 when more than kMaxPhases would be needed.
+MBP_HD MBP_INLINE int32_t fast_phases(int32_t S, int32_t a1, int32_t b1) {
+    const uint64_t a = (uint64_t)(a1 < 0 ? -(int64_t)a1 : (int64_t)a1);
+    const uint64_t b = (uint64_t)(b1 < 0 ? -(int64_t)b1 : (int64_t)b1);
+    const uint64_t step = (uint64_t)S * (a < b ? a : b);
+    const uint64_t need = 2 * (uint64_t)kZOne + ((uint64_t)kZOne >> 10);
+    if (step > need) return 1;
+    if ((uint64_t)kMaxPhases * step <= need) return 0;        // also step == 0
+    return (int32_t)floor((double)need / (double)step) + 1;
+}
+
+// Whether an item takes the fast form (rows 0 .. rows_pad - 1): both ends move the same way,
+// every row spans less than one cell, a lane's rows stay within kFastSpan cells of its
+// origin row, and some number of write phases separates the lanes' cell pairs. a1, b1: the
+// per-row advances in fixed point.
 MBP_HD MBP_INLINE bool gather_fast(int32_t S, int32_t rows_pad, double za0, double za1,
-                                   double zb0, double zb1) {
-    const double a = fabs(za1), b = fabs(zb1);
+                                   double zb0, double zb1, int32_t a1, int32_t b1) {
     const double e0 = fabs(zb0 - za0), e1 = fabs(zb0 - za0 + (double)(rows_pad - 1) * (zb1 - za1));
-    return za1 * zb1 > 0.0 && (double)S * fmin(a, b) > 2.0 + 1e-6 &&
-           (double)(S - 1) * fmax(a, b) <= 12.0 && fmax(e0, e1) < 1.0 - 1e-6;
+    return za1 * zb1 > 0.0 && (double)fast_span_rows(S) * fmax(fabs(za1), fabs(zb1)) <= kFastSpan &&
+           fmax(e0, e1) < 1.0 - 1e-6 && fast_phases(S, a1, b1) > 0;
 }
 
 // The item of column line L crossing the cell, or false when it misses.
@@ -589,40 +629,42 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
     it.zb1 = L.c2 + t1 * L.c3;
     it.dt = (float)(t1 - t0);
     it.yoff = yoff;
-    if (gather_fast(S, rows_pad, it.za0, it.za1, it.zb0, it.zb1)) {
-        it.a1fx = (int32_t)rint(it.za1 * kZScale);
-        it.b1fx = (int32_t)rint(it.zb1 * kZScale);
-    } else {
-        it.a1fx = kNotFast;
-        it.b1fx = gather_exclusive(S, rows, it.za0, it.za1, it.zb0, it.zb1) ? 1 : 0;
-    }
+    // the per-row advances in fixed point (only meaningful when they fit; checked below)
+    const bool fits = fabs(it.za1) < kFastSpan && fabs(it.zb1) < kFastSpan;
+    it.a1fx = fits ? (int32_t)rint(it.za1 * kZScale) : 0;
+    it.b1fx = fits ? (int32_t)rint(it.zb1 * kZScale) : 0;
+    if (fits && gather_fast(S, rows_pad, it.za0, it.za1, it.zb0, it.zb1, it.a1fx, it.b1fx))
+        it.form = fast_phases(S, it.a1fx, it.b1fx);
+    else
+        it.form = gather_exclusive(S, rows, it.za0, it.za1, it.zb0, it.zb1) ? kGeneralExclusive
+                                                                          : kGeneralAtomic;
+    it.pad_[0] = it.pad_[1] = it.pad_[2] = 0;
     return true;
 }
 
-// A lane's origin for the fast form: its first row k (as a double), the integer cell I below
-// that row's lower end and the row's ends relative to I in fixed point. `base` is I minus
-// `cell0` (the cell held at index 0); lanes whose rows are far outside (|I| >= 2^30) get a
-// base that puts every pair out of range.
+// A lane's origin for the fast form from its origin row k (as a double): the integer cell I
+// below that row's lower end and the row's ends relative to I in fixed point, rounded to
+// nearest. `base` is I minus `cell0` (the cell held at index 0); lanes whose rows are far
+// outside (|I| >= 2^30) get a base that puts every pair out of range.
 MBP_HD MBP_INLINE void fast_origin(const GatherItem& it, double k, int32_t cell0, int32_t& la,
                                    int32_t& lb, int32_t& base) {
     const double za = fma(k, it.za1, it.za0), zb = fma(k, it.zb1, it.zb0);
     const double I = floor(fmin(za, zb));
     const bool far = !(fabs(I) < 1073741824.0);
-    la = far ? 0 : (int32_t)((za - I) * kZScale);
-    lb = far ? 0 : (int32_t)((zb - I) * kZScale);
+    la = far ? 0 : (int32_t)rint((za - I) * kZScale);
+    lb = far ? 0 : (int32_t)rint((zb - I) * kZScale);
     base = far ? 1073741824 : (int32_t)I - cell0;
 }
 
 // One row of the fast form with ends za, zb (fixed point, relative to the lane origin): the
-// lower cell fa (relative to the origin), and the lower cell's share num / ext of the row when
-// it crosses the plane above fa (split), else the whole row.
-MBP_HD MBP_INLINE void fast_row(int32_t za, int32_t zb, int32_t& fa, int32_t& num, int32_t& ext,
-                                bool& split) {
+// lower cell fa (relative to the origin), the distance num from the lower end to the plane
+// above fa and the extent ext. The row crosses that plane exactly when num < ext; then the
+// lower cell's share is num / ext and the upper one's (ext - num) / ext.
+MBP_HD MBP_INLINE void fast_row(int32_t za, int32_t zb, int32_t& fa, uint32_t& num, uint32_t& ext) {
     const int32_t lo = za < zb ? za : zb, hi = za < zb ? zb : za;
     fa = lo >> kZFrac;                              // arithmetic shift: floor
-    num = kZOne - (lo & (kZOne - 1));               // distance from lo to the plane above
-    ext = hi - lo;
-    split = num < ext;
+    num = (uint32_t)(kZOne - (lo & (kZOne - 1)));
+    ext = (uint32_t)(hi - lo);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -32,7 +32,7 @@ def _load():
         lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P]
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
-        lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, P, P, P]
+        lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, I, P, P, P]
         lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
         lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_gather_conflicts.restype = I64
@@ -135,10 +135,12 @@ def check_rays(path: str, geom: dict, traj: dict, ray_ids) -> tuple:
     return int(visits), int(viol.value)
 
 
-def gather(geom: dict, traj: dict, sino: np.ndarray, kernel_shares: bool = True):
+def gather(geom: dict, traj: dict, sino: np.ndarray, kernel_shares: bool = True,
+           general_only: bool = False):
     """Replay the cell-gather adjoint item by item (fast fixed-point items with fp32 shares as
     the kernel computes them, or fp64 shares from the same integers; fp64 sums) on a
-    (views, rows, cols) sinogram. Returns (volume, violations, items in the fast form)."""
+    (views, rows, cols) sinogram; general_only takes every item in the fp64 general form.
+    Returns (volume, violations, items in the fast form)."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
     rows = int(geom.get("rows", 1))
@@ -148,7 +150,8 @@ def gather(geom: dict, traj: dict, sino: np.ndarray, kernel_shares: bool = True)
     viol, fast = ctypes.c_longlong(0), ctypes.c_longlong(0)
     lib.mbph_gather(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n), views, rows, cols,
                     float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)), _ptr(s),
-                    int(kernel_shares), _ptr(vol), ctypes.byref(viol), ctypes.byref(fast))
+                    int(kernel_shares), int(general_only), _ptr(vol), ctypes.byref(viol),
+                    ctypes.byref(fast))
     return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value), int(fast.value)
 
 
