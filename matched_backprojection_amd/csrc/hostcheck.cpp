@@ -281,13 +281,14 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                         w[k] = (double)sino[((int64_t)v * rows + k) * cols + j] * len;
                     }
                     // the kernel carries the crossing length in fp32; the fp64 replay takes it
-                    // from the clip again
-                    double dt = (double)it.dt;
-                    if (!kernel_shares) {
-                        double t0, t1;
-                        cell_clip(lines[(size_t)v * cols + j], line, x0, x1, y0, y1, t0, t1);
-                        dt = t1 - t0;
-                    }
+                    // from the clip again, and so the general form's positions (a fast item
+                    // holds them in fixed point)
+                    const ColLine& L = lines[(size_t)v * cols + j];
+                    double t0, t1;
+                    cell_clip(L, line, x0, x1, y0, y1, t0, t1);
+                    const double dt = kernel_shares ? (double)it.dt : t1 - t0;
+                    const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
+                    const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
                     if (it.form > 0 && !general_only) {
                         ++*fast;
                         for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S)
@@ -295,7 +296,7 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                                 const int32_t k0 = g0 + S * lane;
                                 const int32_t c0 = fast_origin_row(S);
                                 int32_t la, lb, base;
-                                fast_origin(it, (double)(k0 + c0), -1, la, lb, base);
+                                fast_origin(it, k0 + c0, -1, la, lb, base);
                                 for (int32_t c = 0; c < S; ++c) {
                                     // the row's ends must stay inside the fixed point's range
                                     const int64_t pa = (int64_t)la + (int64_t)(c - c0) * it.a1fx;
@@ -329,8 +330,8 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                     }
                     for (int k = 0; k < rows; ++k) {
                         auto piece = [&](int32_t iz, double share) { add(iz, share, w[k]); };
-                        const double za = std::fma((double)k, it.za1, it.za0);
-                        const double zb = std::fma((double)k, it.zb1, it.zb0);
+                        const double za = std::fma((double)k, za1, za0);
+                        const double zb = std::fma((double)k, zb1, zb0);
                         const double fa = std::floor(std::fmin(za, zb)), fb = std::floor(std::fmax(za, zb));
                         if (fa == fb && fa >= 0.0 && fa < (double)D) piece((int32_t)fa, dt);
                         else row_pieces_split(za, zb, dt, 0, D, false, piece);
@@ -395,7 +396,7 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                                         const int32_t c0 = fast_origin_row(S);
                                         int32_t la, lb, base, fa;
                                         uint32_t num, ext;
-                                        fast_origin(it, (double)(k0 + c0), -1, la, lb, base);
+                                        fast_origin(it, k0 + c0, -1, la, lb, base);
                                         fast_row(la + (c - c0) * it.a1fx, lb + (c - c0) * it.b1fx, fa, num, ext);
                                         const int32_t i0 = base + fa;
                                         if ((uint32_t)i0 > (uint32_t)D) continue;   // discard pair

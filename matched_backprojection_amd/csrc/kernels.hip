@@ -552,6 +552,39 @@ __device__ __forceinline__ int32_t clamp_pair(int32_t i, int32_t hi) {
     return r;
 }
 
+// i clamped to [lo, hi] (lo in a vector register, hi uniform): one v_med3_i32.
+__device__ __forceinline__ int32_t clamp_range(int32_t i, int32_t lo, int32_t hi) {
+    int32_t r;
+    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(i), "v"(lo), "s"(hi));
+    return r;
+}
+
+// (i << SH) + b: one v_lshl_add_u32, kept as written (the compiler would otherwise fold the
+// per-lane base back into each row's index).
+template <int SH>
+__device__ __forceinline__ int32_t shl_add(int32_t i, int32_t b) {
+    int32_t r;
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(i), "i"(SH), "v"(b));
+    return r;
+}
+
+// A uniform value held in a vector register (one v_mov_b32, made once).
+__device__ __forceinline__ int32_t in_vgpr(int32_t v) {
+    int32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+    return r;
+}
+
+typedef __attribute__((address_space(3))) float lds_float;
+
+// The LDS byte address of a pointer into the kernel's shared memory, and back.
+__device__ __forceinline__ int32_t lds_addr(float* p) {
+    return (int32_t)(uintptr_t)(lds_float*)p;
+}
+__device__ __forceinline__ lds_float* lds_ptr(int32_t a) {
+    return (lds_float*)(uintptr_t)(uint32_t)a;
+}
+
 // a * b with 0 * anything = 0 (also 0 * inf): one v_mul_legacy_f32.
 __device__ __forceinline__ float mul_legacy(float a, float b) {
     float r;
@@ -580,7 +613,19 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
     }
     constexpr int c0 = FULL ? kGroup / 2 : 0;
     int32_t la, lb, base;
-    fast_origin(it, (double)(k0 + c0), z0 - 1, la, lb, base);
+    fast_origin(it, k0 + c0, z0 - 1, la, lb, base);
+    // A row's pair index base + fa (fa within 8 cells of the origin) is clamped to [-2, n + 1].
+    // One member: the clamp works on byte addresses. The base is first clamped to
+    // [-16, n + 16], which leaves every clamped index unchanged and keeps the address far from
+    // overflow, so each row forms its address with one shift-add and one clamp (two and four
+    // members keep the index form, which needs fewer registers).
+    const int32_t a0 = lds_addr(col);
+    int32_t abase = 0, alo = 0, ahi = 0;
+    if constexpr (NB == 1) {
+        abase = (clamp_range(base, -16, n + 16) << 2) + a0;
+        alo = in_vgpr(a0 - 8);
+        ahi = a0 + ((n + 1) << 2);
+    }
     int32_t za[kGroup], zb[kGroup];
     za[c0] = la;
     zb[c0] = lb;
@@ -609,8 +654,11 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         const float r = __builtin_amdgcn_rcpf((float)ext);
         const float f = fminf((float)num * r, 1.0f);
         const float g = mul_legacy((float)__builtin_elementwise_sub_sat(ext, num), r);
-        const int32_t idx = clamp_pair(base + fa, n + 1);
-        float* dst = col + idx * NB;
+        lds_float* dst;
+        if constexpr (NB == 1)
+            dst = lds_ptr(clamp_range(shl_add<2>(fa, abase), alo, ahi));
+        else
+            dst = lds_ptr(a0 + clamp_pair(base + fa, n + 1) * (4 * NB));
         float qa[NB], qb[NB];
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
@@ -619,16 +667,24 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
             qb[m] = g * q;
         }
         auto rmw = [&]() {
-            float v[2 * NB];
+            if constexpr (NB == 1) {
+                const float lo = dst[0], hi = dst[1];
+                dst[0] = lo + qa[0];
+                dst[1] = hi + qb[0];
+            } else {
+                // through the cell's own vector type, so that the compiler knows its alignment
+                // (4 * NB bytes) and moves each cell with one access
+                typedef __attribute__((address_space(3))) float __attribute__((ext_vector_type(NB))) cell_t;
+                cell_t* cp = (cell_t*)dst;
+                cell_t lo = cp[0], hi = cp[1];
 #pragma unroll
-            for (int m = 0; m < 2 * NB; ++m) v[m] = dst[m];
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-                v[m] += qa[m];
-                v[NB + m] += qb[m];
+                for (int m = 0; m < NB; ++m) {
+                    lo[m] += qa[m];
+                    hi[m] += qb[m];
+                }
+                cp[0] = lo;
+                cp[1] = hi;
             }
-#pragma unroll
-            for (int m = 0; m < 2 * NB; ++m) dst[m] = v[m];
         };
         if constexpr (PHASED) {
             for (int32_t q = 0; q < G; ++q)
@@ -681,14 +737,13 @@ __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool 
     }
 }
 
+// Occupancy: four waves per SIMD (at most 128 vector registers) for one and two members, three
+// (168) for four.
 template <int NB>
-__global__ void __launch_bounds__(256) column_gather_kernel(const ColumnLaunch A,
-                                                            const ColLine* __restrict__ lines,
-                                                            const float* __restrict__ ysc,
-                                                            float* __restrict__ vol,
-                                                            int32_t zchunk, int32_t nchunks,
-                                                            int32_t tx, int32_t ty,
-                                                            int32_t accumulate) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 4 ? 3 : 4)))
+column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
+                     const float* __restrict__ ysc, float* __restrict__ vol, int32_t zchunk,
+                     int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate) {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);

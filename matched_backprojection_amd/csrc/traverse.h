@@ -567,9 +567,21 @@ constexpr double kFastSpan = 5.5;
 constexpr int32_t kGeneralExclusive = 0;
 constexpr int32_t kGeneralAtomic = -1;
 
+// Fast items hold their positions as signed fixed point with kPosFrac fraction bits instead
+// of fp64, so that a lane's origin needs only integer multiply-adds. The start positions carry
+// half a unit of 2^-kZFrac, so that truncating to kZFrac bits rounds to nearest.
+constexpr int kPosFrac = 40;
+constexpr double kPosScale = 1099511627776.0;      // 2^kPosFrac
+// Fast items keep |z| below this many cells at every row, so positions fit in 64 bits.
+constexpr double kPosLimit = 4194304.0;            // 2^22
+
 struct GatherItem {
-    double za0, za1;    // z cell coordinate where row k enters the cell: za0 + k za1
-    double zb0, zb1;    // ... and where it leaves: zb0 + k zb1
+    // z cell coordinate where row k enters the cell, za0 + k za1, and where it leaves,
+    // zb0 + k zb1; fast items: the same four values in fixed point (fa0 ... fb1)
+    union { double za0; int64_t fa0; };
+    union { double za1; int64_t fa1; };
+    union { double zb0; int64_t fb0; };
+    union { double zb1; int64_t fb1; };
     float dt;           // parameter length of the crossing
     int32_t yoff;       // view * cols + column: the line of the reordered sinogram
     int32_t a1fx;       // fast form: za1 in fixed point
@@ -629,31 +641,54 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
     it.zb1 = L.c2 + t1 * L.c3;
     it.dt = (float)(t1 - t0);
     it.yoff = yoff;
-    // the per-row advances in fixed point (only meaningful when they fit; checked below)
-    const bool fits = fabs(it.za1) < kFastSpan && fabs(it.zb1) < kFastSpan;
+    // the per-row advances in fixed point (only meaningful when they fit; checked below), and
+    // the positions' range at the first and last padded rows
+    const double kl = (double)(rows_pad - 1);
+    const bool fits = fabs(it.za1) < kFastSpan && fabs(it.zb1) < kFastSpan &&
+                      fmax(fmax(fabs(it.za0), fabs(it.zb0)),
+                           fmax(fabs(fma(kl, it.za1, it.za0)), fabs(fma(kl, it.zb1, it.zb0)))) < kPosLimit;
     it.a1fx = fits ? (int32_t)rint(it.za1 * kZScale) : 0;
     it.b1fx = fits ? (int32_t)rint(it.zb1 * kZScale) : 0;
-    if (fits && gather_fast(S, rows_pad, it.za0, it.za1, it.zb0, it.zb1, it.a1fx, it.b1fx))
+    if (fits && gather_fast(S, rows_pad, it.za0, it.za1, it.zb0, it.zb1, it.a1fx, it.b1fx)) {
         it.form = fast_phases(S, it.a1fx, it.b1fx);
-    else
+        const double half = 0.5 / kZScale;
+        const int64_t a0 = (int64_t)rint((it.za0 + half) * kPosScale);
+        const int64_t a1 = (int64_t)rint(it.za1 * kPosScale);
+        const int64_t b0 = (int64_t)rint((it.zb0 + half) * kPosScale);
+        const int64_t b1 = (int64_t)rint(it.zb1 * kPosScale);
+        it.fa0 = a0;
+        it.fa1 = a1;
+        it.fb0 = b0;
+        it.fb1 = b1;
+    } else {
         it.form = gather_exclusive(S, rows, it.za0, it.za1, it.zb0, it.zb1) ? kGeneralExclusive
                                                                           : kGeneralAtomic;
+    }
     it.pad_[0] = it.pad_[1] = it.pad_[2] = 0;
     return true;
 }
 
-// A lane's origin for the fast form from its origin row k (as a double): the integer cell I
-// below that row's lower end and the row's ends relative to I in fixed point, rounded to
-// nearest. `base` is I minus `cell0` (the cell held at index 0); lanes whose rows are far
-// outside (|I| >= 2^30) get a base that puts every pair out of range.
-MBP_HD MBP_INLINE void fast_origin(const GatherItem& it, double k, int32_t cell0, int32_t& la,
+// A lane's origin for the fast form from its origin row k: the integer cell I of that row's
+// entry end and the row's ends relative to I in fixed point (the entry end in [0, 1) cell, the
+// exit end in (-1, 2)), rounded to nearest. `base` is I minus `cell0` (the cell held at index
+// 0).
+// k * f for a row index 0 <= k < 2^16 and |f| < 2^43: the low word's 32 x 32 -> 64 product
+// plus the high word's product (below 2^27 in magnitude) shifted up, modulo 2^64.
+MBP_HD MBP_INLINE int64_t row_times(int32_t k, int64_t f) {
+    const uint32_t lo = (uint32_t)f;
+    const int32_t hi = (int32_t)(f >> 32);
+    return (int64_t)((uint64_t)(uint32_t)k * lo + ((uint64_t)(uint32_t)(k * hi) << 32));
+}
+
+MBP_HD MBP_INLINE void fast_origin(const GatherItem& it, int32_t k, int32_t cell0, int32_t& la,
                                    int32_t& lb, int32_t& base) {
-    const double za = fma(k, it.za1, it.za0), zb = fma(k, it.zb1, it.zb0);
-    const double I = floor(fmin(za, zb));
-    const bool far = !(fabs(I) < 1073741824.0);
-    la = far ? 0 : (int32_t)rint((za - I) * kZScale);
-    lb = far ? 0 : (int32_t)rint((zb - I) * kZScale);
-    base = far ? 1073741824 : (int32_t)I - cell0;
+    const int64_t pa = it.fa0 + row_times(k, it.fa1);
+    const int64_t pb = it.fb0 + row_times(k, it.fb1);
+    const int32_t I = (int32_t)(pa >> kPosFrac);                   // arithmetic shift: floor
+    const int64_t ref = (int64_t)I * ((int64_t)1 << kPosFrac);
+    la = (int32_t)((pa - ref) >> (kPosFrac - kZFrac));
+    lb = (int32_t)((pb - ref) >> (kPosFrac - kZFrac));
+    base = I - cell0;
 }
 
 // One row of the fast form with ends za, zb (fixed point, relative to the lane origin): the
