@@ -190,6 +190,13 @@ __device__ __forceinline__ void load_vals(const float* __restrict__ p, float* v)
     }
 }
 
+// a * b with 0 * anything = 0 (also 0 * inf): one v_mul_legacy_f32.
+__device__ __forceinline__ float mul_legacy(float a, float b) {
+    float r;
+    asm("v_mul_legacy_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Third dword of a raw buffer resource (32-bit elements, unformatted access).
 constexpr int kBufferFlags = 0x00020000;
 
@@ -345,7 +352,13 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                                 const_cast<float*>(vol + (size_t)cell[q] * D * NB), (short)0, colbytes, kBufferFlags);
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
-                                if (len[2 * q + h] != 0.0f) {
+                                // one member: the first piece (empty only when the row meets a
+                                // z plane exactly at the cell's entry) is loaded unconditionally
+                                // and multiplied with 0 * anything = 0, so an empty piece adds
+                                // nothing even next to a non-finite voxel; the second piece is
+                                // empty whenever the row does not cross a z plane in this cell
+                                // (it then names the first piece's voxel) and keeps its branch
+                                if ((NB == 1 && h == 0) || len[2 * q + h] != 0.0f) {
                                     buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h]);
                                 } else {
 #pragma unroll
@@ -354,9 +367,17 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                             }
                         }
 #pragma unroll
-                        for (int q = 0; q < 2 * kCellGroup; ++q)
+                        for (int q = 0; q < 2 * kCellGroup; ++q) {
+                            if constexpr (NB == 1) {
+                                if (q % 2 == 0)
+                                    acc[0] += mul_legacy(len[q], val[q][0]);
+                                else
+                                    acc[0] = fmaf(len[q], val[q][0], acc[0]);
+                            } else {
 #pragma unroll
-                            for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
+                                for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
+                            }
+                        }
                     }
                 } else {
                     groups([&](double tb, int32_t& z0, float& l0, int32_t& z1, float& l1) {
@@ -585,12 +606,6 @@ __device__ __forceinline__ lds_float* lds_ptr(int32_t a) {
     return (lds_float*)(uintptr_t)(uint32_t)a;
 }
 
-// a * b with 0 * anything = 0 (also 0 * inf): one v_mul_legacy_f32.
-__device__ __forceinline__ float mul_legacy(float a, float b) {
-    float r;
-    asm("v_mul_legacy_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
 
 // Fast form of one item for one group of rows (see gather_fast): every row adds its two
 // pieces to the cell pair {fa, fa + 1} with one paired read and write. The lane's rows are
