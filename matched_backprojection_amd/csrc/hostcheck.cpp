@@ -345,14 +345,15 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
 
 // Emulates the gather's instruction grouping and checks its race-freedom claims. Fast items:
 // for every instruction (row c of each lane), the cell pairs {fa, fa + 1} that in-range lanes
-// read and write must be disjoint. General items that the kernel treats as exclusive: for
+// read and write must be disjoint (kFastPairs), or, per write phase, their lower cells and
+// then their upper cells must be distinct (kFastSplit). General items that the kernel treats as exclusive: for
 // every instruction and every step (the single-piece add, then step i of the aligned piece
 // walk), the z cells the active lanes add into must be distinct. Returns the number of items
 // checked; *conflicts counts instructions or steps with a repeated cell, *fast the fast items.
 // mode 0 replays the kernel; three planted mistakes show the check can fail: mode 1 starts
 // the walk of rows that span several cells at the first in-range cell (rows entering from
 // below the box then meet in its bottom cell), mode 2 deals adjacent rows to the lanes of one
-// instruction, mode 3 lets all lanes of a fast item write in one phase.
+// instruction, mode 3 writes the cell pairs of split fast items at once, without phases.
 int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, const double* pitch,
                               const int32_t* n, int views, int rows, int cols, double du, double dv,
                               int mode, long long* conflicts, long long* fast) {
@@ -385,26 +386,31 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                     for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S) {
                         for (int32_t c = 0; c < S; ++c) {
                             if (is_fast) {
-                                // lane l writes in phase l mod G; modes 2 and 3 ignore the phases
-                                const int32_t G = mode >= 2 ? 1 : it.form;
+                                // pairs: every lane's pair at once; split: lower cells, then
+                                // upper cells, lane l in phase l mod G; mode 2 ignores the
+                                // phases, mode 3 writes split items as pairs at once
+                                const bool split = it.form == kFastSplit && mode != 3;
+                                const int32_t G = mode >= 2 || !split ? 1 : it.split;
                                 if (G < 1) ++*conflicts;
-                                for (int32_t q = 0; q < std::max(G, 1); ++q) {
-                                    seen.clear();
-                                    for (int lane = q; lane < 64; lane += std::max(G, 1)) {
-                                        // mode 2: adjacent rows in one instruction
-                                        const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
-                                        const int32_t c0 = fast_origin_row(S);
-                                        int32_t la, lb, base, fa;
-                                        uint32_t num, ext;
-                                        fast_origin(it, k0 + c0, -1, la, lb, base);
-                                        fast_row(la + (c - c0) * it.a1fx, lb + (c - c0) * it.b1fx, fa, num, ext);
-                                        const int32_t i0 = base + fa;
-                                        if ((uint32_t)i0 > (uint32_t)D) continue;   // discard pair
-                                        seen.push_back(i0);
-                                        seen.push_back(i0 + 1);
+                                for (int pass = 0; pass < (split ? 2 : 1); ++pass) {
+                                    for (int32_t q = 0; q < std::max(G, 1); ++q) {
+                                        seen.clear();
+                                        for (int lane = q; lane < 64; lane += std::max(G, 1)) {
+                                            // mode 2: adjacent rows in one instruction
+                                            const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
+                                            const int32_t c0 = fast_origin_row(S);
+                                            int32_t la, lb, base, fa;
+                                            uint32_t num, ext;
+                                            fast_origin(it, k0 + c0, -1, la, lb, base);
+                                            fast_row(la + (c - c0) * it.a1fx, lb + (c - c0) * it.b1fx, fa, num, ext);
+                                            const int32_t i0 = base + fa;
+                                            if ((uint32_t)i0 > (uint32_t)D) continue;   // discard pair
+                                            if (!split || pass == 0) seen.push_back(i0);
+                                            if (!split || pass == 1) seen.push_back(i0 + 1);
+                                        }
+                                        std::sort(seen.begin(), seen.end());
+                                        if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
                                     }
-                                    std::sort(seen.begin(), seen.end());
-                                    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
                                 }
                                 continue;
                             }

@@ -608,12 +608,13 @@ __device__ __forceinline__ lds_float* lds_ptr(int32_t a) {
 
 
 // Fast form of one item for one group of rows (see gather_fast): every row adds its two
-// pieces to the cell pair {fa, fa + 1} with one paired read and write. The lane's rows are
-// placed relative to its origin row c0 (fast_origin_row): row c lies (c - c0) per-row
-// advances a1, b1 from it, an exact integer step. PHASED: the lanes write in G phases (lane l
-// in phase l mod G); lanes of one phase are S * G rows apart and so hold disjoint pairs;
-// otherwise all lanes write at once. FULL: the lane takes all kGroup rows (S == kGroup), so
-// the unrolled rows need no guard.
+// pieces to the cell pair {fa, fa + 1}. The lane's rows are placed relative to its origin row
+// c0 (fast_origin_row): row c lies (c - c0) per-row advances a1, b1 from it, an exact integer
+// step. Not PHASED (kFastPairs): all lanes update their pairs at once with one paired read and
+// write. PHASED (kFastSplit): all lanes update their lower cells, then their upper cells, each
+// in G write phases (lane l in phase l mod G); lanes of one phase are S * G rows apart and so
+// hold distinct cells. FULL: the lane takes all kGroup rows (S == kGroup), so the unrolled rows
+// need no guard.
 template <int NB, bool FULL, bool PHASED>
 __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
                                                   float dt, const float (&w)[kGroup][NB],
@@ -681,31 +682,42 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
             qa[m] = f * q;
             qb[m] = g * q;
         }
-        auto rmw = [&]() {
-            if constexpr (NB == 1) {
-                const float lo = dst[0], hi = dst[1];
-                dst[0] = lo + qa[0];
-                dst[1] = hi + qb[0];
-            } else {
-                // through the cell's own vector type, so that the compiler knows its alignment
-                // (4 * NB bytes) and moves each cell with one access
-                typedef __attribute__((address_space(3))) float __attribute__((ext_vector_type(NB))) cell_t;
-                cell_t* cp = (cell_t*)dst;
-                cell_t lo = cp[0], hi = cp[1];
-#pragma unroll
-                for (int m = 0; m < NB; ++m) {
-                    lo[m] += qa[m];
-                    hi[m] += qb[m];
-                }
-                cp[0] = lo;
-                cp[1] = hi;
-            }
-        };
+        // cells are moved through their own vector type, so that the compiler knows their
+        // alignment (4 * NB bytes) and moves each with one access
+        typedef __attribute__((address_space(3))) float __attribute__((ext_vector_type(NB))) cell_t;
         if constexpr (PHASED) {
-            for (int32_t q = 0; q < G; ++q)
-                if (phase == q) rmw();
+            // lower cells in G phases, then upper cells in G phases
+            cell_t* cp = (cell_t*)dst;
+            for (int32_t q = 0; q < G; ++q) {
+                if (phase == q) {
+                    cell_t v = cp[0];
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) v[m] += qa[m];
+                    cp[0] = v;
+                }
+            }
+            for (int32_t q = 0; q < G; ++q) {
+                if (phase == q) {
+                    cell_t v = cp[1];
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) v[m] += qb[m];
+                    cp[1] = v;
+                }
+            }
+        } else if constexpr (NB == 1) {
+            const float lo = dst[0], hi = dst[1];
+            dst[0] = lo + qa[0];
+            dst[1] = hi + qb[0];
         } else {
-            rmw();
+            cell_t* cp = (cell_t*)dst;
+            cell_t lo = cp[0], hi = cp[1];
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                lo[m] += qa[m];
+                hi[m] += qb[m];
+            }
+            cp[0] = lo;
+            cp[1] = hi;
         }
     }
 }
@@ -752,10 +764,10 @@ __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool 
     }
 }
 
-// Occupancy: four waves per SIMD (at most 128 vector registers) for one and two members, three
-// (168) for four.
+// Occupancy: four waves per SIMD (at most 128 vector registers) for one member, three (168)
+// for two and four.
 template <int NB>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 4 ? 3 : 4)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 3)))
 column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                      const float* __restrict__ ysc, float* __restrict__ vol, int32_t zchunk,
                      int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate) {
@@ -809,16 +821,17 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                     const float dt = __uint_as_float(uniform(__float_as_uint(it.dt)));
                     const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
                     const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
-                    if (form == 1) {
+                    if (form == kFastPairs) {
                         if (S == kGroup)
                             gather_fast_group<NB, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
                         else
                             gather_fast_group<NB, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
                     } else {
+                        const int32_t G = (int32_t)uniform((uint32_t)it.split);
                         if (S == kGroup)
-                            gather_fast_group<NB, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, form, lane);
+                            gather_fast_group<NB, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
                         else
-                            gather_fast_group<NB, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, form, lane);
+                            gather_fast_group<NB, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
                     }
                 } else {
                     gather_general_group<NB>(it, form == kGeneralExclusive, w, k0, S, z0, z1, col);

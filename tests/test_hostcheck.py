@@ -194,9 +194,9 @@ def test_fast_gather_cell_pairs_never_collide(flip):
 def test_gather_plain_lds_adds_never_collide(name):
     """Where the gather adds into LDS without atomics, the lanes that write together hit
     distinct z cells (emulated instruction by instruction and write phase by write phase;
-    these twins have one to eight rows per lane, so their fast items need several phases).
-    Dealing adjacent rows to one instruction, or letting all lanes write in one phase,
-    collides, so the check has teeth."""
+    these twins have one to eight rows per lane, so many fast items split their writes into
+    lower- and upper-cell passes with phases). Dealing adjacent rows to one instruction, or
+    writing the split items' cell pairs at once, collides, so the check has teeth."""
     cfg = SMALL_CONFIGS[name]
     geom, traj = _geom(cfg), config_trajectory(cfg)
     checked, conflicts, fast = HC.gather_conflicts(geom, traj, mode=0)
