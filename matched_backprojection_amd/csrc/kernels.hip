@@ -557,13 +557,19 @@ __device__ __forceinline__ void gather_tile_cell(uint32_t xy, int32_t H, int32_t
     iy = (int32_t)((tile % tiles_y) * (uint32_t)ty + within % (uint32_t)ty);
 }
 
-// A lane's kGroup consecutive rows starting at row k0 of one sinogram line (rows past the
-// lane's S are loaded and ignored: a fixed count keeps the loads unconditional, so the next
-// unit's loads can be in flight while the current one is summed).
-template <int NB>
-__device__ __forceinline__ void gather_load_rows(const float* __restrict__ p, float (&w)[kGroup][NB]) {
+// A lane's KR consecutive rows starting at row k0 of one sinogram line, KR being S rounded up
+// to a power of two (rows past the lane's S are loaded and ignored: a fixed count keeps the
+// loads unconditional, so the next unit's loads can be in flight while the current one is
+// summed).
+template <int NB, int KR>
+__device__ __forceinline__ void gather_load_rows(const float* __restrict__ p, float (&w)[KR][NB]) {
 #pragma unroll
-    for (int c = 0; c < kGroup; ++c) load_vals<NB>(p + c * NB, w[c]);
+    for (int c = 0; c < KR; ++c) load_vals<NB>(p + c * NB, w[c]);
+}
+
+// Rows a lane loads per unit for S rows per lane: S rounded up to a power of two.
+__host__ __device__ constexpr int32_t gather_rows_loaded(int32_t S) {
+    return S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : kGroup;
 }
 
 // Pair index clamped to [-2, hi]: one v_med3_i32 (the compiler emits a max and a min).
@@ -613,11 +619,11 @@ __device__ __forceinline__ lds_float* lds_ptr(int32_t a) {
 // step. Not PHASED (kFastPairs): all lanes update their pairs at once with one paired read and
 // write. PHASED (kFastSplit): all lanes update their lower cells, then their upper cells, each
 // in G write phases (lane l in phase l mod G); lanes of one phase are S * G rows apart and so
-// hold distinct cells. FULL: the lane takes all kGroup rows (S == kGroup), so the unrolled rows
+// hold distinct cells. FULL: the lane takes all KR loaded rows (S == KR), so the unrolled rows
 // need no guard.
-template <int NB, bool FULL, bool PHASED>
+template <int NB, int KR, bool FULL, bool PHASED>
 __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
-                                                  float dt, const float (&w)[kGroup][NB],
+                                                  float dt, const float (&w)[KR][NB],
                                                   int32_t k0, int32_t S, int32_t z0, int32_t n,
                                                   float* col, int32_t G, int32_t lane) {
     int32_t phase = 0;
@@ -627,7 +633,8 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         const uint32_t qt = (uint32_t)(((float)lane + 0.5f) * __builtin_amdgcn_rcpf((float)G));
         phase = lane - (int32_t)qt * G;
     }
-    constexpr int c0 = FULL ? kGroup / 2 : 0;
+    // the origin row of fast_origin_row(S): the middle one when S == kGroup
+    constexpr int c0 = FULL && KR == kGroup ? kGroup / 2 : 0;
     int32_t la, lb, base;
     fast_origin(it, k0 + c0, z0 - 1, la, lb, base);
     // A row's pair index base + fa (fa within 8 cells of the origin) is clamped to [-2, n + 1].
@@ -642,11 +649,11 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         alo = in_vgpr(a0 - 8);
         ahi = a0 + ((n + 1) << 2);
     }
-    int32_t za[kGroup], zb[kGroup];
+    int32_t za[KR], zb[KR];
     za[c0] = la;
     zb[c0] = lb;
 #pragma unroll
-    for (int c = c0 + 1; c < kGroup; ++c) {
+    for (int c = c0 + 1; c < KR; ++c) {
         za[c] = za[c - 1] + a1;
         zb[c] = zb[c - 1] + b1;
     }
@@ -656,7 +663,7 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         zb[c] = zb[c + 1] - b1;
     }
 #pragma unroll
-    for (int c = 0; c < kGroup; ++c) {
+    for (int c = 0; c < KR; ++c) {
         if (!FULL && c >= S) continue;
         int32_t fa;
         uint32_t num, ext;
@@ -724,9 +731,9 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
 
 // General form of one item for one group of rows: rows of any z extent, pieces walked in
 // fp64; plain LDS read-add-write when the item's lanes add exclusively, else LDS atomics.
-template <int NB>
+template <int NB, int KR>
 __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool exclusive,
-                                                     const float (&w)[kGroup][NB], int32_t k0,
+                                                     const float (&w)[KR][NB], int32_t k0,
                                                      int32_t S, int32_t z0, int32_t z1,
                                                      float* col) {
     const double dt = (double)it.dt;
@@ -742,7 +749,7 @@ __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool 
         }
     };
 #pragma unroll
-    for (int c = 0; c < kGroup; ++c) {
+    for (int c = 0; c < KR; ++c) {
         if (c >= S) continue;
         const double kd = (double)(k0 + c);
         const double za = fma(kd, it.za1, it.za0);
@@ -766,7 +773,7 @@ __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool 
 
 // Occupancy: four waves per SIMD (at most 128 vector registers) for one member, three (168)
 // for two and four.
-template <int NB>
+template <int NB, int KR>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 3)))
 column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                      const float* __restrict__ ysc, float* __restrict__ vol, int32_t zchunk,
@@ -809,10 +816,10 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
         auto drain = [&](int32_t count) {
             const int32_t units = count * ngroups;
             if (units == 0) return;
-            float w[kGroup][NB], wn[kGroup][NB];
-            gather_load_rows<NB>(unit_rows(0), w);
+            float w[KR][NB], wn[KR][NB];
+            gather_load_rows<NB, KR>(unit_rows(0), w);
             for (int32_t u = 0; u < units; ++u) {
-                gather_load_rows<NB>(unit_rows(u + 1 < units ? u + 1 : u), wn);
+                gather_load_rows<NB, KR>(unit_rows(u + 1 < units ? u + 1 : u), wn);
                 const int32_t i = u / ngroups;
                 const int32_t k0 = (u - i * ngroups) * 64 * S + S * lane;
                 const GatherItem it = Q[i];
@@ -822,22 +829,22 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                     const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
                     const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
                     if (form == kFastPairs) {
-                        if (S == kGroup)
-                            gather_fast_group<NB, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
+                        if (S == KR)
+                            gather_fast_group<NB, KR, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
                         else
-                            gather_fast_group<NB, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
+                            gather_fast_group<NB, KR, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
                     } else {
                         const int32_t G = (int32_t)uniform((uint32_t)it.split);
-                        if (S == kGroup)
-                            gather_fast_group<NB, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
+                        if (S == KR)
+                            gather_fast_group<NB, KR, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
                         else
-                            gather_fast_group<NB, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
+                            gather_fast_group<NB, KR, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
                     }
                 } else {
-                    gather_general_group<NB>(it, form == kGeneralExclusive, w, k0, S, z0, z1, col);
+                    gather_general_group<NB, KR>(it, form == kGeneralExclusive, w, k0, S, z0, z1, col);
                 }
 #pragma unroll
-                for (int c = 0; c < kGroup; ++c)
+                for (int c = 0; c < KR; ++c)
 #pragma unroll
                     for (int m = 0; m < NB; ++m) w[c][m] = wn[c][m];
             }
@@ -1137,12 +1144,15 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
                                     (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
-    switch (nb) {
-        case 1: column_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
-        case 2: column_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
-        case 4: column_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
-        default: return hipErrorInvalidValue;
-    }
+    const int32_t kr = gather_rows_loaded(gather_stride(a.rows));
+#define MBP_GATHER(NB_, KR_) \
+    if (nb == NB_ && kr == KR_) \
+        column_gather_kernel<NB_, KR_><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate)
+    MBP_GATHER(1, 1); else MBP_GATHER(1, 2); else MBP_GATHER(1, 4); else MBP_GATHER(1, 8);
+    else MBP_GATHER(2, 1); else MBP_GATHER(2, 2); else MBP_GATHER(2, 4); else MBP_GATHER(2, 8);
+    else MBP_GATHER(4, 1); else MBP_GATHER(4, 2); else MBP_GATHER(4, 4); else MBP_GATHER(4, 8);
+    else return hipErrorInvalidValue;
+#undef MBP_GATHER
     return hipGetLastError();
 }
 

@@ -183,6 +183,36 @@ def test_tall_detector_parity(torch_dev, mbp, oracle, flip):
     plan.close()
 
 
+@pytest.mark.parametrize("rows", [150, 200])
+def test_mid_detector_parity(torch_dev, mbp, oracle, rows):
+    """Three and four rows per lane (the gather loads four rows per lane; with three, the
+    fourth is loaded and ignored), unbatched and with a batch of four."""
+    from dataclasses import replace
+    from tests.test_hostcheck import tall_detector_config
+    torch, dev = torch_dev
+    cfg = replace(tall_detector_config(), rows=rows, name=f"c4m_rows{rows}")
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(rows)
+    x = rng.random(cfg.shape).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    ys = rng.random((4,) + ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    plan = make_plan(mbp, cfg, traj=traj)
+    assert plan.info["path"] == "column"
+    say(f"case mid detector rows={rows} forward")
+    p = plan.project(to_device_volume(torch, dev, x, cfg.layout)).cpu().numpy().astype(np.float64)
+    check(p, ref, "forward")
+    for B in (0, 4):
+        say(f"case mid detector rows={rows} adjoint B={B}")
+        yd = torch.from_numpy(ys[0] if B == 0 else ys[:B]).to(dev)
+        b = plan.backproject(yd).cpu().numpy().astype(np.float64)
+        if B == 0:
+            check(b, bref[0], "adjoint")
+        for m in range(B):
+            check(b[m], bref[m], f"adjoint member {m}")
+    plan.close()
+
+
 def test_parallel3d_parity(torch_dev, mbp, oracle):
     """3-D parallel beam (infinite lines): circular with detector rows along z (column walk
     with the gather adjoint, and the generic walk), random directions with tilted detectors
