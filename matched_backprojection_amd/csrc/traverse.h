@@ -648,10 +648,10 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
     it.zb1 = L.c2 + t1 * L.c3;
     it.dt = (float)(t1 - t0);
     it.yoff = yoff;
-    // the per-row advances in fixed point (only meaningful when they fit; checked below), and
-    // the positions' range at the first and last padded rows
+    // the per-row advances in fixed point (only meaningful when they fit; checked below), the
+    // row count (row_times) and the positions' range at the first and last padded rows
     const double kl = (double)(rows_pad - 1);
-    const bool fits = fabs(it.za1) < kFastSpan && fabs(it.zb1) < kFastSpan &&
+    const bool fits = rows_pad <= (1 << 20) && fabs(it.za1) < kFastSpan && fabs(it.zb1) < kFastSpan &&
                       fmax(fmax(fabs(it.za0), fabs(it.zb0)),
                            fmax(fabs(fma(kl, it.za1, it.za0)), fabs(fma(kl, it.zb1, it.zb0)))) < kPosLimit;
     it.a1fx = fits ? (int32_t)rint(it.za1 * kZScale) : 0;
@@ -685,8 +685,8 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
 // entry end and the row's ends relative to I in fixed point (the entry end in [0, 1) cell, the
 // exit end in (-1, 2)), rounded to nearest. `base` is I minus `cell0` (the cell held at index
 // 0).
-// k * f for a row index 0 <= k < 2^16 and |f| < 2^43: the low word's 32 x 32 -> 64 product
-// plus the high word's product (below 2^27 in magnitude) shifted up, modulo 2^64.
+// k * f for a row index 0 <= k < 2^20 and |f| < 2^43: the low word's 32 x 32 -> 64 product
+// plus the high word's product (below 2^31 in magnitude) shifted up, modulo 2^64.
 MBP_HD MBP_INLINE int64_t row_times(int32_t k, int64_t f) {
     const uint32_t lo = (uint32_t)f;
     const int32_t hi = (int32_t)(f >> 32);
