@@ -270,6 +270,26 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    # context: the HBM bandwidth a plain device-to-device copy reaches on this GPU (2 GiB read
+    # and 2 GiB written per copy), and each kernel's algorithmic rate against it
+    src = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = []
+    for _ in range(5):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        copy_ms.append(ev[0].elapsed_time(ev[1]))
+    copy_gbs = 2.0 * src.numel() * 4 / (float(np.median(copy_ms)) * 1e-3) / 1e9
+    del src, dst
+    log(f"device-to-device copy: {copy_gbs:.0f} GB/s")
+    result["config"]["hbm_copy_GBs"] = copy_gbs
+    result["config"]["forward_GBs_algorithmic"] = alg_bytes / (f_avg * 1e-3) / 1e9
+    result["config"]["adjoint_GBs_algorithmic"] = alg_bytes / (b_avg * 1e-3) / 1e9
+    result["config"]["pct_copy_bandwidth_pair"] = 100.0 * pair_gbs / copy_gbs
     if args.cgls > 0:
         # context, not the headline: one CGLS solve of args.cgls iterations on the same
         # workload after a two-iteration warm-up solve (the pages time ten-iteration solves
