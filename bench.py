@@ -150,7 +150,7 @@ def main() -> int:
     ap.add_argument("--cgls", type=int, default=10,
                     help="iterations of the CGLS solve timed for context (0: skip)")
     ap.add_argument("--no-others", dest="others", action="store_false",
-                    help="skip timing the 256^3 cone and the batched helical cone")
+                    help="skip timing the 256^3 cone, the batched helical cone and the tilted cone")
     ap.add_argument("--probe", action="store_true",
                     help="for hardware-counter runs: one forward, one adjoint and a 1 GiB "
                          "device-to-device copy (the counters' calibration), no timing")
@@ -310,10 +310,15 @@ def main() -> int:
         result["config"]["cgls_iters"] = args.cgls
         del ws, xc
     if args.others:
-        # the 256^3 cone of the metric and the batched helical cone, timed the same way
+        # the 256^3 cone of the metric, the batched helical cone, and the 256^3 cone with its
+        # detector tilted by a few degrees in its plane (rows no longer along z: the generic
+        # walk with the atomic adjoint), volume z-fastest; timed the same way
+        from dataclasses import replace
+        tilted = replace(CONFIGS["c3_cone256"], name="c3_cone256_tilted",
+                         trajectory="circular_tilted", layout="WHD")
         result["config"]["other_workloads"] = [
-            measure_pair(mbp, torch, CONFIGS[name], steps=5, warmup=2)
-            for name in ("c3_cone256", "c5_helical_b4")]
+            measure_pair(mbp, torch, c, steps=5, warmup=2)
+            for c in (CONFIGS["c3_cone256"], CONFIGS["c5_helical_b4"], tilted)]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, traj, x)
     print(json.dumps(result), flush=True)

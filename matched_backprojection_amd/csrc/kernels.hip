@@ -51,15 +51,30 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
 // ------------------------------------------------------------------------------------------
 // Generic walk
 
+// Pixel (row k, column j) of thread index `rem` within a view: columns fastest, or rows
+// fastest for z-fastest volumes (A.rows_fast); `rem` becomes the pixel's sinogram offset
+// k * cols + j.
+__device__ __forceinline__ void generic_pixel(const GenericLaunch& A, uint32_t& rem, int32_t& k,
+                                              int32_t& j) {
+    if (A.rows_fast) {
+        j = (int32_t)(rem / (uint32_t)A.rows);
+        k = (int32_t)(rem - (uint32_t)j * (uint32_t)A.rows);
+        rem = (uint32_t)k * (uint32_t)A.cols + (uint32_t)j;
+    } else {
+        k = (int32_t)(rem / (uint32_t)A.cols);
+        j = (int32_t)(rem - (uint32_t)k * (uint32_t)A.cols);
+    }
+}
+
 __global__ void __launch_bounds__(256) generic_forward_kernel(const GenericLaunch A,
                                                               const Ptrs4 vol, const MPtrs4 sino) {
     const uint32_t per_view = (uint32_t)A.rows * (uint32_t)A.cols;
     const uint32_t rid = blockIdx.x * 256u + threadIdx.x;
     if (rid >= (uint32_t)A.nviews * per_view) return;
     const uint32_t vl = rid / per_view;
-    const uint32_t rem = rid - vl * per_view;
-    const int32_t k = (int32_t)(rem / (uint32_t)A.cols);
-    const int32_t j = (int32_t)(rem - (uint32_t)k * (uint32_t)A.cols);
+    uint32_t rem = rid - vl * per_view;
+    int32_t k, j;
+    generic_pixel(A, rem, k, j);
     const int32_t view = A.view0 + (int32_t)vl;
     const Frame F = A.frames[view];
     RayWalk r;
@@ -87,9 +102,9 @@ __global__ void __launch_bounds__(256) generic_adjoint_kernel(const GenericLaunc
     const uint32_t rid = blockIdx.x * 256u + threadIdx.x;
     if (rid >= (uint32_t)A.nviews * per_view) return;
     const uint32_t vl = rid / per_view;
-    const uint32_t rem = rid - vl * per_view;
-    const int32_t k = (int32_t)(rem / (uint32_t)A.cols);
-    const int32_t j = (int32_t)(rem - (uint32_t)k * (uint32_t)A.cols);
+    uint32_t rem = rid - vl * per_view;
+    int32_t k, j;
+    generic_pixel(A, rem, k, j);
     const int32_t view = A.view0 + (int32_t)vl;
     const int64_t ray = (int64_t)view * per_view + rem;
     const int nb = A.nb;
@@ -611,7 +626,6 @@ __device__ __forceinline__ int32_t lds_addr(float* p) {
 __device__ __forceinline__ lds_float* lds_ptr(int32_t a) {
     return (lds_float*)(uintptr_t)(uint32_t)a;
 }
-
 
 // Fast form of one item for one group of rows (see gather_fast): every row adds its two
 // pieces to the cell pair {fa, fa + 1}. The lane's rows are placed relative to its origin row

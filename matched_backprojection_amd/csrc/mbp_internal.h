@@ -20,7 +20,7 @@ struct GenericLaunch {
     int32_t nb;
     Box box;
     int32_t sx, sy, sz;       // volume element strides along world x, y, z
-    int32_t pad_;
+    int32_t rows_fast;        // consecutive threads take consecutive rows (z-fastest volumes)
 };
 
 // Arguments of one column-walk launch: waves over (view, column, block of 64 rows). The

@@ -256,6 +256,8 @@ mbp::GenericLaunch generic_args(const mbp_plan* p, const DeviceState* d, int32_t
     const int32_t D = (int32_t)g.D, H = (int32_t)g.H, W = (int32_t)g.W;
     if (whd) { a.sz = 1; a.sy = D; a.sx = D * H; }
     else     { a.sx = 1; a.sy = W; a.sz = W * H; }
+    // in a z-fastest volume, rays of neighbouring detector rows read neighbouring voxels
+    a.rows_fast = whd && g.rows > 1;
     return a;
 }
 

@@ -115,13 +115,18 @@ def test_configs_plan_and_pick_walks(lib, name):
 
 
 def test_tilted_detector_uses_generic_walk(lib):
+    """Random tilted frames, and a circular orbit whose detector is rotated by a few degrees
+    in its plane: the row axis is not along z, so only the generic walk applies."""
+    from dataclasses import replace
     cfg = SMALL_CONFIGS["c3_cone256"]
-    rc, h = _create(lib, _geometry(cfg), random_cone_trajectory(cfg.views, seed=1, radius=200.0,
-                                                                  sdd=350.0))
-    assert rc == 0
-    inf = _info(lib, h)
-    assert inf.column_capable == 0 and inf.path == 1
-    lib.mbp_plan_destroy(h)
+    tilted = replace(cfg, trajectory="circular_tilted")
+    for traj in (random_cone_trajectory(cfg.views, seed=1, radius=200.0, sdd=350.0),
+                 config_trajectory(tilted)):
+        rc, h = _create(lib, _geometry(cfg), traj)
+        assert rc == 0
+        inf = _info(lib, h)
+        assert inf.column_capable == 0 and inf.path == 1
+        lib.mbp_plan_destroy(h)
 
 
 def test_batch_zero_and_bad_calls_do_no_device_work(lib):

@@ -269,6 +269,34 @@ def test_general_trajectory_parity(torch_dev, mbp, oracle):
     plan.close()
 
 
+@pytest.mark.parametrize("layout", ["DHW", "WHD"])
+def test_tilted_circular_parity(torch_dev, mbp, oracle, layout):
+    """A circular cone whose detector is rotated by a few degrees in its plane (rows not
+    along z): the generic walk, with threads taking consecutive columns (DHW volume) or
+    consecutive rows (z-fastest volume), unbatched and with a batch of two."""
+    from dataclasses import replace
+    torch, dev = torch_dev
+    cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory="circular_tilted", layout=layout)
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(41)
+    xs = rng.random((2,) + cfg.shape).astype(np.float32)
+    ref = oracle.project(geom, traj, xs)
+    ys = rng.random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    plan = make_plan(mbp, cfg, traj=traj)
+    assert plan.info["path"] == "generic"
+    for B in (0, 2):
+        say(f"case tilted circular cone layout={layout} B={B}")
+        x_in = xs[0] if B == 0 else xs
+        p = plan.project(to_device_volume(torch, dev, x_in, layout)).cpu().numpy().astype(np.float64)
+        y_in = ys[0] if B == 0 else ys
+        b = plan.backproject(torch.from_numpy(y_in).to(dev)).cpu().numpy().astype(np.float64)
+        for m in range(max(B, 1)):
+            check(p if B == 0 else p[m], ref[m], f"forward member {m}")
+            check(b if B == 0 else b[m], bref[m], f"adjoint member {m}")
+    plan.close()
+
+
 def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
     """Ragged view batches, both layouts, batch sizes 0..5, accumulation, caller workspace."""
     torch, dev = torch_dev

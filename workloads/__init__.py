@@ -17,6 +17,7 @@ from .trajectories import (
     circular_cone_trajectory,
     helical_cone_trajectory,
     random_cone_trajectory,
+    tilted_cone_trajectory,
     parallel_3d_trajectory,
     random_parallel_3d_trajectory,
     config_trajectory,
@@ -26,6 +27,7 @@ __all__ = [
     "CONFIGS", "SMALL_CONFIGS", "Config", "get_config",
     "ellipsoid_phantom", "add_noise", "sinogram_field", "config_phantom",
     "parallel_2d_trajectory", "fan_2d_trajectory", "circular_cone_trajectory",
-    "helical_cone_trajectory", "random_cone_trajectory", "parallel_3d_trajectory",
+    "helical_cone_trajectory", "random_cone_trajectory",
+    "tilted_cone_trajectory", "parallel_3d_trajectory",
     "random_parallel_3d_trajectory", "config_trajectory",
 ]

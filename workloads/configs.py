@@ -28,7 +28,7 @@ from typing import Optional, Tuple
 class Config:
     name: str
     beam: str                      # "parallel" | "fan" | "cone" | "parallel3d"
-    trajectory: str                # "parallel_half" | "circular" | "helical"
+    trajectory: str                # "parallel_half" | "circular" | "circular_tilted" | "helical"
     shape: Tuple[int, ...]         # (H, W) or (D, H, W)
     spacing: Tuple[float, ...]     # tensor order
     views: int

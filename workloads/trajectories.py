@@ -107,6 +107,21 @@ def random_cone_trajectory(views: int, seed: int, radius: float = 150.0,
     return {"src": src, "det": det, "eu": eu, "ev": ev}
 
 
+# In-plane detector rotation of the tilted circular cone (a calibration-sized tilt).
+TILT_DEG = 2.0
+
+
+def tilted_cone_trajectory(views: int, sid: float, sdd: float, tilt_deg: float = TILT_DEG) -> dict:
+    """Circular cone trajectory whose detector axes are rotated in the detector plane by
+    tilt_deg about the viewing direction, so the row axis is no longer parallel to z."""
+    t = circular_cone_trajectory(views, sid, sdd)
+    c, s = np.cos(np.radians(tilt_deg)), np.sin(np.radians(tilt_deg))
+    eu, ev = t["eu"].copy(), t["ev"].copy()
+    t["eu"] = c * eu + s * ev
+    t["ev"] = -s * eu + c * ev
+    return t
+
+
 def parallel_3d_trajectory(views: int, tilt: float = 0.0) -> dict:
     """3-D parallel beam on a circle: view k looks along (cos t, sin t, 0), t = k*pi/views, at
     a detector through the origin with eu = (-sin t, cos t, 0) and ev = z; with tilt != 0 the
@@ -157,4 +172,6 @@ def config_trajectory(cfg: Config) -> dict:
         return fan_2d_trajectory(cfg.views, cfg.sid, cfg.sdd)
     if cfg.trajectory == "helical":
         return helical_cone_trajectory(cfg.views, cfg.turns, cfg.rise_per_turn, cfg.sid, cfg.sdd)
+    if cfg.trajectory == "circular_tilted":
+        return tilted_cone_trajectory(cfg.views, cfg.sid, cfg.sdd)
     return circular_cone_trajectory(cfg.views, cfg.sid, cfg.sdd)
