@@ -573,7 +573,7 @@ __device__ __forceinline__ void gather_tile_cell(uint32_t xy, int32_t H, int32_t
 }
 
 // A lane's KR consecutive rows starting at row k0 of one sinogram line, KR being S rounded up
-// to a power of two (rows past the lane's S are loaded and ignored: a fixed count keeps the
+// (gather_rows_loaded; rows past the lane's S are loaded and ignored: a fixed count keeps the
 // loads unconditional, so the next unit's loads can be in flight while the current one is
 // summed).
 template <int NB, int KR>
@@ -582,9 +582,9 @@ __device__ __forceinline__ void gather_load_rows(const float* __restrict__ p, fl
     for (int c = 0; c < KR; ++c) load_vals<NB>(p + c * NB, w[c]);
 }
 
-// Rows a lane loads per unit for S rows per lane: S rounded up to a power of two.
+// Rows a lane loads per unit for S rows per lane: S rounded up to 1, 2, 4, 6 or 8.
 __host__ __device__ constexpr int32_t gather_rows_loaded(int32_t S) {
-    return S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : kGroup;
+    return S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : S <= 6 ? 6 : kGroup;
 }
 
 // Pair index clamped to [-2, hi]: one v_med3_i32 (the compiler emits a max and a min).
@@ -1162,9 +1162,9 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
 #define MBP_GATHER(NB_, KR_) \
     if (nb == NB_ && kr == KR_) \
         column_gather_kernel<NB_, KR_><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate)
-    MBP_GATHER(1, 1); else MBP_GATHER(1, 2); else MBP_GATHER(1, 4); else MBP_GATHER(1, 8);
-    else MBP_GATHER(2, 1); else MBP_GATHER(2, 2); else MBP_GATHER(2, 4); else MBP_GATHER(2, 8);
-    else MBP_GATHER(4, 1); else MBP_GATHER(4, 2); else MBP_GATHER(4, 4); else MBP_GATHER(4, 8);
+    MBP_GATHER(1, 1); else MBP_GATHER(1, 2); else MBP_GATHER(1, 4); else MBP_GATHER(1, 6); else MBP_GATHER(1, 8);
+    else MBP_GATHER(2, 1); else MBP_GATHER(2, 2); else MBP_GATHER(2, 4); else MBP_GATHER(2, 6); else MBP_GATHER(2, 8);
+    else MBP_GATHER(4, 1); else MBP_GATHER(4, 2); else MBP_GATHER(4, 4); else MBP_GATHER(4, 6); else MBP_GATHER(4, 8);
     else return hipErrorInvalidValue;
 #undef MBP_GATHER
     return hipGetLastError();

@@ -183,10 +183,11 @@ def test_tall_detector_parity(torch_dev, mbp, oracle, flip):
     plan.close()
 
 
-@pytest.mark.parametrize("rows", [150, 200])
+@pytest.mark.parametrize("rows", [150, 200, 300])
 def test_mid_detector_parity(torch_dev, mbp, oracle, rows):
-    """Three and four rows per lane (the gather loads four rows per lane; with three, the
-    fourth is loaded and ignored), unbatched and with a batch of four."""
+    """Three, four and five rows per lane (the gather loads four rows per lane for three and
+    four, six for five; rows past a lane's own are loaded and ignored), unbatched and with a
+    batch of four."""
     from dataclasses import replace
     from tests.test_hostcheck import tall_detector_config
     torch, dev = torch_dev
