@@ -549,19 +549,20 @@ MBP_HD MBP_INLINE bool gather_exclusive(int32_t S, int32_t rows, double za0, dou
 // row has at most two pieces (cells fa and fa + 1), and lanes that write together are more
 // than two cells apart, so their cell pairs {fa, fa + 1} are disjoint. A lane takes S
 // consecutive rows. Its origin row (the middle one when the lane holds kGatherGroup rows,
-// else the first) is placed in fp64: the integer cell I below that row's lower end, and the
-// row's two ends relative to I in signed fixed point with kZFrac fraction bits, rounded to
-// nearest. The other rows move from it by whole multiples of the per-row advance (rounded to
-// the same resolution), which keeps every row of the lane within kFastSpan cells of it and so
-// inside the fixed point's range. Differences of positions are exact integers: the share of
+// else the first) is placed from the item's 64-bit fixed-point positions: the integer cell I
+// of that row's entry end, and the row's two ends relative to I in signed fixed point with
+// kZFrac fraction bits, rounded to nearest. The other rows move from it by whole multiples of
+// the per-row advance (rounded to the same resolution), which keeps every row of the lane
+// within kFastSpan cells of it and so inside the fixed point's range. Differences of positions are exact integers: the share of
 // each cell, (distance to the plane between them) / extent, keeps full relative precision
 // however flat the row is.
 
 constexpr int kZFrac = 28;
 constexpr int32_t kZOne = 1 << kZFrac;
 constexpr double kZScale = 268435456.0;            // 2^kZFrac
-// Most cells a lane's rows move from its origin row: positions stay below 1 + 1 + kFastSpan
-// cells in magnitude, inside the 8 cells of the fixed point.
+// Most cells a lane's rows move from its origin row: positions (the origin's ends within
+// (-1, 2) cells of its integer cell) stay below 2 + kFastSpan cells in magnitude, inside the
+// 8 cells of the fixed point.
 constexpr double kFastSpan = 5.5;
 // GatherItem::form. Fast form: all lanes update their cell pairs at once (kFastPairs), or
 // update lower and then upper cells in separate passes of GatherItem::split write phases
@@ -681,10 +682,6 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
     return true;
 }
 
-// A lane's origin for the fast form from its origin row k: the integer cell I of that row's
-// entry end and the row's ends relative to I in fixed point (the entry end in [0, 1) cell, the
-// exit end in (-1, 2)), rounded to nearest. `base` is I minus `cell0` (the cell held at index
-// 0).
 // k * f for a row index 0 <= k < 2^20 and |f| < 2^43: the low word's 32 x 32 -> 64 product
 // plus the high word's product (below 2^31 in magnitude) shifted up, modulo 2^64.
 MBP_HD MBP_INLINE int64_t row_times(int32_t k, int64_t f) {
@@ -693,6 +690,10 @@ MBP_HD MBP_INLINE int64_t row_times(int32_t k, int64_t f) {
     return (int64_t)((uint64_t)(uint32_t)k * lo + ((uint64_t)(uint32_t)(k * hi) << 32));
 }
 
+// A lane's origin for the fast form from its origin row k: the integer cell I of that row's
+// entry end and the row's ends relative to I in fixed point (the entry end in [0, 1) cell, the
+// exit end in (-1, 2)), rounded to nearest. `base` is I minus `cell0` (the cell held at index
+// 0); |I| < 2^22 (kPosLimit).
 MBP_HD MBP_INLINE void fast_origin(const GatherItem& it, int32_t k, int32_t cell0, int32_t& la,
                                    int32_t& lb, int32_t& base) {
     const int64_t pa = it.fa0 + row_times(k, it.fa1);
