@@ -544,8 +544,11 @@ __global__ void __launch_bounds__(256) column_line_kernel(const ColumnLaunch A, 
 // more than one z cell, so the 64 LDS additions of one instruction go to different addresses.
 constexpr int kGroup = kGatherGroup;
 // Items a wave queues before it processes them (the queue is drained once it holds more
-// than kQueue - 64, so one more round of 64 always fits).
-constexpr int kQueue = 96;
+// than kQueue - 64, so one more round of 64 always fits). 80 items are 5 KiB per wave: with a
+// column of up to 5 KiB (256 cells of four members, or 1280 of one) a block of four waves
+// takes at most 40 KiB, so four blocks share a CU's 160 KiB and the register budget, not
+// LDS, sets the occupancy.
+constexpr int kQueue = 80;
 // Lanes per view when items are built.
 constexpr int kViewLanes = 4;
 
@@ -707,23 +710,24 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         // alignment (4 * NB bytes) and moves each with one access
         typedef __attribute__((address_space(3))) float __attribute__((ext_vector_type(NB))) cell_t;
         if constexpr (PHASED) {
-            // lower cells in G phases, then upper cells in G phases
-            cell_t* cp = (cell_t*)dst;
+            // lower cells in G phases, then upper cells in G phases; a lane outside the
+            // current phase adds to the parked pair at index -2 instead (never written out),
+            // so every phase is one unmasked read-add-write
+            cell_t* const cp = (cell_t*)dst;
+            cell_t* const park = (cell_t*)lds_ptr(a0 - 8 * NB);
             for (int32_t q = 0; q < G; ++q) {
-                if (phase == q) {
-                    cell_t v = cp[0];
+                cell_t* const p = phase == q ? cp : park;
+                cell_t v = p[0];
 #pragma unroll
-                    for (int m = 0; m < NB; ++m) v[m] += qa[m];
-                    cp[0] = v;
-                }
+                for (int m = 0; m < NB; ++m) v[m] += qa[m];
+                p[0] = v;
             }
             for (int32_t q = 0; q < G; ++q) {
-                if (phase == q) {
-                    cell_t v = cp[1];
+                cell_t* const p = phase == q ? cp : park;
+                cell_t v = p[1];
 #pragma unroll
-                    for (int m = 0; m < NB; ++m) v[m] += qb[m];
-                    cp[1] = v;
-                }
+                for (int m = 0; m < NB; ++m) v[m] += qb[m];
+                p[1] = v;
             }
         } else if constexpr (NB == 1) {
             const float lo = dst[0], hi = dst[1];
