@@ -343,17 +343,85 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
     return 0;
 }
 
+namespace {
+
+// One instruction of a kFastRuns item as the kernel performs it, on sets of lanes in place of
+// values: lane l starts with its own lower-cell share {l} and upper-cell share {l}; `steps`
+// one-lane shifts sum each run's lower-cell shares into its first lane and its upper-cell
+// shares into its last lane; the first lane takes the upper-cell sum of the run before it when
+// that run's upper cell is its lower cell. key: the lanes' clamped pair indices, monotone
+// along the wave (rising with the lane when up); cells 1 .. D are the column's own. Returns
+// whether a share bound for one of those cells is lost, taken twice or sent to another cell,
+// or two lanes write one such cell in one store.
+bool runs_fail(const int32_t* key, bool up, int32_t D, int32_t steps) {
+    auto at = [&](int l, int d) {                       // lane d steps forward of l, or -1
+        const int s = up ? l + d : l - d;
+        return s >= 0 && s < 64 ? s : -1;
+    };
+    auto real = [&](int32_t cell) { return cell >= 1 && cell <= D; };
+    bool first[64], last[64], adj[64];
+    uint64_t T[64], U[64], T2[64], U2[64];
+    for (int l = 0; l < 64; ++l) {
+        const int f = at(l, 1), b = at(l, -1);
+        first[l] = b < 0 || key[b] != key[l];
+        last[l] = f < 0 || key[f] != key[l];
+        adj[l] = f >= 0 && key[f] == key[l] + 1;
+        T[l] = U[l] = 1ull << l;
+    }
+    for (int32_t k = 0; k < steps; ++k) {
+        for (int l = 0; l < 64; ++l) {
+            const int f = at(l, 1), b = at(l, -1);
+            T2[l] = (1ull << l) | (f >= 0 && !first[f] ? T[f] : 0);
+            U2[l] = (1ull << l) | (b >= 0 && !last[b] ? U[b] : 0);
+        }
+        std::copy(T2, T2 + 64, T);
+        std::copy(U2, U2 + 64, U);
+    }
+    bool bad = false;
+    int ca[64] = {}, cb[64] = {};
+    std::vector<int32_t> w1, w2;
+    for (int l = 0; l < 64; ++l) {
+        if (first[l]) {
+            const int b = at(l, -1);
+            const uint64_t h = b >= 0 && adj[b] ? U[b] : 0;
+            if (real(key[l])) w1.push_back(key[l]);
+            for (int j = 0; j < 64; ++j) {
+                if (T[l] >> j & 1) { bad |= key[j] != key[l]; ++ca[j]; }
+                if (h >> j & 1) { bad |= key[j] + 1 != key[l]; ++cb[j]; }
+            }
+        }
+        if (last[l] && !adj[l]) {
+            if (real(key[l] + 1)) w2.push_back(key[l] + 1);
+            for (int j = 0; j < 64; ++j)
+                if (U[l] >> j & 1) { bad |= key[j] != key[l]; ++cb[j]; }
+        }
+    }
+    for (int j = 0; j < 64; ++j) {
+        if (real(key[j]) && ca[j] != 1) bad = true;
+        if (real(key[j] + 1) && cb[j] != 1) bad = true;
+    }
+    for (auto* w : {&w1, &w2}) {
+        std::sort(w->begin(), w->end());
+        if (std::adjacent_find(w->begin(), w->end()) != w->end()) bad = true;
+    }
+    return bad;
+}
+
+}  // namespace
+
 // Emulates the gather's instruction grouping and checks its race-freedom claims. Fast items:
 // for every instruction (row c of each lane), the cell pairs {fa, fa + 1} that in-range lanes
-// read and write must be disjoint (kFastPairs), or, per write phase, their lower cells and
-// then their upper cells must be distinct (kFastSplit). General items that the kernel treats as exclusive: for
-// every instruction and every step (the single-piece add, then step i of the aligned piece
-// walk), the z cells the active lanes add into must be distinct. Returns the number of items
-// checked; *conflicts counts instructions or steps with a repeated cell, *fast the fast items.
-// mode 0 replays the kernel; three planted mistakes show the check can fail: mode 1 starts
-// the walk of rows that span several cells at the first in-range cell (rows entering from
-// below the box then meet in its bottom cell), mode 2 deals adjacent rows to the lanes of one
-// instruction, mode 3 writes the cell pairs of split fast items at once, without phases.
+// read and write must be disjoint (kFastPairs), or the combine of runs of lanes sharing a
+// pair must deliver every share to its cell once, with distinct cells per store (kFastRuns,
+// runs_fail). General items that the kernel treats as exclusive: for every instruction and
+// every step (the single-piece add, then step i of the aligned piece walk), the z cells the
+// active lanes add into must be distinct. Returns the number of items checked; *conflicts
+// counts instructions or steps that fail, *fast the fast items. mode 0 replays the kernel;
+// planted mistakes show the check can fail: mode 1 starts the walk of rows that span several
+// cells at the first in-range cell (rows entering from below the box then meet in its bottom
+// cell), mode 2 deals adjacent rows to the lanes of one instruction, mode 3 writes the cell
+// pairs of kFastRuns items at once without combining, mode 4 shifts their runs one step
+// fewer than the kernel.
 int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, const double* pitch,
                               const int32_t* n, int views, int rows, int cols, double du, double dv,
                               int mode, long long* conflicts, long long* fast) {
@@ -386,32 +454,35 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                     for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S) {
                         for (int32_t c = 0; c < S; ++c) {
                             if (is_fast) {
-                                // pairs: every lane's pair at once; split: lower cells, then
-                                // upper cells, lane l in phase l mod G; mode 2 ignores the
-                                // phases, mode 3 writes split items as pairs at once
-                                const bool split = it.form == kFastSplit && mode != 3;
-                                const int32_t G = mode >= 2 || !split ? 1 : it.split;
-                                if (G < 1) ++*conflicts;
-                                for (int pass = 0; pass < (split ? 2 : 1); ++pass) {
-                                    for (int32_t q = 0; q < std::max(G, 1); ++q) {
-                                        seen.clear();
-                                        for (int lane = q; lane < 64; lane += std::max(G, 1)) {
-                                            // mode 2: adjacent rows in one instruction
-                                            const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
-                                            const int32_t c0 = fast_origin_row(S);
-                                            int32_t la, lb, base, fa;
-                                            uint32_t num, ext;
-                                            fast_origin(it, k0 + c0, -1, la, lb, base);
-                                            fast_row(la + (c - c0) * it.a1fx, lb + (c - c0) * it.b1fx, fa, num, ext);
-                                            const int32_t i0 = base + fa;
-                                            if ((uint32_t)i0 > (uint32_t)D) continue;   // discard pair
-                                            if (!split || pass == 0) seen.push_back(i0);
-                                            if (!split || pass == 1) seen.push_back(i0 + 1);
-                                        }
-                                        std::sort(seen.begin(), seen.end());
-                                        if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
-                                    }
+                                // the lanes' pair indices; mode 2: adjacent rows in one instruction
+                                int32_t key[64];
+                                for (int lane = 0; lane < 64; ++lane) {
+                                    const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
+                                    const int32_t c0 = fast_origin_row(S);
+                                    int32_t la, lb, base, fa;
+                                    uint32_t num, ext;
+                                    fast_origin(it, k0 + c0, -1, la, lb, base);
+                                    fast_row(la + (c - c0) * it.a1fx, lb + (c - c0) * it.b1fx, fa, num, ext);
+                                    key[lane] = base + fa;
                                 }
+                                if (it.form == kFastRuns && mode != 3) {
+                                    // the kernel's clamp of the pair index to [-2, D + 1]
+                                    int32_t kc[64];
+                                    for (int lane = 0; lane < 64; ++lane)
+                                        kc[lane] = std::min(std::max(key[lane], -2), D + 1);
+                                    const int32_t steps = it.run - (mode == 4 ? 2 : 1);
+                                    if (it.run < 1 || runs_fail(kc, it.a1fx > 0, D, steps)) ++*conflicts;
+                                    continue;
+                                }
+                                // every lane's pair at once
+                                seen.clear();
+                                for (int lane = 0; lane < 64; ++lane) {
+                                    if ((uint32_t)key[lane] > (uint32_t)D) continue;   // discard pair
+                                    seen.push_back(key[lane]);
+                                    seen.push_back(key[lane] + 1);
+                                }
+                                std::sort(seen.begin(), seen.end());
+                                if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) ++*conflicts;
                                 continue;
                             }
                             // steps: the two-piece adds (cell fa, then cell fb), then the

@@ -545,9 +545,9 @@ __global__ void __launch_bounds__(256) column_line_kernel(const ColumnLaunch A, 
 constexpr int kGroup = kGatherGroup;
 // Items a wave queues before it processes them (the queue is drained once it holds more
 // than kQueue - 64, so one more round of 64 always fits). 80 items are 5 KiB per wave: with a
-// column of up to 5 KiB (256 cells of four members, or 1280 of one) a block of four waves
-// takes at most 40 KiB, so four blocks share a CU's 160 KiB and the register budget, not
-// LDS, sets the occupancy.
+// column of at most 5 KiB (about 1280 cells of one member, 640 of two, 320 of four) a block
+// of four waves takes at most 40 KiB, so four blocks share a CU's 160 KiB and the register
+// budget, not LDS, sets the occupancy.
 constexpr int kQueue = 80;
 // Lanes per view when items are built.
 constexpr int kViewLanes = 4;
@@ -630,26 +630,89 @@ __device__ __forceinline__ lds_float* lds_ptr(int32_t a) {
     return (lds_float*)(uintptr_t)(uint32_t)a;
 }
 
+// Values of the neighbouring lane one step along the wave (DPP wave_shl:1 takes lane l + 1's
+// value, wave_shr:1 lane l - 1's; both cross the 16-lane rows). UP: the neighbour "forward"
+// is lane l + 1. Floats read 0 past the wave's ends; keys read -1 there.
+constexpr int kDppWaveShl1 = 0x130;
+constexpr int kDppWaveShr1 = 0x138;
+template <bool UP>
+__device__ __forceinline__ float from_fwd(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v),
+                                                      UP ? kDppWaveShl1 : kDppWaveShr1, 0xF, 0xF, true));
+}
+template <bool UP>
+__device__ __forceinline__ float from_bwd(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v),
+                                                      UP ? kDppWaveShr1 : kDppWaveShl1, 0xF, 0xF, true));
+}
+template <bool UP>
+__device__ __forceinline__ int32_t key_fwd(int32_t k) {
+    return __builtin_amdgcn_update_dpp(-1, k, UP ? kDppWaveShl1 : kDppWaveShr1, 0xF, 0xF, false);
+}
+template <bool UP>
+__device__ __forceinline__ int32_t key_bwd(int32_t k) {
+    return __builtin_amdgcn_update_dpp(-1, k, UP ? kDppWaveShr1 : kDppWaveShl1, 0xF, 0xF, false);
+}
+
+// The adds of one instruction of a kFastRuns item: lane l adds qa to the cell pair's lower
+// cell and qb to its upper cell (pair address dst, monotone along the wave: rising with the
+// lane when UP). Lanes with the same pair form runs of at most G consecutive lanes. Each run's
+// lower-cell shares are summed into its first lane (towards lower cells) and its upper-cell
+// shares into its last lane, by G - 1 steps of a one-lane shift; the first lane also takes
+// the upper-cell sum of the run just below when that run's upper cell is its lower cell.
+// Then the first lane of every run writes its lower cell, and the last lane of a run whose
+// upper cell no other run holds writes that one: the cells written by one instruction are
+// distinct. Lanes with nothing to write add into the parked pair at index -2 (park). Needs
+// all 64 lanes active.
+template <int NB, bool UP>
+__device__ __forceinline__ void gather_runs_add(lds_float* dst, lds_float* park, const float (&qa)[NB],
+                                                const float (&qb)[NB], int32_t G) {
+    typedef __attribute__((address_space(3))) float __attribute__((ext_vector_type(NB))) cell_t;
+    const int32_t key = (int32_t)(uintptr_t)dst;
+    const int32_t kb = key_bwd<UP>(key), kf = key_fwd<UP>(key);
+    const bool first = kb != key, last = kf != key;
+    const bool adj = kf == key + 4 * NB;             // the next run's lower cell is our upper cell
+    // the first shift step for any G (with G == 1 every lane is a run of its own and the step
+    // adds zeros), the rest in a loop
+    float T[NB], U[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        T[m] = qa[m] + from_fwd<UP>(first ? 0.0f : qa[m]);
+        U[m] = qb[m] + from_bwd<UP>(last ? 0.0f : qb[m]);
+    }
+    for (int32_t k = 2; k < G; ++k) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            T[m] = qa[m] + from_fwd<UP>(first ? 0.0f : T[m]);
+            U[m] = qb[m] + from_bwd<UP>(last ? 0.0f : U[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NB; ++m) T[m] += from_bwd<UP>(adj ? U[m] : 0.0f);
+    cell_t* const p0 = (cell_t*)(first ? dst : park);
+    cell_t* const p1 = (cell_t*)(last && !adj ? dst : park);
+    cell_t lo = p0[0], hi = p1[1];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        lo[m] += T[m];
+        hi[m] += U[m];
+    }
+    p0[0] = lo;
+    p1[1] = hi;
+}
+
 // Fast form of one item for one group of rows (see gather_fast): every row adds its two
 // pieces to the cell pair {fa, fa + 1}. The lane's rows are placed relative to its origin row
 // c0 (fast_origin_row): row c lies (c - c0) per-row advances a1, b1 from it, an exact integer
-// step. Not PHASED (kFastPairs): all lanes update their pairs at once with one paired read and
-// write. PHASED (kFastSplit): all lanes update their lower cells, then their upper cells, each
-// in G write phases (lane l in phase l mod G); lanes of one phase are S * G rows apart and so
-// hold distinct cells. FULL: the lane takes all KR loaded rows (S == KR), so the unrolled rows
-// need no guard.
-template <int NB, int KR, bool FULL, bool PHASED>
+// step. Not RUNS (kFastPairs): all lanes update their pairs at once with one paired read and
+// write. RUNS (kFastRuns): lanes that share a pair are combined first (gather_runs_add); lanes
+// S * G rows apart never share one. FULL: the lane takes all KR loaded rows (S == KR), so the
+// unrolled rows need no guard.
+template <int NB, int KR, bool FULL, bool RUNS>
 __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
                                                   float dt, const float (&w)[KR][NB],
                                                   int32_t k0, int32_t S, int32_t z0, int32_t n,
-                                                  float* col, int32_t G, int32_t lane) {
-    int32_t phase = 0;
-    if constexpr (PHASED) {
-        // lane mod G from a float quotient: (lane + 1/2) / G stays at least 1/32 away from an
-        // integer, so the rounding of the reciprocal cannot move it
-        const uint32_t qt = (uint32_t)(((float)lane + 0.5f) * __builtin_amdgcn_rcpf((float)G));
-        phase = lane - (int32_t)qt * G;
-    }
+                                                  float* col, int32_t G) {
     // the origin row of fast_origin_row(S): the middle one when S == kGroup
     constexpr int c0 = FULL && KR == kGroup ? kGroup / 2 : 0;
     int32_t la, lb, base;
@@ -709,26 +772,12 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         // cells are moved through their own vector type, so that the compiler knows their
         // alignment (4 * NB bytes) and moves each with one access
         typedef __attribute__((address_space(3))) float __attribute__((ext_vector_type(NB))) cell_t;
-        if constexpr (PHASED) {
-            // lower cells in G phases, then upper cells in G phases; a lane outside the
-            // current phase adds to the parked pair at index -2 instead (never written out),
-            // so every phase is one unmasked read-add-write
-            cell_t* const cp = (cell_t*)dst;
-            cell_t* const park = (cell_t*)lds_ptr(a0 - 8 * NB);
-            for (int32_t q = 0; q < G; ++q) {
-                cell_t* const p = phase == q ? cp : park;
-                cell_t v = p[0];
-#pragma unroll
-                for (int m = 0; m < NB; ++m) v[m] += qa[m];
-                p[0] = v;
-            }
-            for (int32_t q = 0; q < G; ++q) {
-                cell_t* const p = phase == q ? cp : park;
-                cell_t v = p[1];
-#pragma unroll
-                for (int m = 0; m < NB; ++m) v[m] += qb[m];
-                p[1] = v;
-            }
+        if constexpr (RUNS) {
+            lds_float* const park = lds_ptr(a0 - 8 * NB);
+            if (a1 > 0)
+                gather_runs_add<NB, true>(dst, park, qa, qb, G);
+            else
+                gather_runs_add<NB, false>(dst, park, qa, qb, G);
         } else if constexpr (NB == 1) {
             const float lo = dst[0], hi = dst[1];
             dst[0] = lo + qa[0];
@@ -823,23 +872,29 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
         const int32_t rows_pad = gather_rows_padded(A.rows);
         const int32_t vend = A.view0 + A.nviews;
 
-        // Units of work: (item, row group) in queue order. The rows of the next unit are
-        // loaded while the current one is summed.
+        // Units of work: (item, row group) in queue order, counted without divisions. The rows
+        // of the next unit are loaded while the current one is summed.
         const int32_t ngroups = rows_pad / (64 * S);
-        auto unit_rows = [&](int32_t u) {
-            const int32_t i = u / ngroups, g0 = (u - i * ngroups) * 64 * S;
+        int32_t lane_row = S * lane;
+        asm volatile("" : "+v"(lane_row));    // kept as one value: a unit's first row is one add
+        auto unit_rows = [&](int32_t i, int32_t gi) {
             const int32_t yoff = (int32_t)uniform((uint32_t)Q[i].yoff);
-            return ysc + ((int64_t)yoff * rows_pad + g0 + S * lane) * NB;
+            return ysc + ((int64_t)yoff * rows_pad + gi * 64 * S + lane_row) * NB;
         };
         auto drain = [&](int32_t count) {
-            const int32_t units = count * ngroups;
-            if (units == 0) return;
+            if (count == 0) return;
             float w[KR][NB], wn[KR][NB];
-            gather_load_rows<NB, KR>(unit_rows(0), w);
-            for (int32_t u = 0; u < units; ++u) {
-                gather_load_rows<NB, KR>(unit_rows(u + 1 < units ? u + 1 : u), wn);
-                const int32_t i = u / ngroups;
-                const int32_t k0 = (u - i * ngroups) * 64 * S + S * lane;
+            gather_load_rows<NB, KR>(unit_rows(0, 0), w);
+            int32_t i = 0, gi = 0;
+            for (;;) {
+                int32_t ni = i, ngi = gi + 1;
+                if (ngi == ngroups) {
+                    ngi = 0;
+                    ++ni;
+                }
+                const bool more = ni < count;
+                gather_load_rows<NB, KR>(unit_rows(more ? ni : i, more ? ngi : gi), wn);
+                const int32_t k0 = gi * 64 * S + lane_row;
                 const GatherItem it = Q[i];
                 const int32_t form = (int32_t)uniform((uint32_t)it.form);
                 if (form > 0) {
@@ -848,23 +903,26 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                     const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
                     if (form == kFastPairs) {
                         if (S == KR)
-                            gather_fast_group<NB, KR, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
+                            gather_fast_group<NB, KR, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
                         else
-                            gather_fast_group<NB, KR, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1, lane);
+                            gather_fast_group<NB, KR, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
                     } else {
-                        const int32_t G = (int32_t)uniform((uint32_t)it.split);
+                        const int32_t G = (int32_t)uniform((uint32_t)it.run);
                         if (S == KR)
-                            gather_fast_group<NB, KR, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
+                            gather_fast_group<NB, KR, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
                         else
-                            gather_fast_group<NB, KR, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G, lane);
+                            gather_fast_group<NB, KR, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
                     }
                 } else {
                     gather_general_group<NB, KR>(it, form == kGeneralExclusive, w, k0, S, z0, z1, col);
                 }
+                if (!more) break;
 #pragma unroll
                 for (int c = 0; c < KR; ++c)
 #pragma unroll
                     for (int m = 0; m < NB; ++m) w[c][m] = wn[c][m];
+                i = ni;
+                gi = ngi;
             }
         };
 

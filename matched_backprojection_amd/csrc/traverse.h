@@ -546,8 +546,9 @@ MBP_HD MBP_INLINE bool gather_exclusive(int32_t S, int32_t rows, double za0, dou
 // processed one at a time by the whole wave (lanes = rows).
 //
 // The fast form applies when each row's z extent inside the cell is below one cell, so a
-// row has at most two pieces (cells fa and fa + 1), and lanes that write together are more
-// than two cells apart, so their cell pairs {fa, fa + 1} are disjoint. A lane takes S
+// row has at most two pieces (cells fa and fa + 1). When lanes that write together are more
+// than two cells apart their cell pairs {fa, fa + 1} are disjoint; otherwise lanes that share
+// a pair are consecutive, and their shares are combined across lanes first. A lane takes S
 // consecutive rows. Its origin row (the middle one when the lane holds kGatherGroup rows,
 // else the first) is placed from the item's 64-bit fixed-point positions: the integer cell I
 // of that row's entry end, and the row's two ends relative to I in signed fixed point with
@@ -565,10 +566,11 @@ constexpr double kZScale = 268435456.0;            // 2^kZFrac
 // 8 cells of the fixed point.
 constexpr double kFastSpan = 5.5;
 // GatherItem::form. Fast form: all lanes update their cell pairs at once (kFastPairs), or
-// update lower and then upper cells in separate passes of GatherItem::split write phases
-// each (kFastSplit). General form: lanes add exclusively, or need atomics.
+// lanes that share a pair, in runs of at most GatherItem::run consecutive lanes, combine
+// their shares before the run's ends write (kFastRuns). General form: lanes add exclusively,
+// or need atomics.
 constexpr int32_t kFastPairs = 1;
-constexpr int32_t kFastSplit = 2;
+constexpr int32_t kFastRuns = 2;
 constexpr int32_t kGeneralExclusive = 0;
 constexpr int32_t kGeneralAtomic = -1;
 
@@ -591,8 +593,8 @@ struct GatherItem {
     int32_t yoff;       // view * cols + column: the line of the reordered sinogram
     int32_t a1fx;       // fast form: za1 in fixed point
     int32_t b1fx;       // fast form: zb1 in fixed point
-    int32_t form;       // kFastPairs, kFastSplit, kGeneralExclusive or kGeneralAtomic
-    int32_t split;      // kFastSplit: write phases of single cells (see fast_phases)
+    int32_t form;       // kFastPairs, kFastRuns, kGeneralExclusive or kGeneralAtomic
+    int32_t run;        // kFastRuns: most consecutive lanes with one lower cell (fast_run)
     int32_t pad_[2];    // 64 bytes: the wave reads an item with four aligned 16-byte loads
 };
 
@@ -605,36 +607,35 @@ MBP_HD MBP_INLINE int32_t fast_span_rows(int32_t S) {
     return S == kGatherGroup ? kGatherGroup / 2 : S - 1;
 }
 
-// Most write phases of the fast form.
-constexpr int32_t kMaxPhases = 16;
+// Longest run of lanes that the fast form combines.
+constexpr int32_t kMaxRun = 16;
 
-// Write phases of a fast item whose rows advance by a1 and b1 per row (fixed point): lanes
-// that write in the same phase are S * G rows apart, which must move z by more than `cells`
-// cells (plus a margin of 2^-10 cell, far above the fixed point's rounding): two when each
-// lane updates its cell pair at once, so that the pairs are disjoint; one when all lanes
-// update their lower cells and then their upper cells in separate passes, so that the single
-// cells are distinct. G = floor(need / step) + 1 from an fp64 quotient of integers below
-// 2^53: should the quotient round up to an integer, G comes out one larger, which still
-// separates the cells. 0 when more than kMaxPhases would be needed.
-MBP_HD MBP_INLINE int32_t fast_phases(int32_t S, int32_t a1, int32_t b1, int32_t cells = 2) {
+// For a fast item whose rows advance by a1 and b1 per row (fixed point): the least G such
+// that lanes G apart (S * G rows) are more than `cells` cells apart (plus a margin of 2^-10
+// cell, far above the fixed point's rounding). With cells = 2, G = 1 means that the lanes'
+// cell pairs are disjoint; with cells = 1, lanes sharing a lower cell come in runs of at most
+// G consecutive lanes. G = floor(need / step) + 1 from an fp64 quotient of integers below
+// 2^53: should the quotient round up to an integer, G comes out one larger, which is still a
+// bound. 0 when more than kMaxRun would be needed.
+MBP_HD MBP_INLINE int32_t fast_run(int32_t S, int32_t a1, int32_t b1, int32_t cells = 2) {
     const uint64_t a = (uint64_t)(a1 < 0 ? -(int64_t)a1 : (int64_t)a1);
     const uint64_t b = (uint64_t)(b1 < 0 ? -(int64_t)b1 : (int64_t)b1);
     const uint64_t step = (uint64_t)S * (a < b ? a : b);
     const uint64_t need = (uint64_t)cells * (uint64_t)kZOne + ((uint64_t)kZOne >> 10);
     if (step > need) return 1;
-    if ((uint64_t)kMaxPhases * step <= need) return 0;        // also step == 0
+    if ((uint64_t)kMaxRun * step <= need) return 0;           // also step == 0
     return (int32_t)floor((double)need / (double)step) + 1;
 }
 
 // Whether an item takes the fast form (rows 0 .. rows_pad - 1): both ends move the same way,
 // every row spans less than one cell, a lane's rows stay within kFastSpan cells of its
-// origin row, and some number of write phases separates the lanes' single cells. a1, b1: the
+// origin row, and runs of lanes sharing a lower cell are at most kMaxRun long. a1, b1: the
 // per-row advances in fixed point.
 MBP_HD MBP_INLINE bool gather_fast(int32_t S, int32_t rows_pad, double za0, double za1,
                                    double zb0, double zb1, int32_t a1, int32_t b1) {
     const double e0 = fabs(zb0 - za0), e1 = fabs(zb0 - za0 + (double)(rows_pad - 1) * (zb1 - za1));
     return za1 * zb1 > 0.0 && (double)fast_span_rows(S) * fmax(fabs(za1), fabs(zb1)) <= kFastSpan &&
-           fmax(e0, e1) < 1.0 - 1e-6 && fast_phases(S, a1, b1, 1) > 0;
+           fmax(e0, e1) < 1.0 - 1e-6 && fast_run(S, a1, b1, 1) > 0;
 }
 
 // The item of column line L crossing the cell, or false when it misses.
@@ -657,13 +658,13 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
                            fmax(fabs(fma(kl, it.za1, it.za0)), fabs(fma(kl, it.zb1, it.zb0)))) < kPosLimit;
     it.a1fx = fits ? (int32_t)rint(it.za1 * kZScale) : 0;
     it.b1fx = fits ? (int32_t)rint(it.zb1 * kZScale) : 0;
-    it.split = 0;
+    it.run = 0;
     if (fits && gather_fast(S, rows_pad, it.za0, it.za1, it.zb0, it.zb1, it.a1fx, it.b1fx)) {
-        if (fast_phases(S, it.a1fx, it.b1fx) == 1) {
+        if (fast_run(S, it.a1fx, it.b1fx) == 1) {
             it.form = kFastPairs;
         } else {
-            it.form = kFastSplit;
-            it.split = fast_phases(S, it.a1fx, it.b1fx, 1);
+            it.form = kFastRuns;
+            it.run = fast_run(S, it.a1fx, it.b1fx, 1);
         }
         const double half = 0.5 / kZScale;
         const int64_t a0 = (int64_t)rint((it.za0 + half) * kPosScale);

@@ -156,9 +156,9 @@ def gather(geom: dict, traj: dict, sino: np.ndarray, kernel_shares: bool = True,
 
 
 def gather_conflicts(geom: dict, traj: dict, mode: int = 0):
-    """(items checked, instructions or steps whose lanes would touch one z cell twice, fast
-    items checked). mode 0: the kernel's grouping; 1 and 2: planted mistakes (see
-    hostcheck.cpp)."""
+    """(items checked, instructions or steps that fail: lanes that would touch one z cell
+    twice, or a combined run that loses, repeats or misdirects a share; fast items checked).
+    mode 0: the kernel's grouping; 1 to 4: planted mistakes (see hostcheck.cpp)."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
     viol, fast = ctypes.c_longlong(0), ctypes.c_longlong(0)

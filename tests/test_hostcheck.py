@@ -190,19 +190,27 @@ def test_fast_gather_cell_pairs_never_collide(flip):
     assert HC.gather_conflicts(geom, traj, mode=2)[1] > 0
 
 
-@pytest.mark.parametrize("name", ["c3_cone256", "c4_cone512_aniso", "c5_helical_b4"])
-def test_gather_plain_lds_adds_never_collide(name):
+@pytest.mark.parametrize("name,flip", [("c3_cone256", False), ("c4_cone512_aniso", False),
+                                       ("c5_helical_b4", False), ("c5_helical_b4", True)])
+def test_gather_plain_lds_adds_never_collide(name, flip):
     """Where the gather adds into LDS without atomics, the lanes that write together hit
-    distinct z cells (emulated instruction by instruction and write phase by write phase;
-    these twins have one to eight rows per lane, so many fast items split their writes into
-    lower- and upper-cell passes with phases). Dealing adjacent rows to one instruction, or
-    writing the split items' cell pairs at once, collides, so the check has teeth."""
+    distinct z cells, and where lanes share a cell pair (runs of lanes, combined across the
+    wave before one lane per run writes) every share reaches its cell exactly once. Emulated
+    instruction by instruction on these twins, which have one to eight rows per lane, so many
+    fast items have such runs; flipped, the runs fall along the wave. Dealing adjacent rows to
+    one instruction (with one row per lane, as on the c5 twin, that is the kernel's own
+    dealing), writing the runs' cell pairs lane by lane, or shifting the runs one step fewer
+    than the kernel fails, so the check has teeth (the c3 twin's runs are single lanes, so
+    there the short shift loses nothing)."""
     cfg = SMALL_CONFIGS[name]
     geom, traj = _geom(cfg), config_trajectory(cfg)
+    if flip:
+        traj = flipped(traj)
     checked, conflicts, fast = HC.gather_conflicts(geom, traj, mode=0)
     assert checked > 10000 and conflicts == 0 and fast == checked
-    assert HC.gather_conflicts(geom, traj, mode=2)[1] > 0
+    assert (HC.gather_conflicts(geom, traj, mode=2)[1] > 0) == (name != "c5_helical_b4")
     assert HC.gather_conflicts(geom, traj, mode=3)[1] > 0
+    assert (HC.gather_conflicts(geom, traj, mode=4)[1] > 0) == (name != "c3_cone256")
 
 
 def steep_cone_config():
