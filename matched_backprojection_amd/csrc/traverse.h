@@ -185,20 +185,24 @@ MBP_HD MBP_INLINE void ray_setup(const Frame& F, const Box& B, int beam, double 
         t0 = 0.0; t1 = 1.0;
     }
     r.hit = clip_slab(a, d, B.lo, B.hi, 3, t0, t1) ? 1 : 0;
-    if (!r.hit) {
-        r.T = 0.0;
-        for (int k = 0; k < 3; ++k) { r.ax[k].c0 = 0; r.ax[k].step = 0; r.ax[k].steps = 0;
-                                      r.ax[k].pad_ = 0; r.ax[k].t_first = INFINITY;
-                                      r.ax[k].t_step = 0.0; }
-        return;
+    // both outcomes fill locals that are stored once (see column_setup)
+    AxisWalk w[3];
+    double T = 0.0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) w[k] = AxisWalk{0, 0, 0, 0, INFINITY, 0.0};
+    if (r.hit) {
+        const double dn = sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const double e = a[k] + t0 * d[k];
+            const double x = a[k] + t1 * d[k];
+            w[k] = axis_walk(e, x, d[k] / dn, 0.0, B.lo[k], B.pitch[k], B.n[k]);
+        }
+        T = (t1 - t0) * dn;
     }
-    const double dn = sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
-    for (int k = 0; k < 3; ++k) {
-        const double e = a[k] + t0 * d[k];
-        const double x = a[k] + t1 * d[k];
-        r.ax[k] = axis_walk(e, x, d[k] / dn, 0.0, B.lo[k], B.pitch[k], B.n[k]);
-    }
-    r.T = (t1 - t0) * dn;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) r.ax[k] = w[k];
+    r.T = T;
 }
 
 // Visit the segments of a generic walk. `visit(cx, cy, cz, length)` once per segment, in
@@ -285,18 +289,21 @@ MBP_HD MBP_INLINE void column_setup(const Frame& F, const Box& B, int beam, doub
     c.dxy = sqrt(d[0] * d[0] + d[1] * d[1]);
     c.hit = (c.dxy > 0.0 && clip_slab(a, d, B.lo, B.hi, 2, t0, t1)) ? 1 : 0;
     c.t_in = t0;
-    if (!c.hit) {
-        c.T = 0.0;
-        c.x.c0 = c.y.c0 = 0; c.x.step = c.y.step = 0; c.x.steps = c.y.steps = 0;
-        c.x.pad_ = c.y.pad_ = 0;
-        c.x.t_first = c.y.t_first = INFINITY; c.x.t_step = c.y.t_step = 0.0;
-        return;
+    // both outcomes fill locals that are stored once (stores to the struct's fields in two
+    // branches were merged by the device compiler into one store through a chosen pointer,
+    // which kept the struct in scratch memory)
+    AxisWalk wx = {0, 0, 0, 0, INFINITY, 0.0}, wy = wx;
+    double T = 0.0;
+    if (c.hit) {
+        const double ex = a[0] + t0 * d[0], ey = a[1] + t0 * d[1];
+        const double xx = a[0] + t1 * d[0], xy = a[1] + t1 * d[1];
+        wx = axis_walk(ex, xx, d[0] / c.dxy, 0.0, B.lo[0], B.pitch[0], B.n[0]);
+        wy = axis_walk(ey, xy, d[1] / c.dxy, 0.0, B.lo[1], B.pitch[1], B.n[1]);
+        T = (t1 - t0) * c.dxy;
     }
-    const double ex = a[0] + t0 * d[0], ey = a[1] + t0 * d[1];
-    const double xx = a[0] + t1 * d[0], xy = a[1] + t1 * d[1];
-    c.x = axis_walk(ex, xx, d[0] / c.dxy, 0.0, B.lo[0], B.pitch[0], B.n[0]);
-    c.y = axis_walk(ey, xy, d[1] / c.dxy, 0.0, B.lo[1], B.pitch[1], B.n[1]);
-    c.T = (t1 - t0) * c.dxy;
+    c.x = wx;
+    c.y = wy;
+    c.T = T;
 }
 
 // Row setup: `v` is the row's detector coordinate, `evz` the z component of the row axis.
