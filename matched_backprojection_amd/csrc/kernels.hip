@@ -216,14 +216,15 @@ __device__ __forceinline__ float mul_legacy(float a, float b) {
 constexpr int kBufferFlags = 0x00020000;
 
 template <int NB>
-__device__ __forceinline__ void buffer_vals(__amdgpu_buffer_rsrc_t r, uint32_t off, float* v) {
+__device__ __forceinline__ void buffer_vals(__amdgpu_buffer_rsrc_t r, uint32_t off, float* v,
+                                            uint32_t soff = 0) {
     if constexpr (NB == 1) {
-        v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+        v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, 0));
     } else if constexpr (NB == 2) {
-        const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0);
         v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
     } else {
-        const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0);
         v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
         v[2] = __uint_as_float(t[2]); v[3] = __uint_as_float(t[3]);
     }
@@ -264,7 +265,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NB>
+// FLAT: the volume's bytes fit a 31-bit offset, so one buffer resource spans it and each
+// cell's column is reached through the load's scalar offset (one scalar multiply per cell);
+// otherwise each cell gets a resource based at its column.
+template <int NB, bool FLAT>
 __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch A,
                                                              const float* __restrict__ vol,
                                                              const MPtrs4 sino) {
@@ -346,6 +350,8 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                     // at the cell's z column, so each load takes a 32-bit offset
                     nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
                     const int32_t colbytes = (int32_t)(D * NB * sizeof(float));
+                    const __amdgpu_buffer_rsrc_t rs_all = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<float*>(vol), (short)0, 0x7FFFFFFF, kBufferFlags);
                     for (; p + kCellGroup <= count; p += kCellGroup) {
                         uint32_t zoff[2 * kCellGroup];
                         float len[2 * kCellGroup];
@@ -363,8 +369,11 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                         float val[2 * kCellGroup][NB];
 #pragma unroll
                         for (int q = 0; q < kCellGroup; ++q) {
-                            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                                const_cast<float*>(vol + (size_t)cell[q] * D * NB), (short)0, colbytes, kBufferFlags);
+                            const __amdgpu_buffer_rsrc_t rs = FLAT ? rs_all
+                                : __builtin_amdgcn_make_buffer_rsrc(
+                                      const_cast<float*>(vol + (size_t)cell[q] * D * NB), (short)0,
+                                      colbytes, kBufferFlags);
+                            const uint32_t soff = FLAT ? cell[q] * (uint32_t)colbytes : 0u;
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
                                 // one member: the first piece (empty only when the row meets a
@@ -374,7 +383,7 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                                 // empty whenever the row does not cross a z plane in this cell
                                 // (it then names the first piece's voxel) and keeps its branch
                                 if ((NB == 1 && h == 0) || len[2 * q + h] != 0.0f) {
-                                    buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h]);
+                                    buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h], soff);
                                 } else {
 #pragma unroll
                                     for (int m = 0; m < NB; ++m) val[2 * q + h][m] = 0.0f;
@@ -1136,12 +1145,14 @@ hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol
     MPtrs4 o{};
     for (int m = 0; m < nb; ++m) o.p[m] = sino[m];
     const dim3 grid((a.tasks + 3) / 4);
-    switch (nb) {
-        case 1: column_forward_kernel<1><<<grid, dim3(256), 0, s>>>(a, vol, o); break;
-        case 2: column_forward_kernel<2><<<grid, dim3(256), 0, s>>>(a, vol, o); break;
-        case 4: column_forward_kernel<4><<<grid, dim3(256), 0, s>>>(a, vol, o); break;
-        default: return hipErrorInvalidValue;
-    }
+    const bool flat = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)a.box.n[2] * (uint64_t)nb *
+                          sizeof(float) < (1ull << 31);
+#define MBP_FORWARD(NB_, FLAT_) \
+    if (nb == NB_ && flat == FLAT_) column_forward_kernel<NB_, FLAT_><<<grid, dim3(256), 0, s>>>(a, vol, o)
+    MBP_FORWARD(1, true); else MBP_FORWARD(1, false); else MBP_FORWARD(2, true); else MBP_FORWARD(2, false);
+    else MBP_FORWARD(4, true); else MBP_FORWARD(4, false);
+    else return hipErrorInvalidValue;
+#undef MBP_FORWARD
     return hipGetLastError();
 }
 
