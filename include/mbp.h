@@ -84,13 +84,17 @@ typedef enum mbp_path {
 } mbp_path;
 
 typedef enum mbp_adjoint {
-    MBP_ADJOINT_AUTO = 0,     /* the gather for the column walk                               */
-    MBP_ADJOINT_GATHER = 1,   /* column walk: each wave owns one xy cell's z column in LDS and
-                                 sums, over views, crossing columns and rows, the exact chord
-                                 of every ray through each of its voxels; no global atomics   */
-    MBP_ADJOINT_SCATTER = 2   /* column walk: each ray scatters its value along its segments
-                                 with global float atomics (64 adjacent rows per wave, z-inner
-                                 stepping); always used by the generic walk                   */
+    MBP_ADJOINT_AUTO = 0,     /* the gather                                                   */
+    MBP_ADJOINT_GATHER = 1,   /* each wave owns one xy cell's z column in LDS and sums, over
+                                 views, crossing columns and rows, the exact chord of every
+                                 ray through each of its voxels; no global atomics. Column
+                                 walk: rows share their column's xy line. Cone geometries off
+                                 the column walk (detector rows not along z), with the walk
+                                 chosen automatically: each row's ray is clipped on its own  */
+    MBP_ADJOINT_SCATTER = 2   /* each ray scatters its value along its segments with global
+                                 float atomics: column walk with 64 adjacent rows per wave and
+                                 z-inner stepping, or the generic walk (also always used when
+                                 MBP_PATH_GENERIC is forced)                                   */
 } mbp_adjoint;
 
 typedef struct mbp_geometry {
@@ -137,8 +141,8 @@ int mbp_plan_get_info(const mbp_plan* plan, mbp_plan_info* info);
    geometry that cannot use it returns MBP_EINVAL. Both walks visit the same segments. */
 int mbp_plan_set_path(mbp_plan* plan, int32_t path);
 
-/* Choose the adjoint kernel of the column walk. Both compute the same sums (the chord of
-   every ray through every voxel times the ray's value); they differ in summation order. */
+/* Choose the adjoint kernel (mbp_adjoint). All compute the same sums (the chord of every ray
+   through every voxel times the ray's value); they differ in summation order. */
 int mbp_plan_set_adjoint(mbp_plan* plan, int32_t kind);
 
 /* Limit the views of one kernel launch (0 = automatic: as many as index and grid limits

@@ -343,7 +343,56 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
     return 0;
 }
 
+// Checks that the tilted gather's bands (tilt_column_range, tilt_row_range) hold every pixel
+// whose cone ray crosses an xy cell with positive length (fp64 slab clip, t in [0, 1]), over
+// the cells (ix, iy) with ix, iy = stride / 2 + i * stride. Returns the crossings found;
+// *misses counts crossings outside the bands, *candidates the pixels inside them.
+int64_t mbph_tilt_band(const double* frames, const double* lo, const double* pitch, const int32_t* n,
+                       int views, int rows, int cols, double du, double dv, int stride,
+                       long long* misses, long long* candidates) {
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *misses = 0;
+    *candidates = 0;
+    int64_t hits = 0;
+    std::vector<int32_t> k0(cols), k1(cols);
+    for (int ix = stride / 2; ix < n[0]; ix += stride) {
+        for (int iy = stride / 2; iy < n[1]; iy += stride) {
+            const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
+            const double y0 = B.lo[1] + iy * B.pitch[1], y1 = y0 + B.pitch[1];
+            const double clo[2] = {x0, y0}, chi[2] = {x1, y1};
+            for (int v = 0; v < views; ++v) {
+                TiltCorners T;
+                tilt_corners(F[v], x0, x1, y0, y1, T);
+                int32_t j0 = 0, j1 = -1;
+                if (!tilt_column_range(T, rows, cols, du, dv, j0, j1)) j1 = -1;
+                for (int j = 0; j < cols; ++j) {
+                    k0[j] = 0;
+                    k1[j] = -1;
+                    if (j >= j0 && j <= j1 && tilt_row_range(T, j, rows, cols, du, dv, k0[j], k1[j]))
+                        *candidates += k1[j] - k0[j] + 1;
+                }
+                for (int j = 0; j < cols; ++j) {
+                    for (int k = 0; k < rows; ++k) {
+                        double p[3];
+                        pixel_point(F[v], centred(j, cols, du), centred(k, rows, dv), p);
+                        const double d[2] = {p[0] - F[v].s[0], p[1] - F[v].s[1]};
+                        double t0 = 0.0, t1 = 1.0;
+                        if (!clip_slab(F[v].s, d, clo, chi, 2, t0, t1)) continue;
+                        ++hits;
+                        if (k < k0[j] || k > k1[j]) ++*misses;
+                    }
+                }
+            }
+        }
+    }
+    return hits;
+}
+
 namespace {
+
+// One instruction of a kFastRuns itemnamespace {
 
 // One instruction of a kFastRuns item as the kernel performs it, on sets of lanes in place of
 // values: lane l starts with its own lower-cell share {l} and upper-cell share {l}; `steps`

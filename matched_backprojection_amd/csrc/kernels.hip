@@ -986,6 +986,285 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
 }
 
 // ------------------------------------------------------------------------------------------
+// Gather for cone geometries whose detector rows do not run along z (tilted detectors, any
+// frame): a wave owns one xy cell's z column in LDS as in column_gather_kernel, but each lane
+// takes one row of an item (view, column, up to 64 rows) and clips that row's own ray
+// against the cell in fp64.
+
+// The adds of one instruction when the lanes' pair addresses are monotone along the wave
+// (rising with the lane when UP): as gather_runs_add, with as many shift steps as the longest
+// run of equal addresses strictly between the parked pairs (park, at index -2, and top, at
+// the column's upper end) needs, found by comparing each lane's address with the one t lanes
+// ahead. Runs on the parked pairs hold only shares that are never written out and are left
+// unmerged. Needs all 64 lanes active.
+template <int NB, bool UP>
+__device__ __forceinline__ void gather_runs_add_any(lds_float* dst, lds_float* park, lds_float* top,
+                                                    const float (&qa)[NB], const float (&qb)[NB]) {
+    typedef __attribute__((address_space(3))) float __attribute__((ext_vector_type(NB))) cell_t;
+    const int32_t key = (int32_t)(uintptr_t)dst;
+    const int32_t kb = key_bwd<UP>(key), kf = key_fwd<UP>(key);
+    const bool first = kb != key, last = kf != key;
+    const bool adj = kf == key + 4 * NB;
+    float T[NB], U[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        T[m] = qa[m];
+        U[m] = qb[m];
+    }
+    const bool inner = key > (int32_t)(uintptr_t)park && key < (int32_t)(uintptr_t)top;
+    int32_t ahead = kf;                              // the address t lanes ahead (t = 1, 2, ...)
+    while (__ballot(inner && ahead == key) != 0) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            T[m] = qa[m] + from_fwd<UP>(first ? 0.0f : T[m]);
+            U[m] = qb[m] + from_bwd<UP>(last ? 0.0f : U[m]);
+        }
+        ahead = key_fwd<UP>(ahead);
+    }
+#pragma unroll
+    for (int m = 0; m < NB; ++m) T[m] += from_bwd<UP>(adj ? U[m] : 0.0f);
+    cell_t* const p0 = (cell_t*)(first ? dst : park);
+    cell_t* const p1 = (cell_t*)(last && !adj ? dst : park);
+    cell_t lo = p0[0], hi = p1[1];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        lo[m] += T[m];
+        hi[m] += U[m];
+    }
+    p0[0] = lo;
+    p1[1] = hi;
+}
+
+// 1 / x in fp64 for x != 0: the hardware reciprocal refined by two Newton steps (each
+// squares the relative error), within a unit or two in the last place.
+__device__ __forceinline__ double rcp_f64(double x) {
+    double r = __builtin_amdgcn_rcp(x);
+    r = fma(fma(-x, r, 1.0), r, r);
+    return fma(fma(-x, r, 1.0), r, r);
+}
+
+// tilt_clip with rcp_f64 in place of the divisions.
+__device__ __forceinline__ void tilt_clip_rcp(const double* s, const double* d, double x0, double x1,
+                                              double y0, double y1, double& t0, double& t1) {
+    double a = 0.0, b = 1.0;
+    const double lo[2] = {x0, y0}, hi[2] = {x1, y1};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (d[k] != 0.0) {
+            const double r = rcp_f64(d[k]);
+            const double p = (lo[k] - s[k]) * r, q = (hi[k] - s[k]) * r;
+            a = fmax(a, fmin(p, q));
+            b = fmin(b, fmax(p, q));
+        } else if (s[k] < lo[k] || s[k] >= hi[k]) {
+            b = -1.0;
+        }
+    }
+    t0 = a;
+    t1 = b;
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* __restrict__ vol,
+                   int32_t zchunk, int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate) {
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    const int32_t lane = (int32_t)(threadIdx.x & 63u);
+    const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
+    const uint32_t task = blk * 4u + wave;
+    const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
+    const int32_t zc = (int32_t)(task % (uint32_t)nchunks);
+    const bool live = task < (uint32_t)W * (uint32_t)H * (uint32_t)nchunks;
+    int32_t ix, iy;
+    gather_tile_cell(task / (uint32_t)nchunks, H, tx, ty, ix, iy);
+    const int32_t z0 = zc * zchunk;
+    const int32_t z1 = live ? (z0 + zchunk < D ? z0 + zchunk : D) : z0;
+    const int32_t n = z1 - z0;
+    const int32_t colf = gather_column_floats(zchunk, NB);
+    float* const cols = reinterpret_cast<float*>(lds_raw) + wave * colf;
+    float* const col = cols + 2 * NB;                   // the guard cell below the chunk
+    TiltItem* Q = reinterpret_cast<TiltItem*>(lds_raw + 4 * (size_t)colf * sizeof(float)) + wave * kQueue;
+    for (int32_t i = lane; i < colf; i += 64) cols[i] = 0.0f;
+    __syncthreads();
+    if (live) {
+        const double x0 = A.box.lo[0] + ix * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
+        const double y0 = A.box.lo[1] + iy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
+        const int32_t rows_pad = gather_rows_padded(A.rows);
+        const int32_t vend = A.view0 + A.nviews;
+        const double ipz = 1.0 / A.box.pitch[2];
+        const int32_t a0 = lds_addr(col);
+        lds_float* const park = lds_ptr(a0 - 8 * NB);
+        lds_float* const top = lds_ptr(a0 + 4 * NB * (n + 1));
+
+        // one lane's row values of item i (zero past the item's rows)
+        auto load_rows = [&](int32_t i, float (&w)[NB]) {
+            const int32_t view = (int32_t)uniform((uint32_t)Q[i].view);
+            const int32_t j = (int32_t)uniform((uint32_t)Q[i].j);
+            const int32_t k0 = (int32_t)uniform((uint32_t)Q[i].k0);
+            const int32_t nrows = (int32_t)uniform((uint32_t)Q[i].nrows);
+#pragma unroll
+            for (int m = 0; m < NB; ++m) w[m] = 0.0f;
+            if (lane < nrows) {
+                const float* yp = ysc + (((int64_t)view * A.cols + j) * rows_pad + k0 + lane) * NB;
+#pragma unroll
+                for (int m = 0; m < NB; ++m) w[m] = yp[m];
+            }
+        };
+        // The adds of one item (rows k0 + lane) with the lanes' row values w.
+        auto sum_item = [&](const TiltItem& it, const float (&w)[NB]) {
+            const int32_t view = (int32_t)uniform((uint32_t)it.view);
+            const int32_t j = (int32_t)uniform((uint32_t)it.j);
+            const int32_t k0 = (int32_t)uniform((uint32_t)it.k0);
+            const int32_t nrows = (int32_t)uniform((uint32_t)it.nrows);
+            // the frame through the constant address space: read with scalar loads
+            typedef const __attribute__((address_space(4))) double cdouble;
+            const cdouble* const fp = reinterpret_cast<cdouble*>(reinterpret_cast<uintptr_t>(A.frames + view));
+            Frame F;
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                F.s[a] = fp[a];
+                F.c[a] = fp[3 + a];
+                F.u[a] = fp[6 + a];
+                F.v[a] = fp[9 + a];
+            }
+            const double u = centred(j, A.cols, A.du);
+            const double v = centred(k0 + lane, A.rows, A.dv);
+            double d[3];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) d[a] = fma(v, F.v[a], (F.c[a] - F.s[a]) + u * F.u[a]);
+            double t0, t1;
+            tilt_clip_rcp(F.s, d, x0, x1, y0, y1, t0, t1);
+            const bool active = lane < nrows && t1 > t0;
+            const double szc = (F.s[2] - A.box.lo[2]) * ipz, dzc = d[2] * ipz;
+            const double za = fma(t0, dzc, szc), zb = fma(t1, dzc, szc);
+            const double zmin = fmin(za, zb), zmax = fmax(za, zb);
+            const double fa = floor(zmin);
+            const bool lng = active && !(zmax < fa + 2.0);          // spans more than two cells
+            // the shares of cells fa and fa + 1: (fa + 1 - zmin) / ext and (zmax - fa - 1) / ext,
+            // the second 0 when the row stays in cell fa
+            const float dt = (float)(t1 - t0);
+            const float r = __builtin_amdgcn_rcpf((float)(zmax - zmin));
+            const float f = fminf((float)(fa + 1.0 - zmin) * r, 1.0f);
+            const float g = mul_legacy(fmaxf((float)(zmax - (fa + 1.0)), 0.0f), r);
+            const bool two = active && !lng;
+            float qa[NB], qb[NB];
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                const float q = two ? dt * w[m] : 0.0f;
+                qa[m] = f * q;
+                qb[m] = g * q;
+            }
+            // pair address, clamped to the parked pairs below and above the chunk; lanes past
+            // the item's crossing rows take the parked pair at their end of the column, so the
+            // addresses stay monotone when the rows' cells are
+            const bool up = F.v[2] >= 0.0;
+            const uint64_t act = __ballot(active);
+            const int32_t i0 = (int32_t)fmax(fmin(fa - (double)(z0 - 1), (double)(n + 1)), -2.0);
+            int32_t key = a0 + i0 * 4 * NB;
+            const int32_t kpark = lds_addr((float*)park), ktop = lds_addr((float*)top);
+            if (act != 0) {
+                const int32_t lo_lane = (int32_t)__builtin_ctzll(act), hi_lane = 63 - (int32_t)__builtin_clzll(act);
+                if (lane < lo_lane) key = up ? kpark : ktop;
+                if (lane > hi_lane) key = up ? ktop : kpark;
+            } else {
+                key = kpark;
+            }
+            lds_float* const dst = lds_ptr(key);
+            // addresses monotone along the wave in the rows' direction: combine runs; else LDS
+            // atomics
+            const int32_t kf = up ? key_fwd<true>(key) : key_fwd<false>(key);
+            if (__ballot(kf != -1 && kf < key) == 0) {
+                if (up)
+                    gather_runs_add_any<NB, true>(dst, park, top, qa, qb);
+                else
+                    gather_runs_add_any<NB, false>(dst, park, top, qa, qb);
+            } else if (two) {
+                float* const c0 = col + i0 * NB;
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    atomicAdd(c0 + m, qa[m]);
+                    atomicAdd(c0 + NB + m, qb[m]);
+                }
+            }
+            if (lng) {
+                auto piece = [&](int32_t iz, double share) {
+                    float* const c = col + (iz - z0 + 1) * NB;
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) atomicAdd(c + m, (float)share * w[m]);
+                };
+                row_pieces_split(za, zb, t1 - t0, z0, z1, false, piece);
+            }
+        };
+        auto drain = [&](int32_t count) {
+            for (int32_t i = 0; i < count; ++i) {
+                // an item whose rows are all zero adds nothing
+                float w[NB];
+                load_rows(i, w);
+                bool nonzero = false;
+#pragma unroll
+                for (int m = 0; m < NB; ++m) nonzero |= w[m] != 0.0f;
+                if (__ballot(nonzero) != 0) sum_item(Q[i], w);
+            }
+        };
+
+        // Items: kViewLanes lanes take one view of a round; lane r of a view walks its
+        // candidate columns j0 + r, j0 + r + kViewLanes, ... and emits the column's rows that
+        // can cross the cell in pieces of at most 64.
+        int32_t count = 0;
+        for (int32_t vb = A.view0; vb < vend; vb += 64 / kViewLanes) {
+            const int32_t view = vb + lane / kViewLanes;
+            TiltCorners T;
+            int32_t jn = 0, j1 = -1;
+            if (view < vend) {
+                tilt_corners(A.frames[view], x0, x1, y0, y1, T);
+                if (!tilt_column_range(T, A.rows, A.cols, A.du, A.dv, jn, j1)) j1 = -1;
+            }
+            jn += lane % kViewLanes;
+            int32_t jc = 0, kk = 0, kl = -1;
+            for (;;) {
+                if (kk > kl && jn <= j1) {
+                    jc = jn;
+                    jn += kViewLanes;
+                    if (!tilt_row_range(T, jc, A.rows, A.cols, A.du, A.dv, kk, kl)) {
+                        kk = 0;
+                        kl = -1;
+                    }
+                }
+                const bool emit = kk <= kl;
+                if (__ballot(emit || jn <= j1) == 0) break;
+                const uint64_t m = __ballot(emit);
+                if (emit) {
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    TiltItem t;
+                    t.view = view;
+                    t.j = jc;
+                    t.k0 = kk;
+                    t.nrows = kl - kk + 1 < 64 ? kl - kk + 1 : 64;
+                    Q[count + (int32_t)below] = t;
+                    kk += 64;
+                }
+                count += (int32_t)__popcll(m);
+                if (count > kQueue - 64) {
+                    wave_lds_sync();
+                    drain(count);
+                    count = 0;
+                    wave_lds_sync();
+                }
+            }
+        }
+        wave_lds_sync();
+        drain(count);
+    }
+    __syncthreads();
+    if (live) {
+        const int64_t base = (((int64_t)ix * H + iy) * D + z0) * NB;
+        for (int32_t i = lane; i < n * NB; i += 64)
+            vol[base + i] = accumulate ? vol[base + i] + col[NB + i] : col[NB + i];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Layout conversion. DHW member m: element (z, y, x) at m*ms + (z*H + y)*W + x.
 // Native: element (x, y, z, m) at ((x*H + y)*D + z)*NB + m.
 
@@ -1240,6 +1519,27 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     else MBP_GATHER(4, 1); else MBP_GATHER(4, 2); else MBP_GATHER(4, 4); else MBP_GATHER(4, 6); else MBP_GATHER(4, 8);
     else return hipErrorInvalidValue;
 #undef MBP_GATHER
+    return hipGetLastError();
+}
+
+hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol, int accumulate,
+                              hipStream_t s) {
+    const int32_t D = a.box.n[2];
+    const int32_t zchunk = gather_zchunk(D, nb);
+    const int32_t nchunks = (D + zchunk - 1) / zchunk;
+    const uint64_t tasks = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)nchunks;
+    const bool tiled = a.box.n[0] % 16 == 0 && a.box.n[1] % 32 == 0;
+    const int32_t tx = tiled ? 16 : 1, ty = tiled ? 32 : a.box.n[1];
+    if (tasks == 0) return hipSuccess;
+    const dim3 grid((unsigned)((tasks + 3) / 4));
+    const size_t lds = (size_t)4 * (kQueue * sizeof(TiltItem) +
+                                    (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
+    switch (nb) {
+        case 1: tilt_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
+        case 2: tilt_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
+        case 4: tilt_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -59,6 +59,11 @@ hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const
                                hipStream_t s);
 hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* lines, const float* ysc,
                                 float* vol, int accumulate, hipStream_t s);
+// The gather for cone geometries whose detector rows do not run along z: the same pre-pass
+// sinogram (ysc) and output as launch_column_gather, each ray clipped against each cell on
+// its own.
+hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol, int accumulate,
+                              hipStream_t s);
 // Per-(view, column) line constants of the gather, for views [0, views) (lines holds
 // views * cols entries); computed once per plan and device.
 hipError_t launch_column_lines(const ColumnLaunch& a, int32_t views, ColLine* lines, hipStream_t s);

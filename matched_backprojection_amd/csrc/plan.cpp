@@ -90,6 +90,7 @@ struct mbp_plan {
     Box box{};
     std::vector<Frame> frames;
     bool column_capable = false;
+    bool tilt_capable = false;        // cone geometry off the column walk: per-ray gather
     int32_t forced_path = MBP_PATH_AUTO;
     int32_t adjoint_kind = MBP_ADJOINT_AUTO;
     int64_t view_batch = 0;           // 0: automatic
@@ -321,6 +322,12 @@ int32_t adjoint_kind(const mbp_plan* p) {
     return p->adjoint_kind == MBP_ADJOINT_SCATTER ? MBP_ADJOINT_SCATTER : MBP_ADJOINT_GATHER;
 }
 
+// Whether the adjoint takes the per-ray gather (cone geometry off the column walk, walk chosen
+// automatically, gather adjoint).
+bool tilt_gather(const mbp_plan* p) {
+    return p->tilt_capable && p->forced_path == MBP_PATH_AUTO && adjoint_kind(p) == MBP_ADJOINT_GATHER;
+}
+
 // Workspace of one column-walk pass over nb members: the interleaved z-fastest volume (not
 // needed when the caller's own z-fastest buffer is used directly) and, for the gather
 // adjoint, the reordered sinogram.
@@ -492,6 +499,7 @@ int mbp_plan_create(const mbp_geometry* geometry, const double* src, const doubl
     const int rc = validate_frames(*p);
     if (rc != MBP_OK) { delete p; return rc; }
     p->column_capable = column_ok(*p);
+    p->tilt_capable = !p->column_capable && g.beam == MBP_CONE && g.D < ((int64_t)1 << 26);
     *out = p;
     return MBP_OK;
 }
@@ -547,10 +555,11 @@ int mbp_workspace_size(const mbp_plan* plan, int64_t batch, size_t* bytes) {
     if (!plan || !bytes) return fail(MBP_EINVAL, "plan and bytes must be non-NULL");
     if (batch < 0) return fail(MBP_EINVAL, "batch must be >= 0");
     *bytes = 0;
-    if (batch == 0 || active_path(plan) != MBP_PATH_COLUMN) return MBP_OK;
+    const bool tilt = tilt_gather(plan);
+    if (batch == 0 || (active_path(plan) != MBP_PATH_COLUMN && !tilt)) return MBP_OK;
     const bool direct = plan->g.layout == MBP_LAYOUT_WHD && batch == 1;
     const int nb = direct ? 1 : interleave_for(plan, batch);
-    *bytes = column_ws_bytes(plan, nb, direct, adjoint_kind(plan) == MBP_ADJOINT_GATHER);
+    *bytes = column_ws_bytes(plan, nb, direct, tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER);
     return MBP_OK;
 }
 
@@ -632,10 +641,11 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
     const mbp_geometry& g = plan->g;
     const int64_t vox = g.D * g.H * g.W, rays = g.views * g.rows * g.cols;
     int64_t m0 = 0;
-    if (active_path(plan) == MBP_PATH_COLUMN) {
+    const bool tilt = tilt_gather(plan);
+    if (active_path(plan) == MBP_PATH_COLUMN || tilt) {
         const bool whd = g.layout == MBP_LAYOUT_WHD;
         const bool direct = whd && batch == 1;
-        bool gather = adjoint_kind(plan) == MBP_ADJOINT_GATHER;
+        bool gather = tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER;
         while (m0 < batch) {
             int nb = direct ? 1 : interleave_for(plan, batch - m0);
             bool fits = false;
@@ -645,10 +655,10 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
                 if (rc != MBP_OK) return rc;
                 if (fits) break;
                 if (nb > 1) { nb /= 2; continue; }
-                if (gather) { gather = false; continue; }   // no room for the sinogram copy
+                if (gather && !tilt) { gather = false; continue; }   // no room for the sinogram copy
                 break;
             }
-            if (!fits) break;   // not even the volume copy fits: generic walk for the rest
+            if (!fits) break;   // the workspace does not fit: generic walk for the rest
             float* target = direct ? volume : ws;
             float* ysc = direct ? ws : ws + (size_t)nb * (size_t)vox;
             const int acc_target = direct ? accumulate : 0;
@@ -659,7 +669,7 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
             }
             const float* si[4] = {nullptr, nullptr, nullptr, nullptr};
             for (int m = 0; m < nb; ++m) si[m] = sinogram + (m0 + m) * rays;
-            if (gather && !d->lines) {
+            if (gather && !tilt && !d->lines) {
                 const size_t bytes = (size_t)g.views * (size_t)g.cols * sizeof(mbp::ColLine);
                 e = hipMalloc(reinterpret_cast<void**>(&d->lines), bytes);
                 if (e != hipSuccess) { d->lines = nullptr; return hip_fail(e, "hipMalloc(column lines)"); }
@@ -675,8 +685,10 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
                     a.nviews = (int32_t)std::min(vb, g.views - v0);
                     e = mbp::launch_sino_prepass(a, nb, si, ysc, s);
                     if (e != hipSuccess) return hip_fail(e, "sinogram pre-pass launch");
-                    e = mbp::launch_column_gather(a, nb, d->lines, ysc, target, v0 == 0 ? acc_target : 1, s);
-                    if (e != hipSuccess) return hip_fail(e, "column gather launch");
+                    const int acc = v0 == 0 ? acc_target : 1;
+                    e = tilt ? mbp::launch_tilt_gather(a, nb, ysc, target, acc, s)
+                             : mbp::launch_column_gather(a, nb, d->lines, ysc, target, acc, s);
+                    if (e != hipSuccess) return hip_fail(e, tilt ? "tilt gather launch" : "column gather launch");
                 }
             } else {
                 rc = run_column(plan, d, true, nullptr, target, si, nullptr, nb, s);

@@ -467,6 +467,122 @@ MBP_HD MBP_INLINE bool cell_column_range(const Frame& F, int beam, int32_t cols,
     return j0 <= j1;
 }
 
+// ------------------------------------------------------------------------------------------
+// Gather for detectors whose rows do not run along z (cone beam, any frame).
+//
+// Pixel (u, v) lies at c + u eu + v ev; its ray's xy line runs from the source through
+// c_xy + u eu_xy + v ev_xy. For a corner q of an xy cell, F_q(u, v) = cross(p_xy - s_xy,
+// q - s_xy) = A_q + u Bu_q + v Bv_q is affine in u and v, and the pixel's xy line meets the
+// cell exactly when the four F_q do not all have one strict sign. The bands below are
+// supersets (widened by a pixel or a row) of the pixels whose rays can cross the cell; each
+// ray's own clip decides.
+
+struct TiltCorners {
+    double A[4], Bu[4], Bv[4];
+};
+
+MBP_HD MBP_INLINE void tilt_corners(const Frame& F, double x0, double x1, double y0, double y1,
+                                    TiltCorners& T) {
+    const double bx = F.c[0] - F.s[0], by = F.c[1] - F.s[1];
+    for (int c = 0; c < 4; ++c) {
+        const double ax = ((c & 1) ? x1 : x0) - F.s[0], ay = ((c & 2) ? y1 : y0) - F.s[1];
+        T.A[c] = bx * ay - by * ax;
+        T.Bu[c] = F.u[0] * ay - F.u[1] * ax;
+        T.Bv[c] = F.v[0] * ay - F.v[1] * ax;
+    }
+}
+
+// Columns j0 .. j1 whose pixels, in some row, can have rays crossing the cell: at each row
+// the crossing pixels lie between the corners' projections u_q(v) = -(A_q + v Bv_q) / Bu_q,
+// affine in v, so the extremes over all rows are taken at the first and last rows. All
+// columns when the corners' Bu_q do not share a sign. False when no column can.
+MBP_HD MBP_INLINE bool tilt_column_range(const TiltCorners& T, int32_t rows, int32_t cols, double du,
+                                         double dv, int32_t& j0, int32_t& j1) {
+    j0 = 0;
+    j1 = cols - 1;
+    const double va = centred(0, rows, dv), vb = centred(rows - 1, rows, dv);
+    double umin = INFINITY, umax = -INFINITY;
+    for (int c = 0; c < 4; ++c) {
+        if (!(T.Bu[c] != 0.0) || (T.Bu[c] < 0.0) != (T.Bu[0] < 0.0)) return true;
+        const double ua = -(T.A[c] + va * T.Bv[c]) / T.Bu[c];
+        const double ub = -(T.A[c] + vb * T.Bv[c]) / T.Bu[c];
+        umin = fmin(umin, fmin(ua, ub));
+        umax = fmax(umax, fmax(ua, ub));
+    }
+    if (!(umin == umin) || !(umax == umax)) return true;
+    const double coff = 0.5 * (double)(cols - 1);
+    const double f0 = ceil(umin / du + coff) - 1.0, f1 = floor(umax / du + coff) + 1.0;
+    if (!(f1 >= 0.0) || !(f0 <= (double)(cols - 1))) return false;
+    j0 = f0 < 0.0 ? 0 : (int32_t)f0;
+    j1 = f1 > (double)(cols - 1) ? cols - 1 : (int32_t)f1;
+    return j0 <= j1;
+}
+
+// Whether the xy line of pixel (u, v) meets the cell (the corners' F_q do not share a strict
+// sign).
+MBP_HD MBP_INLINE bool tilt_hits(const TiltCorners& T, double u, double v) {
+    double lo = INFINITY, hi = -INFINITY;
+    for (int c = 0; c < 4; ++c) {
+        const double f = T.A[c] + u * T.Bu[c] + v * T.Bv[c];
+        lo = fmin(lo, f);
+        hi = fmax(hi, f);
+    }
+    return lo <= 0.0 && hi >= 0.0;
+}
+
+// Rows k0 .. k1 of column j whose rays can cross the cell. Along the column each F_q is
+// affine in v, so the rows that cross form a set whose ends are roots of some F_q or ends of
+// the column: its hull is the span of the roots inside the column and of the column's ends
+// that cross, widened by a row. False when no row can.
+MBP_HD MBP_INLINE bool tilt_row_range(const TiltCorners& T, int32_t j, int32_t rows, int32_t cols,
+                                      double du, double dv, int32_t& k0, int32_t& k1) {
+    const double u = centred(j, cols, du);
+    const double va = centred(0, rows, dv), vb = centred(rows - 1, rows, dv);
+    const double vlo = fmin(va, vb), vhi = fmax(va, vb);
+    double lo = INFINITY, hi = -INFINITY;
+    if (tilt_hits(T, u, va)) { lo = fmin(lo, va); hi = fmax(hi, va); }
+    if (tilt_hits(T, u, vb)) { lo = fmin(lo, vb); hi = fmax(hi, vb); }
+    for (int c = 0; c < 4; ++c) {
+        if (T.Bv[c] == 0.0) continue;
+        const double r = -(T.A[c] + u * T.Bu[c]) / T.Bv[c];
+        if (r >= vlo && r <= vhi) { lo = fmin(lo, r); hi = fmax(hi, r); }
+    }
+    if (!(lo <= hi)) return false;
+    const double coff = 0.5 * (double)(rows - 1);
+    const double ka = lo / dv + coff, kb = hi / dv + coff;
+    const double f0 = floor(fmin(ka, kb)) - 1.0, f1 = ceil(fmax(ka, kb)) + 1.0;
+    k0 = f0 < 0.0 ? 0 : (int32_t)f0;
+    k1 = f1 > (double)(rows - 1) ? rows - 1 : (int32_t)f1;
+    return k0 <= k1;
+}
+
+// One item of the tilted gather: rows k0 .. k0 + nrows - 1 (at most 64) of column j in view
+// `view` (16 bytes).
+struct TiltItem {
+    int32_t view, j, k0, nrows;
+};
+
+// The clip of ray s + t d (t in [0, 1]) against the xy cell [x0, x1) x [y0, y1) with one
+// reciprocal per axis: [t0, t1], empty unless t1 > t0.
+MBP_HD MBP_INLINE void tilt_clip(const double* s, const double* d, double x0, double x1, double y0,
+                                 double y1, double& t0, double& t1) {
+    double a = 0.0, b = 1.0;
+    const double lo[2] = {x0, y0}, hi[2] = {x1, y1};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (d[k] != 0.0) {
+            const double r = 1.0 / d[k];
+            const double p = (lo[k] - s[k]) * r, q = (hi[k] - s[k]) * r;
+            a = fmax(a, fmin(p, q));
+            b = fmin(b, fmax(p, q));
+        } else if (s[k] < lo[k] || s[k] >= hi[k]) {
+            b = -1.0;
+        }
+    }
+    t0 = a;
+    t1 = b;
+}
+
 // Clip column line L to the cell: t in [t0, t1] (segments start from [0, 1]).
 MBP_HD MBP_INLINE bool cell_clip(const ColLine& L, bool line, double x0, double x1, double y0,
                                  double y1, double& t0, double& t1) {

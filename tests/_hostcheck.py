@@ -35,7 +35,9 @@ def _load():
         lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, I, P, P, P]
         lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
         lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P, P]
+        lib.mbph_tilt_band.argtypes = [P, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_gather_conflicts.restype = I64
+        lib.mbph_tilt_band.restype = I64
         lib.mbph_check_rays.restype = I64
         _lib = lib
     return _lib
@@ -183,3 +185,16 @@ def project_chunked(geom: dict, traj: dict, vol: np.ndarray):
                              cols, float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)),
                              _ptr(vol), _ptr(sino), ctypes.byref(viol))
     return sino, int(viol.value)
+
+
+def tilt_band(geom: dict, traj: dict, stride: int):
+    """(crossings, crossings outside the tilted gather's bands, pixels inside the bands) over
+    the xy cells every `stride` cells (see hostcheck.cpp)."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    misses, cand = ctypes.c_longlong(0), ctypes.c_longlong(0)
+    hits = lib.mbph_tilt_band(_ptr(f), _ptr(lo), _ptr(p), _ptr(n), int(geom["views"]),
+                              int(geom.get("rows", 1)), int(geom["cols"]), float(geom.get("du", 1.0)),
+                              float(geom.get("dv", 1.0)), int(stride), ctypes.byref(misses),
+                              ctypes.byref(cand))
+    return int(hits), int(misses.value), int(cand.value)

@@ -281,7 +281,9 @@ def test_parallel3d_parity(torch_dev, mbp, oracle):
 
 
 def test_general_trajectory_parity(torch_dev, mbp, oracle):
-    """Tilted detectors (row axis not parallel to z): the generic walk, anisotropic grid."""
+    """Random tilted frames (row axis not parallel to z), anisotropic grid: the generic walk
+    forward; adjoint by the per-ray gather (rows that do not keep their cells in order along
+    the wave fall back to LDS atomics) and by the generic walk's global atomics."""
     torch, dev = torch_dev
     cfg = SMALL_CONFIGS["c4_cone512_aniso"]
     traj = random_cone_trajectory(30, seed=12, radius=150.0, sdd=260.0, tilt=0.5)
@@ -297,37 +299,53 @@ def test_general_trajectory_parity(torch_dev, mbp, oracle):
     assert plan.info["path"] == "generic"
     p = plan.project(to_device_volume(torch, dev, x, cfg.layout)).cpu().numpy().astype(np.float64)
     check(p, ref, "forward")
-    b = plan.backproject(torch.from_numpy(y).to(dev)).cpu().numpy().astype(np.float64)
-    check(b, bref, "adjoint")
+    for kind in ("gather", "scatter"):
+        say(f"case random tilted cone trajectory adjoint={kind}")
+        plan.set_adjoint(kind)
+        b = plan.backproject(torch.from_numpy(y).to(dev)).cpu().numpy().astype(np.float64)
+        check(b, bref, f"adjoint {kind}")
     plan.close()
 
 
 @pytest.mark.parametrize("layout", ["DHW", "WHD"])
 def test_tilted_circular_parity(torch_dev, mbp, oracle, layout):
     """A circular cone whose detector is rotated by a few degrees in its plane (rows not
-    along z): the generic walk, with threads taking consecutive columns (DHW volume) or
-    consecutive rows (z-fastest volume), unbatched and with a batch of two."""
+    along z): the generic walk forward, with threads taking consecutive columns (DHW volume)
+    or consecutive rows (z-fastest volume); adjoint by the per-ray gather and by the generic
+    walk's atomics; unbatched and with batches of two and four, rows running up or down."""
     from dataclasses import replace
+    from tests.test_hostcheck import flipped
     torch, dev = torch_dev
     cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory="circular_tilted", layout=layout)
-    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    geom = geom_of(cfg)
     rng = np.random.default_rng(41)
-    xs = rng.random((2,) + cfg.shape).astype(np.float32)
-    ref = oracle.project(geom, traj, xs)
-    ys = rng.random(ref.shape).astype(np.float32)
-    bref = oracle.backproject(geom, traj, ys)
-    plan = make_plan(mbp, cfg, traj=traj)
-    assert plan.info["path"] == "generic"
-    for B in (0, 2):
-        say(f"case tilted circular cone layout={layout} B={B}")
-        x_in = xs[0] if B == 0 else xs
-        p = plan.project(to_device_volume(torch, dev, x_in, layout)).cpu().numpy().astype(np.float64)
-        y_in = ys[0] if B == 0 else ys
-        b = plan.backproject(torch.from_numpy(y_in).to(dev)).cpu().numpy().astype(np.float64)
-        for m in range(max(B, 1)):
-            check(p if B == 0 else p[m], ref[m], f"forward member {m}")
-            check(b if B == 0 else b[m], bref[m], f"adjoint member {m}")
-    plan.close()
+    xs = rng.random((4,) + cfg.shape).astype(np.float32)
+    for flip in (False, True):
+        traj = config_trajectory(cfg)
+        if flip:
+            traj = flipped(traj)
+        ref = oracle.project(geom, traj, xs)
+        ys = rng.random(ref.shape).astype(np.float32)
+        bref = oracle.backproject(geom, traj, ys)
+        plan = make_plan(mbp, cfg, traj=traj)
+        assert plan.info["path"] == "generic"
+        for B in (0, 2, 4):
+            x_in = xs[0] if B == 0 else xs[:B]
+            say(f"case tilted circular cone layout={layout} flip={flip} B={B} forward")
+            p = plan.project(to_device_volume(torch, dev, x_in, layout)).cpu().numpy().astype(np.float64)
+            for m in range(max(B, 1)):
+                check(p if B == 0 else p[m], ref[m], f"forward member {m}")
+            y_in = ys[0] if B == 0 else ys[:B]
+            for kind in ("gather", "scatter"):
+                if flip and kind == "scatter":
+                    continue
+                say(f"case tilted circular cone layout={layout} flip={flip} B={B} adjoint={kind}")
+                plan.set_adjoint(kind)
+                b = plan.backproject(torch.from_numpy(y_in).to(dev)).cpu().numpy().astype(np.float64)
+                for m in range(max(B, 1)):
+                    check(b if B == 0 else b[m], bref[m], f"adjoint {kind} member {m}")
+            plan.set_adjoint("gather")
+        plan.close()
 
 
 def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):

@@ -275,3 +275,27 @@ def test_chunked_column_walk_full_size_views(oracle, name):
     s, viol = HC.project_chunked(geom, traj, x)
     assert viol == 0
     assert np.linalg.norm(s - ref) / np.linalg.norm(ref) < 1e-6
+
+
+@pytest.mark.parametrize("case", ["tilted", "tilted_flipped", "random"])
+def test_tilt_gather_bands_hold_every_crossing(case):
+    """The gather for detectors whose rows do not run along z takes, per view and xy cell, the
+    candidate columns and each column's candidate rows from the cell corners' projections. On
+    sampled cells every pixel whose ray crosses the cell with positive length (brute force:
+    fp64 slab clip of every pixel's ray) lies inside those bands, for a circular cone with its
+    detector rotated in its plane (rows up or down) and for random frames; the bands stay
+    close to the crossings on the tilted circle."""
+    from dataclasses import replace
+    from workloads import random_cone_trajectory
+    if case == "random":
+        cfg = replace(SMALL_CONFIGS["c4_cone512_aniso"], views=30)
+        traj = random_cone_trajectory(30, seed=12, radius=150.0, sdd=260.0, tilt=0.5)
+    else:
+        cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory="circular_tilted")
+        traj = config_trajectory(cfg)
+        if case == "tilted_flipped":
+            traj = flipped(traj)
+    hits, misses, cand = HC.tilt_band(_geom(cfg), traj, 3)
+    assert hits > 100000 and misses == 0
+    if case != "random":
+        assert cand < 1.2 * hits
