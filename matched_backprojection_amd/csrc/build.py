@@ -58,7 +58,7 @@ def build_hostcheck(verbose: bool = False) -> str:
     """Compile the CPU replay of the walks (test harness) with g++."""
     os.makedirs(os.path.dirname(HOSTCHECK_LIB), exist_ok=True)
     tmp = HOSTCHECK_LIB + ".tmp%d" % os.getpid()
-    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-Wall",
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-Wall", "-Wno-unknown-pragmas",
            "-I", HERE, "-o", tmp, HOSTCHECK_SRC]
     if verbose:
         print(" ".join(cmd), flush=True)

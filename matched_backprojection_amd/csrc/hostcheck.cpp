@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <vector>
 
@@ -456,7 +457,123 @@ bool runs_fail(const int32_t* key, bool up, int32_t D, int32_t steps) {
     return bad;
 }
 
+// The tilted gather's combine of one unit (gather_runs_add_any): keys are column indices,
+// monotone along the wave; the run length is found as the kernel finds it (shift steps while
+// some lane strictly between the parked pairs, index -2 and D + 1, has its key t lanes
+// ahead), then the combine is checked as in runs_fail.
+bool runs_fail_any(const int32_t* key, bool up, int32_t D, int32_t short_by) {
+    auto ahead = [&](int l, int t) {
+        const int s = up ? l + t : l - t;
+        return s >= 0 && s < 64 ? key[s] : INT32_MIN;
+    };
+    int32_t steps = 0;
+    for (int t = 1; t < 64; ++t) {
+        bool any = false;
+        for (int l = 0; l < 64; ++l)
+            any |= key[l] > -2 && key[l] < D + 1 && ahead(l, t) == key[l];
+        if (!any) break;
+        ++steps;
+    }
+    return runs_fail(key, up, D, steps > short_by ? steps - short_by : 0);
+}
+
 }  // namespace
+
+// Replays the gather for cone geometries off the column walk (tilt_gather_kernel) on the CPU,
+// item by item, with one column per xy cell (no z chunks): the bands, each row's fp64 clip
+// (with divisions where the kernel refines a reciprocal), the two-cell shares in fp64 (pieces
+// of rows spanning more cells from row_pieces_split), the row values of the pre-pass (value
+// times ray length), and the pair keys of every unit as the kernel forms them (parked pairs
+// for rows outside the crossing rows). Adds every share times its row's value into vol (fp64,
+// element (x, y, z) at (z * H + y) * W + x). Units whose keys are monotone along the wave are
+// replayed through the run combine on lane sets: *conflicts counts those that would lose,
+// repeat or misdirect a share or write a cell twice; *atomic counts units that take the LDS
+// atomics instead. Returns the units replayed. mode 1 plants a mistake: the run combine takes
+// one shift step fewer than the kernel.
+int64_t mbph_tilt_gather(const double* frames, const double* lo, const double* pitch, const int32_t* n,
+                         int views, int rows, int cols, double du, double dv, const float* sino,
+                         int mode, double* vol, long long* conflicts, long long* atomic) {
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    const int32_t D = n[2];
+    *conflicts = 0;
+    *atomic = 0;
+    int64_t units = 0;
+    for (int ix = 0; ix < n[0]; ++ix) {
+        for (int iy = 0; iy < n[1]; ++iy) {
+            const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
+            const double y0 = B.lo[1] + iy * B.pitch[1], y1 = y0 + B.pitch[1];
+            auto add = [&](int32_t iz, double value) {
+                if (iz >= 0 && iz < D) vol[((int64_t)iz * n[1] + iy) * n[0] + ix] += value;
+            };
+            for (int v = 0; v < views; ++v) {
+                TiltCorners T;
+                tilt_corners(F[v], x0, x1, y0, y1, T);
+                int32_t j0, j1;
+                if (!tilt_column_range(T, rows, cols, du, dv, j0, j1)) continue;
+                for (int32_t j = j0; j <= j1; ++j) {
+                    int32_t ka, kb;
+                    if (!tilt_row_range(T, j, rows, cols, du, dv, ka, kb)) continue;
+                    for (int32_t k0 = ka; k0 <= kb; k0 += 64) {
+                        const int32_t nrows = std::min(64, kb - k0 + 1);
+                        ++units;
+                        int32_t key[64];
+                        bool active[64];
+                        const double u = centred(j, cols, du);
+                        for (int l = 0; l < 64; ++l) {
+                            const int32_t k = k0 + l;
+                            double p[3], d[3];
+                            pixel_point(F[v], u, centred(k, rows, dv), p);
+                            for (int a = 0; a < 3; ++a) d[a] = p[a] - F[v].s[a];
+                            double t0, t1;
+                            tilt_clip(F[v].s, d, x0, x1, y0, y1, t0, t1);
+                            active[l] = l < nrows && t1 > t0;
+                            const double za = (F[v].s[2] + t0 * d[2] - B.lo[2]) / B.pitch[2];
+                            const double zb = (F[v].s[2] + t1 * d[2] - B.lo[2]) / B.pitch[2];
+                            const double zmin = std::fmin(za, zb), zmax = std::fmax(za, zb);
+                            const double fa = std::floor(zmin);
+                            key[l] = (int32_t)std::fmax(std::fmin(fa + 1.0, (double)(D + 1)), -2.0);
+                            if (!active[l]) continue;
+                            const double len = std::sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+                            const double w = (double)sino[((int64_t)v * rows + k) * cols + j] * len;
+                            const double dt = t1 - t0;
+                            if (zmax < fa + 2.0) {
+                                const double ext = zmax - zmin;
+                                const double f = ext > 0.0 ? std::fmin((fa + 1.0 - zmin) / ext, 1.0) : 1.0;
+                                const double g = ext > 0.0 ? std::fmax(zmax - (fa + 1.0), 0.0) / ext : 0.0;
+                                add((int32_t)fa, f * dt * w);
+                                add((int32_t)fa + 1, g * dt * w);
+                            } else {
+                                auto piece = [&](int32_t iz, double share) { add(iz, share * w); };
+                                row_pieces_split(za, zb, dt, 0, D, false, piece);
+                            }
+                        }
+                        // the kernel's keys: rows before and after the crossing rows take the
+                        // parked pair at their end of the column
+                        const bool up = F[v].v[2] >= 0.0;
+                        int lo_lane = 64, hi_lane = -1;
+                        for (int l = 0; l < 64; ++l)
+                            if (active[l]) { lo_lane = std::min(lo_lane, l); hi_lane = l; }
+                        for (int l = 0; l < 64; ++l) {
+                            if (hi_lane < 0) key[l] = -2;
+                            else if (l < lo_lane) key[l] = up ? -2 : D + 1;
+                            else if (l > hi_lane) key[l] = up ? D + 1 : -2;
+                        }
+                        bool monotone = true;
+                        for (int l = 0; l + 1 < 64; ++l) {
+                            const int32_t a = key[up ? l : l + 1], b = key[up ? l + 1 : l];
+                            if (b < a) monotone = false;
+                        }
+                        if (!monotone) ++*atomic;
+                        else if (runs_fail_any(key, up, D, mode == 1 ? 1 : 0)) ++*conflicts;
+                    }
+                }
+            }
+        }
+    }
+    return units;
+}
 
 // Emulates the gather's instruction grouping and checks its race-freedom claims. Fast items:
 // for every instruction (row c of each lane), the cell pairs {fa, fa + 1} that in-range lanes

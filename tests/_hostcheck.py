@@ -36,8 +36,10 @@ def _load():
         lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
         lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_tilt_band.argtypes = [P, P, P, P, I, I, I, D, D, I, P, P]
+        lib.mbph_tilt_gather.argtypes = [P, P, P, P, I, I, I, D, D, P, I, P, P, P]
         lib.mbph_gather_conflicts.restype = I64
         lib.mbph_tilt_band.restype = I64
+        lib.mbph_tilt_gather.restype = I64
         lib.mbph_check_rays.restype = I64
         _lib = lib
     return _lib
@@ -198,3 +200,20 @@ def tilt_band(geom: dict, traj: dict, stride: int):
                               float(geom.get("dv", 1.0)), int(stride), ctypes.byref(misses),
                               ctypes.byref(cand))
     return int(hits), int(misses.value), int(cand.value)
+
+
+def tilt_gather(geom: dict, traj: dict, sino: np.ndarray, mode: int = 0):
+    """Replay the gather for detectors whose rows do not run along z on a (views, rows, cols)
+    sinogram: (volume (D, H, W) fp64, units, units whose run combine fails, units taking LDS
+    atomics); mode 1 plants a mistake (see hostcheck.cpp)."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    rows, views, cols = int(geom.get("rows", 1)), int(geom["views"]), int(geom["cols"])
+    s = np.ascontiguousarray(sino, dtype=np.float32).reshape(views, rows, cols)
+    vol = np.zeros(int(n[0]) * int(n[1]) * int(n[2]), dtype=np.float64)
+    conflicts, atomic = ctypes.c_longlong(0), ctypes.c_longlong(0)
+    units = lib.mbph_tilt_gather(_ptr(f), _ptr(lo), _ptr(p), _ptr(n), views, rows, cols,
+                                 float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)), _ptr(s),
+                                 int(mode), _ptr(vol), ctypes.byref(conflicts), ctypes.byref(atomic))
+    return (vol.reshape(tuple(int(x) for x in geom["shape"])), int(units), int(conflicts.value),
+            int(atomic.value))

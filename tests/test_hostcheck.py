@@ -299,3 +299,35 @@ def test_tilt_gather_bands_hold_every_crossing(case):
     assert hits > 100000 and misses == 0
     if case != "random":
         assert cand < 1.2 * hits
+
+
+@pytest.mark.parametrize("case", ["tilted", "tilted_flipped", "random"])
+def test_tilt_gather_replay_reproduces_oracle_adjoint(oracle, case):
+    """The gather for detectors whose rows do not run along z, replayed on the CPU unit by
+    unit (bands, each row's fp64 clip, two-cell shares or the piece walk, the pre-pass row
+    value) gives the oracle's adjoint to fp64 rounding. Every unit whose pair keys are
+    monotone along the wave goes through the run combine, replayed on lane sets with the
+    kernel's run-length loop and parked lanes, without losing, repeating or misdirecting a
+    share; on the tilted circle every unit is monotone (rows up or down), random frames send
+    some units to the LDS atomics. A combine one shift step short loses shares."""
+    from dataclasses import replace
+    from workloads import random_cone_trajectory
+    if case == "random":
+        cfg = replace(SMALL_CONFIGS["c4_cone512_aniso"], views=10)
+        traj = random_cone_trajectory(10, seed=12, radius=150.0, sdd=260.0, tilt=0.5)
+    else:
+        cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory="circular_tilted")
+        traj = config_trajectory(cfg)
+        if case == "tilted_flipped":
+            traj = flipped(traj)
+    geom = _geom(cfg)
+    y = np.random.default_rng(7).random((cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    b, units, conflicts, atomic = HC.tilt_gather(geom, traj, y)
+    bref = oracle.backproject(geom, traj, y)
+    floor = 1e-6 * np.abs(bref).max()
+    assert units > 100000 and conflicts == 0
+    assert (atomic > 0) == (case == "random")
+    assert np.linalg.norm(b - bref) / np.linalg.norm(bref) < 1e-12
+    assert (np.abs(b - bref) / np.maximum(np.abs(bref), floor)).max() < 1e-10
+    if case != "random":
+        assert HC.tilt_gather(geom, traj, y, mode=1)[2] > 0
