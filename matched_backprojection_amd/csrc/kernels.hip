@@ -1113,29 +1113,25 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
         // The adds of one item (rows k0 + lane) with the lanes' row values w.
         auto sum_item = [&](const TiltItem& it, const float (&w)[NB]) {
             const int32_t view = (int32_t)uniform((uint32_t)it.view);
-            const int32_t j = (int32_t)uniform((uint32_t)it.j);
             const int32_t k0 = (int32_t)uniform((uint32_t)it.k0);
             const int32_t nrows = (int32_t)uniform((uint32_t)it.nrows);
-            // the frame through the constant address space: read with scalar loads
+            // the frame's source and row axis through the constant address space: scalar loads
             typedef const __attribute__((address_space(4))) double cdouble;
             const cdouble* const fp = reinterpret_cast<cdouble*>(reinterpret_cast<uintptr_t>(A.frames + view));
-            Frame F;
+            double src[3], ev[3];
 #pragma unroll
             for (int a = 0; a < 3; ++a) {
-                F.s[a] = fp[a];
-                F.c[a] = fp[3 + a];
-                F.u[a] = fp[6 + a];
-                F.v[a] = fp[9 + a];
+                src[a] = fp[a];
+                ev[a] = fp[9 + a];
             }
-            const double u = centred(j, A.cols, A.du);
             const double v = centred(k0 + lane, A.rows, A.dv);
             double d[3];
 #pragma unroll
-            for (int a = 0; a < 3; ++a) d[a] = fma(v, F.v[a], (F.c[a] - F.s[a]) + u * F.u[a]);
+            for (int a = 0; a < 3; ++a) d[a] = fma(v, ev[a], it.b[a]);
             double t0, t1;
-            tilt_clip_rcp(F.s, d, x0, x1, y0, y1, t0, t1);
+            tilt_clip_rcp(src, d, x0, x1, y0, y1, t0, t1);
             const bool active = lane < nrows && t1 > t0;
-            const double szc = (F.s[2] - A.box.lo[2]) * ipz, dzc = d[2] * ipz;
+            const double szc = it.szc, dzc = d[2] * ipz;
             const double za = fma(t0, dzc, szc), zb = fma(t1, dzc, szc);
             const double zmin = fmin(za, zb), zmax = fmax(za, zb);
             const double fa = floor(zmin);
@@ -1157,7 +1153,7 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
             // pair address, clamped to the parked pairs below and above the chunk; lanes past
             // the item's crossing rows take the parked pair at their end of the column, so the
             // addresses stay monotone when the rows' cells are
-            const bool up = F.v[2] >= 0.0;
+            const bool up = ev[2] >= 0.0;
             const uint64_t act = __ballot(active);
             const int32_t i0 = (int32_t)fmax(fmin(fa - (double)(z0 - 1), (double)(n + 1)), -2.0);
             int32_t key = a0 + i0 * 4 * NB;
@@ -1236,7 +1232,12 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
                 if (emit) {
                     const uint32_t below = __builtin_amdgcn_mbcnt_hi(
                         (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    const Frame& F = A.frames[view];
+                    const double u = centred(jc, A.cols, A.du);
                     TiltItem t;
+#pragma unroll
+                    for (int a = 0; a < 3; ++a) t.b[a] = (F.c[a] - F.s[a]) + u * F.u[a];
+                    t.szc = (F.s[2] - A.box.lo[2]) * ipz;
                     t.view = view;
                     t.j = jc;
                     t.k0 = kk;

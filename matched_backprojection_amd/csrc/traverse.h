@@ -557,8 +557,12 @@ MBP_HD MBP_INLINE bool tilt_row_range(const TiltCorners& T, int32_t j, int32_t r
 }
 
 // One item of the tilted gather: rows k0 .. k0 + nrows - 1 (at most 64) of column j in view
-// `view` (16 bytes).
+// `view`, with what its rows share: the ray direction of the column at v = 0, b = c - s + u eu
+// (row k's direction is b + v_k ev), and the source's z in cells above the box, szc
+// (48 bytes).
 struct TiltItem {
+    double b[3];
+    double szc;
     int32_t view, j, k0, nrows;
 };
 
