@@ -116,7 +116,10 @@ def test_configs_plan_and_pick_walks(lib, name):
 
 def test_tilted_detector_uses_generic_walk(lib):
     """Random tilted frames, and a circular orbit whose detector is rotated by a few degrees
-    in its plane: the row axis is not along z, so only the generic walk applies."""
+    in its plane: the row axis is not along z, so the forward takes the generic walk. The
+    adjoint's gather (the default) needs a workspace of the volume copy and the reordered
+    sinogram, as the column gather does; the scatter adjoint (the generic walk's atomics), or
+    a forced generic walk, needs none."""
     from dataclasses import replace
     cfg = SMALL_CONFIGS["c3_cone256"]
     tilted = replace(cfg, trajectory="circular_tilted")
@@ -126,6 +129,13 @@ def test_tilted_detector_uses_generic_walk(lib):
         assert rc == 0
         inf = _info(lib, h)
         assert inf.column_capable == 0 and inf.path == 1
+        ws = ctypes.c_size_t()
+        assert lib.mbp_workspace_size(h, 3, ctypes.byref(ws)) == 0
+        assert ws.value == 4 * 2 * (cfg.n_voxels + gather_sino_floats(cfg))
+        assert lib.mbp_plan_set_adjoint(h, 2) == 0
+        assert lib.mbp_workspace_size(h, 3, ctypes.byref(ws)) == 0 and ws.value == 0
+        assert lib.mbp_plan_set_adjoint(h, 0) == 0 and lib.mbp_plan_set_path(h, 1) == 0
+        assert lib.mbp_workspace_size(h, 3, ctypes.byref(ws)) == 0 and ws.value == 0
         lib.mbp_plan_destroy(h)
 
 

@@ -396,6 +396,32 @@ def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
     plan.close()
 
 
+def test_tilted_view_batches_and_accumulate(torch_dev, mbp, oracle):
+    """The per-row gather over ragged view batches (each launch adds into the previous ones),
+    both layouts, batches of one, three and five members (groups of four and one), and
+    accumulation into a prefilled volume."""
+    from dataclasses import replace
+    torch, dev = torch_dev
+    cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory="circular_tilted")
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(9)
+    ys = rng.random((5, cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    for layout in ("DHW", "WHD"):
+        plan = make_plan(mbp, cfg, traj=traj, layout=layout)
+        plan.set_view_batch(7)                # 36 views -> launches of 7 + ragged 1
+        for B in (1, 3, 5):
+            say(f"case tilted view-batch 7 layout={layout} B={B}")
+            b = plan.backproject(torch.from_numpy(ys[:B]).to(dev)).cpu().numpy().astype(np.float64)
+            for m in range(B):
+                check(b[m], bref[m], f"adjoint member {m}")
+        pre = rng.random(cfg.shape).astype(np.float32)
+        out = to_device_volume(torch, dev, pre, layout)
+        plan.backproject(torch.from_numpy(ys[0]).to(dev), out=out, accumulate=True)
+        check(out.cpu().numpy().astype(np.float64), bref[0] + pre.astype(np.float64), "accumulate")
+        plan.close()
+
+
 def test_layout_conversion_roundtrip(torch_dev, mbp):
     torch, dev = torch_dev
     x = torch.rand((3, 37, 41, 29), device=dev)
