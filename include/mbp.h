@@ -112,7 +112,8 @@ typedef struct mbp_geometry {
 typedef struct mbp_plan mbp_plan;
 
 typedef struct mbp_plan_info {
-    int32_t path;              /* MBP_PATH_GENERIC or MBP_PATH_COLUMN (the one that runs)   */
+    int32_t path;              /* MBP_PATH_GENERIC or MBP_PATH_COLUMN: the walk that runs
+                                  (the forward's; the adjoint kernel follows mbp_adjoint)   */
     int32_t column_capable;    /* 1 if the geometry allows the column walk                  */
     int64_t views_per_launch;  /* view batch of one kernel launch                           */
     int64_t launches;          /* kernel launches per member group and operation            */
