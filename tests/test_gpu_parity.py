@@ -422,6 +422,30 @@ def test_tilted_view_batches_and_accumulate(torch_dev, mbp, oracle):
         plan.close()
 
 
+@pytest.mark.parametrize("trajectory", ["circular", "circular_tilted"])
+def test_z_chunked_gathers_parity(torch_dev, mbp, oracle, trajectory):
+    """A column too tall for one wave's LDS (600 cells of four interleaved members, more than
+    the 2048 floats a wave holds): the gathers split it into z chunks of 512 cells, each wave
+    building its items for its own chunk (rows 460, eight per lane, fast cell pairs on the
+    circle; per-row clips when tilted); one member fits a single chunk."""
+    from dataclasses import replace
+    torch, dev = torch_dev
+    cfg = replace(SMALL_CONFIGS["c4_cone512_aniso"], name="tall_column", shape=(600, 8, 8),
+                  spacing=(0.5, 1.0, 1.0), sid=400.0, sdd=600.0, rows=460, cols=24, views=8,
+                  trajectory=trajectory, layout="DHW")
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(17)
+    ys = rng.random((4, cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    plan = make_plan(mbp, cfg, traj=traj)
+    for B in (1, 4):
+        say(f"case z-chunked {trajectory} B={B}")
+        b = plan.backproject(torch.from_numpy(ys[:B]).to(dev)).cpu().numpy().astype(np.float64)
+        for m in range(B):
+            check(b[m], bref[m], f"adjoint member {m}")
+    plan.close()
+
+
 def test_layout_conversion_roundtrip(torch_dev, mbp):
     torch, dev = torch_dev
     x = torch.rand((3, 37, 41, 29), device=dev)
