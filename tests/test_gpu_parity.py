@@ -128,12 +128,16 @@ def test_small_config_parity(torch_dev, mbp, oracle, name):
         plan.close()
 
 
-def test_steep_cone_parity(torch_dev, mbp, oracle):
+@pytest.mark.parametrize("trajectory", ["circular", "circular_tilted"])
+def test_steep_cone_parity(torch_dev, mbp, oracle, trajectory):
     """Rows crossing several z cells per xy cell and leaving through the box's z faces: the
-    gather's general piece walk, in both its plain-LDS and its atomic mode."""
+    gather's general piece walk, in both its plain-LDS and its atomic mode; with the detector
+    tilted, the per-row gather's piece walk and its LDS atomics for units whose cells are out
+    of order."""
+    from dataclasses import replace
     from tests.test_hostcheck import steep_cone_config
     torch, dev = torch_dev
-    cfg = steep_cone_config()
+    cfg = replace(steep_cone_config(), trajectory=trajectory)
     geom, traj = geom_of(cfg), config_trajectory(cfg)
     rng = np.random.default_rng(21)
     x = rng.random(cfg.shape).astype(np.float32)

@@ -277,7 +277,7 @@ def test_chunked_column_walk_full_size_views(oracle, name):
     assert np.linalg.norm(s - ref) / np.linalg.norm(ref) < 1e-6
 
 
-@pytest.mark.parametrize("case", ["tilted", "tilted_flipped", "random"])
+@pytest.mark.parametrize("case", ["tilted", "tilted_flipped", "random", "steep"])
 def test_tilt_gather_bands_hold_every_crossing(case):
     """The gather for detectors whose rows do not run along z takes, per view and xy cell, the
     candidate columns and each column's candidate rows from the cell corners' projections. On
@@ -290,18 +290,21 @@ def test_tilt_gather_bands_hold_every_crossing(case):
     if case == "random":
         cfg = replace(SMALL_CONFIGS["c4_cone512_aniso"], views=30)
         traj = random_cone_trajectory(30, seed=12, radius=150.0, sdd=260.0, tilt=0.5)
+    elif case == "steep":
+        cfg = replace(steep_cone_config(), trajectory="circular_tilted")
+        traj = config_trajectory(cfg)
     else:
         cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory="circular_tilted")
         traj = config_trajectory(cfg)
         if case == "tilted_flipped":
             traj = flipped(traj)
     hits, misses, cand = HC.tilt_band(_geom(cfg), traj, 3)
-    assert hits > 100000 and misses == 0
-    if case != "random":
+    assert hits > 50000 and misses == 0
+    if case in ("tilted", "tilted_flipped"):
         assert cand < 1.2 * hits
 
 
-@pytest.mark.parametrize("case", ["tilted", "tilted_flipped", "random"])
+@pytest.mark.parametrize("case", ["tilted", "tilted_flipped", "random", "steep"])
 def test_tilt_gather_replay_reproduces_oracle_adjoint(oracle, case):
     """The gather for detectors whose rows do not run along z, replayed on the CPU unit by
     unit (bands, each row's fp64 clip, two-cell shares or the piece walk, the pre-pass row
@@ -309,12 +312,16 @@ def test_tilt_gather_replay_reproduces_oracle_adjoint(oracle, case):
     monotone along the wave goes through the run combine, replayed on lane sets with the
     kernel's run-length loop and parked lanes, without losing, repeating or misdirecting a
     share; on the tilted circle every unit is monotone (rows up or down), random frames send
-    some units to the LDS atomics. A combine one shift step short loses shares."""
+    some units to the LDS atomics, and so does the tilted steep cone (rows spanning several
+    cells walk their pieces). A combine one shift step short loses shares."""
     from dataclasses import replace
     from workloads import random_cone_trajectory
     if case == "random":
         cfg = replace(SMALL_CONFIGS["c4_cone512_aniso"], views=10)
         traj = random_cone_trajectory(10, seed=12, radius=150.0, sdd=260.0, tilt=0.5)
+    elif case == "steep":
+        cfg = replace(steep_cone_config(), trajectory="circular_tilted")
+        traj = config_trajectory(cfg)
     else:
         cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory="circular_tilted")
         traj = config_trajectory(cfg)
@@ -325,9 +332,9 @@ def test_tilt_gather_replay_reproduces_oracle_adjoint(oracle, case):
     b, units, conflicts, atomic = HC.tilt_gather(geom, traj, y)
     bref = oracle.backproject(geom, traj, y)
     floor = 1e-6 * np.abs(bref).max()
-    assert units > 100000 and conflicts == 0
-    assert (atomic > 0) == (case == "random")
+    assert units > 10000 and conflicts == 0
+    assert (atomic > 0) == (case in ("random", "steep"))
     assert np.linalg.norm(b - bref) / np.linalg.norm(bref) < 1e-12
     assert (np.abs(b - bref) / np.maximum(np.abs(bref), floor)).max() < 1e-10
-    if case != "random":
+    if case in ("tilted", "tilted_flipped"):
         assert HC.tilt_gather(geom, traj, y, mode=1)[2] > 0
