@@ -858,6 +858,8 @@ MBP_HD MBP_INLINE void fast_row(int32_t za, int32_t zb, int32_t& fa, uint32_t& n
 // the distance at which a cell ends and the cell's xy index, the cell before that crossing.
 
 constexpr int32_t kXYChunk = 128;
+// xy_chunk_fill gives each of a wave's 64 lanes two window indices of each axis.
+static_assert(kXYChunk == 2 * 64, "xy_chunk_fill covers two crossings per lane");
 // Cells per group when a row's pieces are computed ahead of their loads.
 constexpr int32_t kCellGroup = 4;
 
