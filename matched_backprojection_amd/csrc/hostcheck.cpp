@@ -296,16 +296,18 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                             for (int lane = 0; lane < 64; ++lane) {
                                 const int32_t k0 = g0 + S * lane;
                                 const int32_t c0 = fast_origin_row(S);
-                                int32_t la, lb, base;
+                                uint32_t la, lb;
+                                int32_t base;
                                 fast_origin(it, k0 + c0, -1, la, lb, base);
                                 for (int32_t c = 0; c < S; ++c) {
                                     // the row's ends must stay inside the fixed point's range
                                     const int64_t pa = (int64_t)la + (int64_t)(c - c0) * it.a1fx;
                                     const int64_t pb = (int64_t)lb + (int64_t)(c - c0) * it.b1fx;
-                                    if (pa != (int32_t)pa || pb != (int32_t)pb) ++*violations;
-                                    int32_t fa;
+                                    if (pa < 0 || pa > (int64_t)UINT32_MAX || pb < 0 || pb > (int64_t)UINT32_MAX)
+                                        ++*violations;
+                                    int32_t fb;
                                     uint32_t num, ext;
-                                    fast_row((int32_t)pa, (int32_t)pb, fa, num, ext);
+                                    fast_row((uint32_t)pa, (uint32_t)pb, fb, num, ext);
                                     // both shares from integers: the lower cell's num / ext and
                                     // the upper one's (ext - num) / ext
                                     double f = 1.0, g = 0.0;
@@ -319,7 +321,7 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                                             g = (double)(ext - num) / (double)ext;
                                         }
                                     }
-                                    const int32_t i0 = base + fa;
+                                    const int32_t i0 = base + fb;
                                     if ((uint32_t)i0 > (uint32_t)D) continue;     // outside: discarded
                                     const int32_t z = i0 - 1;                      // cell of index i0
                                     const double wk = w[k0 + c];
@@ -625,11 +627,12 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
                                 for (int lane = 0; lane < 64; ++lane) {
                                     const int32_t k0 = mode == 2 ? g0 + 64 * c + lane - c : g0 + S * lane;
                                     const int32_t c0 = fast_origin_row(S);
-                                    int32_t la, lb, base, fa;
-                                    uint32_t num, ext;
+                                    uint32_t la, lb, num, ext;
+                                    int32_t base, fb;
                                     fast_origin(it, k0 + c0, -1, la, lb, base);
-                                    fast_row(la + (c - c0) * it.a1fx, lb + (c - c0) * it.b1fx, fa, num, ext);
-                                    key[lane] = base + fa;
+                                    fast_row(la + (uint32_t)((c - c0) * it.a1fx), lb + (uint32_t)((c - c0) * it.b1fx),
+                                             fb, num, ext);
+                                    key[lane] = base + fb;
                                 }
                                 if (it.form == kFastRuns && mode != 3) {
                                     // the kernel's clamp of the pair index to [-2, D + 1]
@@ -688,6 +691,71 @@ int64_t mbph_gather_conflicts(const double* frames, int beam, const double* lo, 
         }
     }
     return checked;
+}
+
+// Checks kFastInside, under which the gather writes a fast item's cell pairs without clamping
+// their indices: for every fast item and every z chunk of `zchunk` cells (the last one ragged)
+// for which gather_item sets it, every row of every lane (padded rows too) must have its pair
+// index, replayed in the kernel's fixed point, in [-2, n + 1]. Returns the fast items met;
+// *inside counts the (item, chunk) pairs accepted, *violations the rows outside. mode 1
+// plants a mistake: the range test looks at the first row only.
+int64_t mbph_fast_inside(const double* frames, int beam, const double* lo, const double* pitch,
+                         const int32_t* n, int views, int rows, int cols, double du, double dv,
+                         int zchunk, int mode, long long* inside, long long* violations) {
+    std::vector<Frame> F;
+    frames_from(frames, views, F);
+    const Box B = box_from(lo, pitch, n);
+    *inside = 0;
+    *violations = 0;
+    const bool line = beam == BEAM_PARALLEL;
+    const int32_t S = gather_stride(rows), rows_pad = gather_rows_padded(rows), D = n[2];
+    int64_t fast = 0;
+    for (int ix = 0; ix < n[0]; ++ix) {
+        for (int iy = 0; iy < n[1]; ++iy) {
+            const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
+            const double y0 = B.lo[1] + iy * B.pitch[1], y1 = y0 + B.pitch[1];
+            for (int v = 0; v < views; ++v) {
+                int32_t j0, j1;
+                if (!cell_column_range(F[v], beam, cols, du, x0, x1, y0, y1, j0, j1)) continue;
+                for (int32_t j = j0; j <= j1; ++j) {
+                    ColLine L;
+                    column_line(F[v], B, beam, j, cols, rows, du, dv, L);
+                    GatherItem it;
+                    if (!gather_item(L, line, x0, x1, y0, y1, S, rows, rows_pad, v * cols + j, it)) continue;
+                    if (it.form <= 0) continue;
+                    ++fast;
+                    for (int32_t z0 = 0; z0 < D; z0 += zchunk) {
+                        const int32_t nz = std::min(zchunk, D - z0);
+                        const float in_lo = fast_inside_lo(z0, nz), in_hi = fast_inside_hi(z0, nz);
+                        GatherItem ci;
+                        gather_item(L, line, x0, x1, y0, y1, S, rows, rows_pad, v * cols + j, ci, in_lo, in_hi);
+                        bool accepted = (ci.form & kFastInside) != 0;
+                        if (mode == 1) {
+                            double t0, t1;
+                            cell_clip(L, line, x0, x1, y0, y1, t0, t1);
+                            const double za0 = L.c0 + t0 * L.c1, zb0 = L.c0 + t1 * L.c1;
+                            accepted = rows_inside(za0, zb0, za0, zb0, in_lo, in_hi);
+                        }
+                        if (!accepted) continue;
+                        ++*inside;
+                        const int32_t c0 = fast_origin_row(S);
+                        for (int32_t k0 = 0; k0 < rows_pad; k0 += S) {
+                            uint32_t la, lb, num, ext;
+                            int32_t base, fb;
+                            fast_origin(it, k0 + c0, z0 - 1, la, lb, base);
+                            for (int32_t c = 0; c < S; ++c) {
+                                fast_row(la + (uint32_t)((c - c0) * it.a1fx), lb + (uint32_t)((c - c0) * it.b1fx),
+                                         fb, num, ext);
+                                const int32_t pi = base + fb;
+                                if (pi < -2 || pi > nz + 1) ++*violations;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+    return fast;
 }
 
 // Bounds-only sweep of selected rays (flat ids) with either walk; returns visits.

@@ -716,47 +716,53 @@ __device__ __forceinline__ void gather_runs_add(lds_float* dst, lds_float* park,
 // step. Not RUNS (kFastPairs): all lanes update their pairs at once with one paired read and
 // write. RUNS (kFastRuns): lanes that share a pair are combined first (gather_runs_add); lanes
 // S * G rows apart never share one. FULL: the lane takes all KR loaded rows (S == KR), so the
-// unrolled rows need no guard.
-template <int NB, int KR, bool FULL, bool RUNS>
+// unrolled rows need no guard. CLAMP: some row may leave the chunk's pair indices (the item is
+// not kFastInside), so every pair index is clamped.
+template <int NB, int KR, bool FULL, bool RUNS, bool CLAMP>
 __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
                                                   float dt, const float (&w)[KR][NB],
                                                   int32_t k0, int32_t S, int32_t z0, int32_t n,
                                                   float* col, int32_t G) {
     // the origin row of fast_origin_row(S): the middle one when S == kGroup
     constexpr int c0 = FULL && KR == kGroup ? kGroup / 2 : 0;
-    int32_t la, lb, base;
+    uint32_t la, lb;
+    int32_t base;
     fast_origin(it, k0 + c0, z0 - 1, la, lb, base);
-    // A row's pair index base + fa (fa within 8 cells of the origin) is clamped to [-2, n + 1].
-    // One member: the clamp works on byte addresses. The base is first clamped to
-    // [-16, n + 16], which leaves every clamped index unchanged and keeps the address far from
-    // overflow, so each row forms its address with one shift-add and one clamp (two and four
-    // members keep the index form, which needs fewer registers).
+    // A row's pair index is base + fb (fb in [0, 15]); with CLAMP it is clamped to [-2, n + 1].
+    // One member: the index is a byte address, and the clamp works on it. The base is first
+    // clamped to [-24, n + 8], which leaves every clamped index unchanged and keeps the address
+    // far from overflow, so each row forms its address with one shift-add and one clamp (two
+    // and four members keep the index form, which needs fewer registers).
     const int32_t a0 = lds_addr(col);
     int32_t abase = 0, alo = 0, ahi = 0;
     if constexpr (NB == 1) {
-        abase = (clamp_range(base, -16, n + 16) << 2) + a0;
-        alo = in_vgpr(a0 - 8);
-        ahi = a0 + ((n + 1) << 2);
+        if constexpr (CLAMP) {
+            abase = (clamp_range(base, -24, n + 8) << 2) + a0;
+            alo = in_vgpr(a0 - 8);
+            ahi = a0 + ((n + 1) << 2);
+        } else {
+            abase = (base << 2) + a0;
+        }
     }
-    int32_t za[KR], zb[KR];
+    uint32_t za[KR], zb[KR];
     za[c0] = la;
     zb[c0] = lb;
 #pragma unroll
     for (int c = c0 + 1; c < KR; ++c) {
-        za[c] = za[c - 1] + a1;
-        zb[c] = zb[c - 1] + b1;
+        za[c] = za[c - 1] + (uint32_t)a1;
+        zb[c] = zb[c - 1] + (uint32_t)b1;
     }
 #pragma unroll
     for (int c = c0 - 1; c >= 0; --c) {
-        za[c] = za[c + 1] - a1;
-        zb[c] = zb[c + 1] - b1;
+        za[c] = za[c + 1] - (uint32_t)a1;
+        zb[c] = zb[c + 1] - (uint32_t)b1;
     }
 #pragma unroll
     for (int c = 0; c < KR; ++c) {
         if (!FULL && c >= S) continue;
-        int32_t fa;
+        int32_t fb;
         uint32_t num, ext;
-        fast_row(za[c], zb[c], fa, num, ext);
+        fast_row(za[c], zb[c], fb, num, ext);
         // the shares of the lower and upper cells, num / ext and (ext - num) / ext, when the
         // row crosses the plane above fa, else 1 and 0: num >= ext exactly when it does not,
         // so a min with 1 and a saturating difference select both cases; a row of zero extent
@@ -767,10 +773,13 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         const float f = fminf((float)num * r, 1.0f);
         const float g = mul_legacy((float)__builtin_elementwise_sub_sat(ext, num), r);
         lds_float* dst;
-        if constexpr (NB == 1)
-            dst = lds_ptr(clamp_range(shl_add<2>(fa, abase), alo, ahi));
-        else
-            dst = lds_ptr(a0 + clamp_pair(base + fa, n + 1) * (4 * NB));
+        if constexpr (NB == 1) {
+            const int32_t ad = shl_add<2>(fb, abase);
+            dst = lds_ptr(CLAMP ? clamp_range(ad, alo, ahi) : ad);
+        } else {
+            const int32_t pi = base + fb;
+            dst = lds_ptr(a0 + (CLAMP ? clamp_pair(pi, n + 1) : pi) * (4 * NB));
+        }
         float qa[NB], qb[NB];
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
@@ -884,6 +893,13 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
         // Units of work: (item, row group) in queue order, counted without divisions. The rows
         // of the next unit are loaded while the current one is summed.
         const int32_t ngroups = rows_pad / (64 * S);
+        // Fast items that keep to the chunk skip the clamp when a lane holds several rows. With
+        // one row per lane a unit is short, and the unclamped variants' extra code costs more
+        // than the clamp (measured on the helical batch), so those items keep it and skip the
+        // range test.
+        constexpr bool kUnclamped = KR > 1;
+        const float in_lo = kUnclamped ? fast_inside_lo(z0, n) : INFINITY;
+        const float in_hi = kUnclamped ? fast_inside_hi(z0, n) : -INFINITY;
         int32_t lane_row = S * lane;
         asm volatile("" : "+v"(lane_row));    // kept as one value: a unit's first row is one add
         auto unit_rows = [&](int32_t i, int32_t gi) {
@@ -910,17 +926,24 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                     const float dt = __uint_as_float(uniform(__float_as_uint(it.dt)));
                     const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
                     const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
-                    if (form == kFastPairs) {
-                        if (S == KR)
-                            gather_fast_group<NB, KR, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
+                    // items whose rows all stay inside the chunk skip the clamp (full groups of
+                    // several rows per lane only)
+                    const bool inside = kUnclamped && (form & kFastInside) != 0;
+                    if ((form & ~kFastInside) == kFastPairs) {
+                        if (S == KR && inside)
+                            gather_fast_group<NB, KR, true, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
+                        else if (S == KR)
+                            gather_fast_group<NB, KR, true, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
                         else
-                            gather_fast_group<NB, KR, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
+                            gather_fast_group<NB, KR, false, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
                     } else {
                         const int32_t G = (int32_t)uniform((uint32_t)it.run);
-                        if (S == KR)
-                            gather_fast_group<NB, KR, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
+                        if (S == KR && inside)
+                            gather_fast_group<NB, KR, true, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
+                        else if (S == KR)
+                            gather_fast_group<NB, KR, true, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
                         else
-                            gather_fast_group<NB, KR, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
+                            gather_fast_group<NB, KR, false, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
                     }
                 } else {
                     gather_general_group<NB, KR>(it, form == kGeneralExclusive, w, k0, S, z0, z1, col);
@@ -956,7 +979,8 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                 bool hit = false;
                 if (jn <= j1) {
                     const int32_t yoff = view * A.cols + jn;
-                    hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff, it);
+                    hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff, it,
+                                      in_lo, in_hi);
                     jn += kViewLanes;
                 }
                 const uint64_t m = __ballot(hit);

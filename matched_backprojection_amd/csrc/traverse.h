@@ -698,6 +698,10 @@ constexpr double kFastSpan = 5.5;
 // or need atomics.
 constexpr int32_t kFastPairs = 1;
 constexpr int32_t kFastRuns = 2;
+// Added to a fast form when every row's cell pair lies inside the column chunk's range of pair
+// indices (gather_item with fast_inside_lo and fast_inside_hi), so that the kernel needs no
+// clamp.
+constexpr int32_t kFastInside = 4;
 constexpr int32_t kGeneralExclusive = 0;
 constexpr int32_t kGeneralAtomic = -1;
 
@@ -765,10 +769,33 @@ MBP_HD MBP_INLINE bool gather_fast(int32_t S, int32_t rows_pad, double za0, doub
            fmax(e0, e1) < 1.0 - 1e-6 && fast_run(S, a1, b1, 1) > 0;
 }
 
-// The item of column line L crossing the cell, or false when it misses.
+// Whether both ends of every row of an item lie in [lo, hi), from the ends of its first and
+// last rows (positions are linear in the row, so the extremes are there), tested on the ends
+// rounded to fp32.
+MBP_HD MBP_INLINE bool rows_inside(double za_first, double zb_first, double za_last, double zb_last,
+                                   float lo, float hi) {
+    const float a0 = (float)za_first, b0 = (float)zb_first, a1 = (float)za_last, b1 = (float)zb_last;
+    return fminf(fminf(a0, a1), fminf(b0, b1)) >= lo && fmaxf(fmaxf(a0, a1), fmaxf(b0, b1)) < hi;
+}
+
+// The z range, in cells, that a fast item's rows must keep to for the gather to write their
+// cell pairs unclamped in the column chunk of n cells from z0 >= 0: the lower end's cell then
+// lies in [z0 - 3, z0 + n] (pair indices [-2, n + 1] from the guard cell z0 - 1). The quarter
+// cell of margin covers the fixed point's rounding (a few units of 2^-28) and the fp32
+// rounding of rows_inside, which is below 2^-5 cell for ends that pass when z0 + n <= 2^19;
+// deeper chunks accept nothing.
+MBP_HD MBP_INLINE float fast_inside_lo(int32_t z0, int32_t n) {
+    return z0 + n <= (1 << 19) ? (float)z0 - 2.75f : INFINITY;
+}
+MBP_HD MBP_INLINE float fast_inside_hi(int32_t z0, int32_t n) { return (float)(z0 + n) + 0.75f; }
+
+// The item of column line L crossing the cell, or false when it misses. A fast item whose
+// rows (padded ones too) keep both ends in [in_lo, in_hi) gets kFastInside (never with an
+// empty range, such as the default, which skips the test).
 MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, double x1, double y0,
                                    double y1, int32_t S, int32_t rows, int32_t rows_pad,
-                                   int32_t yoff, GatherItem& it) {
+                                   int32_t yoff, GatherItem& it, float in_lo = INFINITY,
+                                   float in_hi = -INFINITY) {
     double t0, t1;
     if (!cell_clip(L, line, x0, x1, y0, y1, t0, t1)) return false;
     it.za0 = L.c0 + t0 * L.c1;
@@ -780,9 +807,10 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
     // the per-row advances in fixed point (only meaningful when they fit; checked below), the
     // row count (row_times) and the positions' range at the first and last padded rows
     const double kl = (double)(rows_pad - 1);
+    const double za_last = fma(kl, it.za1, it.za0), zb_last = fma(kl, it.zb1, it.zb0);
     const bool fits = rows_pad <= (1 << 20) && fabs(it.za1) < kFastSpan && fabs(it.zb1) < kFastSpan &&
-                      fmax(fmax(fabs(it.za0), fabs(it.zb0)),
-                           fmax(fabs(fma(kl, it.za1, it.za0)), fabs(fma(kl, it.zb1, it.zb0)))) < kPosLimit;
+                      fmax(fmax(fabs(it.za0), fabs(it.zb0)), fmax(fabs(za_last), fabs(zb_last))) < kPosLimit;
+    const bool inside = in_lo < in_hi && rows_inside(it.za0, it.zb0, za_last, zb_last, in_lo, in_hi);
     it.a1fx = fits ? (int32_t)rint(it.za1 * kZScale) : 0;
     it.b1fx = fits ? (int32_t)rint(it.zb1 * kZScale) : 0;
     it.run = 0;
@@ -793,6 +821,7 @@ MBP_HD MBP_INLINE bool gather_item(const ColLine& L, bool line, double x0, doubl
             it.form = kFastRuns;
             it.run = fast_run(S, it.a1fx, it.b1fx, 1);
         }
+        if (inside) it.form |= kFastInside;
         const double half = 0.5 / kZScale;
         const int64_t a0 = (int64_t)rint((it.za0 + half) * kPosScale);
         const int64_t a1 = (int64_t)rint(it.za1 * kPosScale);
@@ -818,30 +847,50 @@ MBP_HD MBP_INLINE int64_t row_times(int32_t k, int64_t f) {
     return (int64_t)((uint64_t)(uint32_t)k * lo + ((uint64_t)(uint32_t)(k * hi) << 32));
 }
 
+// Row ends are held unsigned, offset by kZBias (8 cells): a signed position p in (-8, 8) cells
+// becomes p + 2^31, so that order, floor and differences are those of unsigned integers, and
+// the cell of an end is its top four bits minus kZBiasCells.
+constexpr uint32_t kZBias = 0x80000000u;
+constexpr int32_t kZBiasCells = 8;
+static_assert(kZBias == (uint32_t)kZBiasCells << kZFrac, "the offset is kZBiasCells cells");
+
 // A lane's origin for the fast form from its origin row k: the integer cell I of that row's
 // entry end and the row's ends relative to I in fixed point (the entry end in [0, 1) cell, the
-// exit end in (-1, 2)), rounded to nearest. `base` is I minus `cell0` (the cell held at index
-// 0); |I| < 2^22 (kPosLimit).
-MBP_HD MBP_INLINE void fast_origin(const GatherItem& it, int32_t k, int32_t cell0, int32_t& la,
-                                   int32_t& lb, int32_t& base) {
+// exit end in (-1, 2)), rounded to nearest, offset by kZBias: they are taken relative to the
+// cell I - kZBiasCells. `base` is I - kZBiasCells - cell0 (cell0: the cell held at index 0),
+// so that a row's pair index, its lower end's cell minus cell0, is base + fb (fast_row);
+// |I| < 2^22 (kPosLimit).
+MBP_HD MBP_INLINE void fast_origin(const GatherItem& it, int32_t k, int32_t cell0, uint32_t& la,
+                                   uint32_t& lb, int32_t& base) {
     const int64_t pa = it.fa0 + row_times(k, it.fa1);
     const int64_t pb = it.fb0 + row_times(k, it.fb1);
-    const int32_t I = (int32_t)(pa >> kPosFrac);                   // arithmetic shift: floor
-    const int64_t ref = (int64_t)I * ((int64_t)1 << kPosFrac);
-    la = (int32_t)((pa - ref) >> (kPosFrac - kZFrac));
-    lb = (int32_t)((pb - ref) >> (kPosFrac - kZFrac));
-    base = I - cell0;
+    const int32_t Ib = (int32_t)(pa >> kPosFrac) - kZBiasCells;    // arithmetic shift: floor
+    const int64_t ref = (int64_t)Ib * ((int64_t)1 << kPosFrac);
+    la = (uint32_t)((pa - ref) >> (kPosFrac - kZFrac));
+    lb = (uint32_t)((pb - ref) >> (kPosFrac - kZFrac));
+    base = Ib - cell0;
 }
 
-// One row of the fast form with ends za, zb (fixed point, relative to the lane origin): the
-// lower cell fa (relative to the origin), the distance num from the lower end to the plane
-// above fa and the extent ext. The row crosses that plane exactly when num < ext; then the
-// lower cell's share is num / ext and the upper one's (ext - num) / ext.
-MBP_HD MBP_INLINE void fast_row(int32_t za, int32_t zb, int32_t& fa, uint32_t& num, uint32_t& ext) {
-    const int32_t lo = za < zb ? za : zb, hi = za < zb ? zb : za;
-    fa = lo >> kZFrac;                              // arithmetic shift: floor
-    num = (uint32_t)(kZOne - (lo & (kZOne - 1)));
-    ext = (uint32_t)(hi - lo);
+// |a - b| (one v_sad_u32 on the device).
+MBP_HD MBP_INLINE uint32_t abs_diff(uint32_t a, uint32_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t r;
+    asm("v_sad_u32 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+#else
+    return a > b ? a - b : b - a;
+#endif
+}
+
+// One row of the fast form with ends za, zb (offset fixed point, relative to the lane
+// origin): the lower end's cell relative to the origin's cell, plus kZBiasCells, fb; the
+// distance num from the lower end to the plane above that cell; and the extent ext. The row crosses that plane exactly when num < ext; then the lower cell's share
+// is num / ext and the upper one's (ext - num) / ext.
+MBP_HD MBP_INLINE void fast_row(uint32_t za, uint32_t zb, int32_t& fb, uint32_t& num, uint32_t& ext) {
+    const uint32_t lo = za < zb ? za : zb;
+    fb = (int32_t)(lo >> kZFrac);
+    num = kZOne - (lo & (kZOne - 1));
+    ext = abs_diff(za, zb);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -38,6 +38,8 @@ def _load():
         lib.mbph_tilt_band.argtypes = [P, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_tilt_gather.argtypes = [P, P, P, P, I, I, I, D, D, P, I, P, P, P]
         lib.mbph_gather_conflicts.restype = I64
+        lib.mbph_fast_inside.argtypes = [P, I, P, P, P, I, I, I, D, D, I, I, P, P]
+        lib.mbph_fast_inside.restype = I64
         lib.mbph_tilt_band.restype = I64
         lib.mbph_tilt_gather.restype = I64
         lib.mbph_check_rays.restype = I64
@@ -172,6 +174,20 @@ def gather_conflicts(geom: dict, traj: dict, mode: int = 0):
                                         float(geom.get("dv", 1.0)), int(mode), ctypes.byref(viol),
                                         ctypes.byref(fast))
     return int(checked), int(viol.value), int(fast.value)
+
+
+def fast_inside(geom: dict, traj: dict, zchunk: int, mode: int = 0):
+    """(fast items, (item, z chunk) pairs the gather writes without clamping pair indices, rows
+    of those whose pair index leaves the chunk's range). mode 1: a planted mistake (the test
+    looks at the first row only)."""
+    lib = _load()
+    f, lo, hi, p, n = _common(geom, traj)
+    inside, viol = ctypes.c_longlong(0), ctypes.c_longlong(0)
+    fast = lib.mbph_fast_inside(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n),
+                                int(geom["views"]), int(geom.get("rows", 1)), int(geom["cols"]),
+                                float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)),
+                                int(zchunk), int(mode), ctypes.byref(inside), ctypes.byref(viol))
+    return int(fast), int(inside.value), int(viol.value)
 
 
 def project_chunked(geom: dict, traj: dict, vol: np.ndarray):

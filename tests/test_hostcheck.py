@@ -213,6 +213,37 @@ def test_gather_plain_lds_adds_never_collide(name, flip):
     assert (HC.gather_conflicts(geom, traj, mode=4)[1] > 0) == (name != "c3_cone256")
 
 
+def short_detector_config():
+    """The small anisotropic cone with 512 rows at 0.1 pitch (eight rows per lane, no padded
+    rows): every row's ray stays inside the volume's z range."""
+    from dataclasses import replace
+    return replace(SMALL_CONFIGS["c4_cone512_aniso"], name="c4s_short_detector", rows=512, dv=0.1,
+                   cols=40, views=12)
+
+
+@pytest.mark.parametrize("name,zchunk", [("short", None), ("short", 36), ("c3_cone256", None),
+                                         ("c5_helical_b4", None), ("c5_helical_b4", 7)])
+def test_fast_inside_items_need_no_clamp(name, zchunk):
+    """The gather writes a fast item's cell pairs without clamping their indices when
+    fast_inside accepts the item for the wave's z chunk. Replayed in the kernel's fixed point
+    over every row of every lane (padded rows too), the accepted items' pair indices stay in
+    the chunk's range [-2, n + 1], on whole columns and on ragged chunks. With a detector whose
+    rays stay inside the volume's z range, every item is accepted on whole columns and many on
+    a 36-cell chunk; on the twins whose rays (or padded rows) leave the volume, fewer or none
+    are. A test that looks at the first row only lets rows out of chunks."""
+    cfg = short_detector_config() if name == "short" else SMALL_CONFIGS[name]
+    geom, traj = _geom(cfg), config_trajectory(cfg)
+    D = int(cfg.shape[0])
+    fast, inside, viol = HC.fast_inside(geom, traj, zchunk or D)
+    assert fast > 1000 and viol == 0
+    if name == "short":
+        assert inside == fast if zchunk is None else inside > fast // 2
+    if name == "c5_helical_b4" and zchunk is None:
+        assert inside > 0
+    if zchunk is not None:
+        assert HC.fast_inside(geom, traj, zchunk, mode=1)[2] > 0
+
+
 def steep_cone_config():
     """A tall, narrow volume next to the source: rows cross several z cells inside one xy cell
     and leave through the bottom and top faces (the gather's general piece walk)."""
