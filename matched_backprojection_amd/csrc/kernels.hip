@@ -908,17 +908,19 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
         };
         auto drain = [&](int32_t count) {
             if (count == 0) return;
-            float w[KR][NB], wn[KR][NB];
-            gather_load_rows<NB, KR>(unit_rows(0, 0), w);
+            float wa[KR][NB], wb[KR][NB];
+            gather_load_rows<NB, KR>(unit_rows(0, 0), wa);
             int32_t i = 0, gi = 0;
-            for (;;) {
+            // One unit: the next unit's rows are loaded into nxt while cur is summed; false
+            // after the last unit.
+            auto unit = [&](const float (&cur)[KR][NB], float (&nxt)[KR][NB]) {
                 int32_t ni = i, ngi = gi + 1;
                 if (ngi == ngroups) {
                     ngi = 0;
                     ++ni;
                 }
                 const bool more = ni < count;
-                gather_load_rows<NB, KR>(unit_rows(more ? ni : i, more ? ngi : gi), wn);
+                gather_load_rows<NB, KR>(unit_rows(more ? ni : i, more ? ngi : gi), nxt);
                 const int32_t k0 = gi * 64 * S + lane_row;
                 const GatherItem it = Q[i];
                 const int32_t form = (int32_t)uniform((uint32_t)it.form);
@@ -931,30 +933,41 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                     const bool inside = kUnclamped && (form & kFastInside) != 0;
                     if ((form & ~kFastInside) == kFastPairs) {
                         if (S == KR && inside)
-                            gather_fast_group<NB, KR, true, false, false>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
+                            gather_fast_group<NB, KR, true, false, false>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
                         else if (S == KR)
-                            gather_fast_group<NB, KR, true, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
+                            gather_fast_group<NB, KR, true, false, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
                         else
-                            gather_fast_group<NB, KR, false, false, true>(it, a1, b1, dt, w, k0, S, z0, n, col, 1);
+                            gather_fast_group<NB, KR, false, false, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
                     } else {
                         const int32_t G = (int32_t)uniform((uint32_t)it.run);
                         if (S == KR && inside)
-                            gather_fast_group<NB, KR, true, true, false>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
+                            gather_fast_group<NB, KR, true, true, false>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
                         else if (S == KR)
-                            gather_fast_group<NB, KR, true, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
+                            gather_fast_group<NB, KR, true, true, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
                         else
-                            gather_fast_group<NB, KR, false, true, true>(it, a1, b1, dt, w, k0, S, z0, n, col, G);
+                            gather_fast_group<NB, KR, false, true, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
                     }
                 } else {
-                    gather_general_group<NB, KR>(it, form == kGeneralExclusive, w, k0, S, z0, z1, col);
+                    gather_general_group<NB, KR>(it, form == kGeneralExclusive, cur, k0, S, z0, z1, col);
                 }
-                if (!more) break;
-#pragma unroll
-                for (int c = 0; c < KR; ++c)
-#pragma unroll
-                    for (int m = 0; m < NB; ++m) w[c][m] = wn[c][m];
                 i = ni;
                 gi = ngi;
+                return more;
+            };
+            if constexpr (NB == 1 && KR > 1) {
+                // the buffers swap roles from unit to unit, so no rows are copied
+                while (unit(wa, wb) && unit(wb, wa)) {
+                }
+            } else {
+                // one copy of the unit's code and the prefetched rows moved over: with one row
+                // per lane the short units are sensitive to code size, and with several members
+                // two copies would not stay inlined
+                while (unit(wa, wb)) {
+#pragma unroll
+                    for (int c = 0; c < KR; ++c)
+#pragma unroll
+                        for (int m = 0; m < NB; ++m) wa[c][m] = wb[c][m];
+                }
             }
         };
 
