@@ -265,6 +265,18 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef __attribute__((address_space(3))) XYEvent lds_event;
+
+// The LDS address of a wave's run of events (a uniform address), copied once into a vector
+// register: the reads of a group of cells then take it with immediate offsets, where the
+// compiler would otherwise copy the scalar address into a vector register before each read.
+__device__ __forceinline__ const lds_event* events_in_vgpr(const XYEvent* e) {
+    const int32_t a = (int32_t)(uintptr_t)(const lds_event*)e;
+    int32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(a));
+    return (const lds_event*)(uintptr_t)(uint32_t)r;
+}
+
 // FLAT: the volume's bytes fit a 31-bit offset, so one buffer resource spans it and each
 // cell's column is reached through the load's scalar offset (one scalar multiply per cell);
 // otherwise each cell gets a resource based at its column.
@@ -356,10 +368,11 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                         uint32_t zoff[2 * kCellGroup];
                         float len[2 * kCellGroup];
                         uint32_t cell[kCellGroup];
+                        const lds_event* const Eg = events_in_vgpr(E + p);
 #pragma unroll
                         for (int q = 0; q < kCellGroup; ++q) {
-                            const double tb = E[p + q].tb;
-                            cell[q] = uniform((uint32_t)E[p + q].cxy);
+                            const double tb = Eg[q].tb;
+                            cell[q] = uniform((uint32_t)Eg[q].cxy);
                             int32_t z0, z1;
                             row_cell_two_inside(r, ta, tb, cz, kz, nz, z0, len[2 * q], z1, len[2 * q + 1]);
                             zoff[2 * q] = (uint32_t)z0 * (NB * sizeof(float));
