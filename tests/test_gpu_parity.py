@@ -188,6 +188,39 @@ def test_tall_detector_parity(torch_dev, mbp, oracle, flip):
 
 
 @pytest.mark.parametrize("flip", [False, True])
+def test_short_detector_parity(torch_dev, mbp, oracle, flip):
+    """Eight rows per lane with every ray inside the volume's z range (512 rows at 0.1 pitch):
+    every fast item keeps to the column (the host replay's fast_inside check accepts all of
+    them), so the gather writes their cell pairs without clamping, for one volume and
+    batches of two and four interleaved members, with detector rows running up or down."""
+    from tests.test_hostcheck import flipped, short_detector_config
+    torch, dev = torch_dev
+    cfg = short_detector_config()
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    if flip:
+        traj = flipped(traj)
+    rng = np.random.default_rng(37)
+    x = rng.random(cfg.shape).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    ys = rng.random((4,) + ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    plan = make_plan(mbp, cfg, traj=traj)
+    assert plan.info["path"] == "column"
+    say(f"case short detector flip={flip} forward")
+    p = plan.project(to_device_volume(torch, dev, x, cfg.layout)).cpu().numpy().astype(np.float64)
+    check(p, ref, "forward")
+    for B in (0, 2, 4):
+        say(f"case short detector flip={flip} adjoint B={B}")
+        yd = torch.from_numpy(ys[0] if B == 0 else ys[:B]).to(dev)
+        b = plan.backproject(yd).cpu().numpy().astype(np.float64)
+        if B == 0:
+            check(b, bref[0], "adjoint")
+        for m in range(B):
+            check(b[m], bref[m], f"adjoint member {m}")
+    plan.close()
+
+
+@pytest.mark.parametrize("flip", [False, True])
 def test_helical_runs_parity(torch_dev, mbp, oracle, flip):
     """The helical twin (one row per lane): its lanes share cell pairs in runs that the gather
     combines across the wave before writing, along the wave when the detector rows run up and
