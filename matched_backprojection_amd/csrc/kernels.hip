@@ -586,8 +586,9 @@ __host__ __device__ constexpr int32_t gather_column_floats(int32_t zchunk, int n
 // Cells are dealt in tiles of tx x ty (y fastest inside a tile): the tasks that run at the
 // same time on one XCD then cover a compact patch of the grid, whose shadow on the detector
 // is a few dozen columns in every view, so its waves share sinogram lines in L2 (a line of
-// cells along y would cover the whole detector width in views along x). The launcher picks
-// 16 x 32 when the grid is a whole number of such tiles, else 1 x H (plain y-fastest order).
+// cells along y would cover the whole detector width in views along x). Each launcher takes
+// the first of its tile shapes that the grid holds a whole number of, else 1 x H (plain
+// y-fastest order).
 __device__ __forceinline__ void gather_tile_cell(uint32_t xy, int32_t H, int32_t tx, int32_t ty,
                                                  int32_t& ix, int32_t& iy) {
     const uint32_t per = (uint32_t)(tx * ty);
@@ -1555,8 +1556,11 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     const int32_t zchunk = gather_zchunk(D, nb);
     const int32_t nchunks = (D + zchunk - 1) / zchunk;
     const uint64_t tasks = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)nchunks;
-    const bool tiled = a.box.n[0] % 16 == 0 && a.box.n[1] % 32 == 0;
-    const int32_t tx = tiled ? 16 : 1, ty = tiled ? 32 : a.box.n[1];
+    // tiles of 64 x 8 cells (measured against 16 x 32, 32 x 16, 32 x 32, 64 x 16 and 16 x 64:
+    // 2.5% faster than 16 x 32 on the 512^3 cone), else 16 x 32, else plain y-fastest order
+    const bool wide = a.box.n[0] % 64 == 0 && a.box.n[1] % 8 == 0;
+    const bool tiled = wide || (a.box.n[0] % 16 == 0 && a.box.n[1] % 32 == 0);
+    const int32_t tx = wide ? 64 : tiled ? 16 : 1, ty = wide ? 8 : tiled ? 32 : a.box.n[1];
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
