@@ -514,13 +514,38 @@ def test_segment_counts_match_oracle(torch_dev, mbp, oracle):
 # Full-size configurations: sampled rays and voxels, adjoint identity
 
 
+def _unit_columns(cfg, rng):
+    """(view, column) pairs whose whole detector column (every row) is compared: the forward
+    kernel's unit of work is 64 rows of one column of one view, so whole columns cover every
+    unit of them, ragged last unit included; first, middle and last columns of the first view,
+    a view a quarter turn on, and two random views with random columns."""
+    views = [0, cfg.views // 4 + 3] + [int(v) for v in rng.integers(0, cfg.views, 2)]
+    cols = [0, cfg.cols // 2, cfg.cols - 1]
+    pairs = [(v, j) for v in views[:2] for j in cols]
+    pairs += [(v, int(j)) for v in views[2:] for j in rng.integers(0, cfg.cols, 3)]
+    return pairs
+
+
 def _sample_rays(cfg, n, rng):
     per_view = cfg.rows * cfg.cols
     ids = [rng.integers(0, cfg.n_rays, n)]
     v = int(rng.integers(cfg.views))
     ids.append(v * per_view + (cfg.rows - 1) * cfg.cols + np.arange(0, cfg.cols, 7))   # last row
-    ids.append(v * per_view + np.arange(0, cfg.rows, 5) * cfg.cols)                   # first column
+    for view, col in _unit_columns(cfg, rng):                                          # columns
+        ids.append(view * per_view + np.arange(cfg.rows) * cfg.cols + col)
     return np.unique(np.concatenate(ids))
+
+
+def _unit_z_columns(cfg):
+    """(x, y) of the xy cells whose whole z column is compared: the gather's unit of work is
+    one z column, and its cells are dealt in 64 x 8 tiles (x by y) when the grid holds them,
+    else 16 x 32; the columns sit on the volume's faces and on both sides of the first tile
+    edges in x and y."""
+    D, H, W = cfg.shape
+    tx, ty = (64, 8) if W % 64 == 0 and H % 8 == 0 else (16, 32)
+    xs = sorted({0, min(tx - 1, W - 1), min(tx, W - 1), W - 1})
+    ys = sorted({0, min(ty - 1, H - 1), min(ty, H - 1), H - 1})
+    return [(x, y) for x in xs for y in ys]
 
 
 def _sample_voxels(cfg, n, rng):
@@ -528,6 +553,10 @@ def _sample_voxels(cfg, n, rng):
     shape = cfg.shape
     corners = np.array(np.meshgrid(*[[0, s - 1] for s in shape], indexing="ij")).reshape(len(shape), -1)
     ids.append(np.ravel_multi_index(corners, shape))
+    if len(shape) == 3:
+        D, H, W = shape
+        for x, y in _unit_z_columns(cfg):
+            ids.append((np.arange(D) * H + y) * W + x)
     return np.unique(np.concatenate(ids))
 
 
@@ -584,3 +613,131 @@ def test_full_size_parity(torch_dev, mbp, oracle, name):
     plan.close()
     del p_dev, b_dev, xd, yd
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------------------
+# Volumes of 2 GiB or more: the forward's buffer resource per cell
+
+
+def _whd_on_device(torch, dev, x):
+    """numpy (B?, D, H, W) in C order -> a device tensor of the same shape with z-fastest
+    strides (the transpose runs on the device: a host transpose of 2 GiB takes many seconds)."""
+    t = torch.from_numpy(x).to(dev)
+    perm = (2, 1, 0) if x.ndim == 3 else (0, 3, 2, 1)
+    return t.permute(perm).contiguous().permute(perm)
+
+
+def _check_rays(plan_out, cfg, geom, traj, x, ids, oracle, torch, dev, label):
+    ref = oracle.project_rays(geom, traj, x, ids)
+    B = x.shape[0] if x.ndim == 4 else 1
+    flat = plan_out.reshape(B, -1)[:, torch.from_numpy(ids).to(dev)].cpu().numpy().astype(np.float64)
+    for m in range(B):
+        check(flat[m], ref if x.ndim == 3 else ref[m], f"{label} member {m} ({ids.size} rays)")
+
+
+def test_interleaved_batch_over_2gib_forward_parity(torch_dev, mbp, oracle):
+    """The 512^3 cone with a batch of four: the interleaved pass holds 2 GiB, more than one
+    buffer resource's 31-bit offsets span, so the forward bases a resource at every cell's
+    column (the four-member variant). Sampled rays and whole detector columns of several
+    views against the oracle, for every member."""
+    torch, dev = torch_dev
+    cfg = CONFIGS["c4_cone512_aniso"]
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(71)
+    x = np.empty((4,) + cfg.shape, np.float32)
+    x[0] = config_phantom(cfg)
+    for m in range(1, 4):
+        x[m] = rng.random(cfg.shape, dtype=np.float32)
+    plan = make_plan(mbp, cfg)
+    assert plan.info["path"] == "column" and plan.info["members_per_pass"] == 4
+    assert 4 * cfg.n_voxels * 4 >= 2 ** 31
+    say("case c4 batch 4 (interleaved pass of 2 GiB) forward")
+    xd = _whd_on_device(torch, dev, x)
+    p = plan.project(xd)
+    torch.cuda.synchronize()
+    ids = _sample_rays(cfg, 2000, rng)
+    _check_rays(p, cfg, geom, traj, x, ids, oracle, torch, dev, "forward")
+    plan.close()
+    del xd, p
+    torch.cuda.empty_cache()
+
+
+def test_single_volume_over_2gib_parity(torch_dev, mbp, oracle):
+    """One 512 x 1024 x 1024 volume (2 GiB, z-fastest): the one-member forward with a buffer
+    resource per cell, and the gather writing a column of a volume beyond 2^31 bytes; the
+    detector (96 rows: a ragged second wave) covers the whole grid. Sampled rays and whole
+    detector columns, sampled voxels and whole z columns against the oracle, and the adjoint
+    identity over the whole arrays."""
+    from dataclasses import replace
+    torch, dev = torch_dev
+    cfg = replace(CONFIGS["c4_cone512_aniso"], name="cone_2gib", shape=(512, 1024, 1024),
+                  spacing=(1.0, 1.0, 1.0), sid=2000.0, sdd=3000.0, views=16, rows=96, cols=192,
+                  du=8.0, dv=8.0, layout="WHD", background=0.0)
+    assert cfg.n_voxels * 4 >= 2 ** 31
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(73)
+    say("case single 2 GiB volume: drawing the volume")
+    xw = rng.random(cfg.shape[::-1], dtype=np.float32)        # (W, H, D): z fastest
+    xd = torch.from_numpy(xw).to(dev).permute(2, 1, 0)          # (D, H, W) view, z-fastest strides
+    del xw
+    x = xd.contiguous().cpu().numpy()                           # C-order (D, H, W) for the oracle
+    plan = make_plan(mbp, cfg)
+    assert plan.info["path"] == "column"
+    say("case single 2 GiB volume forward")
+    p = plan.project(xd)
+    torch.cuda.synchronize()
+    ids = _sample_rays(cfg, 2000, rng)
+    _check_rays(p, cfg, geom, traj, x, ids, oracle, torch, dev, "forward")
+    say("case single 2 GiB volume adjoint")
+    y = rng.random((cfg.views, cfg.rows, cfg.cols), dtype=np.float32)
+    yd = torch.from_numpy(y).to(dev)
+    b = plan.backproject(yd)
+    torch.cuda.synchronize()
+    vids = _sample_voxels(cfg, 400, rng)
+    bref = oracle.backproject_voxels(geom, traj, y, vids)
+    g = b.permute(2, 1, 0).reshape(-1)          # the (W, H, D) storage, flat
+    D, H, W = cfg.shape
+    z, rem = np.divmod(vids, H * W)
+    yy, xx = np.divmod(rem, W)
+    store = (xx * H + yy) * D + z
+    gv = g[torch.from_numpy(store).to(dev)].cpu().numpy().astype(np.float64)
+    check(gv, bref, f"adjoint ({vids.size} sampled voxels)")
+    lhs = torch.dot(p.double().reshape(-1), yd.double().reshape(-1)).item()
+    rhs = torch.dot(xd.permute(2, 1, 0).double().reshape(-1), b.permute(2, 1, 0).double().reshape(-1)).item()
+    say(f"  adjoint identity {abs(lhs - rhs) / abs(lhs):.2e}")
+    assert abs(lhs - rhs) <= RTOL_ADJ * abs(lhs)
+    plan.close()
+    del xd, p, b, yd
+    torch.cuda.empty_cache()
+
+
+def test_segment_count_full_size_oblique_views(torch_dev, mbp, oracle):
+    """The metric's numerator at full size: the counting kernel over 24 oblique views of the
+    512^3 cone (every 30th view from view 7, at 3.5 + 15 k degrees) against the oracle's
+    exact count of positive-length segments on the same views.
+
+    Bound: the kernel counts segments longer than eps = 1e-6 of the smallest pitch, with
+    lengths formed from fp64 crossing distances (accurate to far below eps), so it can only
+    miss the oracle's pieces in (0, eps]: a plane crossing of one axis that falls within eps
+    of another axis' crossing. Crossings of axis a lie p_a / |c_a| apart along the ray
+    (c_a the direction component per unit of the walk's parameter; |c_x|, |c_y| <= 1, and
+    |c_z| < 0.2 with p_z = 1.5 here), so each crossing meets such a neighbour with probability
+    at most 2 eps (1/p_x + 1/p_y + |c_z|/p_z) < 4.3e-6; the count may fall short of the
+    oracle's by at most 1e-5 of it (over 2x that rate), and never exceed it."""
+    torch, dev = torch_dev
+    cfg = CONFIGS["c4_cone512_aniso"]
+    full = config_trajectory(cfg)
+    sel = 7 + 30 * np.arange(24)
+    traj = {k: (None if v is None else np.ascontiguousarray(v[sel])) for k, v in full.items()}
+    from dataclasses import replace
+    sub = replace(cfg, views=24)
+    geom = geom_of(sub)
+    say("case segment count, c4 at full size, 24 oblique views")
+    plan = make_plan(mbp, sub, traj=traj)
+    n = plan.segment_count()
+    _, cnt = oracle.project(geom, traj, np.zeros(sub.shape, np.float32), counts=True)
+    o = int(cnt.sum())
+    say(f"  gpu {n} oracle {o} short by {(o - n) / o:.2e}")
+    assert n <= o
+    assert o - n <= 1e-5 * o
+    plan.close()

@@ -223,3 +223,25 @@ def test_segment_counts_match_cell_steps(oracle):
         assert counts[r] == np.abs(cx - ce).sum() + 1
         checked += 1
     assert checked > 100
+
+
+@pytest.mark.parametrize("name", ["c3_cone256", "c4_cone512_aniso", "c5_helical_b4"])
+def test_voxel_adjoint_matches_scatter_adjoint_on_twins(oracle, name):
+    """The adjoint at chosen voxels (the chord definition, which the full-size GPU parity
+    tests use as their reference) equals the scatter adjoint at every voxel of the cone
+    twins. On these grids a voxel's pixel window (the detector box of its corner projections,
+    widened by one pixel) keeps a few dozen of the view's thousands of rays, so a window cut
+    too tight, or a corner left out of it, loses chords and fails here; the 3x4x5 grid above
+    keeps nearly every pixel and cannot show that."""
+    from workloads import SMALL_CONFIGS, config_trajectory
+    from oracle.oracle import geom_from_config
+    cfg = SMALL_CONFIGS[name]
+    geom, traj = geom_from_config(cfg), config_trajectory(cfg)
+    y = np.random.default_rng(61).random((cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    bp = oracle.backproject(geom, traj, y).ravel()
+    bv = oracle.backproject_voxels(geom, traj, y, np.arange(cfg.n_voxels))
+    scale = float(np.abs(bp).max())
+    assert scale > 0
+    err = float(np.abs(bv - bp).max()) / scale
+    print(f"{cfg.name}: max |voxel - scatter| / max = {err:.2e}")
+    assert err <= 1e-12

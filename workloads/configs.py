@@ -114,6 +114,25 @@ C5 = Config(
 
 CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
 
+# The workload of the pages' own timings (page "diffct 2.2.1 -> 2.4.0", README, multi-GPU
+# scaling table; the same shape on "diffct 2.1.0 -> 2.2.1" and "diffct 2.4.3 -> 2.4.4"): a
+# 512^3 circular cone beam, 360 views, a 1024 x 768 flat detector at pitch 1.25. The pages
+# state neither the source distances nor the phantom: SID 1000 and SDD 1500 are taken, with
+# c4's phantom recipe on an isotropic grid (own seed), the volume z-fastest. It is timed for
+# context next to the headline, and its sampled parity is checked like the five
+# configurations'.
+PAGES_CONE512 = Config(
+    name="pages_cone512_360v", beam="cone", trajectory="circular",
+    shape=(512, 512, 512), spacing=(1.0, 1.0, 1.0), views=360, rows=768, cols=1024,
+    du=1.25, dv=1.25, sid=1000.0, sdd=1500.0, layout="WHD", n_ellipsoids=20,
+    axis_range=(10.0, 100.0), phantom_seeds=(6,), background=0.05,
+    description=("circular cone beam, 512^3 stored (W,H,D)-contiguous, spacing 1, SID 1000, "
+                 "SDD 1500 (taken: the pages do not state them), 360 views, 1024 cols x 768 rows, "
+                 "pitch 1.25"),
+)
+
+CONTEXT_CONFIGS = {PAGES_CONE512.name: PAGES_CONE512}
+
 # Reduced twins: same beam/trajectory/layout/batch, small enough for a full fp64 oracle run.
 SMALL_CONFIGS = {
     "c1_parallel2d": C1,
