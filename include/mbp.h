@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 1
+#define MBP_ABI_VERSION 2
 
 typedef enum mbp_status {
     MBP_OK = 0,
@@ -120,6 +120,13 @@ typedef struct mbp_plan_info {
     int64_t rays;              /* views * rows * cols                                       */
     int64_t voxels;            /* D * H * W                                                 */
     int64_t members_per_pass;  /* batch members one walk serves (volume interleave)         */
+    /* What the last mbp_backproject of this plan ran (all 0 before the first call with B > 0): */
+    int32_t last_adjoint;      /* MBP_ADJOINT_GATHER or MBP_ADJOINT_SCATTER (global atomics)   */
+    int32_t last_adjoint_walk; /* MBP_PATH_COLUMN (rows share their column's xy line) or
+                                  MBP_PATH_GENERIC (each ray on its own: the per-row gather,
+                                  or the generic walk's atomics)                              */
+    int64_t last_adjoint_views_per_launch;  /* views per adjoint launch: below
+                                  views_per_launch when the gather's workspace held fewer  */
 } mbp_plan_info;
 
 /* Validate the geometry and trajectory and build a plan. Trajectory arrays are host fp64,
@@ -148,7 +155,9 @@ int mbp_plan_set_adjoint(mbp_plan* plan, int32_t kind);
 
 /* Limit the views of one kernel launch (0 = automatic: as many as index and grid limits
    allow). Results do not depend on it (page "diffct 2.1.0 -> 2.2.1", CHANGELOG 2.2.0,
-   "Changed": backprojection accumulators span all contributing view batches). */
+   "Changed": backprojection accumulators span all contributing view batches). The gather
+   adjoint's workspace holds the reordered sinogram of one launch, so a smaller batch also
+   shrinks mbp_workspace_size. */
 int mbp_plan_set_view_batch(mbp_plan* plan, int64_t views_per_launch);
 
 /* Forward projection of `batch` volumes (caller's layout) into `sinogram` [batch][views]
@@ -158,8 +167,12 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
 
 /* Matched backprojection: volume = sum over rays of len * sinogram (accumulate = 0), or
    volume += that sum (accumulate = 1), in the caller's layout, for `batch` members. The
-   segments are exactly those of mbp_project. Floating-point atomics make the summation
-   order, and so the last bits, vary from run to run. */
+   segments are exactly those of mbp_project. The gather adjoint runs in view batches sized to
+   its workspace (all views in one launch when the memory rule or the caller's workspace
+   allows, else as many as fit, each launch adding into the previous ones); only when not even
+   one view's share fits does the call take the generic walk's atomics, and mbp_plan_get_info
+   then says so. The scatter adjoints' floating-point atomics make the summation order, and
+   so the last bits, vary from run to run. */
 int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
                     int32_t accumulate, void* stream);
 
@@ -169,14 +182,18 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
    metric. Runs a counting kernel on `stream`, then waits. */
 int mbp_segment_count(mbp_plan* plan, int64_t* count, void* stream);
 
-/* Device workspace the plan needs for `batch` members on the column walk: a z-fastest copy of
-   up to four interleaved volumes (not needed for one z-fastest volume) plus, for the gather
-   adjoint, a reordered copy of their sinograms. 0 when none is needed. */
+/* Device workspace the plan needs for `batch` members on the column walk, or for the gather:
+   a z-fastest copy of up to four interleaved volumes (not needed for one z-fastest volume)
+   plus, for the gather adjoint, a reordered copy of their sinograms over the views of one
+   launch (views_per_launch; see mbp_plan_set_view_batch). 0 when none is needed. A smaller
+   workspace serves the gather as long as it holds the volume part and one view's share: the
+   gather then takes as many views per launch as fit. */
 int mbp_workspace_size(const mbp_plan* plan, int64_t batch, size_t* bytes);
 
 /* Hand the plan a caller-owned device workspace (NULL, 0 = let the library allocate its
    own on first use). The caller keeps ownership and must keep it alive while work that uses
-   it is enqueued. A call that needs more than `bytes` returns MBP_ENOMEM. */
+   it is enqueued. A call whose least need (the volume part, plus one view's share for the
+   gather) exceeds `bytes` returns MBP_ENOMEM. */
 int mbp_set_workspace(mbp_plan* plan, void* device_ptr, size_t bytes);
 
 /* Convert `batch` volumes between MBP_LAYOUT_DHW and MBP_LAYOUT_WHD (to_whd = 1: DHW ->
@@ -215,6 +232,12 @@ int mbp_cgls_workspace_size(const mbp_plan* plan, int64_t batch, int32_t iters, 
 int mbp_cgls(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume, int32_t iters,
              double rtol, void* workspace, size_t workspace_bytes, double* residual_norms,
              void* stream);
+
+/* Copy n floats from `in` to `out` (device pointers, 16-byte aligned, not overlapping) with a
+   streaming kernel: 16-byte loads and stores over a fixed grid. It is the
+   bandwidth reference of the measurements (the HBM rate a plain copy reaches on this GPU) and
+   the kernel of known traffic that hardware byte counters are calibrated with. */
+int mbp_stream_copy(const float* in, float* out, int64_t n, void* stream);
 
 const char* mbp_status_string(int status);
 const char* mbp_last_error(void);

@@ -22,8 +22,8 @@ import numpy as np
 from . import _capi
 from ._capi import MbpError, MbpValueError
 
-__all__ = ["Plan", "project", "backproject", "convert_layout", "MbpError", "MbpValueError",
-           "library_path"]
+__all__ = ["Plan", "project", "backproject", "convert_layout", "stream_copy", "MbpError",
+           "MbpValueError", "library_path"]
 
 library_path = _capi.LIB_PATH
 
@@ -129,7 +129,10 @@ class Plan:
         _capi.check(self._lib.mbp_plan_get_info(self._handle, ctypes.byref(inf)), "mbp_plan_get_info")
         return {"path": _capi.PATH_NAMES[inf.path], "column_capable": bool(inf.column_capable),
                 "views_per_launch": inf.views_per_launch, "launches": inf.launches,
-                "rays": inf.rays, "voxels": inf.voxels, "members_per_pass": inf.members_per_pass}
+                "rays": inf.rays, "voxels": inf.voxels, "members_per_pass": inf.members_per_pass,
+                "last_adjoint": _capi.ADJOINT_NAMES[inf.last_adjoint],
+                "last_adjoint_walk": _capi.PATH_NAMES[inf.last_adjoint_walk] if inf.last_adjoint else None,
+                "last_adjoint_views_per_launch": inf.last_adjoint_views_per_launch}
 
     def set_path(self, path: str) -> None:
         _capi.check(self._lib.mbp_plan_set_path(self._handle, _capi.PATHS[path]), "mbp_plan_set_path")
@@ -358,3 +361,19 @@ def convert_layout(volume, to_whd: bool):
                                            int(bool(to_whd)), ctypes.c_void_p(out.data_ptr()),
                                            ctypes.c_void_p(stream)), "mbp_convert_layout")
     return out
+
+
+def stream_copy(src, dst) -> None:
+    """``dst[:] = src`` for contiguous float32 device tensors of the same size, with the
+    library's streaming copy kernel (the bandwidth reference of the measurements)."""
+    torch = _torch()
+    for t in (src, dst):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("src and dst must be contiguous float32 tensors on a HIP device")
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst must have the same number of elements")
+    lib = _capi.load()
+    with torch.cuda.device(src.device):
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+        _capi.check(lib.mbp_stream_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                        src.numel(), ctypes.c_void_p(stream)), "mbp_stream_copy")

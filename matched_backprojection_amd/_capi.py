@@ -26,6 +26,7 @@ LAYOUTS = {"DHW": 0, "WHD": 1}
 PATHS = {"auto": 0, "generic": 1, "column": 2}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 ADJOINTS = {"auto": 0, "gather": 1, "scatter": 2}
+ADJOINT_NAMES = {0: None, 1: "gather", 2: "scatter"}
 
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = (
@@ -33,7 +34,7 @@ EXPORTS = (
     "mbp_plan_set_view_batch", "mbp_plan_set_adjoint", "mbp_project", "mbp_backproject", "mbp_segment_count",
     "mbp_workspace_size", "mbp_set_workspace", "mbp_convert_layout", "mbp_normal",
     "mbp_cgls_workspace_size", "mbp_cgls", "mbp_status_string", "mbp_last_error",
-    "mbp_abi_version",
+    "mbp_abi_version", "mbp_stream_copy",
 )
 
 
@@ -53,6 +54,8 @@ class PlanInfo(ctypes.Structure):
         ("views_per_launch", ctypes.c_int64), ("launches", ctypes.c_int64),
         ("rays", ctypes.c_int64), ("voxels", ctypes.c_int64),
         ("members_per_pass", ctypes.c_int64),
+        ("last_adjoint", ctypes.c_int32), ("last_adjoint_walk", ctypes.c_int32),
+        ("last_adjoint_views_per_launch", ctypes.c_int64),
     ]
 
 
@@ -99,6 +102,7 @@ def load():
     lib.mbp_cgls_workspace_size.argtypes = [P, I64, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.mbp_cgls.argtypes = [P, P, I64, P, I32, ctypes.c_double, P, ctypes.c_size_t,
                              ctypes.POINTER(ctypes.c_double), P]
+    lib.mbp_stream_copy.argtypes = [P, P, I64, P]
     lib.mbp_status_string.argtypes = [ctypes.c_int]
     lib.mbp_status_string.restype = ctypes.c_char_p
     lib.mbp_last_error.argtypes = []

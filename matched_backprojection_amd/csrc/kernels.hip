@@ -544,7 +544,7 @@ __global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A,
                 len = sqrt(dx * dx + dy * dy + dz * dz);
             }
             const float scale = (float)len;
-            const int64_t o = (((int64_t)view * A.cols + j) * rows_pad + k) * NB;
+            const int64_t o = (((int64_t)blockIdx.z * A.cols + j) * rows_pad + k) * NB;
 #pragma unroll
             for (int m = 0; m < NB; ++m) ysc[o + m] = tile[m][tx][ty + 8 * i] * scale;
         }
@@ -555,7 +555,7 @@ __global__ void __launch_bounds__(256) column_line_kernel(const ColumnLaunch A, 
                                                           ColLine* __restrict__ out) {
     const int64_t n = (int64_t)views * A.cols;
     for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const int32_t view = (int32_t)(i / A.cols), j = (int32_t)(i % A.cols);
+        const int32_t view = A.view0 + (int32_t)(i / A.cols), j = (int32_t)(i % A.cols);
         column_line(A.frames[view], A.box, A.beam, j, A.cols, A.rows, A.du, A.dv, out[i]);
     }
 }
@@ -1005,7 +1005,7 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                 GatherItem it;
                 bool hit = false;
                 if (jn <= j1) {
-                    const int32_t yoff = view * A.cols + jn;
+                    const int32_t yoff = (view - A.view0) * A.cols + jn;
                     hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff, it,
                                       in_lo, in_hi);
                     jn += kViewLanes;
@@ -1156,7 +1156,7 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
 #pragma unroll
             for (int m = 0; m < NB; ++m) w[m] = 0.0f;
             if (lane < nrows) {
-                const float* yp = ysc + (((int64_t)view * A.cols + j) * rows_pad + k0 + lane) * NB;
+                const float* yp = ysc + (((int64_t)(view - A.view0) * A.cols + j) * rows_pad + k0 + lane) * NB;
 #pragma unroll
                 for (int m = 0; m < NB; ++m) w[m] = yp[m];
             }
@@ -1407,6 +1407,21 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* __restrict__ p, i
         p[i] = 0.0f;
 }
 
+// Streaming copy, the bandwidth reference of the measurements and the kernel of known traffic
+// that the byte counters are calibrated with: plain 16-byte loads and stores, the same kind of
+// access as the walks' loads (nontemporal ones were no faster), grid-stride over a fixed grid
+// (1024 blocks of 256 threads was the fastest of the grids tried on MI355X, 2 GiB copies),
+// then the tail of fewer than 4 floats.
+__global__ void __launch_bounds__(256) stream_copy_kernel(const float* __restrict__ in,
+                                                          float* __restrict__ out, int64_t n) {
+    const int64_t n4 = n >> 2;
+    const float4* const in4 = reinterpret_cast<const float4*>(in);
+    float4* const out4 = reinterpret_cast<float4*>(out);
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) out4[i] = in4[i];
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) out[4 * n4 + threadIdx.x] = in[4 * n4 + threadIdx.x];
+}
+
 constexpr int32_t kMaxGridYZ = 65535;
 
 template <int NB>
@@ -1527,10 +1542,11 @@ hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const
         b.view0 = a.view0 + v0;
         b.nviews = a.nviews - v0 < 65535 ? a.nviews - v0 : 65535;
         const dim3 grid((a.cols + 31) / 32, (rows_pad + 31) / 32, b.nviews);
+        float* const out = ysc + (int64_t)v0 * a.cols * rows_pad * nb;
         switch (nb) {
-            case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, ysc); break;
-            case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, ysc); break;
-            case 4: sino_prepass_kernel<4><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, ysc); break;
+            case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
+            case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
+            case 4: sino_prepass_kernel<4><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
             default: return hipErrorInvalidValue;
         }
     }
@@ -1622,6 +1638,13 @@ hipError_t launch_convert(const float* in, int32_t D, int32_t H, int32_t W, int 
                           hipStream_t s) {
     if (to_whd) return to_native_nb<1>(in, 0, D, H, W, 0, out, s);
     return from_native_nb<1>(in, D, H, W, 0, out, 0, 0, s);
+}
+
+hipError_t launch_stream_copy(const float* in, float* out, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t want = (n / 4 + 255) / 256;
+    stream_copy_kernel<<<dim3((unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024)), dim3(256), 0, s>>>(in, out, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {

@@ -50,11 +50,12 @@ hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* con
                                  float* vol, hipStream_t s);
 
 // Matched adjoint of the column geometry without global atomics: a pre-pass copies the
-// sinogram to [view][col][row] order (nb members interleaved innermost) scaled by each ray's
-// length per unit of its parameter, rows zero-padded to gather_rows_padded(rows); the gather
-// then writes every voxel of the z-fastest interleaved volume once (optionally adding into
-// it). ysc holds nb * views * cols * gather_rows_padded(rows) floats; the launch covers
-// views [view0, view0 + nviews).
+// sinogram of the launch's views [view0, view0 + nviews) to [view - view0][col][row] order
+// (nb members interleaved innermost) scaled by each ray's length per unit of its parameter,
+// rows zero-padded to gather_rows_padded(rows), into ysc (gather_sino_floats(nviews, ...)
+// floats); the gather then writes every voxel of the z-fastest interleaved volume once
+// (optionally adding into it), reading the line constants of view view0 + i at lines[i * cols
+// + column].
 hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const* sino, float* ysc,
                                hipStream_t s);
 hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* lines, const float* ysc,
@@ -64,8 +65,8 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
 // its own.
 hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol, int accumulate,
                               hipStream_t s);
-// Per-(view, column) line constants of the gather, for views [0, views) (lines holds
-// views * cols entries); computed once per plan and device.
+// Per-(view, column) line constants of the gather, for views [a.view0, a.view0 + views)
+// (lines holds views * cols entries).
 hipError_t launch_column_lines(const ColumnLaunch& a, int32_t views, ColLine* lines, hipStream_t s);
 
 // Positive-length segments walked by the launch's rays; adds into *count (device, zeroed by
@@ -85,6 +86,7 @@ hipError_t launch_from_native(const float* ws, int nb, int32_t D, int32_t H, int
 hipError_t launch_convert(const float* in, int32_t D, int32_t H, int32_t W, int to_whd,
                           float* out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_stream_copy(const float* in, float* out, int64_t n, hipStream_t s);
 
 // Record the calling thread's error message (mbp_last_error) and return `code`.
 int set_error(int code, const char* fmt, ...);

@@ -97,6 +97,10 @@ struct mbp_plan {
     void* user_ws = nullptr;
     size_t user_ws_bytes = 0;
     std::vector<DeviceState> devs;
+    // what the last backprojection ran (reported by mbp_plan_get_info)
+    int32_t last_adjoint = MBP_ADJOINT_AUTO;
+    int32_t last_walk = MBP_PATH_AUTO;
+    int64_t last_views = 0;
     std::mutex mu;
 };
 
@@ -287,23 +291,35 @@ int interleave_for(const mbp_plan* p, int64_t remaining) {
     return nb;
 }
 
-// Make sure a workspace of `need` bytes exists; returns it or nullptr (rc set). `fits`
-// reports whether the memory rule allows it (a quarter of free device memory).
-float* get_workspace(mbp_plan* p, DeviceState* d, size_t need, bool* fits, int* rc) {
+// A workspace of at least `least` bytes, as close to `want` as the memory rule allows; its size
+// in *got. A caller workspace is used whole when it holds `least` (else MBP_ENOMEM). The
+// library's own grows on demand: free device memory is queried only then, and one call uses at
+// most a quarter of it ("diffct 2.4.3 -> 2.4.4", CHANGELOG 2.4.4). Returns nullptr with rc
+// MBP_OK when not even `least` bytes fit that rule.
+float* get_workspace(mbp_plan* p, DeviceState* d, size_t want, size_t least, size_t* got, int* rc) {
     *rc = MBP_OK;
-    *fits = true;
+    *got = 0;
     if (p->user_ws) {
-        if (p->user_ws_bytes < need) {
-            *rc = fail(MBP_ENOMEM, "caller workspace holds %zu bytes, the call needs %zu", p->user_ws_bytes, need);
+        if (p->user_ws_bytes < least) {
+            *rc = fail(MBP_ENOMEM, "caller workspace holds %zu bytes, the call needs at least %zu", p->user_ws_bytes, least);
             return nullptr;
         }
+        *got = p->user_ws_bytes;
         return static_cast<float*>(p->user_ws);
     }
-    if (d->ws_bytes >= need) return d->ws;
+    if (d->ws_bytes >= want) {
+        *got = d->ws_bytes;
+        return d->ws;
+    }
     size_t free_b = 0, total_b = 0;
     hipError_t e = hipMemGetInfo(&free_b, &total_b);
     if (e != hipSuccess) { *rc = hip_fail(e, "hipMemGetInfo"); return nullptr; }
-    if (need > (free_b + d->ws_bytes) / 4) { *fits = false; return nullptr; }
+    const size_t target = std::min(want, (free_b + d->ws_bytes) / 4);
+    if (target < least) return nullptr;
+    if (d->ws_bytes >= target) {
+        *got = d->ws_bytes;
+        return d->ws;
+    }
     if (d->ws) {
         e = hipDeviceSynchronize();
         if (e != hipSuccess) { *rc = hip_fail(e, "hipDeviceSynchronize"); return nullptr; }
@@ -311,9 +327,10 @@ float* get_workspace(mbp_plan* p, DeviceState* d, size_t need, bool* fits, int* 
         d->ws = nullptr;
         d->ws_bytes = 0;
     }
-    e = hipMalloc(reinterpret_cast<void**>(&d->ws), need);
+    e = hipMalloc(reinterpret_cast<void**>(&d->ws), target);
     if (e != hipSuccess) { *rc = hip_fail(e, "hipMalloc(workspace)"); return nullptr; }
-    d->ws_bytes = need;
+    d->ws_bytes = target;
+    *got = target;
     return d->ws;
 }
 
@@ -329,14 +346,23 @@ bool tilt_gather(const mbp_plan* p) {
 }
 
 // Workspace of one column-walk pass over nb members: the interleaved z-fastest volume (not
-// needed when the caller's own z-fastest buffer is used directly) and, for the gather
-// adjoint, the reordered sinogram.
-size_t column_ws_bytes(const mbp_plan* p, int nb, bool direct, bool gather) {
+// needed when the caller's own z-fastest buffer is used directly) and, for the gather adjoint,
+// the reordered sinogram of one launch of `views` views.
+size_t column_ws_bytes(const mbp_plan* p, int nb, bool direct, bool gather, int64_t views) {
     const mbp_geometry& g = p->g;
     size_t n = 0;
     if (!direct) n += (size_t)nb * (size_t)(g.D * g.H * g.W);
-    if (gather) n += (size_t)mbp::gather_sino_floats((int32_t)g.views, (int32_t)g.cols, (int32_t)g.rows, nb);
+    if (gather) n += (size_t)mbp::gather_sino_floats((int32_t)views, (int32_t)g.cols, (int32_t)g.rows, nb);
     return n * sizeof(float);
+}
+
+// Views per gather launch whose reordered sinogram fits `bytes` of workspace next to the
+// volume part (at most vmax; 0 when not even one view fits).
+int64_t gather_views_fit(const mbp_plan* p, int nb, bool direct, size_t bytes, int64_t vmax) {
+    const size_t fixed = column_ws_bytes(p, nb, direct, true, 0);
+    const size_t per_view = column_ws_bytes(p, nb, direct, true, 1) - fixed;
+    if (bytes < fixed + per_view) return 0;
+    return std::min<int64_t>(vmax, (int64_t)((bytes - fixed) / per_view));
 }
 
 int check_call(const mbp_plan* p, const void* a, const void* b, int64_t batch) {
@@ -531,6 +557,9 @@ int mbp_plan_get_info(const mbp_plan* plan, mbp_plan_info* info) {
     info->members_per_pass = 1;
     if (info->path == MBP_PATH_COLUMN) info->members_per_pass = interleave_for(plan, 4);
     else info->members_per_pass = 4;
+    info->last_adjoint = plan->last_adjoint;
+    info->last_adjoint_walk = plan->last_walk;
+    info->last_adjoint_views_per_launch = plan->last_views;
     return MBP_OK;
 }
 
@@ -559,7 +588,8 @@ int mbp_workspace_size(const mbp_plan* plan, int64_t batch, size_t* bytes) {
     if (batch == 0 || (active_path(plan) != MBP_PATH_COLUMN && !tilt)) return MBP_OK;
     const bool direct = plan->g.layout == MBP_LAYOUT_WHD && batch == 1;
     const int nb = direct ? 1 : interleave_for(plan, batch);
-    *bytes = column_ws_bytes(plan, nb, direct, tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER);
+    *bytes = column_ws_bytes(plan, nb, direct, tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER,
+                             views_per_launch(plan));
     return MBP_OK;
 }
 
@@ -601,15 +631,16 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
                 break;
             }
             int nb = interleave_for(plan, batch - m0);
-            bool fits = false;
             float* ws = nullptr;
             for (;;) {
-                ws = get_workspace(plan, d, column_ws_bytes(plan, nb, false, false), &fits, &rc);
+                const size_t need = column_ws_bytes(plan, nb, false, false, 0);
+                size_t got = 0;
+                ws = get_workspace(plan, d, need, need, &got, &rc);
                 if (rc != MBP_OK) return rc;
-                if (fits || nb == 1) break;
+                if (ws || nb == 1) break;
                 nb /= 2;
             }
-            if (!fits) break;   // not even one member fits: generic walk for the rest
+            if (!ws) break;   // not even one member fits: generic walk for the rest
             hipError_t e = mbp::launch_to_native(volume + m0 * vox, vox, nb, (int32_t)g.D, (int32_t)g.H,
                                                  (int32_t)g.W, whd ? 1 : 0, ws, s);
             if (e != hipSuccess) return hip_fail(e, "layout conversion launch");
@@ -642,23 +673,31 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
     const int64_t vox = g.D * g.H * g.W, rays = g.views * g.rows * g.cols;
     int64_t m0 = 0;
     const bool tilt = tilt_gather(plan);
+    plan->last_adjoint = MBP_ADJOINT_SCATTER;
+    plan->last_walk = MBP_PATH_GENERIC;
+    plan->last_views = views_per_launch(plan);
     if (active_path(plan) == MBP_PATH_COLUMN || tilt) {
         const bool whd = g.layout == MBP_LAYOUT_WHD;
         const bool direct = whd && batch == 1;
-        bool gather = tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER;
+        const bool gather = tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER;
+        const int64_t vmax = views_per_launch(plan);
         while (m0 < batch) {
             int nb = direct ? 1 : interleave_for(plan, batch - m0);
-            bool fits = false;
             float* ws = nullptr;
+            size_t got = 0;
             for (;;) {
-                ws = get_workspace(plan, d, column_ws_bytes(plan, nb, direct, gather), &fits, &rc);
+                // all views in one gather launch if the memory rule allows, else as many as fit
+                ws = get_workspace(plan, d, column_ws_bytes(plan, nb, direct, gather, vmax),
+                                   column_ws_bytes(plan, nb, direct, gather, 1), &got, &rc);
                 if (rc != MBP_OK) return rc;
-                if (fits) break;
-                if (nb > 1) { nb /= 2; continue; }
-                if (gather && !tilt) { gather = false; continue; }   // no room for the sinogram copy
-                break;
+                if (ws || nb == 1) break;
+                nb /= 2;
             }
-            if (!fits) break;   // the workspace does not fit: generic walk for the rest
+            if (!ws) break;   // not even one member and one view fit: generic walk for the rest
+            const int64_t vb = gather ? gather_views_fit(plan, nb, direct, got, vmax) : vmax;
+            plan->last_adjoint = gather ? MBP_ADJOINT_GATHER : MBP_ADJOINT_SCATTER;
+            plan->last_walk = tilt ? MBP_PATH_GENERIC : MBP_PATH_COLUMN;
+            plan->last_views = vb;
             float* target = direct ? volume : ws;
             float* ysc = direct ? ws : ws + (size_t)nb * (size_t)vox;
             const int acc_target = direct ? accumulate : 0;
@@ -674,12 +713,14 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
                 e = hipMalloc(reinterpret_cast<void**>(&d->lines), bytes);
                 if (e != hipSuccess) { d->lines = nullptr; return hip_fail(e, "hipMalloc(column lines)"); }
                 mbp::ColumnLaunch a = column_args(plan, d);
+                a.view0 = 0;
                 e = mbp::launch_column_lines(a, (int32_t)g.views, d->lines, s);
                 if (e != hipSuccess) return hip_fail(e, "column line launch");
             }
             if (gather) {
+                // one pre-pass and one gather per view batch; every launch after the first adds
+                // into the volume (accumulators span all view batches)
                 mbp::ColumnLaunch a = column_args(plan, d);
-                const int64_t vb = views_per_launch(plan);
                 for (int64_t v0 = 0; v0 < g.views; v0 += vb) {
                     a.view0 = (int32_t)v0;
                     a.nviews = (int32_t)std::min(vb, g.views - v0);
@@ -687,7 +728,8 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
                     if (e != hipSuccess) return hip_fail(e, "sinogram pre-pass launch");
                     const int acc = v0 == 0 ? acc_target : 1;
                     e = tilt ? mbp::launch_tilt_gather(a, nb, ysc, target, acc, s)
-                             : mbp::launch_column_gather(a, nb, d->lines, ysc, target, acc, s);
+                             : mbp::launch_column_gather(a, nb, d->lines + (size_t)v0 * (size_t)g.cols, ysc,
+                                                         target, acc, s);
                     if (e != hipSuccess) return hip_fail(e, tilt ? "tilt gather launch" : "column gather launch");
                 }
             } else {
@@ -701,6 +743,11 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
             }
             m0 += nb;
         }
+    }
+    if (m0 < batch) {
+        plan->last_adjoint = MBP_ADJOINT_SCATTER;
+        plan->last_walk = MBP_PATH_GENERIC;
+        plan->last_views = views_per_launch(plan);
     }
     if (m0 < batch && !accumulate) {
         hipError_t e = mbp::launch_fill_zero(volume + m0 * vox, (batch - m0) * vox, s);
@@ -753,6 +800,20 @@ int mbp_segment_count(mbp_plan* plan, int64_t* count, void* stream) {
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     *count = (int64_t)host;
+    return MBP_OK;
+}
+
+int mbp_stream_copy(const float* in, float* out, int64_t n, void* stream) {
+    if (n < 0) return fail(MBP_EINVAL, "n must be >= 0");
+    if (n == 0) return MBP_OK;
+    if (!in || !out) return fail(MBP_EINVAL, "in and out must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(in) & 15u) || (reinterpret_cast<uintptr_t>(out) & 15u))
+        return fail(MBP_EINVAL, "in and out must be 16-byte aligned");
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(in), a1 = a0 + (uintptr_t)n * 4;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(out), b1 = b0 + (uintptr_t)n * 4;
+    if (a0 < b1 && b0 < a1) return fail(MBP_EINVAL, "in and out must not overlap");
+    hipError_t e = mbp::launch_stream_copy(in, out, n, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "stream copy launch");
     return MBP_OK;
 }
 

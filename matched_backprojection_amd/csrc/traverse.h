@@ -721,7 +721,8 @@ struct GatherItem {
     union { double zb0; int64_t fb0; };
     union { double zb1; int64_t fb1; };
     float dt;           // parameter length of the crossing
-    int32_t yoff;       // view * cols + column: the line of the reordered sinogram
+    int32_t yoff;       // (view - first view of the launch) * cols + column: the line of the
+                        // reordered sinogram and of the line table
     int32_t a1fx;       // fast form: za1 in fixed point
     int32_t b1fx;       // fast form: zb1 in fixed point
     int32_t form;       // kFastPairs, kFastRuns, kGeneralExclusive or kGeneralAtomic

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared) == set(_capi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.mbp_abi_version() == 1
+    assert lib.mbp_abi_version() == 2
     assert lib.mbp_status_string(_capi.MBP_ERANGE) == b"geometry out of range"
 
 
@@ -101,10 +101,16 @@ def test_configs_plan_and_pick_walks(lib, name):
         direct = cfg.layout == "WHD" and cfg.members == 1
         sino = gather_sino_floats(cfg)
         assert ws.value == 4 * nb * ((0 if direct else cfg.n_voxels) + sino)
-    # view batching: a ragged split into launches of 7 views
+    # nothing has been backprojected yet
+    assert inf.last_adjoint == 0 and inf.last_adjoint_walk == 0 and inf.last_adjoint_views_per_launch == 0
+    # view batching: a ragged split into launches of 7 views; the gather's reordered sinogram
+    # then covers the views of one launch
     assert lib.mbp_plan_set_view_batch(h, 7) == 0
     inf = _info(lib, h)
     assert inf.views_per_launch == 7 and inf.launches == -(-cfg.views // 7)
+    assert lib.mbp_workspace_size(h, cfg.members, ctypes.byref(ws)) == 0
+    if cfg.beam == "cone":
+        assert ws.value == 4 * nb * ((0 if direct else cfg.n_voxels) + 7 * cfg.cols * rows_padded(cfg.rows) + 8)
     assert lib.mbp_plan_set_view_batch(h, -1) == _capi.MBP_EINVAL
     # forcing walks
     assert lib.mbp_plan_set_path(h, 1) == 0 and _info(lib, h).path == 1
@@ -161,6 +167,14 @@ def test_batch_zero_and_bad_calls_do_no_device_work(lib):
     assert lib.mbp_set_workspace(h, None, 0) == 0
     lib.mbp_plan_destroy(h)
     lib.mbp_plan_destroy(None)
+    # the streaming copy: nothing to do for n = 0, bad arguments rejected before any launch
+    assert lib.mbp_stream_copy(None, None, 0, None) == 0
+    assert lib.mbp_stream_copy(None, ctypes.c_void_p(64), 4, None) == _capi.MBP_EINVAL
+    assert lib.mbp_stream_copy(ctypes.c_void_p(64), ctypes.c_void_p(128), -1, None) == _capi.MBP_EINVAL
+    assert lib.mbp_stream_copy(ctypes.c_void_p(68), ctypes.c_void_p(256), 4, None) == _capi.MBP_EINVAL
+    assert b"aligned" in lib.mbp_last_error()
+    assert lib.mbp_stream_copy(ctypes.c_void_p(64), ctypes.c_void_p(96), 16, None) == _capi.MBP_EINVAL
+    assert b"overlap" in lib.mbp_last_error()
 
 
 def _bad(lib, mutate_geom=None, mutate_traj=None, cfg=None):

@@ -17,6 +17,7 @@ import pytest
 
 from workloads import (CONFIGS, SMALL_CONFIGS, add_noise, config_phantom, config_trajectory,
                        random_cone_trajectory, sinogram_field)
+from workloads.configs import CONTEXT_CONFIGS
 
 pytestmark = pytest.mark.gpu
 
@@ -560,10 +561,10 @@ def _sample_voxels(cfg, n, rng):
     return np.unique(np.concatenate(ids))
 
 
-@pytest.mark.parametrize("name", list(CONFIGS))
+@pytest.mark.parametrize("name", list(CONFIGS) + list(CONTEXT_CONFIGS))
 def test_full_size_parity(torch_dev, mbp, oracle, name):
     torch, dev = torch_dev
-    cfg = CONFIGS[name]
+    cfg = CONFIGS.get(name) or CONTEXT_CONFIGS[name]
     geom, traj = geom_of(cfg), config_trajectory(cfg)
     rng = np.random.default_rng(100 + len(name))
     x = config_phantom(cfg)
@@ -741,3 +742,84 @@ def test_segment_count_full_size_oblique_views(torch_dev, mbp, oracle):
     assert n <= o
     assert o - n <= 1e-5 * o
     plan.close()
+
+
+# ------------------------------------------------------------------------------------------
+# The gather in view batches sized to its workspace
+
+
+@pytest.mark.parametrize("trajectory", ["circular", "circular_tilted"])
+def test_gather_in_view_batches_of_a_small_workspace(torch_dev, mbp, oracle, trajectory):
+    """A caller workspace that holds the volume part and five views' share of the reordered
+    sinogram: the gather (column or per-row) runs in launches of five views (36 views: seven
+    of five and a ragged one), each adding into the previous ones; unbatched (z-fastest volume
+    used in place, so the workspace is all sinogram) and with a batch of four (interleaved
+    volume in the workspace too). A workspace below one view's share is refused."""
+    from dataclasses import replace
+    torch, dev = torch_dev
+    cfg = replace(SMALL_CONFIGS["c3_cone256"], trajectory=trajectory, layout="WHD")
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(53)
+    ys = rng.random((4, cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    bref = oracle.backproject(geom, traj, ys)
+    for B in (1, 4):
+        plan = make_plan(mbp, cfg, traj=traj)
+        plan.set_view_batch(5)
+        need = plan.workspace_size(B)
+        plan.set_view_batch(1)
+        least = plan.workspace_size(B)
+        plan.set_view_batch(0)
+        assert plan.workspace_size(B) > need > least > 0
+        ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
+        plan.set_workspace(ws)
+        say(f"case gather in view batches {trajectory} B={B}")
+        y_in = ys[0] if B == 1 else ys
+        b = plan.backproject(torch.from_numpy(y_in).to(dev)).cpu().numpy().astype(np.float64)
+        info = plan.info
+        say(f"  {info['last_adjoint']} on the {info['last_adjoint_walk']} walk, "
+            f"{info['last_adjoint_views_per_launch']} views per launch")
+        assert info["last_adjoint"] == "gather" and info["last_adjoint_views_per_launch"] == 5
+        for m in range(B):
+            check(b if B == 1 else b[m], bref[m], f"adjoint member {m}")
+        plan.set_workspace(torch.empty((least - 4) // 4, dtype=torch.float32, device=dev))
+        with pytest.raises(mbp.MbpError):
+            plan.backproject(torch.from_numpy(y_in).to(dev))
+        plan.close()
+
+
+def test_gather_under_the_memory_rule_at_full_size(torch_dev, mbp, oracle):
+    """The 512^3 cone's adjoint with nearly all device memory held elsewhere: one call may
+    use at most a quarter of the free memory, so the library's workspace holds only a few
+    dozen views of the reordered sinogram and the gather runs in many launches (before, this
+    case fell back to the atomic scatter, 38 times slower). Whole z columns and sampled voxels
+    against the oracle."""
+    torch, dev = torch_dev
+    cfg = CONFIGS["c4_cone512_aniso"]
+    geom, traj = geom_of(cfg), config_trajectory(cfg)
+    rng = np.random.default_rng(59)
+    y = sinogram_field((cfg.views, cfg.rows, cfg.cols), seed=11)
+    yd = torch.from_numpy(y).to(dev)
+    plan = make_plan(mbp, cfg)
+    out = plan.empty_volume(device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    hold = torch.empty(max(free - (256 << 20), 0), dtype=torch.uint8, device=dev)
+    say(f"case gather under the memory rule: {hold.numel() / 2**30:.1f} GiB held, "
+        f"{torch.cuda.mem_get_info()[0] / 2**20:.0f} MiB free")
+    plan.backproject(yd, out=out)
+    torch.cuda.synchronize()
+    del hold
+    torch.cuda.empty_cache()
+    info = plan.info
+    say(f"  {info['last_adjoint']} on the {info['last_adjoint_walk']} walk, "
+        f"{info['last_adjoint_views_per_launch']} views per launch")
+    assert info["last_adjoint"] == "gather" and info["last_adjoint_walk"] == "column"
+    assert 1 <= info["last_adjoint_views_per_launch"] < cfg.views
+    vids = _sample_voxels(cfg, 200, rng)
+    bref = oracle.backproject_voxels(geom, traj, y, vids)
+    g = out.contiguous().reshape(-1)[torch.from_numpy(vids).to(dev)].cpu().numpy().astype(np.float64)
+    check(g, bref, f"adjoint ({vids.size} sampled voxels)")
+    plan.close()
+    del yd, out
+    torch.cuda.empty_cache()
