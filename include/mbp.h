@@ -176,6 +176,21 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
 int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
                     int32_t accumulate, void* stream);
 
+/* mbp_backproject for callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments, result
+   and error codes, and no hipMalloc, hipFree or other allocating call. Every device buffer of
+   the call comes from a library array of 128 MiB per device (static device memory, held by
+   each device the library runs on until the process ends): the plan's frames (copied in by
+   each call), the gather's line table of one view batch, the reordered sinogram and, for
+   batches or (D, H, W) volumes, the interleaved z-fastest volume. The gather takes as many
+   views per launch as fit the array; a call that needs more than it holds even for one view
+   (for example the z-fastest copy of a (D, H, W) volume above about 128 MiB) returns
+   MBP_ETOOLARGE before any device work. All calls on one device share that device's array:
+   calls that overlap in time on one device (other streams or host threads, any plan) race
+   and give wrong results; calls in order on one stream are safe. */
+int mbp_backproject_noalloc(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
+                            int32_t accumulate, void* stream);
+
 /* Number of ray/voxel segments one projection of one member walks, counting those longer
    than 1e-6 of the smallest voxel pitch (shorter ones are rounding residue where a ray
    crosses several grid planes at one point). This is the work unit of the throughput

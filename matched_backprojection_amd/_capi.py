@@ -34,7 +34,7 @@ EXPORTS = (
     "mbp_plan_set_view_batch", "mbp_plan_set_adjoint", "mbp_project", "mbp_backproject", "mbp_segment_count",
     "mbp_workspace_size", "mbp_set_workspace", "mbp_convert_layout", "mbp_normal",
     "mbp_cgls_workspace_size", "mbp_cgls", "mbp_status_string", "mbp_last_error",
-    "mbp_abi_version", "mbp_stream_copy",
+    "mbp_abi_version", "mbp_stream_copy", "mbp_backproject_noalloc",
 )
 
 
@@ -94,6 +94,7 @@ def load():
     lib.mbp_plan_set_adjoint.argtypes = [P, I32]
     lib.mbp_project.argtypes = [P, P, I64, P, P]
     lib.mbp_backproject.argtypes = [P, P, I64, P, I32, P]
+    lib.mbp_backproject_noalloc.argtypes = [P, P, I64, P, I32, P]
     lib.mbp_segment_count.argtypes = [P, ctypes.POINTER(I64), P]
     lib.mbp_workspace_size.argtypes = [P, I64, ctypes.POINTER(ctypes.c_size_t)]
     lib.mbp_set_workspace.argtypes = [P, P, ctypes.c_size_t]

@@ -356,11 +356,12 @@ size_t column_ws_bytes(const mbp_plan* p, int nb, bool direct, bool gather, int6
     return n * sizeof(float);
 }
 
-// Views per gather launch whose reordered sinogram fits `bytes` of workspace next to the
-// volume part (at most vmax; 0 when not even one view fits).
-int64_t gather_views_fit(const mbp_plan* p, int nb, bool direct, size_t bytes, int64_t vmax) {
+// Views per gather launch whose reordered sinogram (plus `extra` bytes per view) fits `bytes`
+// of workspace next to the volume part (at most vmax; 0 when not even one view fits).
+int64_t gather_views_fit(const mbp_plan* p, int nb, bool direct, size_t bytes, int64_t vmax,
+                         size_t extra = 0) {
     const size_t fixed = column_ws_bytes(p, nb, direct, true, 0);
-    const size_t per_view = column_ws_bytes(p, nb, direct, true, 1) - fixed;
+    const size_t per_view = column_ws_bytes(p, nb, direct, true, 1) - fixed + extra;
     if (bytes < fixed + per_view) return 0;
     return std::min<int64_t>(vmax, (int64_t)((bytes - fixed) / per_view));
 }
@@ -660,15 +661,28 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
     return MBP_OK;
 }
 
-int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
-                    int32_t accumulate, void* stream) {
-    int rc = check_call(plan, sinogram, volume, batch);
-    if (rc != MBP_OK || batch == 0) return rc;
-    if (accumulate != 0 && accumulate != 1) return fail(MBP_EINVAL, "accumulate must be 0 or 1");
-    std::lock_guard<std::mutex> lock(plan->mu);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    DeviceState* d = device_state(plan, &rc);
-    if (!d) return rc;
+}  // extern "C"
+
+namespace {
+
+// A device region that one backprojection takes every buffer from, in place of the plan's own
+// (the no-allocation entry point): the reordered sinogram, the interleaved volume and, per
+// view batch, the gather's line table.
+struct FixedRegion {
+    char* ptr;
+    size_t bytes;
+};
+
+constexpr size_t kRegionAlign = 256;
+
+size_t align_up(size_t n) { return (n + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
+
+// The backprojection on device state d (frames staged). With `fixed`, the workspace is that
+// region, the line table is built per view batch inside it, and nothing is allocated; a call
+// whose least need exceeds the region fails with MBP_ETOOLARGE.
+int backproject_on(mbp_plan* plan, DeviceState* d, const float* sinogram, int64_t batch, float* volume,
+                   int32_t accumulate, hipStream_t s, const FixedRegion* fixed) {
+    int rc = MBP_OK;
     const mbp_geometry& g = plan->g;
     const int64_t vox = g.D * g.H * g.W, rays = g.views * g.rows * g.cols;
     int64_t m0 = 0;
@@ -681,25 +695,44 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
         const bool direct = whd && batch == 1;
         const bool gather = tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER;
         const int64_t vmax = views_per_launch(plan);
+        // in a fixed region the column gather's line table covers one view batch
+        const size_t lines_per_view = fixed && gather && !tilt ? (size_t)g.cols * sizeof(mbp::ColLine) : 0;
+        const size_t lines_pad = lines_per_view ? kRegionAlign : 0;
         while (m0 < batch) {
             int nb = direct ? 1 : interleave_for(plan, batch - m0);
             float* ws = nullptr;
             size_t got = 0;
             for (;;) {
                 // all views in one gather launch if the memory rule allows, else as many as fit
-                ws = get_workspace(plan, d, column_ws_bytes(plan, nb, direct, gather, vmax),
-                                   column_ws_bytes(plan, nb, direct, gather, 1), &got, &rc);
-                if (rc != MBP_OK) return rc;
+                const size_t want = column_ws_bytes(plan, nb, direct, gather, vmax) + lines_pad + lines_per_view * vmax;
+                const size_t least = column_ws_bytes(plan, nb, direct, gather, 1) + lines_pad + lines_per_view;
+                if (fixed) {
+                    if (fixed->bytes >= least) {
+                        ws = reinterpret_cast<float*>(fixed->ptr);
+                        got = fixed->bytes;
+                    } else if (nb == 1) {
+                        return fail(MBP_ETOOLARGE, "the no-allocation backprojection's scratch holds %zu bytes for this plan; "
+                                    "the call needs at least %zu (%s one view's reordered sinogram)", fixed->bytes, least,
+                                    direct ? "" : "one member's z-fastest volume and");
+                    }
+                } else {
+                    ws = get_workspace(plan, d, want, least, &got, &rc);
+                    if (rc != MBP_OK) return rc;
+                }
                 if (ws || nb == 1) break;
                 nb /= 2;
             }
             if (!ws) break;   // not even one member and one view fit: generic walk for the rest
-            const int64_t vb = gather ? gather_views_fit(plan, nb, direct, got, vmax) : vmax;
+            const int64_t vb = gather ? gather_views_fit(plan, nb, direct, got - lines_pad, vmax, lines_per_view) : vmax;
             plan->last_adjoint = gather ? MBP_ADJOINT_GATHER : MBP_ADJOINT_SCATTER;
             plan->last_walk = tilt ? MBP_PATH_GENERIC : MBP_PATH_COLUMN;
             plan->last_views = vb;
             float* target = direct ? volume : ws;
             float* ysc = direct ? ws : ws + (size_t)nb * (size_t)vox;
+            mbp::ColLine* batch_lines = lines_per_view
+                ? reinterpret_cast<mbp::ColLine*>(reinterpret_cast<char*>(ws) +
+                                                  align_up(column_ws_bytes(plan, nb, direct, gather, vb)))
+                : nullptr;
             const int acc_target = direct ? accumulate : 0;
             hipError_t e;
             if (!gather && !acc_target) {
@@ -708,7 +741,7 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
             }
             const float* si[4] = {nullptr, nullptr, nullptr, nullptr};
             for (int m = 0; m < nb; ++m) si[m] = sinogram + (m0 + m) * rays;
-            if (gather && !tilt && !d->lines) {
+            if (gather && !tilt && !fixed && !d->lines) {
                 const size_t bytes = (size_t)g.views * (size_t)g.cols * sizeof(mbp::ColLine);
                 e = hipMalloc(reinterpret_cast<void**>(&d->lines), bytes);
                 if (e != hipSuccess) { d->lines = nullptr; return hip_fail(e, "hipMalloc(column lines)"); }
@@ -726,10 +759,15 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
                     a.nviews = (int32_t)std::min(vb, g.views - v0);
                     e = mbp::launch_sino_prepass(a, nb, si, ysc, s);
                     if (e != hipSuccess) return hip_fail(e, "sinogram pre-pass launch");
+                    const mbp::ColLine* lines = d->lines ? d->lines + (size_t)v0 * (size_t)g.cols : batch_lines;
+                    if (batch_lines) {
+                        e = mbp::launch_column_lines(a, a.nviews, batch_lines, s);
+                        if (e != hipSuccess) return hip_fail(e, "column line launch");
+                        lines = batch_lines;
+                    }
                     const int acc = v0 == 0 ? acc_target : 1;
                     e = tilt ? mbp::launch_tilt_gather(a, nb, ysc, target, acc, s)
-                             : mbp::launch_column_gather(a, nb, d->lines + (size_t)v0 * (size_t)g.cols, ysc,
-                                                         target, acc, s);
+                             : mbp::launch_column_gather(a, nb, lines, ysc, target, acc, s);
                     if (e != hipSuccess) return hip_fail(e, tilt ? "tilt gather launch" : "column gather launch");
                 }
             } else {
@@ -760,6 +798,82 @@ int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float*
         m0 += nb;
     }
     return MBP_OK;
+}
+
+// Scratch of the no-allocation backprojection: one array per device, resolved to its device
+// address once per device (the array's name in host code is only a stand-in for it).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, char*>> g_scratch;   // (device, device address of `scratch`)
+
+char* scratch_on(int dev, int* rc) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (const auto& e : g_scratch)
+        if (e.first == dev) return e.second;
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+        *rc = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        return nullptr;
+    }
+    g_scratch.emplace_back(dev, static_cast<char*>(ptr));
+    return static_cast<char*>(ptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mbp_backproject(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
+                    int32_t accumulate, void* stream) {
+    int rc = check_call(plan, sinogram, volume, batch);
+    if (rc != MBP_OK || batch == 0) return rc;
+    if (accumulate != 0 && accumulate != 1) return fail(MBP_EINVAL, "accumulate must be 0 or 1");
+    std::lock_guard<std::mutex> lock(plan->mu);
+    DeviceState* d = device_state(plan, &rc);
+    if (!d) return rc;
+    return backproject_on(plan, d, sinogram, batch, volume, accumulate, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int mbp_backproject_noalloc(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume,
+                            int32_t accumulate, void* stream) {
+    int rc = check_call(plan, sinogram, volume, batch);
+    if (rc != MBP_OK || batch == 0) return rc;
+    if (accumulate != 0 && accumulate != 1) return fail(MBP_EINVAL, "accumulate must be 0 or 1");
+    const size_t frame_bytes = align_up(plan->frames.size() * sizeof(Frame));
+    if (frame_bytes >= kScratchBytes)
+        return fail(MBP_ETOOLARGE, "the no-allocation backprojection's scratch (%zu bytes) cannot hold the %zu views' frames",
+                    kScratchBytes, plan->frames.size());
+    // the least the column and per-row gathers need (one member, one view), checked before
+    // any device work
+    const bool tilt = tilt_gather(plan);
+    if (active_path(plan) == MBP_PATH_COLUMN || tilt) {
+        const bool direct = plan->g.layout == MBP_LAYOUT_WHD && batch == 1;
+        const bool gather = tilt || adjoint_kind(plan) == MBP_ADJOINT_GATHER;
+        const size_t lines = gather && !tilt ? kRegionAlign + (size_t)plan->g.cols * sizeof(mbp::ColLine) : 0;
+        const size_t least = frame_bytes + column_ws_bytes(plan, 1, direct, gather, 1) + lines;
+        if (least > kScratchBytes)
+            return fail(MBP_ETOOLARGE, "the no-allocation backprojection's scratch holds %zu bytes; this call needs at "
+                        "least %zu (frames,%s one view's reordered sinogram)", kScratchBytes, least,
+                        direct ? "" : " one member's z-fastest volume,");
+    }
+    std::lock_guard<std::mutex> lock(plan->mu);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    char* base = scratch_on(dev, &rc);
+    if (!base) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the frames go to the start of the scratch, the rest is the call's workspace
+    e = hipMemcpyAsync(base, plan->frames.data(), plan->frames.size() * sizeof(Frame), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(frames)");
+    DeviceState d;
+    d.device = dev;
+    d.frames = reinterpret_cast<Frame*>(base);
+    const FixedRegion region{base + frame_bytes, kScratchBytes - frame_bytes};
+    return backproject_on(plan, &d, sinogram, batch, volume, accumulate, s, &region);
 }
 
 int mbp_segment_count(mbp_plan* plan, int64_t* count, void* stream) {

@@ -167,6 +167,19 @@ def test_batch_zero_and_bad_calls_do_no_device_work(lib):
     assert lib.mbp_set_workspace(h, None, 0) == 0
     lib.mbp_plan_destroy(h)
     lib.mbp_plan_destroy(None)
+    # the no-allocation backprojection: argument checks as mbp_backproject's; a call whose
+    # least need exceeds the library's scratch (four 256 x 512 x 512 members in (D, H, W)
+    # order need a z-fastest volume of 256 MiB for even one member) is refused before any
+    # device work
+    c5 = CONFIGS["c5_helical_b4"]
+    rc, h5 = _create(lib, _geometry(c5), config_trajectory(c5))
+    assert rc == 0
+    assert lib.mbp_backproject_noalloc(h5, None, 0, None, 0, None) == 0
+    assert lib.mbp_backproject_noalloc(h5, None, 1, None, 0, None) == _capi.MBP_EINVAL
+    assert lib.mbp_backproject_noalloc(h5, ctypes.c_void_p(64), 4, ctypes.c_void_p(128), 2, None) == _capi.MBP_EINVAL
+    assert lib.mbp_backproject_noalloc(h5, ctypes.c_void_p(64), 4, ctypes.c_void_p(128), 0, None) == _capi.MBP_ETOOLARGE
+    assert b"scratch" in lib.mbp_last_error()
+    lib.mbp_plan_destroy(h5)
     # the streaming copy: nothing to do for n = 0, bad arguments rejected before any launch
     assert lib.mbp_stream_copy(None, None, 0, None) == 0
     assert lib.mbp_stream_copy(None, ctypes.c_void_p(64), 4, None) == _capi.MBP_EINVAL
