@@ -9,7 +9,11 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmbp.so")
+# MBP_SANITIZED=1 selects the copy whose host code is built with ASan and UBSan (for the
+# sanitizer run of the CPU tests, tests/run_sanitized.py)
+LIB_PATH = (os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "_build", "san", "libmbp.so")
+            if os.environ.get("MBP_SANITIZED") == "1"
+            else os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmbp.so"))
 
 MBP_OK = 0
 MBP_EINVAL = -1

@@ -23,6 +23,10 @@
 // columns of the same view share most voxels, and so each XCD's L2).
 #include <hip/hip_runtime.h>
 
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
 #include "mbp_internal.h"
 
 namespace mbp {
@@ -1430,12 +1434,14 @@ hipError_t to_native_nb(const float* in, int64_t ms, int32_t D, int32_t H, int32
     if (whd_in) {
         const int64_t n = (int64_t)D * H * W;
         const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+        trace_launch("interleave_kernel", dim3((unsigned)blocks), dim3(256), 0, "members %d", NB);
         interleave_kernel<NB><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(in, ms, n, ws);
         return hipGetLastError();
     }
     for (int32_t y0 = 0; y0 < H; y0 += kMaxGridYZ) {
         const int32_t ny = H - y0 < kMaxGridYZ ? H - y0 : kMaxGridYZ;
         dim3 grid((W + 31) / 32, (D + 31) / 32, ny);
+        trace_launch("dhw_to_native_kernel", grid, dim3(256), 0, "members %d rows y %d..", NB, y0);
         dhw_to_native_kernel<NB><<<grid, dim3(256), 0, s>>>(in, ms, D, H, W, y0, ws);
     }
     return hipGetLastError();
@@ -1447,12 +1453,14 @@ hipError_t from_native_nb(const float* ws, int32_t D, int32_t H, int32_t W, int 
     if (whd_out) {
         const int64_t n = (int64_t)D * H * W;
         const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+        trace_launch("deinterleave_kernel", dim3((unsigned)blocks), dim3(256), 0, "members %d", NB);
         deinterleave_kernel<NB><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(ws, n, out, ms, accumulate);
         return hipGetLastError();
     }
     for (int32_t y0 = 0; y0 < H; y0 += kMaxGridYZ) {
         const int32_t ny = H - y0 < kMaxGridYZ ? H - y0 : kMaxGridYZ;
         dim3 grid((W + 31) / 32, (D + 31) / 32, ny);
+        trace_launch("native_to_dhw_kernel", grid, dim3(256), 0, "members %d rows y %d..", NB, y0);
         native_to_dhw_kernel<NB><<<grid, dim3(256), 0, s>>>(ws, D, H, W, y0, out, ms, accumulate);
     }
     return hipGetLastError();
@@ -1463,6 +1471,27 @@ hipError_t from_native_nb(const float* ws, int32_t D, int32_t H, int32_t W, int 
 // ------------------------------------------------------------------------------------------
 // Launchers
 
+// MBP_TRACE set (and not "0") in the environment: each launch prints its kernel, grid, block,
+// dynamic LDS bytes and work range to stderr. Read at every launch, so it can be switched on
+// while a process runs.
+bool trace_on() {
+    const char* e = std::getenv("MBP_TRACE");
+    return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+void trace_launch(const char* kernel, dim3 grid, dim3 block, size_t lds, const char* fmt, ...) {
+    if (!trace_on()) return;
+    char extra[256] = "";
+    if (fmt && fmt[0]) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(extra, sizeof(extra), fmt, ap);
+        va_end(ap);
+    }
+    std::fprintf(stderr, "mbp-trace %s grid %u x %u x %u block %u lds %zu %s\n", kernel, grid.x, grid.y,
+                 grid.z, block.x * block.y * block.z, lds, extra);
+}
+
 hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vol,
                                   float* const* sino, hipStream_t s) {
     const int64_t n = (int64_t)a.nviews * a.rows * a.cols;
@@ -1470,6 +1499,8 @@ hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vo
     Ptrs4 v{};
     MPtrs4 o{};
     for (int m = 0; m < a.nb; ++m) { v.p[m] = vol[m]; o.p[m] = sino[m]; }
+    trace_launch("generic_forward_kernel", dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                 "views %d..%d members %d", a.view0, a.view0 + a.nviews - 1, a.nb);
     generic_forward_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a, v, o);
     return hipGetLastError();
 }
@@ -1481,6 +1512,8 @@ hipError_t launch_generic_adjoint(const GenericLaunch& a, const float* const* si
     Ptrs4 y{};
     MPtrs4 o{};
     for (int m = 0; m < a.nb; ++m) { y.p[m] = sino[m]; o.p[m] = vol[m]; }
+    trace_launch("generic_adjoint_kernel", dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                 "views %d..%d members %d", a.view0, a.view0 + a.nviews - 1, a.nb);
     generic_adjoint_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a, y, o);
     return hipGetLastError();
 }
@@ -1493,6 +1526,8 @@ hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol
     const dim3 grid((a.tasks + 3) / 4);
     const bool flat = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)a.box.n[2] * (uint64_t)nb *
                           sizeof(float) < (1ull << 31);
+    trace_launch(flat ? "column_forward_kernel<flat>" : "column_forward_kernel<resource per cell>", grid,
+                 dim3(256), 0, "views %d..%d members %d", a.view0, a.view0 + a.nviews - 1, nb);
 #define MBP_FORWARD(NB_, FLAT_) \
     if (nb == NB_ && flat == FLAT_) column_forward_kernel<NB_, FLAT_><<<grid, dim3(256), 0, s>>>(a, vol, o)
     MBP_FORWARD(1, true); else MBP_FORWARD(1, false); else MBP_FORWARD(2, true); else MBP_FORWARD(2, false);
@@ -1508,6 +1543,8 @@ hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* con
     Ptrs4 y{};
     for (int m = 0; m < nb; ++m) y.p[m] = sino[m];
     const dim3 grid((a.tasks + 3) / 4);
+    trace_launch("column_adjoint_kernel", grid, dim3(256), 0, "views %d..%d members %d", a.view0,
+                 a.view0 + a.nviews - 1, nb);
     switch (nb) {
         case 1: column_adjoint_kernel<1><<<grid, dim3(256), 0, s>>>(a, y, vol); break;
         case 2: column_adjoint_kernel<2><<<grid, dim3(256), 0, s>>>(a, y, vol); break;
@@ -1521,12 +1558,16 @@ hipError_t launch_count(const GenericLaunch& a, unsigned long long* count, hipSt
     const int64_t n = (int64_t)a.nviews * a.rows * a.cols;
     if (n == 0) return hipSuccess;
     const int64_t want = (n + 255) / 256;
+    trace_launch("generic_count_kernel", dim3((unsigned)(want < 8192 ? want : 8192)), dim3(256), 0,
+                 "views %d..%d", a.view0, a.view0 + a.nviews - 1);
     generic_count_kernel<<<dim3((unsigned)(want < 8192 ? want : 8192)), dim3(256), 0, s>>>(a, count);
     return hipGetLastError();
 }
 
 hipError_t launch_column_count(const ColumnLaunch& a, unsigned long long* count, hipStream_t s) {
     if (a.tasks == 0) return hipSuccess;
+    trace_launch("column_count_kernel", dim3((a.tasks + 3) / 4), dim3(256), 0, "views %d..%d", a.view0,
+                 a.view0 + a.nviews - 1);
     column_count_kernel<<<dim3((a.tasks + 3) / 4), dim3(256), 0, s>>>(a, count);
     return hipGetLastError();
 }
@@ -1543,6 +1584,8 @@ hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const
         b.nviews = a.nviews - v0 < 65535 ? a.nviews - v0 : 65535;
         const dim3 grid((a.cols + 31) / 32, (rows_pad + 31) / 32, b.nviews);
         float* const out = ysc + (int64_t)v0 * a.cols * rows_pad * nb;
+        trace_launch("sino_prepass_kernel", grid, dim3(256), 0, "views %d..%d members %d rows padded %d",
+                     b.view0, b.view0 + b.nviews - 1, nb, rows_pad);
         switch (nb) {
             case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
             case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
@@ -1562,6 +1605,8 @@ hipError_t launch_column_lines(const ColumnLaunch& a, int32_t views, ColLine* li
     const int64_t n = (int64_t)views * a.cols;
     if (n == 0) return hipSuccess;
     const int64_t want = (n + 255) / 256;
+    trace_launch("column_line_kernel", dim3((unsigned)(want < 65536 ? want : 65536)), dim3(256), 0,
+                 "views %d..%d", a.view0, a.view0 + views - 1);
     column_line_kernel<<<dim3((unsigned)(want < 65536 ? want : 65536)), dim3(256), 0, s>>>(a, views, lines);
     return hipGetLastError();
 }
@@ -1582,6 +1627,9 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
                                     (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
     const int32_t kr = gather_rows_loaded(gather_stride(a.rows));
+    trace_launch("column_gather_kernel", grid, dim3(256), lds,
+                 "views %d..%d members %d rows per lane %d z chunk %d tiles %d x %d", a.view0,
+                 a.view0 + a.nviews - 1, nb, kr, zchunk, tx, ty);
 #define MBP_GATHER(NB_, KR_) \
     if (nb == NB_ && kr == KR_) \
         column_gather_kernel<NB_, KR_><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate)
@@ -1605,6 +1653,8 @@ hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, f
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(TiltItem) +
                                     (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
+    trace_launch("tilt_gather_kernel", grid, dim3(256), lds, "views %d..%d members %d z chunk %d tiles %d x %d",
+                 a.view0, a.view0 + a.nviews - 1, nb, zchunk, tx, ty);
     switch (nb) {
         case 1: tilt_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
         case 2: tilt_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
@@ -1643,6 +1693,8 @@ hipError_t launch_convert(const float* in, int32_t D, int32_t H, int32_t W, int 
 hipError_t launch_stream_copy(const float* in, float* out, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int64_t want = (n / 4 + 255) / 256;
+    trace_launch("stream_copy_kernel", dim3((unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024)), dim3(256), 0,
+                 "floats %lld", (long long)n);
     stream_copy_kernel<<<dim3((unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024)), dim3(256), 0, s>>>(in, out, n);
     return hipGetLastError();
 }
@@ -1650,6 +1702,8 @@ hipError_t launch_stream_copy(const float* in, float* out, int64_t n, hipStream_
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int64_t want = (n + 255) / 256;
+    trace_launch("fill_zero_kernel", dim3((unsigned)(want < 65536 ? want : 65536)), dim3(256), 0, "floats %lld",
+                 (long long)n);
     fill_zero_kernel<<<dim3((unsigned)(want < 65536 ? want : 65536)), dim3(256), 0, s>>>(p, n);
     return hipGetLastError();
 }

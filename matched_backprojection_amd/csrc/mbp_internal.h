@@ -88,6 +88,10 @@ hipError_t launch_convert(const float* in, int32_t D, int32_t H, int32_t W, int 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_stream_copy(const float* in, float* out, int64_t n, hipStream_t s);
 
+// With MBP_TRACE set in the environment, print one launch's kernel, grid, block, dynamic LDS
+// bytes and work range (printf-style `fmt`) to stderr.
+void trace_launch(const char* kernel, dim3 grid, dim3 block, size_t lds, const char* fmt, ...);
+
 // Record the calling thread's error message (mbp_last_error) and return `code`.
 int set_error(int code, const char* fmt, ...);
 

@@ -206,7 +206,9 @@ int hip_err(hipError_t e, const char* what) {
 // ||a||^2-style reduction of member vectors a . b of length n, finished as `what`.
 int dot(const Work& w, const float* a, const float* b, int64_t n, int64_t batch, int32_t what,
         int32_t k, int32_t hist_len, double rtol2, hipStream_t st) {
+    mbp::trace_launch("dot_partial_kernel", dim3(kDotBlocks, (unsigned)batch), dim3(kThreads), 0, "members %lld", (long long)batch);
     dot_partial_kernel<<<dim3(kDotBlocks, (unsigned)batch), dim3(kThreads), 0, st>>>(a, b, n, w.part);
+    mbp::trace_launch("dot_finish_kernel", dim3((unsigned)batch), dim3(kThreads), 0, "iteration %d", (int)k);
     dot_finish_kernel<<<dim3((unsigned)batch), dim3(kThreads), 0, st>>>(w.part, w.scal, w.hist, hist_len, k, what, rtol2);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MBP_OK : hip_err(e, "solver reduction launch");
@@ -271,9 +273,11 @@ int mbp_cgls(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume
     const double rtol2 = rtol * rtol;
     const dim3 gv = vec_grid(vox, batch), gs = vec_grid(rays, batch);
 
+    mbp::trace_launch("init_scalars_kernel", dim3((unsigned)((batch * kSlots + 255) / 256)), dim3(256), 0, "");
     init_scalars_kernel<<<dim3((unsigned)((batch * kSlots + 255) / 256)), dim3(256), 0, st>>>(w.scal, (int32_t)batch);
     // r0 = y - A x0, s0 = A^T r0, p0 = s0
     if ((rc = mbp_project(plan, volume, batch, w.q, stream)) != MBP_OK) return rc;
+    mbp::trace_launch("sub_kernel", gs, dim3(kThreads), 0, "");
     sub_kernel<<<gs, dim3(kThreads), 0, st>>>(sinogram, w.q, rays, w.r);
     if ((rc = dot(w, sinogram, sinogram, rays, batch, kStoreY2, 0, hl, rtol2, st)) != MBP_OK) return rc;
     if ((rc = dot(w, w.r, w.r, rays, batch, kStart, 0, hl, rtol2, st)) != MBP_OK) return rc;
@@ -285,12 +289,15 @@ int mbp_cgls(mbp_plan* plan, const float* sinogram, int64_t batch, float* volume
         // q = A p; alpha = gamma / ||q||^2; x += alpha p; r -= alpha q
         if ((rc = mbp_project(plan, w.p, batch, w.q, stream)) != MBP_OK) return rc;
         if ((rc = dot(w, w.q, w.q, rays, batch, kAlphaFromQ, k, hl, rtol2, st)) != MBP_OK) return rc;
+        mbp::trace_launch("axpy_kernel", gv, dim3(kThreads), 0, "x += alpha p");
         axpy_kernel<<<gv, dim3(kThreads), 0, st>>>(w.scal, 1.0f, w.p, vox, volume);
+        mbp::trace_launch("axpy_kernel", gs, dim3(kThreads), 0, "r -= alpha q");
         axpy_kernel<<<gs, dim3(kThreads), 0, st>>>(w.scal, -1.0f, w.q, rays, w.r);
         if ((rc = dot(w, w.r, w.r, rays, batch, kResidual, k, hl, rtol2, st)) != MBP_OK) return rc;
         // s = A^T r; beta = ||s||^2 / gamma; p = s + beta p
         if ((rc = mbp_backproject(plan, w.r, batch, w.s, 0, stream)) != MBP_OK) return rc;
         if ((rc = dot(w, w.s, w.s, vox, batch, kBetaFromS, k, hl, rtol2, st)) != MBP_OK) return rc;
+        mbp::trace_launch("direction_kernel", gv, dim3(kThreads), 0, "");
         direction_kernel<<<gv, dim3(kThreads), 0, st>>>(w.scal, w.s, vox, w.p);
         if ((e = hipGetLastError()) != hipSuccess) return hip_err(e, "solver update launch");
     }

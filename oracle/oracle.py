@@ -23,7 +23,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "siddon_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+# MBP_SANITIZED=1 (set by tests/run_sanitized.py) selects the ASan/UBSan build
+_SANITIZED = os.environ.get("MBP_SANITIZED") == "1"
+_LIB_PATH = os.path.join(_HERE, "_build", "san" if _SANITIZED else "", "liboracle.so")
 _BEAMS = {"parallel": 0, "fan": 1, "cone": 2, "parallel3d": 3}
 _BEAMS_3D = ("cone", "parallel3d")
 
@@ -39,17 +41,25 @@ class _Geom(ctypes.Structure):
     ]
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (fp64, OpenMP, no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call([
-            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-            "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm",
-        ])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, OpenMP, no fast-math, no FMA contraction); with
+    ``sanitize``, a copy built by clang with AddressSanitizer and UndefinedBehaviorSanitizer
+    into ``_build/san/`` (for tests/run_sanitized.py)."""
+    path = os.path.join(_HERE, "_build", "san", "liboracle.so") if sanitize else _LIB_PATH
+    if force or sanitize or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        tmp = path + ".tmp%d" % os.getpid()
+        if sanitize:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fPIC", "-shared",
+                   "-fopenmp=libgomp", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+                   "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+                   "-fno-sanitize-recover=all", "-o", tmp, _SRC, "-lm", "-lgomp"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                   "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, path)
+    return path
 
 
 _lib = None
@@ -59,7 +69,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            build()
+            build(sanitize=_SANITIZED)
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64

@@ -13,7 +13,10 @@ import os
 import numpy as np
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-_LIB = os.path.join(ROOT, "matched_backprojection_amd", "csrc", "_build", "libmbp_hostcheck.so")
+# MBP_SANITIZED=1 (set by tests/run_sanitized.py) selects the ASan/UBSan build
+_SANITIZED = os.environ.get("MBP_SANITIZED") == "1"
+_LIB = os.path.join(ROOT, "matched_backprojection_amd", "csrc", "_build", "san" if _SANITIZED else "",
+                    "libmbp_hostcheck.so")
 _lib = None
 
 
@@ -26,7 +29,7 @@ def _load():
                 "mbp_build", os.path.join(ROOT, "matched_backprojection_amd", "csrc", "build.py"))
             mod = importlib.util.module_from_spec(spec)
             spec.loader.exec_module(mod)
-            mod.build_hostcheck()
+            mod.build_hostcheck(sanitize=_SANITIZED)
         lib = ctypes.CDLL(_LIB)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P]
