@@ -557,12 +557,17 @@ MBP_HD MBP_INLINE bool tilt_row_range(const TiltCorners& T, int32_t j, int32_t r
 }
 
 // One item of the tilted gather: rows k0 .. k0 + nrows - 1 (at most 64) of column j in view
-// `view`, with what its rows share: the ray direction of the column at v = 0, b = c - s + u eu
-// (row k's direction is b + v_k ev), and the source's z in cells above the box, szc
-// (48 bytes).
+// `view`, with everything its rows share, computed once when the item is built: the column's
+// ray direction at v = 0, b = c - s + u eu (xy components, and z in cells per unit parameter),
+// the view's row axis ev (likewise), the offsets of the cell's four walls from the source
+// (x0 - sx, x1 - sx, y0 - sy, y1 - sy), the source's z in cells above the box, and the row
+// coordinate of row k0 (112 bytes). Row k0 + l's ray direction is b + (v0 + l dv) ev.
 struct TiltItem {
-    double b[3];
+    double bx, by, bzc;
+    double evx, evy, evzc;
+    double wx0, wx1, wy0, wy1;
     double szc;
+    double v0;
     int32_t view, j, k0, nrows;
 };
 

@@ -538,14 +538,13 @@ def _sample_rays(cfg, n, rng):
 
 
 def _unit_z_columns(cfg):
-    """(x, y) of the xy cells whose whole z column is compared: the gather's unit of work is
-    one z column, and its cells are dealt in 64 x 8 tiles (x by y) when the grid holds them,
-    else 16 x 32; the columns sit on the volume's faces and on both sides of the first tile
-    edges in x and y."""
+    """(x, y) of the xy cells whose whole z column is compared: the gathers' unit of work is
+    one z column, and their cells are dealt in tiles (64 x 8 for the column gather when the
+    grid holds them, else 16 x 32; 16 x 32 for the per-row gather); the columns sit on the
+    volume's faces and on both sides of the first tile edges of both tilings in x and y."""
     D, H, W = cfg.shape
-    tx, ty = (64, 8) if W % 64 == 0 and H % 8 == 0 else (16, 32)
-    xs = sorted({0, min(tx - 1, W - 1), min(tx, W - 1), W - 1})
-    ys = sorted({0, min(ty - 1, H - 1), min(ty, H - 1), H - 1})
+    xs = sorted({min(x, W - 1) for x in (0, 15, 16, 63, 64, W - 1)})
+    ys = sorted({min(y, H - 1) for y in (0, 7, 8, 31, 32, H - 1)})
     return [(x, y) for x in xs for y in ys]
 
 
@@ -561,10 +560,20 @@ def _sample_voxels(cfg, n, rng):
     return np.unique(np.concatenate(ids))
 
 
-@pytest.mark.parametrize("name", list(CONFIGS) + list(CONTEXT_CONFIGS))
+def _full_size_config(name):
+    """A full-size configuration by name: the five configurations, the pages' context
+    workload, and the 256^3 cone with its detector rotated in its plane (rows not along z;
+    volume z-fastest), the timed workload of the per-row gather."""
+    from dataclasses import replace
+    if name == "c3_cone256_tilted":
+        return replace(CONFIGS["c3_cone256"], name=name, trajectory="circular_tilted", layout="WHD")
+    return CONFIGS.get(name) or CONTEXT_CONFIGS[name]
+
+
+@pytest.mark.parametrize("name", list(CONFIGS) + list(CONTEXT_CONFIGS) + ["c3_cone256_tilted"])
 def test_full_size_parity(torch_dev, mbp, oracle, name):
     torch, dev = torch_dev
-    cfg = CONFIGS.get(name) or CONTEXT_CONFIGS[name]
+    cfg = _full_size_config(name)
     geom, traj = geom_of(cfg), config_trajectory(cfg)
     rng = np.random.default_rng(100 + len(name))
     x = config_phantom(cfg)
