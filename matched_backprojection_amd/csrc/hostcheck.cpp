@@ -161,8 +161,16 @@ int mbph_project_chunked(const double* frames, int beam, const double* lo, const
                         // chunks inside the row's slab (for this row; the kernel requires it of
                         // all 64 rows of a wave) take the clip-free form, with the next z
                         // crossing re-anchored at the chunk start and then stepped
-                        const bool inside = !ch.empty() && r.t_lo <= ta && r.t_hi >= ch.back().tb;
-                        if (inside && grouped > 0) nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
+                        const bool inside = !ch.empty() && r.t_lo <= ta && r.t_hi >= ch.back().tb &&
+                                            stepped_walk_ok(r, kz, (int32_t)ch.size(), ch.back().tb);
+                        std::vector<XYEvent> ce(ch);
+                        const bool more = kz < r.z.steps;
+                        const double t_first = more ? r.z.t_first : INFINITY;
+                        const double t_step = more ? r.z.t_step : 0.0;
+                        if (inside && grouped > 0) {
+                            nz = more ? crossing(r.z, kz) : INFINITY;
+                            for (int lane = 0; lane < 64; ++lane) xy_chunk_chords(ce.data(), (int32_t)ce.size(), ta, lane);
+                        }
                         size_t p = 0;
                         for (; p < grouped; ++p) {
                             const double hi = fmin(ch[p].tb, r.t_hi);
@@ -170,7 +178,15 @@ int mbph_project_chunked(const double* frames, int beam, const double* lo, const
                             float l0, l1;
                             if (inside) {
                                 if (nz < ta && kz < r.z.steps) ++*violations;   // a crossing left behind
-                                row_cell_two_inside(r, ta, ch[p].tb, cz, kz, nz, z0, l0, z1, l1);
+                                z0 = cz;
+                                const double nz_was = nz;
+                                if (row_cell_two_counted(t_first, t_step, ce[p].tb, ce[p].chord, kz, nz, l0, l1))
+                                    cz += r.z.step;
+                                z1 = cz;
+                                if (kz > r.z.steps) ++*violations;   // counted past the last plane
+                                if (kz < r.z.steps && nz != crossing(r.z, kz)) ++*violations;
+                                if (kz == r.z.steps && nz_was < ce[p].tb && !(nz > ch.back().tb)) ++*violations;
+                                if (!(l0 >= 0.0f) || !(l1 >= 0.0f)) ++*violations;
                             } else {
                                 row_cell_two(r, ta, ch[p].tb, cz, kz, nz, z0, l0, z1, l1);
                             }
@@ -179,6 +195,7 @@ int mbph_project_chunked(const double* frames, int beam, const double* lo, const
                             if (l1 != 0.0f) visit(ch[p].cxy, z1, l1);
                             ta = ch[p].tb;
                         }
+                        if (inside && grouped > 0) nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
                         for (; p < ch.size(); ++p) { row_cell(r, ta, ch[p].tb, ch[p].cxy, cz, kz, nz, visit); ta = ch[p].tb; }
                     }
                     row_cell(r, ta, c.T, final_cxy, cz, kz, nz, visit);

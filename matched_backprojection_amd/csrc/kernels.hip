@@ -285,7 +285,7 @@ __device__ __forceinline__ const lds_event* events_in_vgpr(const XYEvent* e) {
 // cell's column is reached through the load's scalar offset (one scalar multiply per cell);
 // otherwise each cell gets a resource based at its column.
 template <int NB, bool FLAT>
-__global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch A,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 8 : 1))) column_forward_kernel(const ColumnLaunch A,
                                                              const float* __restrict__ vol,
                                                              const MPtrs4 sino) {
     __shared__ XYEvent events[4][kXYChunk];
@@ -329,7 +329,8 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                 // after its single z crossing) first, then all their loads, then the sums. When
                 // the chunk lies inside every lane's slab, the pieces need no clip.
                 const double t_end = count > 0 ? E[count - 1].tb : ta;
-                const bool inside = __all(r.t_lo <= ta && r.t_hi >= t_end);
+                const bool inside = __all(r.t_lo <= ta && r.t_hi >= t_end &&
+                                          stepped_walk_ok(r, kz, count, t_end));
                 auto groups = [&](auto pieces) {
                     for (; p + kCellGroup <= count; p += kCellGroup) {
                         uint32_t off[2 * kCellGroup];
@@ -361,13 +362,24 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                     }
                 };
                 if (inside) {
-                    // re-anchor the next z crossing exactly (row_cell_two_inside steps it by
-                    // the spacing); voxels are read through a buffer resource per cell based
-                    // at the cell's z column, so each load takes a 32-bit offset
-                    nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
+                    // the clip-free counted form: the cells' chords computed once for all
+                    // rows, then per cell the crossing count, the next crossing and the z
+                    // offsets (in bytes) without branches. Voxels are read through a buffer
+                    // resource (per cell, based at the cell's z column, unless the volume fits
+                    // one 31-bit resource), so each load takes a 32-bit offset.
+                    // a row with no crossing left keeps nz = +inf (crossing() is not asked for
+                    // its planes again)
+                    if (kz >= r.z.steps) { r.z.t_first = INFINITY; r.z.t_step = 0.0; }
+                    nz = crossing(r.z, kz);
+                    xy_chunk_chords(E, count, ta, lane);
+                    wave_lds_sync();
                     const int32_t colbytes = (int32_t)(D * NB * sizeof(float));
                     const __amdgpu_buffer_rsrc_t rs_all = __builtin_amdgcn_make_buffer_rsrc(
                         const_cast<float*>(vol), (short)0, 0x7FFFFFFF, kBufferFlags);
+                    const int32_t zbytes = NB * sizeof(float);
+                    const int32_t zstep = r.z.step * zbytes;
+                    const int32_t zbase = r.z.c0 * zbytes;
+                    int32_t k = kz;
                     for (; p + kCellGroup <= count; p += kCellGroup) {
                         uint32_t zoff[2 * kCellGroup];
                         float len[2 * kCellGroup];
@@ -375,13 +387,11 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                         const lds_event* const Eg = events_in_vgpr(E + p);
 #pragma unroll
                         for (int q = 0; q < kCellGroup; ++q) {
-                            const double tb = Eg[q].tb;
                             cell[q] = uniform((uint32_t)Eg[q].cxy);
-                            int32_t z0, z1;
-                            row_cell_two_inside(r, ta, tb, cz, kz, nz, z0, len[2 * q], z1, len[2 * q + 1]);
-                            zoff[2 * q] = (uint32_t)z0 * (NB * sizeof(float));
-                            zoff[2 * q + 1] = (uint32_t)z1 * (NB * sizeof(float));
-                            ta = tb;
+                            zoff[2 * q] = (uint32_t)(zbase + __mul24(k, zstep));
+                            row_cell_two_counted(r.z.t_first, r.z.t_step, Eg[q].tb, Eg[q].chord, k, nz,
+                                                 len[2 * q], len[2 * q + 1]);
+                            zoff[2 * q + 1] = (uint32_t)(zbase + __mul24(k, zstep));
                         }
                         float val[2 * kCellGroup][NB];
 #pragma unroll
@@ -393,13 +403,11 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
                             const uint32_t soff = FLAT ? cell[q] * (uint32_t)colbytes : 0u;
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
-                                // one member: the first piece (empty only when the row meets a
-                                // z plane exactly at the cell's entry) is loaded unconditionally
-                                // and multiplied with 0 * anything = 0, so an empty piece adds
-                                // nothing even next to a non-finite voxel; the second piece is
-                                // empty whenever the row does not cross a z plane in this cell
-                                // (it then names the first piece's voxel) and keeps its branch
-                                if ((NB == 1 && h == 0) || len[2 * q + h] != 0.0f) {
+                                // one member: both pieces are loaded unconditionally (a second
+                                // piece without a z crossing names the first piece's voxel) and
+                                // multiplied with 0 * anything = 0, so an empty piece adds
+                                // nothing even next to a non-finite voxel
+                                if (NB == 1 || len[2 * q + h] != 0.0f) {
                                     buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h], soff);
                                 } else {
 #pragma unroll
@@ -410,16 +418,18 @@ __global__ void __launch_bounds__(256) column_forward_kernel(const ColumnLaunch 
 #pragma unroll
                         for (int q = 0; q < 2 * kCellGroup; ++q) {
                             if constexpr (NB == 1) {
-                                if (q % 2 == 0)
-                                    acc[0] += mul_legacy(len[q], val[q][0]);
-                                else
-                                    acc[0] = fmaf(len[q], val[q][0], acc[0]);
+                                acc[0] += mul_legacy(len[q], val[q][0]);
                             } else {
 #pragma unroll
                                 for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
                             }
                         }
                     }
+                    // the state the remaining cells continue from
+                    if (p > 0) ta = E[p - 1].tb;
+                    cz = r.z.c0 + r.z.step * k;
+                    kz = k;
+                    nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
                 } else {
                     groups([&](double tb, int32_t& z0, float& l0, int32_t& z1, float& l1) {
                         row_cell_two(r, ta, tb, cz, kz, nz, z0, l0, z1, l1);

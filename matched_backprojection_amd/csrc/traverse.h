@@ -921,7 +921,7 @@ constexpr int32_t kCellGroup = 4;
 struct XYEvent {
     double tb;          // distance at which the cell ends
     int32_t cxy;        // cx * H + cy
-    int32_t pad_;
+    float chord;        // tb minus the previous cell's tb, rounded to fp32 (xy_chunk_chords)
 };
 
 MBP_HD MBP_INLINE double crossing(const AxisWalk& a, int32_t k) {
@@ -1022,26 +1022,42 @@ MBP_HD MBP_INLINE void row_cell_two(const RowWalk& r, double ta, double tb, int3
     cz1 = cz;
 }
 
-// row_cell_two for a cell inside the row's slab (t_lo <= ta and tb <= t_hi) of a row with
-// row_single_crossing(): no clip is needed, and the row's next z crossing is not before ta
-// (the previous one lies inside an earlier cell, more than a cell diagonal back), so the
-// pieces are (cross ? nz : tb) - ta and tb - nz. The next crossing is the previous one plus
-// the spacing: the caller re-anchors nz = crossing(kz) exactly at every chunk of at most
-// kXYChunk cells, so the running sum drifts by at most ~kXYChunk rounding steps.
-MBP_HD MBP_INLINE void row_cell_two_inside(const RowWalk& r, double ta, double tb, int32_t& cz,
-                                           int32_t& kz, double& nz, int32_t& cz0, float& len0,
-                                           int32_t& cz1, float& len1) {
-    const bool cross = nz < tb;
-    cz0 = cz;
-    len0 = (float)((cross ? nz : tb) - ta);
-    len1 = 0.0f;
-    if (cross) {
-        len1 = (float)(tb - nz);
-        cz += r.z.step;
-        ++kz;
-        nz = kz < r.z.steps ? nz + r.z.t_step : INFINITY;
+// The chords of a filled chunk whose first cell starts at ta, for the entries at positions
+// lane and lane + 64 (every entry must be filled and visible to the lane first).
+MBP_HD MBP_INLINE void xy_chunk_chords(XYEvent* E, int32_t count, double ta, int32_t lane) {
+    for (int32_t q = 0; q < 2; ++q) {
+        const int32_t i = lane + 64 * q;
+        if (i < count) E[i].chord = (float)(E[i].tb - (i > 0 ? E[i - 1].tb : ta));
     }
-    cz1 = cz;
+}
+
+// row_cell_two for a cell inside the row's slab (t_lo <= ta and tb <= t_hi) of a row with
+// row_single_crossing(): no clip is needed, and the row's next z crossing nz is not before ta
+// (the previous one lies inside an earlier cell, more than a cell diagonal back). The row
+// crosses a z plane in the cell when nz < tb; the piece after it is tb - nz and the piece
+// before it the rest of the cell's chord (so the two add up to the chord, and the first is 0
+// exactly when nz == ta). k counts the row's crossings; a crossing recomputes nz from it with
+// the same fma as crossing() (t_first = +inf for a row with no crossing left, so nz stays
+// +inf). The caller checks with stepped_walk_ok() that the count cannot pass the row's last
+// z plane inside the chunk.
+MBP_HD MBP_INLINE bool row_cell_two_counted(double t_first, double t_step, double tb, float chord,
+                                            int32_t& k, double& nz, float& len0, float& len1) {
+    const bool cross = nz < tb;
+    len1 = cross ? (float)(tb - nz) : 0.0f;
+    len0 = chord - len1;
+    k += cross ? 1 : 0;
+    nz = fma((double)k, t_step, t_first);
+    return cross;
+}
+
+// Whether a row that has made kz of its z crossings may take row_cell_two_counted over the
+// cells of a chunk ending at t_end (count cells): with fewer crossings left than cells it
+// could count past its last plane, which is harmless only if the plane after that one (where
+// nz then lands) lies clearly after t_end.
+MBP_HD MBP_INLINE bool stepped_walk_ok(const RowWalk& r, int32_t kz, int32_t count, double t_end) {
+    if (kz >= r.z.steps || r.z.steps - kz >= count) return true;
+    const double beyond = crossing(r.z, r.z.steps);
+    return beyond > t_end + 1e-9 * (fabs(t_end) + r.z.t_step);
 }
 
 }  // namespace mbp
