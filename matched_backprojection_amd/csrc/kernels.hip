@@ -384,12 +384,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
                         uint32_t zoff[2 * kCellGroup];
                         float len[2 * kCellGroup];
                         uint32_t cell[kCellGroup];
+                        bool cross[kCellGroup];
                         const lds_event* const Eg = events_in_vgpr(E + p);
 #pragma unroll
                         for (int q = 0; q < kCellGroup; ++q) {
                             cell[q] = uniform((uint32_t)Eg[q].cxy);
                             zoff[2 * q] = (uint32_t)(zbase + __mul24(k, zstep));
-                            row_cell_two_counted(r.z.t_first, r.z.t_step, Eg[q].tb, Eg[q].chord, k, nz,
+                            cross[q] = row_cell_two_counted(r.z.t_first, r.z.t_step, Eg[q].tb, Eg[q].chord, k, nz,
                                                  len[2 * q], len[2 * q + 1]);
                             zoff[2 * q + 1] = (uint32_t)(zbase + __mul24(k, zstep));
                         }
@@ -403,11 +404,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
                             const uint32_t soff = FLAT ? cell[q] * (uint32_t)colbytes : 0u;
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
-                                // one member: both pieces are loaded unconditionally (a second
-                                // piece without a z crossing names the first piece's voxel) and
-                                // multiplied with 0 * anything = 0, so an empty piece adds
-                                // nothing even next to a non-finite voxel
-                                if (NB == 1 || len[2 * q + h] != 0.0f) {
+                                // one member: the first piece (empty only when the row meets a
+                                // z plane exactly at the cell's entry) is loaded unconditionally
+                                // and multiplied with 0 * anything = 0, so an empty piece adds
+                                // nothing even next to a non-finite voxel; the second piece is
+                                // loaded by the lanes that cross a z plane in the cell (its
+                                // length tb - nz > 0 then rounds to a nonzero fp32 unless it is
+                                // below 2^-150), the others add 0
+                                if (NB == 1 ? (h == 0 || cross[q]) : len[2 * q + h] != 0.0f) {
                                     buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h], soff);
                                 } else {
 #pragma unroll
@@ -418,7 +422,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
 #pragma unroll
                         for (int q = 0; q < 2 * kCellGroup; ++q) {
                             if constexpr (NB == 1) {
-                                acc[0] += mul_legacy(len[q], val[q][0]);
+                                if (q % 2 == 0)
+                                    acc[0] += mul_legacy(len[q], val[q][0]);
+                                else
+                                    acc[0] = fmaf(len[q], val[q][0], acc[0]);
                             } else {
 #pragma unroll
                                 for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
