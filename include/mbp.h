@@ -127,6 +127,13 @@ typedef struct mbp_plan_info {
                                   or the generic walk's atomics)                              */
     int64_t last_adjoint_views_per_launch;  /* views per adjoint launch: below
                                   views_per_launch when the gather's workspace held fewer  */
+    /* What the last mbp_project of this plan ran (0 before the first call with B > 0): */
+    int32_t last_forward_walk; /* MBP_PATH_COLUMN, or MBP_PATH_GENERIC when the geometry needs
+                                  it or when not even one member's z-fastest copy (needed for
+                                  a (D,H,W) volume or a batch) fits the memory rule          */
+    int32_t last_forward_members_per_pass;  /* fewest members one column walk served (1, 2
+                                  or 4; below members_per_pass when the interleaved copy was
+                                  halved to fit the memory rule); 0 on the generic walk     */
 } mbp_plan_info;
 
 /* Validate the geometry and trajectory and build a plan. Trajectory arrays are host fp64,

@@ -132,7 +132,9 @@ class Plan:
                 "rays": inf.rays, "voxels": inf.voxels, "members_per_pass": inf.members_per_pass,
                 "last_adjoint": _capi.ADJOINT_NAMES[inf.last_adjoint],
                 "last_adjoint_walk": _capi.PATH_NAMES[inf.last_adjoint_walk] if inf.last_adjoint else None,
-                "last_adjoint_views_per_launch": inf.last_adjoint_views_per_launch}
+                "last_adjoint_views_per_launch": inf.last_adjoint_views_per_launch,
+                "last_forward_walk": _capi.PATH_NAMES[inf.last_forward_walk] if inf.last_forward_walk else None,
+                "last_forward_members_per_pass": inf.last_forward_members_per_pass}
 
     def set_path(self, path: str) -> None:
         _capi.check(self._lib.mbp_plan_set_path(self._handle, _capi.PATHS[path]), "mbp_plan_set_path")

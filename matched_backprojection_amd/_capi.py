@@ -60,6 +60,7 @@ class PlanInfo(ctypes.Structure):
         ("members_per_pass", ctypes.c_int64),
         ("last_adjoint", ctypes.c_int32), ("last_adjoint_walk", ctypes.c_int32),
         ("last_adjoint_views_per_launch", ctypes.c_int64),
+        ("last_forward_walk", ctypes.c_int32), ("last_forward_members_per_pass", ctypes.c_int32),
     ]
 
 

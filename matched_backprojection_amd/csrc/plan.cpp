@@ -101,6 +101,9 @@ struct mbp_plan {
     int32_t last_adjoint = MBP_ADJOINT_AUTO;
     int32_t last_walk = MBP_PATH_AUTO;
     int64_t last_views = 0;
+    // and what the last forward projection ran
+    int32_t last_fwd_walk = MBP_PATH_AUTO;
+    int32_t last_fwd_members = 0;
     std::mutex mu;
 };
 
@@ -561,6 +564,8 @@ int mbp_plan_get_info(const mbp_plan* plan, mbp_plan_info* info) {
     info->last_adjoint = plan->last_adjoint;
     info->last_adjoint_walk = plan->last_walk;
     info->last_adjoint_views_per_launch = plan->last_views;
+    info->last_forward_walk = plan->last_fwd_walk;
+    info->last_forward_members_per_pass = plan->last_fwd_members;
     return MBP_OK;
 }
 
@@ -621,13 +626,18 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
     const mbp_geometry& g = plan->g;
     const int64_t vox = g.D * g.H * g.W, rays = g.views * g.rows * g.cols;
     int64_t m0 = 0;
+    plan->last_fwd_walk = MBP_PATH_GENERIC;
+    plan->last_fwd_members = 0;
     if (active_path(plan) == MBP_PATH_COLUMN) {
         const bool whd = g.layout == MBP_LAYOUT_WHD;
+        plan->last_fwd_walk = MBP_PATH_COLUMN;
+        plan->last_fwd_members = 4;
         while (m0 < batch) {
             if (whd && batch == 1) {
                 float* so[4] = {sinogram, nullptr, nullptr, nullptr};
                 rc = run_column(plan, d, false, volume, nullptr, nullptr, so, 1, s);
                 if (rc != MBP_OK) return rc;
+                plan->last_fwd_members = 1;
                 m0 = 1;
                 break;
             }
@@ -641,7 +651,15 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
                 if (ws || nb == 1) break;
                 nb /= 2;
             }
-            if (!ws) break;   // not even one member fits: generic walk for the rest
+            if (!ws) {
+                // not even one member's copy fits the memory rule: the generic walk, which
+                // reads the caller's layout in place, takes the rest (reported by
+                // mbp_plan_get_info)
+                plan->last_fwd_walk = MBP_PATH_GENERIC;
+                plan->last_fwd_members = 0;
+                break;
+            }
+            plan->last_fwd_members = std::min(plan->last_fwd_members, nb);
             hipError_t e = mbp::launch_to_native(volume + m0 * vox, vox, nb, (int32_t)g.D, (int32_t)g.H,
                                                  (int32_t)g.W, whd ? 1 : 0, ws, s);
             if (e != hipSuccess) return hip_fail(e, "layout conversion launch");

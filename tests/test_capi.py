@@ -103,6 +103,7 @@ def test_configs_plan_and_pick_walks(lib, name):
         assert ws.value == 4 * nb * ((0 if direct else cfg.n_voxels) + sino)
     # nothing has been backprojected yet
     assert inf.last_adjoint == 0 and inf.last_adjoint_walk == 0 and inf.last_adjoint_views_per_launch == 0
+    assert inf.last_forward_walk == 0 and inf.last_forward_members_per_pass == 0
     # view batching: a ragged split into launches of 7 views; the gather's reordered sinogram
     # then covers the views of one launch
     assert lib.mbp_plan_set_view_batch(h, 7) == 0

@@ -790,6 +790,18 @@ def test_gather_in_view_batches_of_a_small_workspace(torch_dev, mbp, oracle, tra
         assert info["last_adjoint"] == "gather" and info["last_adjoint_views_per_launch"] == 5
         for m in range(B):
             check(b if B == 1 else b[m], bref[m], f"adjoint member {m}")
+        # the forward with the same workspace: the walk and the members it served are reported
+        vol = plan.empty_volume(None if B == 1 else B, device=dev)
+        vol.fill_(1.0)
+        plan.project(vol)
+        torch.cuda.synchronize()
+        info = plan.info
+        say(f"  forward on the {info['last_forward_walk']} walk, "
+            f"{info['last_forward_members_per_pass']} members per pass")
+        if trajectory == "circular":
+            assert info["last_forward_walk"] == "column" and info["last_forward_members_per_pass"] == B
+        else:
+            assert info["last_forward_walk"] == "generic" and info["last_forward_members_per_pass"] == 0
         plan.set_workspace(torch.empty((least - 4) // 4, dtype=torch.float32, device=dev))
         with pytest.raises(mbp.MbpError):
             plan.backproject(torch.from_numpy(y_in).to(dev))
