@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <utility>
 #include <vector>
 
 #include "traverse.h"
@@ -92,7 +93,21 @@ int mbph_project(int path, const double* frames, int beam, const double* lo, con
                 } else {
                     RayWalk r;
                     ray_setup(F[i], B, beam, centred(j, cols, du), centred(k, rows, dv), r);
-                    walk_ray(r, visit);
+                    // the forward kernel's walk keeps the element offset instead of the cell:
+                    // it must name the same cells with the same lengths, in the same order
+                    std::vector<std::pair<int64_t, float>> cells;
+                    auto record = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+                        cells.emplace_back(cx * sx + cy * sy + cz * sz, len);
+                        visit(cx, cy, cz, len);
+                    };
+                    walk_ray(r, record);
+                    size_t q = 0;
+                    auto same = [&](int32_t off, float len) {
+                        if (q >= cells.size() || cells[q].first != off || cells[q].second != len) ++*violations;
+                        ++q;
+                    };
+                    walk_ray_offsets(r, (int32_t)sx, (int32_t)sy, (int32_t)sz, same);
+                    if (q != cells.size()) ++*violations;
                 }
                 const int64_t ray = ((int64_t)i * rows + k) * cols + j;
                 sino[ray] = acc * scale;

@@ -85,14 +85,16 @@ __global__ void __launch_bounds__(256) generic_forward_kernel(const GenericLaunc
     ray_setup(F, A.box, A.beam, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), r);
     float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
     const int nb = A.nb;
-    auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
-        const int32_t idx = cx * A.sx + cy * A.sy + cz * A.sz;
+    // the voxel's element offset is kept by the walk (one add per crossing) rather than formed
+    // from the cell indices and strides (three 32-bit multiplies per segment): -7% on the
+    // tilted 256^3 cone
+    auto visit = [&](int32_t idx, float len) {
         acc0 = fmaf(len, vol.p[0][idx], acc0);
         if (nb > 1) acc1 = fmaf(len, vol.p[1][idx], acc1);
         if (nb > 2) acc2 = fmaf(len, vol.p[2][idx], acc2);
         if (nb > 3) acc3 = fmaf(len, vol.p[3][idx], acc3);
     };
-    walk_ray(r, visit);
+    walk_ray_offsets(r, A.sx, A.sy, A.sz, visit);
     const int64_t ray = (int64_t)view * per_view + rem;
     sino.p[0][ray] = acc0;
     if (nb > 1) sino.p[1][ray] = acc1;
@@ -120,15 +122,14 @@ __global__ void __launch_bounds__(256) generic_adjoint_kernel(const GenericLaunc
     const Frame F = A.frames[view];
     RayWalk r;
     ray_setup(F, A.box, A.beam, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), r);
-    auto visit = [&](int32_t cx, int32_t cy, int32_t cz, float len) {
+    auto visit = [&](int32_t idx, float len) {
         if (!(len > 0.0f)) return;
-        const int32_t idx = cx * A.sx + cy * A.sy + cz * A.sz;
         atomic_add_f32(vol.p[0] + idx, len * w0);
         if (nb > 1) atomic_add_f32(vol.p[1] + idx, len * w1);
         if (nb > 2) atomic_add_f32(vol.p[2] + idx, len * w2);
         if (nb > 3) atomic_add_f32(vol.p[3] + idx, len * w3);
     };
-    walk_ray(r, visit);
+    walk_ray_offsets(r, A.sx, A.sy, A.sz, visit);
 }
 
 // Segment counts: segments of the generic walk longer than 1e-6 of the smallest voxel pitch

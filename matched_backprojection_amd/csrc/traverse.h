@@ -237,6 +237,41 @@ MBP_HD MBP_INLINE void walk_ray(const RayWalk& r, Visit& visit) {
     visit(cx, cy, cz, (float)fmax(r.T - t, 0.0));
 }
 
+// walk_ray with the cell given as its element offset cx * sx + cy * sy + cz * sz, kept by one
+// add per crossing (the offset of every visited cell fits 32 bits: the volume has fewer than
+// 2^31 elements): `visit(offset, length)` once per segment, in order along the ray.
+template <class Visit>
+MBP_HD MBP_INLINE void walk_ray_offsets(const RayWalk& r, int32_t sx, int32_t sy, int32_t sz, Visit& visit) {
+    if (!r.hit) return;
+    int32_t off = r.ax[0].c0 * sx + r.ax[1].c0 * sy + r.ax[2].c0 * sz;
+    const int32_t dx = r.ax[0].step * sx, dy = r.ax[1].step * sy, dz = r.ax[2].step * sz;
+    int32_t kx = 0, ky = 0, kz = 0;
+    double nx = r.ax[0].steps > 0 ? r.ax[0].t_first : INFINITY;
+    double ny = r.ax[1].steps > 0 ? r.ax[1].t_first : INFINITY;
+    double nz = r.ax[2].steps > 0 ? r.ax[2].t_first : INFINITY;
+    const int32_t total = r.ax[0].steps + r.ax[1].steps + r.ax[2].steps;
+    double t = 0.0;
+    for (int32_t m = 0; m < total; ++m) {
+        const bool bx = nx <= ny && nx <= nz;
+        const bool by = !bx && ny <= nz;
+        const double tb = bx ? nx : (by ? ny : nz);
+        visit(off, (float)fmax(tb - t, 0.0));
+        t = fmax(t, tb);
+        off += bx ? dx : (by ? dy : dz);
+        if (bx) {
+            ++kx;
+            nx = kx < r.ax[0].steps ? fma((double)kx, r.ax[0].t_step, r.ax[0].t_first) : INFINITY;
+        } else if (by) {
+            ++ky;
+            ny = ky < r.ax[1].steps ? fma((double)ky, r.ax[1].t_step, r.ax[1].t_first) : INFINITY;
+        } else {
+            ++kz;
+            nz = kz < r.ax[2].steps ? fma((double)kz, r.ax[2].t_step, r.ax[2].t_first) : INFINITY;
+        }
+    }
+    visit(off, (float)fmax(r.T - t, 0.0));
+}
+
 // ------------------------------------------------------------------------------------------
 // Column walk: the rows of one column share their xy line.
 //
