@@ -295,6 +295,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
     XYEvent* E = events[wave];
+    // the wave's first ray (uniform, held in scalar registers through the walk); a lane's ray
+    // adds its row
+    const int64_t ray0 = ((int64_t)t.view * A.rows + (t.row - lane)) * A.cols + t.col;
+    const uint32_t ray_lo = uniform((uint32_t)ray0), ray_hi = uniform((uint32_t)((uint64_t)ray0 >> 32));
     const Frame F = A.frames[t.view];
     ColumnWalk c;
     column_setup(F, A.box, A.beam, centred(t.col, A.cols, A.du), c);
@@ -461,7 +465,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
         }
     }
     if (t.valid) {
-        const int64_t ray = ((int64_t)t.view * A.rows + t.row) * A.cols + t.col;
+        const int64_t ray = (int64_t)(((uint64_t)ray_hi << 32) | ray_lo) + (int64_t)lane * A.cols;
 #pragma unroll
         for (int m = 0; m < NB; ++m) sino.p[m][ray] = acc[m] * r.kappa;
     }
