@@ -77,8 +77,8 @@ def measured_traffic(kernel: str):
 def issue_record(kernel: str, segments: int, kernel_ms: float):
     """Instruction issue of `kernel` from its SQ counters: VALU instructions per segment, the
     issue rate they give over the live launch time against one wave64 32-bit VALU
-    instruction per 2 cycles per SIMD, and the counters' own VALU-busy share of SIMD cycles;
-    None without counters for the current sources."""
+    instruction per 2 cycles per SIMD, the counters' own VALU-busy share of SIMD cycles and
+    LDS-busy share of CU cycles; None without counters for the current sources."""
     k = counter_record(SQ_FILE, "sq-json", kernel)
     if k is None:
         return None
@@ -91,6 +91,8 @@ def issue_record(kernel: str, segments: int, kernel_ms: float):
            "frac": rate / VALU_PEAK_PER_S, "valu_busy": float(k["valu_busy"])}
     if "fp64_insts" in k:
         out["fp64_share_of_valu"] = float(k["fp64_insts"]) / valu
+    if "lds_busy" in k:
+        out["lds_busy"] = float(k["lds_busy"])
     return out
 
 
@@ -392,6 +394,8 @@ def main() -> int:
         if iss is not None:
             result["config"][f"{k}_valu_insts_per_segment"] = iss["valu_insts_per_segment"]
             result["config"][f"{k}_valu_busy"] = iss["valu_busy"]
+            if "lds_busy" in iss:
+                result["config"][f"{k}_lds_busy"] = iss["lds_busy"]
     copy_gbs = copy_bandwidth(mbp, torch, dev)
     log(f"streaming copy: {copy_gbs:.0f} GB/s")
     result["config"]["hbm_copy_GBs"] = copy_gbs
