@@ -318,6 +318,31 @@ def test_parallel3d_parity(torch_dev, mbp, oracle):
             plan.close()
 
 
+def test_lattice_aligned_parity(torch_dev, mbp, oracle):
+    """Lines that meet two or three grid planes at once (exact ties between x, y and z
+    crossings; see lattice_parallel3d): column walk (counted z crossings, the general per-cell
+    form for the (1, 1, 1) lines) and generic walk, forward and adjoint, both layouts."""
+    from tests.test_hostcheck import lattice_parallel3d
+    torch, dev = torch_dev
+    geom, traj = lattice_parallel3d()
+    rng = np.random.default_rng(23)
+    x = rng.random(geom["shape"]).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    y = rng.random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    for layout in ("DHW", "WHD"):
+        plan = mbp.Plan("parallel3d", geom["shape"], geom["spacing"], traj, (geom["rows"], geom["cols"]),
+                        (geom["dv"], geom["du"]), layout=layout)
+        for path in ("column", "generic"):
+            plan.set_path(path)
+            say(f"case lattice-aligned lines layout={layout} path={path}")
+            p = plan.project(to_device_volume(torch, dev, x, layout)).cpu().numpy().astype(np.float64)
+            b = plan.backproject(torch.from_numpy(y).to(dev)).cpu().numpy().astype(np.float64)
+            check(p, ref, "forward")
+            check(b, bref, "adjoint")
+        plan.close()
+
+
 def test_general_trajectory_parity(torch_dev, mbp, oracle):
     """Random tilted frames (row axis not parallel to z), anisotropic grid: the generic walk
     forward; adjoint by the per-ray gather (rows that do not keep their cells in order along

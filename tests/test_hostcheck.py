@@ -31,6 +31,52 @@ def parallel3d_config():
                    layout="DHW", views=30, rows=80, cols=96, du=0.9, dv=1.1)
 
 
+def lattice_parallel3d():
+    """3-D parallel lines through the lattice of a unit grid whose faces lie on integers:
+    along (2, 0, 1) and (0, 2, -1) every other x (or y) plane is met exactly where a z plane
+    is (pixels at half-integer v); along (1, 1, 0) and (1, 1, 1) x and y planes are met
+    together (pixels at half-integer diagonal offsets, du = sqrt 2); (-2, 0, -1) runs the
+    first one backwards. Detector rows along z, so the column walk applies."""
+    import math
+    dirs = [(2.0, 0.0, 1.0), (-2.0, 0.0, -1.0), (0.0, 2.0, -1.0), (1.0, 1.0, 0.0), (1.0, 1.0, 1.0),
+            (2.0, 1.0, 0.5)]
+    src, det, eu, ev = [], [], [], []
+    for d in dirs:
+        h = math.hypot(d[0], d[1])
+        src.append(d)
+        det.append((0.0, 0.0, 0.0))
+        eu.append((-d[1] / h, d[0] / h, 0.0))
+        ev.append((0.0, 0.0, 1.0))
+    traj = {k: np.asarray(v, dtype=np.float64) for k, v in
+            (("src", src), ("det", det), ("eu", eu), ("ev", ev))}
+    geom = {"beam": "parallel3d", "shape": (16, 12, 20), "spacing": (1.0, 1.0, 1.0),
+            "views": len(dirs), "rows": 12, "cols": 16, "du": math.sqrt(2.0), "dv": 1.0}
+    return geom, traj
+
+
+def test_lattice_aligned_lines_reproduce_oracle(oracle):
+    """Lines that meet two or three planes at once (exact ties in the walks' crossing
+    distances): the forward kernel's chunked column walk with its counted z crossings, and
+    both walks' forward and adjoint, replayed on the host, against the oracle."""
+    geom, traj = lattice_parallel3d()
+    rng = np.random.default_rng(17)
+    x = rng.random(geom["shape"]).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    s, viol = HC.project_chunked(geom, traj, x)
+    assert viol == 0
+    assert np.linalg.norm(s - ref) / np.linalg.norm(ref) < 1e-6
+    assert np.abs(s - ref).max() / np.abs(ref).max() < 1e-5
+    y = rng.random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    for path in ("generic", "column"):
+        p_, _, viol = HC.project(path, geom, traj, x)
+        assert viol == 0
+        assert np.linalg.norm(p_ - ref) / np.linalg.norm(ref) < 1e-6
+        b_, viol = HC.backproject(path, geom, traj, y)
+        assert viol == 0
+        assert np.linalg.norm(b_ - bref) / np.linalg.norm(bref) < 1e-6
+
+
 def test_parallel3d_walks_reproduce_oracle(oracle):
     """Infinite parallel rays in 3-D through both walks (circular: column and generic;
     random directions with tilted detectors: generic), forward and adjoint, and the gather."""
