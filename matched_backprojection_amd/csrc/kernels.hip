@@ -257,6 +257,27 @@ __device__ __forceinline__ ColumnTask column_task(const ColumnLaunch& A) {
     return t;
 }
 
+// The forward's waves: a block takes 4 adjacent detector columns of one 64-row block and view
+// (row blocks fastest, then column quadruples, then views), so the waves running together on
+// one compute unit cross the same voxel columns at the same heights and share their cache
+// lines (against 4 row blocks of one column: c3 -5%, the 360-view 512^3 cone -3%, c4 and the
+// helical batch unchanged).
+__device__ __forceinline__ ColumnTask forward_task(const ColumnLaunch& A) {
+    ColumnTask t;
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
+    const uint32_t quads = ((uint32_t)A.cols + 3u) / 4u;
+    const uint32_t rb = blk % (uint32_t)A.row_blocks, rest = blk / (uint32_t)A.row_blocks;
+    const uint32_t cq = rest % quads, vl = rest / quads;
+    t.col = (int32_t)(cq * 4u + wave);
+    t.view = A.view0 + (int32_t)vl;
+    t.row = (int32_t)(rb * 64u + lane);
+    t.live = vl < (uint32_t)A.nviews && t.col < A.cols;
+    t.valid = t.live && t.row < A.rows;
+    return t;
+}
+
 // Sum over the wave of a lane value in {0, 1, 2}.
 __device__ __forceinline__ int32_t wave_sum012(int32_t v) {
     return (int32_t)(__popcll(__ballot(v & 1)) + 2 * __popcll(__ballot((v >> 1) & 1)));
@@ -290,7 +311,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
                                                              const float* __restrict__ vol,
                                                              const MPtrs4 sino) {
     __shared__ XYEvent events[4][kXYChunk];
-    const ColumnTask t = column_task(A);
+    const ColumnTask t = forward_task(A);
     if (!t.live) return;
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
@@ -1591,7 +1612,7 @@ hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol
     if (a.tasks == 0) return hipSuccess;
     MPtrs4 o{};
     for (int m = 0; m < nb; ++m) o.p[m] = sino[m];
-    const dim3 grid((a.tasks + 3) / 4);
+    const dim3 grid((unsigned)((int64_t)a.nviews * ((a.cols + 3) / 4) * a.row_blocks));
     const bool flat = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)a.box.n[2] * (uint64_t)nb *
                           sizeof(float) < (1ull << 31);
     trace_launch(flat ? "column_forward_kernel<flat>" : "column_forward_kernel<resource per cell>", grid,

@@ -43,6 +43,10 @@ def test_trace_prints_each_launch(capfd):
     assert "dhw_to_native_kernel" in kernels and "native_to_dhw_kernel" in kernels
     fwd = [m for m in parsed if m.group(1) == "column_forward_kernel<flat>"]
     assert "views 0..19" in fwd[0].group(7) and "views 20..35" in fwd[1].group(7)
+    # one block per (view, 4 adjacent columns, 64-row block), 4 waves each
+    quads, row_blocks = -(-cfg.cols // 4), -(-cfg.rows // 64)
+    assert [int(m.group(2)) for m in fwd] == [20 * quads * row_blocks, 16 * quads * row_blocks]
+    assert all(int(m.group(5)) == 256 for m in fwd)
     gat = [m for m in parsed if m.group(1) == "column_gather_kernel"]
     assert all(int(m.group(6)) > 0 and int(m.group(5)) == 256 for m in gat)
     # unset: silent
