@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 2
+#define MBP_ABI_VERSION 3
 
 typedef enum mbp_status {
     MBP_OK = 0,
@@ -134,6 +134,10 @@ typedef struct mbp_plan_info {
     int32_t last_forward_members_per_pass;  /* fewest members one column walk served (1, 2
                                   or 4; below members_per_pass when the interleaved copy was
                                   halved to fit the memory rule); 0 on the generic walk     */
+    int32_t orbit;             /* turn symmetry of the views found at plan creation (see
+                                  mbp_plan_set_orbit): 4 (quarter turn), 2 (half turn) or 1   */
+    int32_t last_adjoint_orbit; /* cells that shared each gather crossing in the last
+                                  mbp_backproject: the orbit, or 1 (0 before the first call) */
 } mbp_plan_info;
 
 /* Validate the geometry and trajectory and build a plan. Trajectory arrays are host fp64,
@@ -159,6 +163,21 @@ int mbp_plan_set_path(mbp_plan* plan, int32_t path);
 /* Choose the adjoint kernel (mbp_adjoint). All compute the same sums (the chord of every ray
    through every voxel times the ray's value); they differ in summation order. */
 int mbp_plan_set_adjoint(mbp_plan* plan, int32_t kind);
+
+/* Allow (1, the default) or forbid (0) the gather adjoint to share cell crossings over a turn
+   symmetry of the views. The adjoint sums, over every ray, the ray's value times its chord
+   through each voxel (the pair at the top of this header: page "diffct 2.1.0 -> 2.2.1",
+   README "Why diffct", bullet "Matched operators"). When the views fall
+   into P = 4 (or 2) groups of V / P such that view v + V / P is view v turned a quarter (half)
+   turn about the vertical axis through the volume's xy centre, and the grid maps onto itself
+   under that turn (W even; for a quarter turn also W == H and dx == dy), the chord of ray
+   (v + m V / P, column, row) through a cell equals that of ray (v, column, row) through the
+   cell turned back m steps: one crossing then serves P cells, and the gather forms crossings
+   for the first V / P views only. Taken only for one member with all views in one launch (a
+   (D,H,W) or WHD volume, batch 1, workspace holding every view). Frames are compared to
+   1e-12 of their extent, so the sums equal the unshared ones to fp32 rounding. Plan setting
+   only: no device call. */
+int mbp_plan_set_orbit(mbp_plan* plan, int32_t enable);
 
 /* Limit the views of one kernel launch (0 = automatic: as many as index and grid limits
    allow). Results do not depend on it (page "diffct 2.1.0 -> 2.2.1", CHANGELOG 2.2.0,

@@ -134,7 +134,8 @@ class Plan:
                 "last_adjoint_walk": _capi.PATH_NAMES[inf.last_adjoint_walk] if inf.last_adjoint else None,
                 "last_adjoint_views_per_launch": inf.last_adjoint_views_per_launch,
                 "last_forward_walk": _capi.PATH_NAMES[inf.last_forward_walk] if inf.last_forward_walk else None,
-                "last_forward_members_per_pass": inf.last_forward_members_per_pass}
+                "last_forward_members_per_pass": inf.last_forward_members_per_pass,
+                "orbit": inf.orbit, "last_adjoint_orbit": inf.last_adjoint_orbit}
 
     def set_path(self, path: str) -> None:
         _capi.check(self._lib.mbp_plan_set_path(self._handle, _capi.PATHS[path]), "mbp_plan_set_path")
@@ -142,6 +143,11 @@ class Plan:
     def set_adjoint(self, kind: str) -> None:
         """Adjoint kernel of the column walk: "gather" (default), "scatter" or "auto"."""
         _capi.check(self._lib.mbp_plan_set_adjoint(self._handle, _capi.ADJOINTS[kind]), "mbp_plan_set_adjoint")
+
+    def set_orbit(self, enable: bool) -> None:
+        """Whether the gather adjoint may share cell crossings over a turn symmetry of the
+        views (on by default; info["orbit"] is the symmetry found)."""
+        _capi.check(self._lib.mbp_plan_set_orbit(self._handle, 1 if enable else 0), "mbp_plan_set_orbit")
 
     def set_view_batch(self, views: int) -> None:
         _capi.check(self._lib.mbp_plan_set_view_batch(self._handle, int(views)), "mbp_plan_set_view_batch")

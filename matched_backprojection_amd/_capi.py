@@ -35,7 +35,7 @@ ADJOINT_NAMES = {0: None, 1: "gather", 2: "scatter"}
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = (
     "mbp_plan_create", "mbp_plan_destroy", "mbp_plan_get_info", "mbp_plan_set_path",
-    "mbp_plan_set_view_batch", "mbp_plan_set_adjoint", "mbp_project", "mbp_backproject", "mbp_segment_count",
+    "mbp_plan_set_view_batch", "mbp_plan_set_adjoint", "mbp_plan_set_orbit", "mbp_project", "mbp_backproject", "mbp_segment_count",
     "mbp_workspace_size", "mbp_set_workspace", "mbp_convert_layout", "mbp_normal",
     "mbp_cgls_workspace_size", "mbp_cgls", "mbp_status_string", "mbp_last_error",
     "mbp_abi_version", "mbp_stream_copy", "mbp_backproject_noalloc",
@@ -61,6 +61,7 @@ class PlanInfo(ctypes.Structure):
         ("last_adjoint", ctypes.c_int32), ("last_adjoint_walk", ctypes.c_int32),
         ("last_adjoint_views_per_launch", ctypes.c_int64),
         ("last_forward_walk", ctypes.c_int32), ("last_forward_members_per_pass", ctypes.c_int32),
+        ("orbit", ctypes.c_int32), ("last_adjoint_orbit", ctypes.c_int32),
     ]
 
 
@@ -97,6 +98,7 @@ def load():
     lib.mbp_plan_set_path.argtypes = [P, I32]
     lib.mbp_plan_set_view_batch.argtypes = [P, I64]
     lib.mbp_plan_set_adjoint.argtypes = [P, I32]
+    lib.mbp_plan_set_orbit.argtypes = [P, I32]
     lib.mbp_project.argtypes = [P, P, I64, P, P]
     lib.mbp_backproject.argtypes = [P, P, I64, P, I32, P]
     lib.mbp_backproject_noalloc.argtypes = [P, P, I64, P, I32, P]

@@ -265,11 +265,14 @@ int mbph_backproject(int path, const double* frames, int beam, const double* lo,
 // (rows of a lane relative to the lane's origin cell, shares in fp32 when `kernel_shares`,
 // else in fp64 from the same integers) and in the fp64 general form otherwise; `general_only`
 // takes every item in the general form. Sums in fp64. *violations counts pieces out of range
-// and fast-form positions outside the fixed point's range; *fast counts fast items.
+// and fast-form positions outside the fixed point's range; *fast counts fast items. orbit > 1
+// (2 or 4, with the quarter turn's sense dir): items are formed as the kernel shares them over
+// a turn symmetry of the views (orbit_cell), for the first views / orbit views only, each
+// carrying the rows of the views q apart into the orbit's other cells.
 int mbph_gather(const double* frames, int beam, const double* lo, const double* pitch,
                 const int32_t* n, int views, int rows, int cols, double du, double dv,
                 const float* sino, int kernel_shares, int general_only, double* vol,
-                long long* violations, long long* fast) {
+                long long* violations, long long* fast, int orbit, int dir) {
     std::vector<Frame> F;
     frames_from(frames, views, F);
     const Box B = box_from(lo, pitch, n);
@@ -281,16 +284,24 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
     const bool line = beam == BEAM_PARALLEL;
     const int32_t S = gather_stride(rows), rows_pad = gather_rows_padded(rows), D = n[2];
     std::vector<double> w(rows_pad);
-    for (int ix = 0; ix < n[0]; ++ix) {
-        for (int iy = 0; iy < n[1]; ++iy) {
-            const double x0 = B.lo[0] + ix * B.pitch[0], x1 = x0 + B.pitch[0];
-            const double y0 = B.lo[1] + iy * B.pitch[1], y1 = y0 + B.pitch[1];
-            double* colv = vol;
+    // with an orbit (orbit_cell), the cells that stand for the orbits, each slot's cell in
+    // turn, over the first q views; line (v + m q, j) then goes to slot (a + m) mod orbit
+    int32_t Wr, Hr;
+    orbit_grid(orbit, n[0], n[1], Wr, Hr);
+    const int q = views / orbit;
+    for (int ix = 0; ix < Wr; ++ix) {
+        for (int iy = 0; iy < Hr; ++iy) {
+          for (int a = 0; a < orbit; ++a) {
+            int32_t cx, cy;
+            orbit_cell(orbit, dir, n[0], n[1], ix, iy, a, cx, cy);
+            const double x0 = B.lo[0] + cx * B.pitch[0], x1 = x0 + B.pitch[0];
+            const double y0 = B.lo[1] + cy * B.pitch[1], y1 = y0 + B.pitch[1];
+            int32_t tx = cx, ty = cy;     // the cell the current line's rows go to
             auto add = [&](int32_t iz, double share, double wk) {
                 if (iz < 0 || iz >= D || !(share >= 0.0)) { ++*violations; return; }
-                colv[((int64_t)iz * n[1] + iy) * n[0] + ix] += share * wk;
+                vol[((int64_t)iz * n[1] + ty) * n[0] + tx] += share * wk;
             };
-            for (int v = 0; v < views; ++v) {
+            for (int v = 0; v < q; ++v) {
                 int32_t j0, j1;
                 if (!cell_column_range(F[v], beam, cols, du, x0, x1, y0, y1, j0, j1)) continue;
                 if (j0 < 0 || j1 >= cols) ++*violations;
@@ -299,80 +310,85 @@ int mbph_gather(const double* frames, int beam, const double* lo, const double* 
                     if (!gather_item(lines[(size_t)v * cols + j], line, x0, x1, y0, y1, S, rows,
                                      rows_pad, v * cols + j, it))
                         continue;
-                    // the reordered sinogram line: values times the ray length, zero padded
-                    for (int k = 0; k < rows_pad; ++k) {
-                        if (k >= rows) { w[k] = 0.0; continue; }
-                        double len;
-                        if (line) {
-                            len = std::sqrt(F[v].s[0] * F[v].s[0] + F[v].s[1] * F[v].s[1] + F[v].s[2] * F[v].s[2]);
-                        } else {
-                            double p[3];
-                            pixel_point(F[v], centred(j, cols, du), centred(k, rows, dv), p);
-                            const double a = p[0] - F[v].s[0], b = p[1] - F[v].s[1], c = p[2] - F[v].s[2];
-                            len = std::sqrt(a * a + b * b + c * c);
-                        }
-                        w[k] = (double)sino[((int64_t)v * rows + k) * cols + j] * len;
-                    }
-                    // the kernel carries the crossing length in fp32; the fp64 replay takes it
-                    // from the clip again, and so the general form's positions (a fast item
-                    // holds them in fixed point)
-                    const ColLine& L = lines[(size_t)v * cols + j];
-                    double t0, t1;
-                    cell_clip(L, line, x0, x1, y0, y1, t0, t1);
-                    const double dt = kernel_shares ? (double)it.dt : t1 - t0;
-                    const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
-                    const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
-                    if (it.form > 0 && !general_only) {
-                        ++*fast;
-                        for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S)
-                            for (int lane = 0; lane < 64; ++lane) {
-                                const int32_t k0 = g0 + S * lane;
-                                const int32_t c0 = fast_origin_row(S);
-                                uint32_t la, lb;
-                                int32_t base;
-                                fast_origin(it, k0 + c0, -1, la, lb, base);
-                                for (int32_t c = 0; c < S; ++c) {
-                                    // the row's ends must stay inside the fixed point's range
-                                    const int64_t pa = (int64_t)la + (int64_t)(c - c0) * it.a1fx;
-                                    const int64_t pb = (int64_t)lb + (int64_t)(c - c0) * it.b1fx;
-                                    if (pa < 0 || pa > (int64_t)UINT32_MAX || pb < 0 || pb > (int64_t)UINT32_MAX)
-                                        ++*violations;
-                                    int32_t fb;
-                                    uint32_t num, ext;
-                                    fast_row((uint32_t)pa, (uint32_t)pb, fb, num, ext);
-                                    // both shares from integers: the lower cell's num / ext and
-                                    // the upper one's (ext - num) / ext
-                                    double f = 1.0, g = 0.0;
-                                    if (num < ext) {
-                                        if (kernel_shares) {
-                                            const float r = 1.0f / (float)ext;
-                                            f = (double)((float)num * r);
-                                            g = (double)((float)(ext - num) * r);
-                                        } else {
-                                            f = (double)num / (double)ext;
-                                            g = (double)(ext - num) / (double)ext;
-                                        }
-                                    }
-                                    const int32_t i0 = base + fb;
-                                    if ((uint32_t)i0 > (uint32_t)D) continue;     // outside: discarded
-                                    const int32_t z = i0 - 1;                      // cell of index i0
-                                    const double wk = w[k0 + c];
-                                    if (z >= 0) add(z, f * dt, wk);
-                                    if (z + 1 < D) add(z + 1, g * dt, wk);
-                                }
+                    for (int m = 0; m < orbit; ++m) {
+                        const int vw = v + m * q;
+                        orbit_cell(orbit, dir, n[0], n[1], ix, iy, (a + m) % orbit, tx, ty);
+                        // the reordered sinogram line: values times the ray length, zero padded
+                        for (int k = 0; k < rows_pad; ++k) {
+                            if (k >= rows) { w[k] = 0.0; continue; }
+                            double len;
+                            if (line) {
+                                len = std::sqrt(F[vw].s[0] * F[vw].s[0] + F[vw].s[1] * F[vw].s[1] + F[vw].s[2] * F[vw].s[2]);
+                            } else {
+                                double p[3];
+                                pixel_point(F[vw], centred(j, cols, du), centred(k, rows, dv), p);
+                                const double ex = p[0] - F[vw].s[0], ey = p[1] - F[vw].s[1], ez = p[2] - F[vw].s[2];
+                                len = std::sqrt(ex * ex + ey * ey + ez * ez);
                             }
-                        continue;
-                    }
-                    for (int k = 0; k < rows; ++k) {
-                        auto piece = [&](int32_t iz, double share) { add(iz, share, w[k]); };
-                        const double za = std::fma((double)k, za1, za0);
-                        const double zb = std::fma((double)k, zb1, zb0);
-                        const double fa = std::floor(std::fmin(za, zb)), fb = std::floor(std::fmax(za, zb));
-                        if (fa == fb && fa >= 0.0 && fa < (double)D) piece((int32_t)fa, dt);
-                        else row_pieces_split(za, zb, dt, 0, D, false, piece);
+                            w[k] = (double)sino[((int64_t)vw * rows + k) * cols + j] * len;
+                        }
+                        // the kernel carries the crossing length in fp32; the fp64 replay takes it
+                        // from the clip again, and so the general form's positions (a fast item
+                        // holds them in fixed point)
+                        const ColLine& L = lines[(size_t)v * cols + j];
+                        double t0, t1;
+                        cell_clip(L, line, x0, x1, y0, y1, t0, t1);
+                        const double dt = kernel_shares ? (double)it.dt : t1 - t0;
+                        const double za0 = L.c0 + t0 * L.c1, za1 = L.c2 + t0 * L.c3;
+                        const double zb0 = L.c0 + t1 * L.c1, zb1 = L.c2 + t1 * L.c3;
+                        if (it.form > 0 && !general_only) {
+                            if (m == 0) ++*fast;
+                            for (int32_t g0 = 0; g0 < rows_pad; g0 += 64 * S)
+                                for (int lane = 0; lane < 64; ++lane) {
+                                    const int32_t k0 = g0 + S * lane;
+                                    const int32_t c0 = fast_origin_row(S);
+                                    uint32_t la, lb;
+                                    int32_t base;
+                                    fast_origin(it, k0 + c0, -1, la, lb, base);
+                                    for (int32_t c = 0; c < S; ++c) {
+                                        // the row's ends must stay inside the fixed point's range
+                                        const int64_t pa = (int64_t)la + (int64_t)(c - c0) * it.a1fx;
+                                        const int64_t pb = (int64_t)lb + (int64_t)(c - c0) * it.b1fx;
+                                        if (pa < 0 || pa > (int64_t)UINT32_MAX || pb < 0 || pb > (int64_t)UINT32_MAX)
+                                            ++*violations;
+                                        int32_t fb;
+                                        uint32_t num, ext;
+                                        fast_row((uint32_t)pa, (uint32_t)pb, fb, num, ext);
+                                        // both shares from integers: the lower cell's num / ext and
+                                        // the upper one's (ext - num) / ext
+                                        double f = 1.0, g = 0.0;
+                                        if (num < ext) {
+                                            if (kernel_shares) {
+                                                const float r = 1.0f / (float)ext;
+                                                f = (double)((float)num * r);
+                                                g = (double)((float)(ext - num) * r);
+                                            } else {
+                                                f = (double)num / (double)ext;
+                                                g = (double)(ext - num) / (double)ext;
+                                            }
+                                        }
+                                        const int32_t i0 = base + fb;
+                                        if ((uint32_t)i0 > (uint32_t)D) continue;     // outside: discarded
+                                        const int32_t z = i0 - 1;                      // cell of index i0
+                                        const double wk = w[k0 + c];
+                                        if (z >= 0) add(z, f * dt, wk);
+                                        if (z + 1 < D) add(z + 1, g * dt, wk);
+                                    }
+                                }
+                            continue;
+                        }
+                        for (int k = 0; k < rows; ++k) {
+                            auto piece = [&](int32_t iz, double share) { add(iz, share, w[k]); };
+                            const double za = std::fma((double)k, za1, za0);
+                            const double zb = std::fma((double)k, zb1, zb0);
+                            const double fa = std::floor(std::fmin(za, zb)), fb = std::floor(std::fmax(za, zb));
+                            if (fa == fb && fa >= 0.0 && fa < (double)D) piece((int32_t)fa, dt);
+                            else row_pieces_split(za, zb, dt, 0, D, false, piece);
+                        }
                     }
                 }
             }
+          }
         }
     }
     return 0;

@@ -26,6 +26,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 #include "mbp_internal.h"
 
@@ -559,9 +560,13 @@ __global__ void __launch_bounds__(256) column_count_kernel(const ColumnLaunch A,
 // [view][col][row] order (rows contiguous, so a wave's 64 lanes load 256 contiguous bytes),
 // already multiplied by |d_k|, the ray's length per unit of alpha.
 
+// mview: views between consecutive members (0: the members are volumes of a batch and share
+// the view; q: member m is view view + m q of one sinogram, for the gather shared over a turn
+// symmetry), which also fixes each member's ray lengths.
 template <int NB>
 __global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A, const Ptrs4 sino,
-                                                           int32_t rows_pad, float* __restrict__ ysc) {
+                                                           int32_t rows_pad, int32_t mview,
+                                                           float* __restrict__ ysc) {
     __shared__ float tile[NB][32][33];
     const int32_t j0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int32_t view = A.view0 + (int32_t)blockIdx.z;
@@ -576,24 +581,24 @@ __global__ void __launch_bounds__(256) sino_prepass_kernel(const ColumnLaunch A,
                                           ? sino.p[m][vbase + (int64_t)k * A.cols + j] : 0.0f;
     }
     __syncthreads();
-    const Frame F = A.frames[view];
+    auto ray_len = [&](const Frame& F, int32_t j, int32_t k) {
+        if (A.beam == BEAM_PARALLEL) return sqrt(F.s[0] * F.s[0] + F.s[1] * F.s[1] + F.s[2] * F.s[2]);
+        double p[3];
+        pixel_point(F, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), p);
+        const double dx = p[0] - F.s[0], dy = p[1] - F.s[1], dz = p[2] - F.s[2];
+        return sqrt(dx * dx + dy * dy + dz * dz);
+    };
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int32_t j = j0 + ty + 8 * i, k = k0 + tx;
         if (k < rows_pad && j < A.cols) {
-            double len;
-            if (A.beam == BEAM_PARALLEL) {
-                len = sqrt(F.s[0] * F.s[0] + F.s[1] * F.s[1] + F.s[2] * F.s[2]);
-            } else {
-                double p[3];
-                pixel_point(F, centred(j, A.cols, A.du), centred(k, A.rows, A.dv), p);
-                const double dx = p[0] - F.s[0], dy = p[1] - F.s[1], dz = p[2] - F.s[2];
-                len = sqrt(dx * dx + dy * dy + dz * dz);
-            }
-            const float scale = (float)len;
             const int64_t o = (((int64_t)blockIdx.z * A.cols + j) * rows_pad + k) * NB;
+            float scale = (float)ray_len(A.frames[view], j, k);
 #pragma unroll
-            for (int m = 0; m < NB; ++m) ysc[o + m] = tile[m][tx][ty + 8 * i] * scale;
+            for (int m = 0; m < NB; ++m) {
+                if (m > 0 && mview != 0) scale = (float)ray_len(A.frames[view + m * mview], j, k);
+                ysc[o + m] = tile[m][tx][ty + 8 * i] * scale;
+            }
         }
     }
 }
@@ -778,8 +783,10 @@ __device__ __forceinline__ void gather_runs_add(lds_float* dst, lds_float* park,
 // write. RUNS (kFastRuns): lanes that share a pair are combined first (gather_runs_add); lanes
 // S * G rows apart never share one. FULL: the lane takes all KR loaded rows (S == KR), so the
 // unrolled rows need no guard. CLAMP: some row may leave the chunk's pair indices (the item is
-// not kFastInside), so every pair index is clamped.
-template <int NB, int KR, bool FULL, bool RUNS, bool CLAMP>
+// not kFastInside), so every pair index is clamped. SH: the cell slots take the loaded members
+// turned by SH places (slot m adds member (m - SH) mod NB: the gather shared over a turn
+// symmetry, where the members are the lines of the views the turn relates).
+template <int NB, int KR, bool FULL, bool RUNS, bool CLAMP, int SH = 0>
 __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t a1, int32_t b1,
                                                   float dt, const float (&w)[KR][NB],
                                                   int32_t k0, int32_t S, int32_t z0, int32_t n,
@@ -844,7 +851,7 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         float qa[NB], qb[NB];
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
-            const float q = dt * w[c][m];
+            const float q = dt * w[c][(m + NB - SH) % NB];
             qa[m] = f * q;
             qb[m] = g * q;
         }
@@ -877,7 +884,7 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
 
 // General form of one item for one group of rows: rows of any z extent, pieces walked in
 // fp64; plain LDS read-add-write when the item's lanes add exclusively, else LDS atomics.
-template <int NB, int KR>
+template <int NB, int KR, int SH = 0>
 __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool exclusive,
                                                      const float (&w)[KR][NB], int32_t k0,
                                                      int32_t S, int32_t z0, int32_t z1,
@@ -897,6 +904,9 @@ __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool 
 #pragma unroll
     for (int c = 0; c < KR; ++c) {
         if (c >= S) continue;
+        float wr[NB];      // the members in slot order (turned by SH, as in gather_fast_group)
+#pragma unroll
+        for (int m = 0; m < NB; ++m) wr[m] = w[c][(m + NB - SH) % NB];
         const double kd = (double)(k0 + c);
         const double za = fma(kd, it.za1, it.za0);
         const double zb = fma(kd, it.zb1, it.zb0);
@@ -908,10 +918,10 @@ __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool 
             const float f = fa == fb ? 1.0f
                 : (float)(fa + 1.0 - zmin) * __builtin_amdgcn_rcpf((float)ext);
             const float p1 = f * fdt, p2 = fdt - p1;
-            if (fa >= (double)z0 && fa < (double)z1) add((int32_t)fa, p1, w[c]);
-            if (fb != fa && fb >= (double)z0 && fb < (double)z1) add((int32_t)fb, p2, w[c]);
+            if (fa >= (double)z0 && fa < (double)z1) add((int32_t)fa, p1, wr);
+            if (fb != fa && fb >= (double)z0 && fb < (double)z1) add((int32_t)fb, p2, wr);
         } else {
-            auto piece = [&](int32_t iz, double share) { add(iz, (float)share, w[c]); };
+            auto piece = [&](int32_t iz, double share) { add(iz, (float)share, wr); };
             row_pieces_split(za, zb, dt, z0, z1, exclusive, piece);
         }
     }
@@ -919,21 +929,30 @@ __device__ __forceinline__ void gather_general_group(const GatherItem& it, bool 
 
 // Occupancy: four waves per SIMD (at most 128 vector registers) for one member, three (168)
 // for two and four.
-template <int NB, int KR>
+//
+// P > 1: the gather shared over a turn symmetry of the views (orbit_cell). The launch's views
+// are the first q = nviews / P; NB == P and member m of the reordered sinogram is the line of
+// view v + m q. A wave owns the P cells of one orbit, held as the NB slots of its column (slot
+// a: cell R^a of the orbit's cell in the grid orbit_grid gives), and the item of slot a's cell
+// adds member m to slot (a + m) mod P; the volume written has one member.
+template <int NB, int KR, int P>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 3)))
 column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                      const float* __restrict__ ysc, float* __restrict__ vol, int32_t zchunk,
-                     int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate) {
+                     int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate, int32_t dir) {
+    static_assert(P == 1 || P == NB, "an orbit takes one member per slot");
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
     const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
     const uint32_t task = blk * 4u + wave;
     const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
+    int32_t Wr, Hr;
+    orbit_grid(P, W, H, Wr, Hr);
     const int32_t zc = (int32_t)(task % (uint32_t)nchunks);
-    const bool live = task < (uint32_t)W * (uint32_t)H * (uint32_t)nchunks;
+    const bool live = task < (uint32_t)Wr * (uint32_t)Hr * (uint32_t)nchunks;
     int32_t ix, iy;
-    gather_tile_cell(task / (uint32_t)nchunks, H, tx, ty, ix, iy);
+    gather_tile_cell(task / (uint32_t)nchunks, Hr, tx, ty, ix, iy);
     const int32_t z0 = zc * zchunk;
     const int32_t z1 = live ? (z0 + zchunk < D ? z0 + zchunk : D) : z0;
     const int32_t n = z1 - z0;
@@ -944,12 +963,10 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
     for (int32_t i = lane; i < colf; i += 64) cols[i] = 0.0f;
     __syncthreads();
     if (live) {
-        const double x0 = A.box.lo[0] + ix * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
-        const double y0 = A.box.lo[1] + iy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
         const bool line = A.beam == BEAM_PARALLEL;
         const int32_t S = gather_stride(A.rows);
         const int32_t rows_pad = gather_rows_padded(A.rows);
-        const int32_t vend = A.view0 + A.nviews;
+        const int32_t vend = A.view0 + A.nviews / P;
 
         // Units of work: (item, row group) in queue order, counted without divisions. The rows
         // of the next unit are loaded while the current one is summed.
@@ -967,7 +984,10 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
             const int32_t yoff = (int32_t)uniform((uint32_t)Q[i].yoff);
             return ysc + ((int64_t)yoff * rows_pad + gi * 64 * S + lane_row) * NB;
         };
-        auto drain = [&](int32_t count) {
+        // The queue's items all belong to one cell of the orbit (slot SH = decltype(shift)):
+        // their rows go to the slots turned by SH places.
+        auto drain = [&](auto shift, int32_t count) __attribute__((always_inline)) {
+            constexpr int SH = decltype(shift)::value;
             if (count == 0) return;
             float wa[KR][NB], wb[KR][NB];
             gather_load_rows<NB, KR>(unit_rows(0, 0), wa);
@@ -985,31 +1005,33 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                 const int32_t k0 = gi * 64 * S + lane_row;
                 const GatherItem it = Q[i];
                 const int32_t form = (int32_t)uniform((uint32_t)it.form);
-                if (form > 0) {
-                    const float dt = __uint_as_float(uniform(__float_as_uint(it.dt)));
-                    const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
-                    const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
-                    // items whose rows all stay inside the chunk skip the clamp (full groups of
-                    // several rows per lane only)
-                    const bool inside = kUnclamped && (form & kFastInside) != 0;
-                    if ((form & ~kFastInside) == kFastPairs) {
-                        if (S == KR && inside)
-                            gather_fast_group<NB, KR, true, false, false>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
-                        else if (S == KR)
-                            gather_fast_group<NB, KR, true, false, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
-                        else
-                            gather_fast_group<NB, KR, false, false, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
+                {
+                    if (form > 0) {
+                        const float dt = __uint_as_float(uniform(__float_as_uint(it.dt)));
+                        const int32_t a1 = (int32_t)uniform((uint32_t)it.a1fx);
+                        const int32_t b1 = (int32_t)uniform((uint32_t)it.b1fx);
+                        // items whose rows all stay inside the chunk skip the clamp (full groups
+                        // of several rows per lane only)
+                        const bool inside = kUnclamped && (form & kFastInside) != 0;
+                        if ((form & ~kFastInside) == kFastPairs) {
+                            if (S == KR && inside)
+                                gather_fast_group<NB, KR, true, false, false, SH>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
+                            else if (S == KR)
+                                gather_fast_group<NB, KR, true, false, true, SH>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
+                            else
+                                gather_fast_group<NB, KR, false, false, true, SH>(it, a1, b1, dt, cur, k0, S, z0, n, col, 1);
+                        } else {
+                            const int32_t G = (int32_t)uniform((uint32_t)it.run);
+                            if (S == KR && inside)
+                                gather_fast_group<NB, KR, true, true, false, SH>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
+                            else if (S == KR)
+                                gather_fast_group<NB, KR, true, true, true, SH>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
+                            else
+                                gather_fast_group<NB, KR, false, true, true, SH>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
+                        }
                     } else {
-                        const int32_t G = (int32_t)uniform((uint32_t)it.run);
-                        if (S == KR && inside)
-                            gather_fast_group<NB, KR, true, true, false>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
-                        else if (S == KR)
-                            gather_fast_group<NB, KR, true, true, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
-                        else
-                            gather_fast_group<NB, KR, false, true, true>(it, a1, b1, dt, cur, k0, S, z0, n, col, G);
+                        gather_general_group<NB, KR, SH>(it, form == kGeneralExclusive, cur, k0, S, z0, z1, col);
                     }
-                } else {
-                    gather_general_group<NB, KR>(it, form == kGeneralExclusive, cur, k0, S, z0, z1, col);
                 }
                 i = ni;
                 gi = ngi;
@@ -1036,50 +1058,85 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
         // candidate columns, lane r of a view taking candidates j0 + r, j0 + r + kViewLanes, ...;
         // the crossings found are appended to the queue in lane order. A round spans few
         // views, so the sinogram lines the concurrently running waves of a tile read stay few
-        // enough to share L2.
+        // enough to share L2. With an orbit, the slots' cells take their turns, each over the
+        // launch's views, and the queue is drained at the end of each turn, so that one drain
+        // sees items of one slot only.
         int32_t count = 0;
-        for (int32_t vb = A.view0; vb < vend; vb += 64 / kViewLanes) {
-            const int32_t view = vb + lane / kViewLanes;
-            int32_t jn = 0, j1 = -1;
-            if (view < vend &&
-                !cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, jn, j1)) {
-                jn = 0;
-                j1 = -1;
-            }
-            if (view >= vend) j1 = -1;
-            jn += lane % kViewLanes;
-            while (__ballot(jn <= j1) != 0) {
-                GatherItem it;
-                bool hit = false;
-                if (jn <= j1) {
-                    const int32_t yoff = (view - A.view0) * A.cols + jn;
-                    hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff, it,
-                                      in_lo, in_hi);
-                    jn += kViewLanes;
-                }
-                const uint64_t m = __ballot(hit);
-                if (hit) {
-                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    Q[count + (int32_t)below] = it;
-                }
-                count += (int32_t)__popcll(m);
-                if (count > kQueue - 64) {
-                    wave_lds_sync();
-                    drain(count);
-                    count = 0;
-                    wave_lds_sync();
+        auto flush = [&](int32_t a) __attribute__((always_inline)) {
+            if constexpr (P == 1) {
+                drain(std::integral_constant<int, 0>{}, count);
+            } else {
+                if (a == 0) drain(std::integral_constant<int, 0>{}, count);
+                else if (a == 1) drain(std::integral_constant<int, 1>{}, count);
+                else if constexpr (P == 4) {
+                    if (a == 2) drain(std::integral_constant<int, 2>{}, count);
+                    else drain(std::integral_constant<int, 3>{}, count);
                 }
             }
+            count = 0;
+        };
+        for (int32_t a = 0; a < P; ++a) {
+            int32_t cx, cy;
+            orbit_cell(P, dir, W, H, ix, iy, a, cx, cy);
+            const double x0 = A.box.lo[0] + cx * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
+            const double y0 = A.box.lo[1] + cy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
+            for (int32_t vb = A.view0; vb < vend; vb += 64 / kViewLanes) {
+                const int32_t view = vb + lane / kViewLanes;
+                int32_t jn = 0, j1 = -1;
+                if (view < vend &&
+                    !cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, jn, j1)) {
+                    jn = 0;
+                    j1 = -1;
+                }
+                if (view >= vend) j1 = -1;
+                jn += lane % kViewLanes;
+                while (__ballot(jn <= j1) != 0) {
+                    GatherItem it;
+                    bool hit = false;
+                    if (jn <= j1) {
+                        const int32_t yoff = (view - A.view0) * A.cols + jn;
+                        hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff,
+                                          it, in_lo, in_hi);
+                        jn += kViewLanes;
+                    }
+                    const uint64_t m = __ballot(hit);
+                    if (hit) {
+                        const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        Q[count + (int32_t)below] = it;
+                    }
+                    count += (int32_t)__popcll(m);
+                    if (count > kQueue - 64) {
+                        wave_lds_sync();
+                        flush(a);
+                        wave_lds_sync();
+                    }
+                }
+            }
+            wave_lds_sync();
+            flush(a);
+            wave_lds_sync();
         }
-        wave_lds_sync();
-        drain(count);
     }
     __syncthreads();
     if (live) {
-        const int64_t base = (((int64_t)ix * H + iy) * D + z0) * NB;
-        for (int32_t i = lane; i < n * NB; i += 64)
-            vol[base + i] = accumulate ? vol[base + i] + col[NB + i] : col[NB + i];
+        if constexpr (P == 1) {
+            const int64_t base = (((int64_t)ix * H + iy) * D + z0) * NB;
+            for (int32_t i = lane; i < n * NB; i += 64)
+                vol[base + i] = accumulate ? vol[base + i] + col[NB + i] : col[NB + i];
+        } else {
+            // slot a of z cell i is col[NB (i + 1) + a]; each slot's cell gets its own column
+#pragma unroll
+            for (int32_t a = 0; a < P; ++a) {
+                int32_t cx, cy;
+                orbit_cell(P, dir, W, H, ix, iy, a, cx, cy);
+                const int64_t base = ((int64_t)cx * H + cy) * D + z0;
+                for (int32_t i = lane; i < n; i += 64) {
+                    const float v = col[NB * (i + 1) + a];
+                    vol[base + i] = accumulate ? vol[base + i] + v : v;
+                }
+            }
+        }
     }
 }
 
@@ -1662,7 +1719,7 @@ hipError_t launch_column_count(const ColumnLaunch& a, unsigned long long* count,
 }
 
 hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const* sino, float* ysc,
-                               hipStream_t s) {
+                               hipStream_t s, int32_t mview) {
     if (a.nviews == 0) return hipSuccess;
     Ptrs4 y{};
     for (int m = 0; m < nb; ++m) y.p[m] = sino[m];
@@ -1673,12 +1730,13 @@ hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const
         b.nviews = a.nviews - v0 < 65535 ? a.nviews - v0 : 65535;
         const dim3 grid((a.cols + 31) / 32, (rows_pad + 31) / 32, b.nviews);
         float* const out = ysc + (int64_t)v0 * a.cols * rows_pad * nb;
-        trace_launch("sino_prepass_kernel", grid, dim3(256), 0, "views %d..%d members %d rows padded %d",
-                     b.view0, b.view0 + b.nviews - 1, nb, rows_pad);
+        trace_launch("sino_prepass_kernel", grid, dim3(256), 0,
+                     "views %d..%d members %d rows padded %d member views apart %d",
+                     b.view0, b.view0 + b.nviews - 1, nb, rows_pad, mview);
         switch (nb) {
-            case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
-            case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
-            case 4: sino_prepass_kernel<4><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, out); break;
+            case 1: sino_prepass_kernel<1><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, mview, out); break;
+            case 2: sino_prepass_kernel<2><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, mview, out); break;
+            case 4: sino_prepass_kernel<4><<<grid, dim3(256), 0, s>>>(b, y, rows_pad, mview, out); break;
             default: return hipErrorInvalidValue;
         }
     }
@@ -1701,30 +1759,40 @@ hipError_t launch_column_lines(const ColumnLaunch& a, int32_t views, ColLine* li
 }
 
 hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* lines, const float* ysc,
-                                float* vol, int accumulate, hipStream_t s) {
-    const int32_t D = a.box.n[2];
-    const int32_t zchunk = gather_zchunk(D, nb);
+                                float* vol, int accumulate, hipStream_t s, int orbit, int dir) {
+    const int32_t W = a.box.n[0], H = a.box.n[1], D = a.box.n[2];
+    // an orbit's slots take the place of members: one member, orbit slots per cell
+    if (orbit != 1 && (nb != 1 || (orbit != 2 && orbit != 4) || W % 2 != 0 ||
+                       (orbit == 4 && H != W) || a.nviews % orbit != 0))
+        return hipErrorInvalidValue;
+    const int slots = orbit > 1 ? orbit : nb;
+    const int32_t zchunk = gather_zchunk(D, slots);
     const int32_t nchunks = (D + zchunk - 1) / zchunk;
-    const uint64_t tasks = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)nchunks;
+    int32_t Wr, Hr;
+    orbit_grid(orbit, W, H, Wr, Hr);
+    const uint64_t tasks = (uint64_t)Wr * (uint64_t)Hr * (uint64_t)nchunks;
     // tiles of 64 x 8 cells (measured against 16 x 32, 32 x 16, 32 x 32, 64 x 16 and 16 x 64:
-    // 2.5% faster than 16 x 32 on the 512^3 cone), else 16 x 32, else plain y-fastest order
-    const bool wide = a.box.n[0] % 64 == 0 && a.box.n[1] % 8 == 0;
-    const bool tiled = wide || (a.box.n[0] % 16 == 0 && a.box.n[1] % 32 == 0);
-    const int32_t tx = wide ? 64 : tiled ? 16 : 1, ty = wide ? 8 : tiled ? 32 : a.box.n[1];
+    // 2.5% faster than 16 x 32 on the 512^3 cone), else 16 x 32, else plain y-fastest order;
+    // an orbit's tasks tile the grid of the cells that stand for the orbits
+    const bool wide = Wr % 64 == 0 && Hr % 8 == 0;
+    const bool tiled = wide || (Wr % 16 == 0 && Hr % 32 == 0);
+    const int32_t tx = wide ? 64 : tiled ? 16 : 1, ty = wide ? 8 : tiled ? 32 : Hr;
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
-                                    (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
+                                    (size_t)gather_column_floats(zchunk, slots) * sizeof(float));
     const int32_t kr = gather_rows_loaded(gather_stride(a.rows));
     trace_launch("column_gather_kernel", grid, dim3(256), lds,
-                 "views %d..%d members %d rows per lane %d z chunk %d tiles %d x %d", a.view0,
-                 a.view0 + a.nviews - 1, nb, kr, zchunk, tx, ty);
-#define MBP_GATHER(NB_, KR_) \
-    if (nb == NB_ && kr == KR_) \
-        column_gather_kernel<NB_, KR_><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate)
-    MBP_GATHER(1, 1); else MBP_GATHER(1, 2); else MBP_GATHER(1, 4); else MBP_GATHER(1, 6); else MBP_GATHER(1, 8);
-    else MBP_GATHER(2, 1); else MBP_GATHER(2, 2); else MBP_GATHER(2, 4); else MBP_GATHER(2, 6); else MBP_GATHER(2, 8);
-    else MBP_GATHER(4, 1); else MBP_GATHER(4, 2); else MBP_GATHER(4, 4); else MBP_GATHER(4, 6); else MBP_GATHER(4, 8);
+                 "views %d..%d members %d orbit %d (turn %d) rows per lane %d z chunk %d tiles %d x %d",
+                 a.view0, a.view0 + a.nviews - 1, nb, orbit, dir, kr, zchunk, tx, ty);
+#define MBP_GATHER(NB_, KR_, P_) \
+    if (slots == NB_ && kr == KR_ && orbit == P_) \
+        column_gather_kernel<NB_, KR_, P_><<<grid, dim3(256), lds, s>>>(a, lines, ysc, vol, zchunk, nchunks, tx, ty, accumulate, dir)
+    MBP_GATHER(1, 1, 1); else MBP_GATHER(1, 2, 1); else MBP_GATHER(1, 4, 1); else MBP_GATHER(1, 6, 1); else MBP_GATHER(1, 8, 1);
+    else MBP_GATHER(2, 1, 1); else MBP_GATHER(2, 2, 1); else MBP_GATHER(2, 4, 1); else MBP_GATHER(2, 6, 1); else MBP_GATHER(2, 8, 1);
+    else MBP_GATHER(4, 1, 1); else MBP_GATHER(4, 2, 1); else MBP_GATHER(4, 4, 1); else MBP_GATHER(4, 6, 1); else MBP_GATHER(4, 8, 1);
+    else MBP_GATHER(2, 1, 2); else MBP_GATHER(2, 2, 2); else MBP_GATHER(2, 4, 2); else MBP_GATHER(2, 6, 2); else MBP_GATHER(2, 8, 2);
+    else MBP_GATHER(4, 1, 4); else MBP_GATHER(4, 2, 4); else MBP_GATHER(4, 4, 4); else MBP_GATHER(4, 6, 4); else MBP_GATHER(4, 8, 4);
     else return hipErrorInvalidValue;
 #undef MBP_GATHER
     return hipGetLastError();

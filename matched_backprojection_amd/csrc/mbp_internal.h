@@ -56,10 +56,15 @@ hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* con
 // floats); the gather then writes every voxel of the z-fastest interleaved volume once
 // (optionally adding into it), reading the line constants of view view0 + i at lines[i * cols
 // + column].
+//
+// Turn symmetry (orbit = 2 or 4, nb = 1; see orbit_cell): the pre-pass runs over the first
+// q = V / orbit views with `orbit` members, member m being sino + m q rows cols (the views
+// q m apart, mview = q); the gather then takes a launch over all V views (nviews = V, view0 = 0)
+// and writes every voxel of the one-member volume once. dir: the turn's sense for orbit 4.
 hipError_t launch_sino_prepass(const ColumnLaunch& a, int nb, const float* const* sino, float* ysc,
-                               hipStream_t s);
+                               hipStream_t s, int32_t mview = 0);
 hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* lines, const float* ysc,
-                                float* vol, int accumulate, hipStream_t s);
+                                float* vol, int accumulate, hipStream_t s, int orbit = 1, int dir = 0);
 // The gather for cone geometries whose detector rows do not run along z: the same pre-pass
 // sinogram (ysc) and output as launch_column_gather, each ray clipped against each cell on
 // its own.

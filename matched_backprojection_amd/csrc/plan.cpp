@@ -104,6 +104,11 @@ struct mbp_plan {
     // and what the last forward projection ran
     int32_t last_fwd_walk = MBP_PATH_AUTO;
     int32_t last_fwd_members = 0;
+    // turn symmetry of the views (find_orbit) and whether the gather may share items over it
+    int32_t orbit = 1;
+    int32_t orbit_dir = 0;
+    bool orbit_enabled = true;
+    int32_t last_orbit = 0;           // cells that shared each item in the last backprojection
     std::mutex mu;
 };
 
@@ -348,6 +353,69 @@ bool tilt_gather(const mbp_plan* p) {
     return p->tilt_capable && p->forced_path == MBP_PATH_AUTO && adjoint_kind(p) == MBP_ADJOINT_GATHER;
 }
 
+// Turn symmetry of the views about the vertical axis through the grid's xy centre, for the
+// gather's shared items (orbit_cell): 4 when view v + V/4 is view v turned a quarter turn for
+// every v (square grid of equal x and y pitch), else 2 when view v + V/2 is view v turned a
+// half turn, else 1; the grid's W must be even (no cell is its own image). *dir: the quarter
+// turn's sense (+1 anticlockwise seen from +z). Turned frames are formed exactly (the turns
+// only swap and negate coordinates relative to the axis) and must match the stored ones within
+// 1e-12 of the frame's extent, far below fp32 rounding, so the shared items give the sums of
+// the unshared ones to rounding. Only for the column gather (rows along z).
+int32_t find_orbit(const mbp_plan& P, int32_t* dir) {
+    *dir = 0;
+    const mbp_geometry& g = P.g;
+    if (!P.column_capable || g.W % 2 != 0) return 1;
+    const double ax = 0.5 * (P.box.lo[0] + P.box.hi[0]), ay = 0.5 * (P.box.lo[1] + P.box.hi[1]);
+    const bool line = g.beam == MBP_PARALLEL3D;   // s is a direction, not a point
+    // whether frame B is frame A turned k quarter turns (k = 1 or -1) or a half turn (k = 2)
+    auto turned = [&](const Frame& A, const Frame& B, int k) {
+        auto turn = [&](const double* p, bool point, double* out) {
+            const double x = point ? p[0] - ax : p[0], y = point ? p[1] - ay : p[1];
+            double tx, ty;
+            if (k == 2) { tx = -x; ty = -y; }
+            else if (k == 1) { tx = -y; ty = x; }
+            else { tx = y; ty = -x; }
+            out[0] = point ? tx + ax : tx;
+            out[1] = point ? ty + ay : ty;
+            out[2] = p[2];
+        };
+        auto close = [](const double* a, const double* b, double scale) {
+            double d = 0.0;
+            for (int i = 0; i < 3; ++i) d = std::max(d, std::fabs(a[i] - b[i]));
+            return d <= 1e-12 * scale;
+        };
+        auto norm = [&](const double* p, bool point) {
+            const double x = point ? p[0] - ax : p[0], y = point ? p[1] - ay : p[1];
+            return std::sqrt(x * x + y * y + p[2] * p[2]);
+        };
+        const double pos = std::max(norm(A.c, true), line ? 0.0 : norm(A.s, true));
+        double t[3];
+        turn(A.s, !line, t);
+        if (!close(t, B.s, line ? norm(A.s, false) : pos)) return false;
+        turn(A.c, true, t);
+        if (!close(t, B.c, pos)) return false;
+        turn(A.u, false, t);
+        if (!close(t, B.u, norm(A.u, false))) return false;
+        turn(A.v, false, t);
+        return close(t, B.v, norm(A.v, false));
+    };
+    auto all_turned = [&](int64_t q, int k) {
+        for (int64_t v = 0; v + q < g.views; ++v)
+            if (!turned(P.frames[(size_t)v], P.frames[(size_t)(v + q)], k)) return false;
+        return true;
+    };
+    if (g.views % 4 == 0 && g.W == g.H && g.spacing[1] == g.spacing[2]) {
+        for (int k : {1, -1}) {
+            if (all_turned(g.views / 4, k)) {
+                *dir = k;
+                return 4;
+            }
+        }
+    }
+    if (g.views % 2 == 0 && all_turned(g.views / 2, 2)) return 2;
+    return 1;
+}
+
 // Workspace of one column-walk pass over nb members: the interleaved z-fastest volume (not
 // needed when the caller's own z-fastest buffer is used directly) and, for the gather adjoint,
 // the reordered sinogram of one launch of `views` views.
@@ -530,6 +598,7 @@ int mbp_plan_create(const mbp_geometry* geometry, const double* src, const doubl
     if (rc != MBP_OK) { delete p; return rc; }
     p->column_capable = column_ok(*p);
     p->tilt_capable = !p->column_capable && g.beam == MBP_CONE && g.D < ((int64_t)1 << 26);
+    p->orbit = find_orbit(*p, &p->orbit_dir);
     *out = p;
     return MBP_OK;
 }
@@ -566,6 +635,8 @@ int mbp_plan_get_info(const mbp_plan* plan, mbp_plan_info* info) {
     info->last_adjoint_views_per_launch = plan->last_views;
     info->last_forward_walk = plan->last_fwd_walk;
     info->last_forward_members_per_pass = plan->last_fwd_members;
+    info->orbit = plan->orbit;
+    info->last_adjoint_orbit = plan->last_orbit;
     return MBP_OK;
 }
 
@@ -576,6 +647,13 @@ int mbp_plan_set_path(mbp_plan* plan, int32_t path) {
     if (path == MBP_PATH_COLUMN && !plan->column_capable)
         return fail(MBP_EINVAL, "the column walk needs a 3-D beam whose detector row axis is parallel to z");
     plan->forced_path = path;
+    return MBP_OK;
+}
+
+int mbp_plan_set_orbit(mbp_plan* plan, int32_t enable) {
+    if (!plan) return fail(MBP_EINVAL, "plan is NULL");
+    if (enable != 0 && enable != 1) return fail(MBP_EINVAL, "enable must be 0 or 1 (got %d)", enable);
+    plan->orbit_enabled = enable == 1;
     return MBP_OK;
 }
 
@@ -708,6 +786,7 @@ int backproject_on(mbp_plan* plan, DeviceState* d, const float* sinogram, int64_
     plan->last_adjoint = MBP_ADJOINT_SCATTER;
     plan->last_walk = MBP_PATH_GENERIC;
     plan->last_views = views_per_launch(plan);
+    plan->last_orbit = 1;
     if (active_path(plan) == MBP_PATH_COLUMN || tilt) {
         const bool whd = g.layout == MBP_LAYOUT_WHD;
         const bool direct = whd && batch == 1;
@@ -768,7 +847,31 @@ int backproject_on(mbp_plan* plan, DeviceState* d, const float* sinogram, int64_
                 e = mbp::launch_column_lines(a, (int32_t)g.views, d->lines, s);
                 if (e != hipSuccess) return hip_fail(e, "column line launch");
             }
-            if (gather) {
+            // the turn symmetry's shared items: one member, all views in one launch
+            const int32_t orbit = gather && !tilt && nb == 1 && vb == g.views && plan->orbit_enabled
+                                      ? plan->orbit : 1;
+            if (orbit > 1) {
+                // pre-pass over the first q = V / orbit views with member m the view v + m q;
+                // one gather over all views writes every voxel
+                mbp::ColumnLaunch a = column_args(plan, d);
+                const int64_t q = g.views / orbit;
+                a.view0 = 0;
+                a.nviews = (int32_t)q;
+                const float* so[4] = {nullptr, nullptr, nullptr, nullptr};
+                for (int m = 0; m < orbit; ++m) so[m] = si[0] + m * q * g.rows * g.cols;
+                e = mbp::launch_sino_prepass(a, orbit, so, ysc, s, (int32_t)q);
+                if (e != hipSuccess) return hip_fail(e, "sinogram pre-pass launch");
+                a.nviews = (int32_t)g.views;
+                const mbp::ColLine* lines = d->lines;
+                if (batch_lines) {
+                    e = mbp::launch_column_lines(a, (int32_t)q, batch_lines, s);
+                    if (e != hipSuccess) return hip_fail(e, "column line launch");
+                    lines = batch_lines;
+                }
+                e = mbp::launch_column_gather(a, 1, lines, ysc, target, acc_target, s, orbit, plan->orbit_dir);
+                if (e != hipSuccess) return hip_fail(e, "column gather launch");
+                plan->last_orbit = orbit;
+            } else if (gather) {
                 // one pre-pass and one gather per view batch; every launch after the first adds
                 // into the volume (accumulators span all view batches)
                 mbp::ColumnLaunch a = column_args(plan, d);

@@ -693,6 +693,45 @@ MBP_HD MBP_INLINE int64_t gather_sino_floats(int32_t views, int32_t cols, int32_
     return (int64_t)nb * ((int64_t)views * cols * gather_rows_padded(rows) + kGatherGroup);
 }
 
+// Turn symmetry of a circular scan. When the V views fall into P groups of q = V / P such that
+// view v + m q is view v turned by m P-ths of a full turn about the vertical axis through the
+// grid's xy centre, and that turn maps the grid's cells onto cells, then line (view v + m q,
+// column j) crosses cell C exactly as line (v, j) crosses the cell turned back by m steps: the
+// intersection lengths are a property of the pair, and turning both leaves them unchanged. The
+// gather then gives one wave the P cells of an orbit c, R c, ..., R^(P-1) c (R: one step of the
+// turn) and forms items for views v < q only: the item of line (v, j) with cell R^a c carries the
+// rows of line (v + m q, j) into cell R^(a+m) c, for every m.
+//
+// orbit_cell: cell (ox, oy) = R^a (ix, iy) on a W x H grid. P = 2: the half turn,
+// (ix, iy) -> (W-1-ix, H-1-iy). P = 4 (square grid, W == H): a quarter turn, anticlockwise seen
+// from +z for dir > 0 ((x, y) -> (-y, x), so (ix, iy) -> (W-1-iy, ix)), clockwise otherwise
+// ((x, y) -> (y, -x), so (ix, iy) -> (iy, W-1-ix)). P = 1: the cell itself.
+MBP_HD MBP_INLINE void orbit_cell(int32_t P, int32_t dir, int32_t W, int32_t H, int32_t ix,
+                                  int32_t iy, int32_t a, int32_t& ox, int32_t& oy) {
+    ox = ix;
+    oy = iy;
+    for (int32_t k = 0; k < a; ++k) {
+        const int32_t x = ox, y = oy;
+        if (P == 2) {
+            ox = W - 1 - x;
+            oy = H - 1 - y;
+        } else if (P == 4 && dir > 0) {
+            ox = W - 1 - y;
+            oy = x;
+        } else if (P == 4) {
+            ox = y;
+            oy = W - 1 - x;
+        }
+    }
+}
+
+// The cells that stand for the orbits (one per orbit): ix < W / 2 for P = 2 (W even), ix and
+// iy < W / 2 for P = 4 (W == H even); the whole grid for P = 1.
+MBP_HD MBP_INLINE void orbit_grid(int32_t P, int32_t W, int32_t H, int32_t& Wr, int32_t& Hr) {
+    Wr = P == 1 ? W : W / 2;
+    Hr = P == 4 ? H / 2 : H;
+}
+
 // Whether the lanes of one gather instruction (rows S apart, z cell coordinate at row k
 // za0 + k za1 at the crossing's start and zb0 + k zb1 at its end) always add into different
 // z cells when pieces are walked aligned: S rows move z by more than one cell at both ends,

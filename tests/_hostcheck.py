@@ -35,7 +35,7 @@ def _load():
         lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P]
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
-        lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, I, P, P, P]
+        lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, I, P, P, P, I, I]
         lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
         lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_tilt_band.argtypes = [P, P, P, P, I, I, I, D, D, I, P, P]
@@ -145,11 +145,12 @@ def check_rays(path: str, geom: dict, traj: dict, ray_ids) -> tuple:
 
 
 def gather(geom: dict, traj: dict, sino: np.ndarray, kernel_shares: bool = True,
-           general_only: bool = False):
+           general_only: bool = False, orbit: int = 1, turn: int = 0):
     """Replay the cell-gather adjoint item by item (fast fixed-point items with fp32 shares as
     the kernel computes them, or fp64 shares from the same integers; fp64 sums) on a
     (views, rows, cols) sinogram; general_only takes every item in the fp64 general form.
-    Returns (volume, violations, items in the fast form)."""
+    orbit 2 or 4 (turn: the quarter turn's sense): items shared over the turn symmetry of the
+    views, as the kernel forms them. Returns (volume, violations, items in the fast form)."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
     rows = int(geom.get("rows", 1))
@@ -160,7 +161,7 @@ def gather(geom: dict, traj: dict, sino: np.ndarray, kernel_shares: bool = True,
     lib.mbph_gather(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n), views, rows, cols,
                     float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)), _ptr(s),
                     int(kernel_shares), int(general_only), _ptr(vol), ctypes.byref(viol),
-                    ctypes.byref(fast))
+                    ctypes.byref(fast), int(orbit), int(turn))
     return vol.reshape(tuple(int(x) for x in geom["shape"])), int(viol.value), int(fast.value)
 
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared) == set(_capi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.mbp_abi_version() == 2
+    assert lib.mbp_abi_version() == 3
     assert lib.mbp_status_string(_capi.MBP_ERANGE) == b"geometry out of range"
 
 
@@ -355,3 +355,62 @@ def test_python_plan_maps_errors_and_shapes():
     assert p2.sino_shape == (90, 96) and p2.info["path"] == "generic"
     plan.close()
     p2.close()
+
+
+def _full_circle_parallel3d(views):
+    """A 3-D parallel beam over a full turn (view k along angle 2 pi k / views)."""
+    t = np.arange(views, dtype=np.float64) * (2.0 * np.pi / views)
+    c, s, zero = np.cos(t), np.sin(t), np.zeros(views)
+    return {"src": np.stack([c, s, zero], axis=1), "det": np.zeros((views, 3)),
+            "eu": np.stack([-s, c, zero], axis=1), "ev": np.tile([0.0, 0.0, 1.0], (views, 1))}
+
+
+def _views(traj, order):
+    return {k: (None if v is None else np.ascontiguousarray(np.asarray(v)[order])) for k, v in traj.items()}
+
+
+def test_turn_symmetry_of_the_views(lib):
+    """Plan creation finds the turn symmetry that the gather shares cell crossings over: a
+    quarter turn for a full circle of 4k views on a square grid of equal x and y pitch centred
+    on the turn's axis (anticlockwise or clockwise), a half turn for 2k views or a grid that is
+    not square, none for an odd view count, an off-centre grid, an odd W, a short scan, views
+    out of angular order or a 3-D parallel beam over half a turn (view v + V/2 is then a
+    quarter turn of view v, which pairs no cells). Host logic only."""
+    from dataclasses import replace
+    base = SMALL_CONFIGS["c4_cone512_aniso"]
+
+    def orbit(cfg, traj=None, center=None):
+        g = _geometry(cfg)
+        if center is not None:
+            g.center[0], g.center[1], g.center[2] = center
+        rc, h = _create(lib, g, config_trajectory(cfg) if traj is None else traj)
+        assert rc == 0, lib.mbp_last_error()
+        inf = _info(lib, h)
+        assert inf.last_adjoint_orbit == 0
+        lib.mbp_plan_destroy(h)
+        return inf.orbit
+
+    c48 = replace(base, views=48)
+    assert orbit(c48) == 4
+    assert orbit(c48, traj=_views(config_trajectory(c48), np.arange(48)[::-1])) == 4   # clockwise
+    assert orbit(replace(base, views=46)) == 2
+    assert orbit(replace(base, views=45)) == 1
+    assert orbit(replace(c48, shape=(48, 64, 48))) == 2          # W != H
+    assert orbit(replace(c48, spacing=(1.5, 1.0, 1.25))) == 2    # dx != dy
+    assert orbit(replace(c48, shape=(48, 63, 63))) == 1          # odd W
+    assert orbit(c48, center=(3.0, 0.0, 0.0)) == 1               # axis off the grid's centre
+    assert orbit(c48, center=(0.0, 0.0, 7.0)) == 4               # z offsets keep the symmetry
+    perm = np.random.default_rng(3).permutation(48)
+    assert orbit(c48, traj=_views(config_trajectory(c48), perm)) == 1
+    short = replace(base, views=80)
+    assert orbit(replace(base, views=40), traj=_views(config_trajectory(short), np.arange(40))) == 1
+    p3 = replace(c48, beam="parallel3d", trajectory="parallel3d")
+    assert orbit(p3) == 1
+    assert orbit(p3, traj=_full_circle_parallel3d(48)) == 4
+    # the switch: 0 or 1 only
+    rc, h = _create(lib, _geometry(c48), config_trajectory(c48))
+    assert rc == 0
+    assert lib.mbp_plan_set_orbit(h, 0) == 0 and lib.mbp_plan_set_orbit(h, 1) == 0
+    assert lib.mbp_plan_set_orbit(h, 2) == _capi.MBP_EINVAL
+    assert lib.mbp_plan_set_orbit(None, 1) == _capi.MBP_EINVAL
+    lib.mbp_plan_destroy(h)

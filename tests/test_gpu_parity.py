@@ -411,6 +411,47 @@ def test_tilted_circular_parity(torch_dev, mbp, oracle, layout):
         plan.close()
 
 
+@pytest.mark.parametrize("case", ["quarter", "quarter_clockwise", "half", "half_rect",
+                                  "parallel3d_quarter"])
+def test_orbit_gather_parity(torch_dev, mbp, oracle, case):
+    """The gather shared over a turn symmetry of the views (one crossing serves the P cells of
+    an orbit): the plan finds the symmetry, the backprojection takes it in both layouts and
+    when adding into a volume, and matches the oracle, the unshared gather (to fp32 rounding)
+    and the forward projection's adjoint identity."""
+    from tests.test_hostcheck import _turn_cases
+    torch, dev = torch_dev
+    cfg, traj, P, turn = _turn_cases()[case]
+    geom = geom_of(cfg)
+    x = config_phantom(cfg)
+    y = np.random.default_rng(5).random((cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    pre = np.random.default_rng(6).random(cfg.shape).astype(np.float32)
+    for layout in ("WHD", "DHW"):
+        say(f"case orbit {case} (P={P}, turn {turn}) layout={layout}")
+        plan = make_plan(mbp, cfg, traj=traj, layout=layout)
+        assert plan.info["orbit"] == P
+        yd = torch.from_numpy(y).to(dev)
+        b = plan.backproject(yd).cpu().numpy().astype(np.float64)
+        assert plan.info["last_adjoint_orbit"] == P and plan.info["last_adjoint"] == "gather"
+        check(b, bref, "orbit gather")
+        out = to_device_volume(torch, dev, pre, layout)
+        plan.backproject(yd, out=out, accumulate=True)
+        check(out.cpu().numpy().astype(np.float64), bref + pre.astype(np.float64), "orbit accumulate")
+        p = plan.project(to_device_volume(torch, dev, x, layout)).cpu().numpy().astype(np.float64)
+        lhs = float(np.dot(p.ravel(), y.astype(np.float64).ravel()))
+        rhs = float(np.dot(x.astype(np.float64).ravel(), b.ravel()))
+        say(f"  adjoint identity {abs(lhs - rhs) / abs(lhs):.2e}")
+        assert abs(lhs - rhs) <= RTOL_ADJ * abs(lhs)
+        plan.set_orbit(False)
+        b1 = plan.backproject(yd).cpu().numpy().astype(np.float64)
+        assert plan.info["last_adjoint_orbit"] == 1
+        check(b1, bref, "unshared gather")
+        d = rel_l2(b, b1)
+        say(f"  shared vs unshared rel-L2 {d:.2e}")
+        assert d <= 1e-6
+        plan.close()
+
+
 def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
     """Ragged view batches, both layouts, batch sizes 0..5, accumulation, caller workspace."""
     torch, dev = torch_dev

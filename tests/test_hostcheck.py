@@ -187,6 +187,50 @@ def test_cell_gather_reproduces_oracle_adjoint(oracle, name):
         assert (np.abs(b - bref) / np.maximum(np.abs(bref), floor)).max() < tol_max
 
 
+def _turn_cases():
+    """Scans with a turn symmetry (name, config, trajectory, orbit, turn sense), on the small
+    anisotropic cone: a full circle of 48 views anticlockwise and clockwise (quarter turn), 46
+    views (half turn), a non-square grid (half turn), and a 3-D parallel beam over a full turn."""
+    from dataclasses import replace
+    from tests.test_capi import _full_circle_parallel3d, _views
+    base = SMALL_CONFIGS["c4_cone512_aniso"]
+    c48, c46 = replace(base, views=48), replace(base, views=46)
+    rect = replace(c48, shape=(48, 64, 48))
+    p3 = replace(c48, beam="parallel3d", trajectory="parallel3d")
+    return {
+        "quarter": (c48, config_trajectory(c48), 4, 1),
+        "quarter_clockwise": (c48, _views(config_trajectory(c48), np.arange(48)[::-1]), 4, -1),
+        "half": (c46, config_trajectory(c46), 2, 0),
+        "half_rect": (rect, config_trajectory(rect), 2, 0),
+        "parallel3d_quarter": (p3, _full_circle_parallel3d(48), 4, 1),
+    }
+
+
+@pytest.mark.parametrize("case", ["quarter", "quarter_clockwise", "half", "half_rect",
+                                  "parallel3d_quarter"])
+def test_orbit_gather_reproduces_oracle_adjoint(oracle, case):
+    """The gather shared over a turn symmetry (items of the first V / P views only, each
+    carrying the rows of the views V / P apart into the orbit's other cells) is still the chord
+    definition: in the fp64 general form it equals the oracle to rounding, and in the kernel's
+    forms to the fixed point's resolution, as the unshared replay does. Replayed with the wrong
+    turn sense, the same items land in the wrong cells and miss by percents."""
+    cfg, traj, P, turn = _turn_cases()[case]
+    geom = _geom(cfg)
+    y = np.random.default_rng(2).random((cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    floor = 1e-6 * np.abs(bref).max()
+    for general_only, tol_l2, tol_max in ((True, 1e-13, 1e-10), (False, 3e-9, 2e-5)):
+        b, viol, fast = HC.gather(geom, traj, y, kernel_shares=False, general_only=general_only,
+                                  orbit=P, turn=turn)
+        assert viol == 0
+        assert (fast == 0) == general_only
+        assert np.linalg.norm(b - bref) / np.linalg.norm(bref) < tol_l2
+        assert (np.abs(b - bref) / np.maximum(np.abs(bref), floor)).max() < tol_max
+    if P == 4:
+        b, _, _ = HC.gather(geom, traj, y, general_only=True, orbit=P, turn=-turn)
+        assert np.linalg.norm(b - bref) / np.linalg.norm(bref) > 1e-2
+
+
 def tall_detector_config():
     """The small anisotropic cone with a tall detector (460 rows, so eight rows per lane): the
     gather takes its fast fixed-point form. Most rows pass above or below the volume."""
