@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 3
+#define MBP_ABI_VERSION 4
 
 typedef enum mbp_status {
     MBP_OK = 0,
@@ -138,6 +138,9 @@ typedef struct mbp_plan_info {
                                   mbp_plan_set_orbit): 4 (quarter turn), 2 (half turn) or 1   */
     int32_t last_adjoint_orbit; /* cells that shared each gather crossing in the last
                                   mbp_backproject: the orbit, or 1 (0 before the first call) */
+    int32_t last_forward_orbit; /* rays that shared each column walk in the last mbp_project
+                                  (the fewest over its passes): the orbit, or 1 (0 before the
+                                  first call with B > 0)                                      */
 } mbp_plan_info;
 
 /* Validate the geometry and trajectory and build a plan. Trajectory arrays are host fp64,
@@ -164,19 +167,21 @@ int mbp_plan_set_path(mbp_plan* plan, int32_t path);
    through every voxel times the ray's value); they differ in summation order. */
 int mbp_plan_set_adjoint(mbp_plan* plan, int32_t kind);
 
-/* Allow (1, the default) or forbid (0) the gather adjoint to share cell crossings over a turn
-   symmetry of the views. The adjoint sums, over every ray, the ray's value times its chord
-   through each voxel (the pair at the top of this header: page "diffct 2.1.0 -> 2.2.1",
-   README "Why diffct", bullet "Matched operators"). When the views fall
-   into P = 4 (or 2) groups of V / P such that view v + V / P is view v turned a quarter (half)
-   turn about the vertical axis through the volume's xy centre, and the grid maps onto itself
-   under that turn (W even; for a quarter turn also W == H and dx == dy), the chord of ray
-   (v + m V / P, column, row) through a cell equals that of ray (v, column, row) through the
-   cell turned back m steps: one crossing then serves P cells, and the gather forms crossings
-   for the first V / P views only. Taken only for one member with all views in one launch (a
-   (D,H,W) or WHD volume, batch 1, workspace holding every view). Frames are compared to
-   1e-12 of their extent, so the sums equal the unshared ones to fp32 rounding. Plan setting
-   only: no device call. */
+/* Allow (1, the default) or forbid (0) the column walk and the gather adjoint to share their
+   geometry over a turn symmetry of the views. Both operators are sums of chords, the length
+   of a ray inside a voxel (the pair at the top of this header: page "diffct 2.1.0 -> 2.2.1",
+   README "Why diffct", bullet "Matched operators"). When the views fall into P = 4 (or 2)
+   groups of V / P such that view v + V / P is view v turned a quarter (half) turn about the
+   vertical axis through the volume's xy centre, and the grid maps onto itself under that turn
+   (W even; for a quarter turn also W == H and dx == dy), the chord of ray (v + m V / P,
+   column, row) through a cell equals that of ray (v, column, row) through the cell turned
+   back m steps. The forward then walks the rays of the first V / P views only, each walk
+   summing the P turned cells into the P rays it stands for, and the gather forms its cell
+   crossings for those views only, each serving the P cells of an orbit. Taken for single
+   members (the forward: any pass of one member; the gather: batch 1 with every view in one
+   launch). Frames are compared to 1e-12 of their extent, so the sums equal the unshared
+   ones to fp32 rounding, and the forward and the gather still visit the same segments.
+   Plan setting only: no device call. */
 int mbp_plan_set_orbit(mbp_plan* plan, int32_t enable);
 
 /* Limit the views of one kernel launch (0 = automatic: as many as index and grid limits

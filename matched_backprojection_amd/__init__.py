@@ -135,7 +135,8 @@ class Plan:
                 "last_adjoint_views_per_launch": inf.last_adjoint_views_per_launch,
                 "last_forward_walk": _capi.PATH_NAMES[inf.last_forward_walk] if inf.last_forward_walk else None,
                 "last_forward_members_per_pass": inf.last_forward_members_per_pass,
-                "orbit": inf.orbit, "last_adjoint_orbit": inf.last_adjoint_orbit}
+                "orbit": inf.orbit, "last_adjoint_orbit": inf.last_adjoint_orbit,
+                "last_forward_orbit": inf.last_forward_orbit}
 
     def set_path(self, path: str) -> None:
         _capi.check(self._lib.mbp_plan_set_path(self._handle, _capi.PATHS[path]), "mbp_plan_set_path")
@@ -145,8 +146,8 @@ class Plan:
         _capi.check(self._lib.mbp_plan_set_adjoint(self._handle, _capi.ADJOINTS[kind]), "mbp_plan_set_adjoint")
 
     def set_orbit(self, enable: bool) -> None:
-        """Whether the gather adjoint may share cell crossings over a turn symmetry of the
-        views (on by default; info["orbit"] is the symmetry found)."""
+        """Whether the column walk and the gather adjoint may share their geometry over a turn
+        symmetry of the views (on by default; info["orbit"] is the symmetry found)."""
         _capi.check(self._lib.mbp_plan_set_orbit(self._handle, 1 if enable else 0), "mbp_plan_set_orbit")
 
     def set_view_batch(self, views: int) -> None:

@@ -62,6 +62,7 @@ class PlanInfo(ctypes.Structure):
         ("last_adjoint_views_per_launch", ctypes.c_int64),
         ("last_forward_walk", ctypes.c_int32), ("last_forward_members_per_pass", ctypes.c_int32),
         ("orbit", ctypes.c_int32), ("last_adjoint_orbit", ctypes.c_int32),
+        ("last_forward_orbit", ctypes.c_int32),
     ]
 
 

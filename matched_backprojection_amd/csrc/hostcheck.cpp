@@ -120,49 +120,79 @@ int mbph_project(int path, const double* frames, int beam, const double* lo, con
 
 // Forward projection with the chunked column walk of the forward kernel: per column, the
 // 64 lanes' entries of each chunk of merged xy crossings are filled one lane after another,
-// then every row consumes them (the kernel does the same with one wave per 64 rows).
+// then every row consumes them (the kernel does the same with one wave per 64 rows). orbit > 1
+// (2 or 4, with the quarter turn's sense dir): the walks of the first views / orbit views
+// also give the rays of the views views / orbit apart from the turned cells (orbit_columns),
+// as the kernel shares them over a turn symmetry of the views.
 int mbph_project_chunked(const double* frames, int beam, const double* lo, const double* pitch,
                          const int32_t* n, int views, int rows, int cols, double du, double dv,
-                         const float* vol, float* sino, long long* violations) {
+                         const float* vol, float* sino, long long* violations, int orbit, int dir) {
     std::vector<Frame> F;
     frames_from(frames, views, F);
     const Box B = box_from(lo, pitch, n);
     *violations = 0;
     const int32_t H = n[1], D = n[2];
+    const uint32_t WH1 = (uint32_t)n[0] * (uint32_t)H - 1u;
+    const int q = views / orbit;
     std::vector<XYEvent> E(kXYChunk);
+    std::vector<int32_t> T(kXYChunk);
     std::vector<std::vector<XYEvent>> chunks;
-    for (int i = 0; i < views; ++i) {
+    std::vector<std::vector<int32_t>> turns;     // quarter turn: each event's turned column
+    for (int i = 0; i < q; ++i) {
         for (int j = 0; j < cols; ++j) {
             ColumnWalk c;
             column_setup(F[i], B, beam, centred(j, cols, du), c);
             // the column's chunks, as one wave builds them
             chunks.clear();
+            turns.clear();
             std::vector<int32_t> counts;
-            int32_t final_cxy = 0;
+            int32_t final_cxy = 0, final_c1 = 0;
             if (c.hit) {
                 const int32_t total = c.x.steps + c.y.steps;
                 int32_t done = 0, kx0 = 0, ky0 = 0;
                 while (done < total) {
                     const int32_t count = total - done < kXYChunk ? total - done : kXYChunk;
                     for (auto& e : E) { e.tb = NAN; e.cxy = -1; }
+                    for (auto& t : T) t = -1;
                     int32_t a = 0;
-                    for (int lane = 0; lane < 64; ++lane) a += xy_chunk_fill(c, H, kx0, ky0, count, lane, E.data());
-                    for (int32_t p = 0; p < count; ++p)   // every position filled exactly once
+                    for (int lane = 0; lane < 64; ++lane)
+                        a += xy_chunk_fill(c, H, kx0, ky0, count, lane, E.data(), orbit == 4 ? T.data() : nullptr,
+                                           n[0], dir);
+                    for (int32_t p = 0; p < count; ++p) {  // every position filled exactly once
                         if (E[p].cxy < 0 || E[p].cxy >= n[0] * H || !(E[p].tb == E[p].tb)) ++*violations;
+                        if (orbit == 4 && (T[p] < 0 || T[p] >= n[0] * H)) ++*violations;
+                    }
                     chunks.push_back(std::vector<XYEvent>(E.begin(), E.begin() + count));
+                    turns.push_back(std::vector<int32_t>(T.begin(), T.begin() + count));
                     kx0 += a; ky0 += count - a; done += count;
                 }
                 if (kx0 != c.x.steps || ky0 != c.y.steps) ++*violations;
-                final_cxy = (c.x.c0 + c.x.step * c.x.steps) * H + (c.y.c0 + c.y.step * c.y.steps);
+                const int32_t fx = c.x.c0 + c.x.step * c.x.steps, fy = c.y.c0 + c.y.step * c.y.steps;
+                final_cxy = fx * H + fy;
+                int32_t ox, oy;
+                orbit_cell(4, dir, n[0], H, fx, fy, 1, ox, oy);
+                final_c1 = ox * H + oy;
             }
             for (int k = 0; k < rows; ++k) {
                 RowWalk r;
                 row_setup(c, B, centred(k, rows, dv), F[i].v[2], r);
-                float acc = 0.0f;
+                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                int32_t c1 = 0;       // the turned column of the cell visited next
                 auto visit = [&](int32_t cxy, int32_t cz, float len) {
                     if (cxy < 0 || cxy >= n[0] * H || cz < 0 || cz >= D || !(len >= 0.0f)) { ++*violations; return; }
-                    const int32_t cx = cxy / H, cy = cxy % H;
-                    acc = fmaf(len, vol[((int64_t)cz * H + cy) * n[0] + cx], acc);
+                    uint32_t cell[4] = {(uint32_t)cxy, 0u, 0u, 0u};
+                    if (orbit == 2) {
+                        uint32_t o2[2];
+                        orbit_columns<2>((uint32_t)cxy, 0u, WH1, o2);
+                        cell[1] = o2[1];
+                    } else if (orbit == 4) {
+                        orbit_columns<4>((uint32_t)cxy, (uint32_t)c1, WH1, cell);
+                    }
+                    for (int m = 0; m < orbit; ++m) {
+                        if (cell[m] >= (uint32_t)(n[0] * H)) { ++*violations; continue; }
+                        const int32_t cx = (int32_t)cell[m] / H, cy = (int32_t)cell[m] % H;
+                        acc[m] = fmaf(len, vol[((int64_t)cz * H + cy) * n[0] + cx], acc[m]);
+                    }
                 };
                 if (c.hit) {
                     int32_t cz = r.z.c0, kz = 0;
@@ -171,7 +201,9 @@ int mbph_project_chunked(const double* frames, int beam, const double* lo, const
                     // rows meeting at most one z plane per xy cell take the grouped two-piece
                     // form for whole groups of a chunk, the general one for the rest
                     const bool two = row_single_crossing(r, B);
-                    for (const auto& ch : chunks) {
+                    for (size_t ci = 0; ci < chunks.size(); ++ci) {
+                        const auto& ch = chunks[ci];
+                        const auto& tu = turns[ci];
                         const size_t grouped = two ? ch.size() / kCellGroup * kCellGroup : 0;
                         // chunks inside the row's slab (for this row; the kernel requires it of
                         // all 64 rows of a wave) take the clip-free form, with the next z
@@ -206,16 +238,23 @@ int mbph_project_chunked(const double* frames, int beam, const double* lo, const
                                 row_cell_two(r, ta, ch[p].tb, cz, kz, nz, z0, l0, z1, l1);
                             }
                             if (nz < hi && fmax(ta, r.t_lo) < hi) ++*violations;   // a second crossing
+                            c1 = tu[p];
                             if (l0 != 0.0f) visit(ch[p].cxy, z0, l0);
                             if (l1 != 0.0f) visit(ch[p].cxy, z1, l1);
                             ta = ch[p].tb;
                         }
                         if (inside && grouped > 0) nz = kz < r.z.steps ? crossing(r.z, kz) : INFINITY;
-                        for (; p < ch.size(); ++p) { row_cell(r, ta, ch[p].tb, ch[p].cxy, cz, kz, nz, visit); ta = ch[p].tb; }
+                        for (; p < ch.size(); ++p) {
+                            c1 = tu[p];
+                            row_cell(r, ta, ch[p].tb, ch[p].cxy, cz, kz, nz, visit);
+                            ta = ch[p].tb;
+                        }
                     }
+                    c1 = final_c1;
                     row_cell(r, ta, c.T, final_cxy, cz, kz, nz, visit);
                 }
-                sino[((int64_t)i * rows + k) * cols + j] = acc * r.kappa;
+                for (int m = 0; m < orbit; ++m)
+                    sino[((int64_t)(i + m * q) * rows + k) * cols + j] = acc[m] * r.kappa;
             }
         }
     }

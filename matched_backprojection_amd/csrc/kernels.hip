@@ -307,16 +307,26 @@ __device__ __forceinline__ const lds_event* events_in_vgpr(const XYEvent* e) {
 // FLAT: the volume's bytes fit a 31-bit offset, so one buffer resource spans it and each
 // cell's column is reached through the load's scalar offset (one scalar multiply per cell);
 // otherwise each cell gets a resource based at its column.
-template <int NB, bool FLAT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 8 : 1))) column_forward_kernel(const ColumnLaunch A,
-                                                             const float* __restrict__ vol,
-                                                             const MPtrs4 sino) {
+//
+// P > 1 (one member): the projection shared over a turn symmetry of the views (orbit_cell).
+// The launch's views are among the first q = V / P; a ray (v, column, row) crosses the cells
+// R^m C with the chords it has through C, and so gives ray (v + m q, column, row), which is
+// stored slot_stride elements after it: one walk serves P rays, each summing its own cells.
+template <int NB, bool FLAT, int P>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 && P == 1 ? 8 : P == 1 ? 1 : 4)))
+column_forward_kernel(const ColumnLaunch A, const float* __restrict__ vol, const MPtrs4 sino,
+                      int64_t slot_stride, int32_t dir) {
+    static_assert(P == 1 || NB == 1, "a turn symmetry is taken for one member");
+    constexpr int NA = NB * P;          // sums per lane: the members, or the orbit's rays
     __shared__ XYEvent events[4][kXYChunk];
+    __shared__ int32_t turned[P == 4 ? 4 : 1][P == 4 ? kXYChunk : 1];
     const ColumnTask t = forward_task(A);
     if (!t.live) return;
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
     XYEvent* E = events[wave];
+    int32_t* const C1 = P == 4 ? turned[wave] : nullptr;
+    const uint32_t WH1 = (uint32_t)A.box.n[0] * (uint32_t)A.H - 1u;
     // the wave's first ray (uniform, held in scalar registers through the walk); a lane's ray
     // adds its row
     const int64_t ray0 = ((int64_t)t.view * A.rows + (t.row - lane)) * A.cols + t.col;
@@ -327,13 +337,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
     RowWalk r;
     row_setup(c, A.box, centred(t.row, A.rows, A.dv), F.v[2], r);
     if (!t.valid) { r.t_lo = 0.0; r.t_hi = 0.0; }
-    float acc[NB];
+    float acc[NA];
 #pragma unroll
-    for (int m = 0; m < NB; ++m) acc[m] = 0.0f;
+    for (int m = 0; m < NA; ++m) acc[m] = 0.0f;
     if (c.hit) {
         const uint32_t D = (uint32_t)A.D;
+        uint32_t c1 = 0;        // quarter turn: the turned column of the cell visited next
         auto visit = [&](int32_t cxy, int32_t cz, float len) {
-            load_acc<NB>(vol + ((uint32_t)cxy * D + (uint32_t)cz) * NB, len, acc);
+            if constexpr (P == 1) {
+                load_acc<NB>(vol + ((uint32_t)cxy * D + (uint32_t)cz) * NB, len, acc);
+            } else {
+                uint32_t cell[P];
+                orbit_columns<P>((uint32_t)cxy, c1, WH1, cell);
+#pragma unroll
+                for (int m = 0; m < P; ++m) load_acc<1>(vol + (cell[m] * D + (uint32_t)cz), len, acc + m);
+            }
         };
         int32_t cz = r.z.c0, kz = 0;
         double nz = r.z.steps > 0 ? r.z.t_first : INFINITY;
@@ -347,7 +365,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
             const int32_t count = total - done < kXYChunk ? total - done : kXYChunk;
             int32_t a = 0;
             if (count > 0) {
-                a = wave_sum012(xy_chunk_fill(c, A.H, kx0, ky0, count, lane, E));
+                a = wave_sum012(xy_chunk_fill(c, A.H, kx0, ky0, count, lane, E, C1, A.box.n[0], dir));
                 wave_lds_sync();
             }
             int32_t p = 0;
@@ -362,30 +380,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
                     for (; p + kCellGroup <= count; p += kCellGroup) {
                         uint32_t off[2 * kCellGroup];
                         float len[2 * kCellGroup];
+                        uint32_t cell[kCellGroup][P];
 #pragma unroll
                         for (int q = 0; q < kCellGroup; ++q) {
                             const double tb = E[p + q].tb;
-                            const uint32_t base = uniform((uint32_t)E[p + q].cxy) * D;
+                            orbit_columns<P>(uniform((uint32_t)E[p + q].cxy),
+                                             P == 4 ? uniform((uint32_t)C1[p + q]) : 0u, WH1, cell[q]);
                             int32_t z0, z1;
                             pieces(tb, z0, len[2 * q], z1, len[2 * q + 1]);
-                            off[2 * q] = (base + (uint32_t)z0) * NB;
-                            off[2 * q + 1] = (base + (uint32_t)z1) * NB;
+                            off[2 * q] = (uint32_t)z0 * NB;
+                            off[2 * q + 1] = (uint32_t)z1 * NB;
                             ta = tb;
                         }
-                        float val[2 * kCellGroup][NB];
+                        float val[2 * kCellGroup][NA];
 #pragma unroll
                         for (int q = 0; q < 2 * kCellGroup; ++q) {
-                            if (len[q] != 0.0f) {
-                                load_vals<NB>(vol + off[q], val[q]);
-                            } else {
 #pragma unroll
-                                for (int m = 0; m < NB; ++m) val[q][m] = 0.0f;
+                            for (int m = 0; m < P; ++m) {
+                                if (len[q] != 0.0f) {
+                                    load_vals<NB>(vol + cell[q / 2][m] * D * NB + off[q], val[q] + m * NB);
+                                } else {
+#pragma unroll
+                                    for (int b = 0; b < NB; ++b) val[q][m * NB + b] = 0.0f;
+                                }
                             }
                         }
 #pragma unroll
                         for (int q = 0; q < 2 * kCellGroup; ++q)
 #pragma unroll
-                            for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
+                            for (int m = 0; m < NA; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
                     }
                 };
                 if (inside) {
@@ -410,49 +433,56 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
                     for (; p + kCellGroup <= count; p += kCellGroup) {
                         uint32_t zoff[2 * kCellGroup];
                         float len[2 * kCellGroup];
-                        uint32_t cell[kCellGroup];
+                        uint32_t cell[kCellGroup][P];
                         bool cross[kCellGroup];
                         const lds_event* const Eg = events_in_vgpr(E + p);
 #pragma unroll
                         for (int q = 0; q < kCellGroup; ++q) {
-                            cell[q] = uniform((uint32_t)Eg[q].cxy);
+                            orbit_columns<P>(uniform((uint32_t)Eg[q].cxy),
+                                             P == 4 ? uniform((uint32_t)C1[p + q]) : 0u, WH1, cell[q]);
                             zoff[2 * q] = (uint32_t)(zbase + __mul24(k, zstep));
                             cross[q] = row_cell_two_counted(r.z.t_first, r.z.t_step, Eg[q].tb, Eg[q].chord, k, nz,
                                                  len[2 * q], len[2 * q + 1]);
                             zoff[2 * q + 1] = (uint32_t)(zbase + __mul24(k, zstep));
                         }
-                        float val[2 * kCellGroup][NB];
+                        float val[2 * kCellGroup][NA];
 #pragma unroll
                         for (int q = 0; q < kCellGroup; ++q) {
-                            const __amdgpu_buffer_rsrc_t rs = FLAT ? rs_all
-                                : __builtin_amdgcn_make_buffer_rsrc(
-                                      const_cast<float*>(vol + (size_t)cell[q] * D * NB), (short)0,
-                                      colbytes, kBufferFlags);
-                            const uint32_t soff = FLAT ? cell[q] * (uint32_t)colbytes : 0u;
 #pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                // one member: the first piece (empty only when the row meets a
-                                // z plane exactly at the cell's entry) is loaded unconditionally
-                                // and multiplied with 0 * anything = 0, so an empty piece adds
-                                // nothing even next to a non-finite voxel; the second piece is
-                                // loaded by the lanes that cross a z plane in the cell (its
-                                // length tb - nz > 0 then rounds to a nonzero fp32 unless it is
-                                // below 2^-150), the others add 0
-                                if (NB == 1 ? (h == 0 || cross[q]) : len[2 * q + h] != 0.0f) {
-                                    buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h], soff);
-                                } else {
+                            for (int o = 0; o < P; ++o) {
+                                const __amdgpu_buffer_rsrc_t rs = FLAT ? rs_all
+                                    : __builtin_amdgcn_make_buffer_rsrc(
+                                          const_cast<float*>(vol + (size_t)cell[q][o] * D * NB), (short)0,
+                                          colbytes, kBufferFlags);
+                                const uint32_t soff = FLAT ? cell[q][o] * (uint32_t)colbytes : 0u;
 #pragma unroll
-                                    for (int m = 0; m < NB; ++m) val[2 * q + h][m] = 0.0f;
+                                for (int h = 0; h < 2; ++h) {
+                                    // one member: the first piece (empty only when the row meets
+                                    // a z plane exactly at the cell's entry) is loaded
+                                    // unconditionally and multiplied with 0 * anything = 0, so an
+                                    // empty piece adds nothing even next to a non-finite voxel;
+                                    // the second piece is loaded by the lanes that cross a z plane
+                                    // in the cell (its length tb - nz > 0 then rounds to a nonzero
+                                    // fp32 unless it is below 2^-150), the others add 0
+                                    if (NB == 1 ? (h == 0 || cross[q]) : len[2 * q + h] != 0.0f) {
+                                        buffer_vals<NB>(rs, zoff[2 * q + h], val[2 * q + h] + o * NB, soff);
+                                    } else {
+#pragma unroll
+                                        for (int m = 0; m < NB; ++m) val[2 * q + h][o * NB + m] = 0.0f;
+                                    }
                                 }
                             }
                         }
 #pragma unroll
                         for (int q = 0; q < 2 * kCellGroup; ++q) {
                             if constexpr (NB == 1) {
-                                if (q % 2 == 0)
-                                    acc[0] += mul_legacy(len[q], val[q][0]);
-                                else
-                                    acc[0] = fmaf(len[q], val[q][0], acc[0]);
+#pragma unroll
+                                for (int o = 0; o < P; ++o) {
+                                    if (q % 2 == 0)
+                                        acc[o] += mul_legacy(len[q], val[q][o]);
+                                    else
+                                        acc[o] = fmaf(len[q], val[q][o], acc[o]);
+                                }
                             } else {
 #pragma unroll
                                 for (int m = 0; m < NB; ++m) acc[m] = fmaf(len[q], val[q][m], acc[m]);
@@ -472,6 +502,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
             }
             for (; p < count; ++p) {
                 const double tb = E[p].tb;
+                if constexpr (P == 4) c1 = (uint32_t)C1[p];
                 row_cell(r, ta, tb, E[p].cxy, cz, kz, nz, visit);
                 ta = tb;
             }
@@ -479,8 +510,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
             ky0 += count - a;
             done += count;
             if (done >= total) {
-                const int32_t cxy = (c.x.c0 + c.x.step * c.x.steps) * A.H + (c.y.c0 + c.y.step * c.y.steps);
-                row_cell(r, ta, c.T, cxy, cz, kz, nz, visit);
+                const int32_t ix = c.x.c0 + c.x.step * c.x.steps, iy = c.y.c0 + c.y.step * c.y.steps;
+                if constexpr (P == 4) {
+                    int32_t ox, oy;
+                    orbit_cell(4, dir, A.box.n[0], A.H, ix, iy, 1, ox, oy);
+                    c1 = (uint32_t)(ox * A.H + oy);
+                }
+                row_cell(r, ta, c.T, ix * A.H + iy, cz, kz, nz, visit);
                 break;
             }
             wave_lds_sync();
@@ -488,8 +524,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 
     }
     if (t.valid) {
         const int64_t ray = (int64_t)(((uint64_t)ray_hi << 32) | ray_lo) + (int64_t)lane * A.cols;
+        if constexpr (P == 1) {
 #pragma unroll
-        for (int m = 0; m < NB; ++m) sino.p[m][ray] = acc[m] * r.kappa;
+            for (int m = 0; m < NB; ++m) sino.p[m][ray] = acc[m] * r.kappa;
+        } else {
+#pragma unroll
+            for (int m = 0; m < P; ++m) sino.p[0][ray + m * slot_stride] = acc[m] * r.kappa;
+        }
     }
 }
 
@@ -1665,19 +1706,27 @@ hipError_t launch_generic_adjoint(const GenericLaunch& a, const float* const* si
 }
 
 hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol,
-                                 float* const* sino, hipStream_t s) {
+                                 float* const* sino, hipStream_t s, int orbit, int dir,
+                                 int64_t slot_stride) {
     if (a.tasks == 0) return hipSuccess;
+    if (orbit != 1 && (nb != 1 || (orbit != 2 && orbit != 4) || a.box.n[0] % 2 != 0 ||
+                       (orbit == 4 && a.box.n[0] != a.H)))
+        return hipErrorInvalidValue;
     MPtrs4 o{};
     for (int m = 0; m < nb; ++m) o.p[m] = sino[m];
     const dim3 grid((unsigned)((int64_t)a.nviews * ((a.cols + 3) / 4) * a.row_blocks));
     const bool flat = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)a.box.n[2] * (uint64_t)nb *
                           sizeof(float) < (1ull << 31);
     trace_launch(flat ? "column_forward_kernel<flat>" : "column_forward_kernel<resource per cell>", grid,
-                 dim3(256), 0, "views %d..%d members %d", a.view0, a.view0 + a.nviews - 1, nb);
-#define MBP_FORWARD(NB_, FLAT_) \
-    if (nb == NB_ && flat == FLAT_) column_forward_kernel<NB_, FLAT_><<<grid, dim3(256), 0, s>>>(a, vol, o)
-    MBP_FORWARD(1, true); else MBP_FORWARD(1, false); else MBP_FORWARD(2, true); else MBP_FORWARD(2, false);
-    else MBP_FORWARD(4, true); else MBP_FORWARD(4, false);
+                 dim3(256), 0, "views %d..%d members %d orbit %d (turn %d)", a.view0, a.view0 + a.nviews - 1,
+                 nb, orbit, dir);
+#define MBP_FORWARD(NB_, FLAT_, P_) \
+    if (nb == NB_ && flat == FLAT_ && orbit == P_) \
+        column_forward_kernel<NB_, FLAT_, P_><<<grid, dim3(256), 0, s>>>(a, vol, o, slot_stride, dir)
+    MBP_FORWARD(1, true, 1); else MBP_FORWARD(1, false, 1); else MBP_FORWARD(2, true, 1);
+    else MBP_FORWARD(2, false, 1); else MBP_FORWARD(4, true, 1); else MBP_FORWARD(4, false, 1);
+    else MBP_FORWARD(1, true, 2); else MBP_FORWARD(1, false, 2);
+    else MBP_FORWARD(1, true, 4); else MBP_FORWARD(1, false, 4);
     else return hipErrorInvalidValue;
 #undef MBP_FORWARD
     return hipGetLastError();

@@ -44,8 +44,12 @@ hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vo
                                   float* const* sino, hipStream_t s);
 hipError_t launch_generic_adjoint(const GenericLaunch& a, const float* const* sino,
                                   float* const* vol, hipStream_t s);
+// orbit 2 or 4 (nb = 1): the launch's views lie among the first q = V / orbit, and each ray's
+// walk also gives the rays of the views q m apart (orbit_cell), stored slot_stride * m
+// elements after it (slot_stride = q rows cols); dir: the quarter turn's sense.
 hipError_t launch_column_forward(const ColumnLaunch& a, int nb, const float* vol,
-                                 float* const* sino, hipStream_t s);
+                                 float* const* sino, hipStream_t s, int orbit = 1, int dir = 0,
+                                 int64_t slot_stride = 0);
 hipError_t launch_column_adjoint(const ColumnLaunch& a, int nb, const float* const* sino,
                                  float* vol, hipStream_t s);
 

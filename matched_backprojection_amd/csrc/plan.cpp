@@ -109,6 +109,7 @@ struct mbp_plan {
     int32_t orbit_dir = 0;
     bool orbit_enabled = true;
     int32_t last_orbit = 0;           // cells that shared each item in the last backprojection
+    int32_t last_fwd_orbit = 0;       // rays that shared each walk in the last projection
     std::mutex mu;
 };
 
@@ -478,12 +479,18 @@ int run_column(mbp_plan* p, DeviceState* d, bool adjoint, const float* native_in
     const mbp_geometry& g = p->g;
     mbp::ColumnLaunch a = column_args(p, d);
     const int64_t vb = views_per_launch(p);
-    for (int64_t v0 = 0; v0 < g.views; v0 += vb) {
+    // the forward of one member shares each walk over the views' turn symmetry: launches over
+    // the first V / orbit views, each ray also giving the rays of the views V / orbit apart
+    const int32_t orbit = !adjoint && nb == 1 && p->orbit_enabled ? p->orbit : 1;
+    const int64_t views = g.views / orbit;
+    if (!adjoint) p->last_fwd_orbit = p->last_fwd_orbit ? std::min(p->last_fwd_orbit, orbit) : orbit;
+    for (int64_t v0 = 0; v0 < views; v0 += vb) {
         a.view0 = (int32_t)v0;
-        a.nviews = (int32_t)std::min(vb, g.views - v0);
+        a.nviews = (int32_t)std::min(vb, views - v0);
         a.tasks = (uint32_t)((int64_t)a.nviews * a.cols * a.row_blocks);
         hipError_t e = adjoint ? mbp::launch_column_adjoint(a, nb, sino_in, native_out, s)
-                               : mbp::launch_column_forward(a, nb, native_in, sino_out, s);
+                               : mbp::launch_column_forward(a, nb, native_in, sino_out, s, orbit, p->orbit_dir,
+                                                            views * g.rows * g.cols);
         if (e != hipSuccess) return hip_fail(e, adjoint ? "column adjoint launch" : "column forward launch");
     }
     return MBP_OK;
@@ -637,6 +644,7 @@ int mbp_plan_get_info(const mbp_plan* plan, mbp_plan_info* info) {
     info->last_forward_members_per_pass = plan->last_fwd_members;
     info->orbit = plan->orbit;
     info->last_adjoint_orbit = plan->last_orbit;
+    info->last_forward_orbit = plan->last_fwd_orbit;
     return MBP_OK;
 }
 
@@ -706,6 +714,7 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
     int64_t m0 = 0;
     plan->last_fwd_walk = MBP_PATH_GENERIC;
     plan->last_fwd_members = 0;
+    plan->last_fwd_orbit = 0;         // the fewest rays any column pass shared a walk over
     if (active_path(plan) == MBP_PATH_COLUMN) {
         const bool whd = g.layout == MBP_LAYOUT_WHD;
         plan->last_fwd_walk = MBP_PATH_COLUMN;
@@ -752,6 +761,7 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
         const int nb = (int)std::min<int64_t>(4, batch - m0);
         rc = run_generic(plan, d, false, volume, sinogram, m0, nb, s);
         if (rc != MBP_OK) return rc;
+        plan->last_fwd_orbit = 1;
         m0 += nb;
     }
     return MBP_OK;

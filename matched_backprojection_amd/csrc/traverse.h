@@ -698,9 +698,11 @@ MBP_HD MBP_INLINE int64_t gather_sino_floats(int32_t views, int32_t cols, int32_
 // grid's xy centre, and that turn maps the grid's cells onto cells, then line (view v + m q,
 // column j) crosses cell C exactly as line (v, j) crosses the cell turned back by m steps: the
 // intersection lengths are a property of the pair, and turning both leaves them unchanged. The
-// gather then gives one wave the P cells of an orbit c, R c, ..., R^(P-1) c (R: one step of the
-// turn) and forms items for views v < q only: the item of line (v, j) with cell R^a c carries the
-// rows of line (v + m q, j) into cell R^(a+m) c, for every m.
+// forward then walks the rays of views v < q only: the walk of ray (v, j, row) through cells C
+// gives ray (v + m q, j, row) from the cells R^m C (R: one step of the turn). The gather gives
+// one wave the P cells of an orbit c, R c, ..., R^(P-1) c and forms items for views v < q
+// only: the item of line (v, j) with cell R^a c carries the rows of line (v + m q, j) into
+// cell R^(a+m) c, for every m.
 //
 // orbit_cell: cell (ox, oy) = R^a (ix, iy) on a W x H grid. P = 2: the half turn,
 // (ix, iy) -> (W-1-ix, H-1-iy). P = 4 (square grid, W == H): a quarter turn, anticlockwise seen
@@ -722,6 +724,21 @@ MBP_HD MBP_INLINE void orbit_cell(int32_t P, int32_t dir, int32_t W, int32_t H, 
             ox = y;
             oy = W - 1 - x;
         }
+    }
+}
+
+// The column indices (ix * H + iy) of the cells of an orbit, slot m holding the cell turned m
+// steps (orbit_cell): the half turn of a cell is W H - 1 - cxy; for a quarter turn (W == H)
+// slot 1 is c1, the cell's quarter turn (from its ix and iy), slot 2 its half turn and slot 3
+// the half turn of c1. WH1 = W H - 1.
+template <int P>
+MBP_HD MBP_INLINE void orbit_columns(uint32_t cxy, uint32_t c1, uint32_t WH1, uint32_t (&cell)[P]) {
+    cell[0] = cxy;
+    if (P == 2) cell[1 % P] = WH1 - cxy;
+    if (P == 4) {
+        cell[1 % P] = c1;
+        cell[2 % P] = WH1 - cxy;
+        cell[3 % P] = WH1 - c1;
     }
 }
 
@@ -1018,9 +1035,17 @@ MBP_HD MBP_INLINE int32_t count_before(const AxisWalk& a, int32_t k0, int32_t n,
 // Fill the entries of one lane's candidates (window indices lane and lane + 64 of each axis)
 // for the chunk of `count` crossings after kx0 x and ky0 y crossings. Returns how many of
 // this lane's x candidates fall inside the chunk (their sum over lanes is the number of x
-// crossings the chunk consumes).
+// crossings the chunk consumes). With C1, C1[pos] also receives the column index of the
+// event's cell turned a quarter turn of sense dir on the square W x H grid (orbit_cell).
 MBP_HD MBP_INLINE int32_t xy_chunk_fill(const ColumnWalk& c, int32_t H, int32_t kx0, int32_t ky0,
-                                        int32_t count, int32_t lane, XYEvent* E) {
+                                        int32_t count, int32_t lane, XYEvent* E,
+                                        int32_t* C1 = nullptr, int32_t W = 0, int32_t dir = 0) {
+    auto turned = [&](int32_t pos, int32_t ix, int32_t iy) {
+        if (!C1) return;
+        int32_t ox, oy;
+        orbit_cell(4, dir, W, H, ix, iy, 1, ox, oy);
+        C1[pos] = ox * H + oy;
+    };
     const int32_t nxw = c.x.steps - kx0 < kXYChunk ? c.x.steps - kx0 : kXYChunk;
     const int32_t nyw = c.y.steps - ky0 < kXYChunk ? c.y.steps - ky0 : kXYChunk;
     int32_t xin = 0;
@@ -1031,8 +1056,10 @@ MBP_HD MBP_INLINE int32_t xy_chunk_fill(const ColumnWalk& c, int32_t H, int32_t 
             const int32_t jy = count_before(c.y, ky0, nyw, tx, true);
             const int32_t pos = i + jy;
             if (pos < count) {
+                const int32_t ix = c.x.c0 + c.x.step * (kx0 + i), iy = c.y.c0 + c.y.step * (ky0 + jy);
                 E[pos].tb = tx;
-                E[pos].cxy = (c.x.c0 + c.x.step * (kx0 + i)) * H + (c.y.c0 + c.y.step * (ky0 + jy));
+                E[pos].cxy = ix * H + iy;
+                turned(pos, ix, iy);
                 ++xin;
             }
         }
@@ -1041,8 +1068,10 @@ MBP_HD MBP_INLINE int32_t xy_chunk_fill(const ColumnWalk& c, int32_t H, int32_t 
             const int32_t ix = count_before(c.x, kx0, nxw, ty, false);
             const int32_t pos = i + ix;
             if (pos < count) {
+                const int32_t cx = c.x.c0 + c.x.step * (kx0 + ix), cy = c.y.c0 + c.y.step * (ky0 + i);
                 E[pos].tb = ty;
-                E[pos].cxy = (c.x.c0 + c.x.step * (kx0 + ix)) * H + (c.y.c0 + c.y.step * (ky0 + i));
+                E[pos].cxy = cx * H + cy;
+                turned(pos, cx, cy);
             }
         }
     }

@@ -36,7 +36,7 @@ def _load():
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
         lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, I, P, P, P, I, I]
-        lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P]
+        lib.mbph_project_chunked.argtypes = [P, I, P, P, P, I, I, I, D, D, P, P, P, I, I]
         lib.mbph_gather_conflicts.argtypes = [P, I, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_tilt_band.argtypes = [P, P, P, P, I, I, I, D, D, I, P, P]
         lib.mbph_tilt_gather.argtypes = [P, P, P, P, I, I, I, D, D, P, I, P, P, P]
@@ -194,8 +194,10 @@ def fast_inside(geom: dict, traj: dict, zchunk: int, mode: int = 0):
     return int(fast), int(inside.value), int(viol.value)
 
 
-def project_chunked(geom: dict, traj: dict, vol: np.ndarray):
-    """Replay the forward kernel's chunked column walk on a (D, H, W) float32 volume."""
+def project_chunked(geom: dict, traj: dict, vol: np.ndarray, orbit: int = 1, turn: int = 0):
+    """Replay the forward kernel's chunked column walk on a (D, H, W) float32 volume; orbit 2
+    or 4 (turn: the quarter turn's sense): walks shared over the turn symmetry of the views,
+    as the kernel shares them."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
     rows = int(geom.get("rows", 1))
@@ -205,7 +207,7 @@ def project_chunked(geom: dict, traj: dict, vol: np.ndarray):
     viol = ctypes.c_longlong(0)
     lib.mbph_project_chunked(_ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(p), _ptr(n), views, rows,
                              cols, float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)),
-                             _ptr(vol), _ptr(sino), ctypes.byref(viol))
+                             _ptr(vol), _ptr(sino), ctypes.byref(viol), int(orbit), int(turn))
     return sino, int(viol.value)
 
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared) == set(_capi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.mbp_abi_version() == 3
+    assert lib.mbp_abi_version() == 4
     assert lib.mbp_status_string(_capi.MBP_ERANGE) == b"geometry out of range"
 
 
@@ -386,7 +386,7 @@ def test_turn_symmetry_of_the_views(lib):
         rc, h = _create(lib, g, config_trajectory(cfg) if traj is None else traj)
         assert rc == 0, lib.mbp_last_error()
         inf = _info(lib, h)
-        assert inf.last_adjoint_orbit == 0
+        assert inf.last_adjoint_orbit == 0 and inf.last_forward_orbit == 0
         lib.mbp_plan_destroy(h)
         return inf.orbit
 

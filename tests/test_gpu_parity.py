@@ -413,16 +413,18 @@ def test_tilted_circular_parity(torch_dev, mbp, oracle, layout):
 
 @pytest.mark.parametrize("case", ["quarter", "quarter_clockwise", "half", "half_rect",
                                   "parallel3d_quarter"])
-def test_orbit_gather_parity(torch_dev, mbp, oracle, case):
-    """The gather shared over a turn symmetry of the views (one crossing serves the P cells of
-    an orbit): the plan finds the symmetry, the backprojection takes it in both layouts and
-    when adding into a volume, and matches the oracle, the unshared gather (to fp32 rounding)
-    and the forward projection's adjoint identity."""
+def test_orbit_pair_parity(torch_dev, mbp, oracle, case):
+    """The pair shared over a turn symmetry of the views (one walk gives the P rays of the
+    views V / P apart; one gather crossing serves the P cells of an orbit): the plan finds the
+    symmetry, both operators take it in both layouts (the gather also when adding into a
+    volume, the forward also per member of a batch), and they match the oracle, the unshared
+    operators (to fp32 rounding) and the adjoint identity."""
     from tests.test_hostcheck import _turn_cases
     torch, dev = torch_dev
     cfg, traj, P, turn = _turn_cases()[case]
     geom = geom_of(cfg)
     x = config_phantom(cfg)
+    ref = oracle.project(geom, traj, x)
     y = np.random.default_rng(5).random((cfg.views, cfg.rows, cfg.cols)).astype(np.float32)
     bref = oracle.backproject(geom, traj, y)
     pre = np.random.default_rng(6).random(cfg.shape).astype(np.float32)
@@ -437,18 +439,29 @@ def test_orbit_gather_parity(torch_dev, mbp, oracle, case):
         out = to_device_volume(torch, dev, pre, layout)
         plan.backproject(yd, out=out, accumulate=True)
         check(out.cpu().numpy().astype(np.float64), bref + pre.astype(np.float64), "orbit accumulate")
-        p = plan.project(to_device_volume(torch, dev, x, layout)).cpu().numpy().astype(np.float64)
+        xd = to_device_volume(torch, dev, x, layout)
+        p = plan.project(xd).cpu().numpy().astype(np.float64)
+        assert plan.info["last_forward_orbit"] == P
+        check(p, ref, "orbit forward")
         lhs = float(np.dot(p.ravel(), y.astype(np.float64).ravel()))
         rhs = float(np.dot(x.astype(np.float64).ravel(), b.ravel()))
         say(f"  adjoint identity {abs(lhs - rhs) / abs(lhs):.2e}")
         assert abs(lhs - rhs) <= RTOL_ADJ * abs(lhs)
+        # a batch of three: an interleaved pair, then the last member alone, which alone takes
+        # the symmetry
+        x3 = np.stack([x, 0.5 * x, x[::-1].copy()]).astype(np.float32)
+        p3 = plan.project(to_device_volume(torch, dev, x3, layout)).cpu().numpy().astype(np.float64)
+        assert plan.info["last_forward_orbit"] == 1
+        check(p3[2], oracle.project(geom, traj, x3[2]), "orbit forward, batch member 2")
         plan.set_orbit(False)
         b1 = plan.backproject(yd).cpu().numpy().astype(np.float64)
-        assert plan.info["last_adjoint_orbit"] == 1
+        p1 = plan.project(xd).cpu().numpy().astype(np.float64)
+        assert plan.info["last_adjoint_orbit"] == 1 and plan.info["last_forward_orbit"] == 1
         check(b1, bref, "unshared gather")
-        d = rel_l2(b, b1)
-        say(f"  shared vs unshared rel-L2 {d:.2e}")
-        assert d <= 1e-6
+        check(p1, ref, "unshared forward")
+        d, df = rel_l2(b, b1), rel_l2(p, p1)
+        say(f"  shared vs unshared rel-L2: adjoint {d:.2e}, forward {df:.2e}")
+        assert d <= 1e-6 and df <= 1e-6
         plan.close()
 
 

@@ -22,6 +22,7 @@ def test_trace_prints_each_launch(capfd):
                     (cfg.dv, cfg.du))
     x = torch.from_numpy(config_phantom(cfg)).to("cuda")
     plan.set_view_batch(20)                          # 36 views: launches of 20 and 16
+    plan.set_orbit(False)                            # every view walked (see below for the half turn)
     os.environ["MBP_TRACE"] = "1"
     try:
         y = plan.project(x)
@@ -49,6 +50,30 @@ def test_trace_prints_each_launch(capfd):
     assert all(int(m.group(5)) == 256 for m in fwd)
     gat = [m for m in parsed if m.group(1) == "column_gather_kernel"]
     assert all(int(m.group(6)) > 0 and int(m.group(5)) == 256 for m in gat)
+    # the 36 views on a 56-wide grid have a half-turn symmetry: with all views in one launch,
+    # the forward walks views 0..17 only (each walk also giving the view 18 later), the
+    # pre-pass pairs views 18 apart and one gather serves both cells of each pair
+    assert plan.info["orbit"] == 2
+    plan.set_orbit(True)
+    plan.set_view_batch(0)
+    os.environ["MBP_TRACE"] = "1"
+    try:
+        y = plan.project(x)
+        plan.backproject(y)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["MBP_TRACE"]
+    lines = [l for l in capfd.readouterr().err.splitlines() if l.startswith("mbp-trace ")]
+    print("\n".join(lines))
+    parsed = [pat.match(l) for l in lines]
+    fwd = [m for m in parsed if m.group(1) == "column_forward_kernel<flat>"]
+    assert len(fwd) == 1 and "views 0..17 members 1 orbit 2" in fwd[0].group(7)
+    assert int(fwd[0].group(2)) == 18 * quads * row_blocks
+    pre = [m for m in parsed if m.group(1) == "sino_prepass_kernel"]
+    assert len(pre) == 1 and "views 0..17 members 2" in pre[0].group(7) and "apart 18" in pre[0].group(7)
+    gat = [m for m in parsed if m.group(1) == "column_gather_kernel"]
+    assert len(gat) == 1 and "members 1 orbit 2" in gat[0].group(7)
+    assert plan.info["last_forward_orbit"] == 2 and plan.info["last_adjoint_orbit"] == 2
     # unset: silent
     plan.project(x)
     torch.cuda.synchronize()
