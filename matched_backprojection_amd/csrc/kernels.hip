@@ -1821,11 +1821,15 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     orbit_grid(orbit, W, H, Wr, Hr);
     const uint64_t tasks = (uint64_t)Wr * (uint64_t)Hr * (uint64_t)nchunks;
     // tiles of 64 x 8 cells (measured against 16 x 32, 32 x 16, 32 x 32, 64 x 16 and 16 x 64:
-    // 2.5% faster than 16 x 32 on the 512^3 cone), else 16 x 32, else plain y-fastest order;
-    // an orbit's tasks tile the grid of the cells that stand for the orbits
-    const bool wide = Wr % 64 == 0 && Hr % 8 == 0;
-    const bool tiled = wide || (Wr % 16 == 0 && Hr % 32 == 0);
-    const int32_t tx = wide ? 64 : tiled ? 16 : 1, ty = wide ? 8 : tiled ? 32 : Hr;
+    // 2.5% faster than 16 x 32 on the 512^3 cone), else 16 x 32, else plain y-fastest order.
+    // An orbit's tasks tile the grid of the cells that stand for the orbits, in 8 x 8 tiles:
+    // its lines hold `orbit` views each, and a smaller patch keeps the lines its waves share
+    // in L2 (against 64 x 8: the 256^3 cone -8%, the 360-view 512^3 cone -1%, the 720-view
+    // 512^3 cone unchanged; 16 x 16, 32 x 8, 32 x 16 and 16 x 32 no better)
+    const bool small = orbit > 1 && Wr % 8 == 0 && Hr % 8 == 0;
+    const bool wide = !small && Wr % 64 == 0 && Hr % 8 == 0;
+    const bool tiled = small || wide || (Wr % 16 == 0 && Hr % 32 == 0);
+    const int32_t tx = small ? 8 : wide ? 64 : tiled ? 16 : 1, ty = small || wide ? 8 : tiled ? 32 : Hr;
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
