@@ -61,10 +61,13 @@ extern "C" {
 // Forward projection with the generic (path 1) or column (path 2) walk. frames: views x 12
 // doubles (s, c, u, v); volume element (x, y, z) at x*sx + y*sy + z*sz. Outputs the fp32
 // sinogram [views][rows][cols], per-ray counts of segments longer than 1e-6 min pitch, and the number of bound violations.
+// With orbit 2 or 4 (the generic walk; dir: the quarter turn's sense), the rays of the first
+// views / orbit views are walked as the kernel shares them over a turn symmetry of the views
+// (walk_ray_orbit), each also giving the rays of the views views / orbit apart.
 int mbph_project(int path, const double* frames, int beam, const double* lo, const double* hi,
                  const double* pitch, const int32_t* n, int views, int rows, int cols,
                  double du, double dv, const float* vol, int64_t sx, int64_t sy, int64_t sz,
-                 float* sino, int64_t* counts, long long* violations) {
+                 float* sino, int64_t* counts, long long* violations, int orbit, int dir) {
     (void)hi;
     std::vector<Frame> F;
     frames_from(frames, views, F);
@@ -72,6 +75,43 @@ int mbph_project(int path, const double* frames, int beam, const double* lo, con
     *violations = 0;
     Checked chk{&B, violations};
     const float eps = (float)(1e-6 * std::fmin(B.pitch[0], std::fmin(B.pitch[1], B.pitch[2])));
+    if (orbit > 1) {
+        if (path != 1) return -1;
+        const int q = views / orbit;
+        const int64_t vox = (int64_t)n[0] * n[1] * n[2];
+        int32_t base[4] = {0, 0, 0, 0}, tx[4] = {0, 0, 0, 0}, ty[4] = {0, 0, 0, 0};
+        for (int m = 0; m < orbit; ++m)
+            orbit_strides(orbit, dir, n[0], n[1], (int32_t)sx, (int32_t)sy, m, base[m], tx[m], ty[m]);
+        for (int i = 0; i < q; ++i)
+            for (int j = 0; j < cols; ++j)
+                for (int k = 0; k < rows; ++k) {
+                    RayWalk r;
+                    ray_setup(F[i], B, beam, centred(j, cols, du), centred(k, rows, dv), r);
+                    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    int64_t cnt = 0;
+                    auto visit = [&](const int32_t* off, float len) {
+                        if (len > eps) ++cnt;
+                        for (int m = 0; m < orbit; ++m) {
+                            if (off[m] < 0 || off[m] >= vox || !(len >= 0.0f)) { ++*violations; continue; }
+                            acc[m] = fmaf(len, vol[off[m]], acc[m]);
+                        }
+                    };
+                    if (orbit == 2) {
+                        auto v2 = [&](const int32_t (&off)[2], float len) { visit(off, len); };
+                        const int32_t b2[2] = {base[0], base[1]}, x2[2] = {tx[0], tx[1]}, y2[2] = {ty[0], ty[1]};
+                        walk_ray_orbit<2>(r, b2, x2, y2, (int32_t)sz, v2);
+                    } else {
+                        auto v4 = [&](const int32_t (&off)[4], float len) { visit(off, len); };
+                        walk_ray_orbit<4>(r, base, tx, ty, (int32_t)sz, v4);
+                    }
+                    for (int m = 0; m < orbit; ++m) {
+                        const int64_t ray = ((int64_t)(i + m * q) * rows + k) * cols + j;
+                        sino[ray] = acc[m];
+                        if (counts) counts[ray] = cnt;
+                    }
+                }
+        return 0;
+    }
     for (int i = 0; i < views; ++i) {
         for (int j = 0; j < cols; ++j) {
             ColumnWalk c;

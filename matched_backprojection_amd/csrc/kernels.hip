@@ -71,8 +71,13 @@ __device__ __forceinline__ void generic_pixel(const GenericLaunch& A, uint32_t& 
     }
 }
 
+// P > 1 (one member): the walk shared over a turn symmetry of the views (orbit_cell). The
+// launch's views are among the first q = V / P; each ray's walk also sums the turned cells
+// (walk_ray_orbit) into the rays of the views q m later, stored slot_stride m elements after it.
+template <int P>
 __global__ void __launch_bounds__(256) generic_forward_kernel(const GenericLaunch A,
-                                                              const Ptrs4 vol, const MPtrs4 sino) {
+                                                              const Ptrs4 vol, const MPtrs4 sino,
+                                                              int64_t slot_stride, int32_t dir) {
     const uint32_t per_view = (uint32_t)A.rows * (uint32_t)A.cols;
     const uint32_t rid = blockIdx.x * 256u + threadIdx.x;
     if (rid >= (uint32_t)A.nviews * per_view) return;
@@ -89,18 +94,35 @@ __global__ void __launch_bounds__(256) generic_forward_kernel(const GenericLaunc
     // the voxel's element offset is kept by the walk (one add per crossing) rather than formed
     // from the cell indices and strides (three 32-bit multiplies per segment): -7% on the
     // tilted 256^3 cone
-    auto visit = [&](int32_t idx, float len) {
-        acc0 = fmaf(len, vol.p[0][idx], acc0);
-        if (nb > 1) acc1 = fmaf(len, vol.p[1][idx], acc1);
-        if (nb > 2) acc2 = fmaf(len, vol.p[2][idx], acc2);
-        if (nb > 3) acc3 = fmaf(len, vol.p[3][idx], acc3);
-    };
-    walk_ray_offsets(r, A.sx, A.sy, A.sz, visit);
     const int64_t ray = (int64_t)view * per_view + rem;
-    sino.p[0][ray] = acc0;
-    if (nb > 1) sino.p[1][ray] = acc1;
-    if (nb > 2) sino.p[2][ray] = acc2;
-    if (nb > 3) sino.p[3][ray] = acc3;
+    if constexpr (P == 1) {
+        auto visit = [&](int32_t idx, float len) {
+            acc0 = fmaf(len, vol.p[0][idx], acc0);
+            if (nb > 1) acc1 = fmaf(len, vol.p[1][idx], acc1);
+            if (nb > 2) acc2 = fmaf(len, vol.p[2][idx], acc2);
+            if (nb > 3) acc3 = fmaf(len, vol.p[3][idx], acc3);
+        };
+        walk_ray_offsets(r, A.sx, A.sy, A.sz, visit);
+        sino.p[0][ray] = acc0;
+        if (nb > 1) sino.p[1][ray] = acc1;
+        if (nb > 2) sino.p[2][ray] = acc2;
+        if (nb > 3) sino.p[3][ray] = acc3;
+    } else {
+        int32_t base[P], tx[P], ty[P];
+#pragma unroll
+        for (int m = 0; m < P; ++m)
+            orbit_strides(P, dir, A.box.n[0], A.box.n[1], A.sx, A.sy, m, base[m], tx[m], ty[m]);
+        float acc[P];
+#pragma unroll
+        for (int m = 0; m < P; ++m) acc[m] = 0.0f;
+        auto visit = [&](const int32_t (&idx)[P], float len) {
+#pragma unroll
+            for (int m = 0; m < P; ++m) acc[m] = fmaf(len, vol.p[0][idx[m]], acc[m]);
+        };
+        walk_ray_orbit<P>(r, base, tx, ty, A.sz, visit);
+#pragma unroll
+        for (int m = 0; m < P; ++m) sino.p[0][ray + m * slot_stride] = acc[m];
+    }
 }
 
 __global__ void __launch_bounds__(256) generic_adjoint_kernel(const GenericLaunch A,
@@ -1260,20 +1282,29 @@ __device__ __forceinline__ void tilt_clip_walls(const double (&d)[2], const doub
     t1 = b;
 }
 
-template <int NB>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+// P > 1: shared over a turn symmetry of the views as column_gather_kernel is (orbit_cell): the
+// launch's views are the first q = nviews / P, member m of the reordered sinogram is the line
+// of view v + m q, and a wave owns the P cells of an orbit as the NB == P slots of its column.
+// Occupancy: four waves per SIMD for one member or slot; three (168 registers) for two and
+// four, which at four waves spilled 5 and 23 registers per thread.
+template <int NB, int P>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 3)))
 tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* __restrict__ vol,
-                   int32_t zchunk, int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate) {
+                   int32_t zchunk, int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate,
+                   int32_t dir) {
+    static_assert(P == 1 || P == NB, "an orbit takes one member per slot");
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
     const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
     const uint32_t task = blk * 4u + wave;
     const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
+    int32_t Wr, Hr;
+    orbit_grid(P, W, H, Wr, Hr);
     const int32_t zc = (int32_t)(task % (uint32_t)nchunks);
-    const bool live = task < (uint32_t)W * (uint32_t)H * (uint32_t)nchunks;
+    const bool live = task < (uint32_t)Wr * (uint32_t)Hr * (uint32_t)nchunks;
     int32_t ix, iy;
-    gather_tile_cell(task / (uint32_t)nchunks, H, tx, ty, ix, iy);
+    gather_tile_cell(task / (uint32_t)nchunks, Hr, tx, ty, ix, iy);
     const int32_t z0 = zc * zchunk;
     const int32_t z1 = live ? (z0 + zchunk < D ? z0 + zchunk : D) : z0;
     const int32_t n = z1 - z0;
@@ -1284,10 +1315,8 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
     for (int32_t i = lane; i < colf; i += 64) cols[i] = 0.0f;
     __syncthreads();
     if (live) {
-        const double x0 = A.box.lo[0] + ix * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
-        const double y0 = A.box.lo[1] + iy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
         const int32_t rows_pad = gather_rows_padded(A.rows);
-        const int32_t vend = A.view0 + A.nviews;
+        const int32_t vend = A.view0 + A.nviews / P;
         const double ipz = 1.0 / A.box.pitch[2];
         const int32_t a0 = lds_addr(col);
         lds_float* const park = lds_ptr(a0 - 8 * NB);
@@ -1317,7 +1346,9 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
             int32_t i0;
             bool active, two, lng, up;
         };
-        auto prep = [&](const TiltItem& it, const float (&w)[NB], Row& R) {
+        // SH: the slots take the members turned by SH places (slot m adds member (m - SH) mod NB)
+        auto prep = [&](auto shift, const TiltItem& it, const float (&w)[NB], Row& R) __attribute__((always_inline)) {
+            constexpr int SH = decltype(shift)::value;
             const int32_t nrows = (int32_t)uniform((uint32_t)it.nrows);
             // the row's ray direction: xy in world units, z in cells per unit parameter
             const double v = it.v0 + lane_dv;
@@ -1351,14 +1382,15 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
             R.two = R.active && !R.lng;
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
-                const float q = R.two ? dt * w[m] : 0.0f;
+                const float q = R.two ? dt * w[(m + NB - SH) % NB] : 0.0f;
                 R.qa[m] = f * q;
                 R.qb[m] = g * q;
             }
             R.i0 = (int32_t)fmax(fmin(fa - (double)(z0 - 1), (double)(n + 1)), -2.0);
             R.up = it.evzc >= 0.0;
         };
-        auto commit = [&](const Row& R, const float (&w)[NB]) {
+        auto commit = [&](auto shift, const Row& R, const float (&w)[NB]) __attribute__((always_inline)) {
+            constexpr int SH = decltype(shift)::value;
             // pair address, clamped to the parked pairs below and above the chunk; lanes past
             // the item's crossing rows take the parked pair at their end of the column, so the
             // addresses stay monotone when the rows' cells are
@@ -1394,7 +1426,7 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
                 auto piece = [&](int32_t iz, double share) {
                     float* const c = col + (iz - z0 + 1) * NB;
 #pragma unroll
-                    for (int m = 0; m < NB; ++m) atomicAdd(c + m, (float)share * w[m]);
+                    for (int m = 0; m < NB; ++m) atomicAdd(c + m, (float)share * w[(m + NB - SH) % NB]);
                 };
                 row_pieces_split(R.za, R.zb, R.dtd, z0, z1, false, piece);
             }
@@ -1408,7 +1440,8 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
         // Items in queue order, two at a time; the next two items' row values are loaded while
         // the current ones are summed (the buffers swap roles from step to step). An item whose
         // rows are all zero adds nothing.
-        auto drain = [&](int32_t count) {
+        // The queue's items all belong to one cell of the orbit (slot SH = decltype(shift)).
+        auto drain = [&](auto shift, int32_t count) __attribute__((always_inline)) {
             if (count == 0) return;
             float wa[2][NB], wb[2][NB];
             load_rows(0, wa[0]);
@@ -1424,10 +1457,10 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
                     // both preps unconditionally (the last of an odd count preps a copy of its
                     // predecessor, never committed), so that their instructions can interleave
                     Row r0, r1;
-                    prep(Q[i], cur[0], r0);
-                    prep(Q[two_items ? i + 1 : i], cur[1], r1);
-                    if (nz0) commit(r0, cur[0]);
-                    if (nz1) commit(r1, cur[1]);
+                    prep(shift, Q[i], cur[0], r0);
+                    prep(shift, Q[two_items ? i + 1 : i], cur[1], r1);
+                    if (nz0) commit(shift, r0, cur[0]);
+                    if (nz1) commit(shift, r1, cur[1]);
                 }
                 i += 2;
                 return i < count;
@@ -1440,70 +1473,108 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
         // candidate columns j0 + r, j0 + r + kViewLanes, ... and emits the column's rows that
         // can cross the cell in pieces of at most 64.
         int32_t count = 0;
-        for (int32_t vb = A.view0; vb < vend; vb += 64 / kViewLanes) {
-            const int32_t view = vb + lane / kViewLanes;
-            TiltCorners T;
-            int32_t jn = 0, j1 = -1;
-            if (view < vend) {
-                tilt_corners(A.frames[view], x0, x1, y0, y1, T);
-                if (!tilt_column_range(T, A.rows, A.cols, A.du, A.dv, jn, j1)) j1 = -1;
+        auto flush = [&](int32_t a) __attribute__((always_inline)) {
+            if constexpr (P == 1) {
+                drain(std::integral_constant<int, 0>{}, count);
+            } else {
+                if (a == 0) drain(std::integral_constant<int, 0>{}, count);
+                else if (a == 1) drain(std::integral_constant<int, 1>{}, count);
+                else if constexpr (P == 4) {
+                    if (a == 2) drain(std::integral_constant<int, 2>{}, count);
+                    else drain(std::integral_constant<int, 3>{}, count);
+                }
             }
-            jn += lane % kViewLanes;
-            int32_t jc = 0, kk = 0, kl = -1;
-            for (;;) {
-                if (kk > kl && jn <= j1) {
-                    jc = jn;
-                    jn += kViewLanes;
-                    if (!tilt_row_range(T, jc, A.rows, A.cols, A.du, A.dv, kk, kl)) {
-                        kk = 0;
-                        kl = -1;
+            count = 0;
+        };
+        for (int32_t a = 0; a < P; ++a) {
+            if (a > 0) {
+                // the previous slot's last items
+                wave_lds_sync();
+                flush(a - 1);
+                wave_lds_sync();
+            }
+            int32_t cx, cy;
+            orbit_cell(P, dir, W, H, ix, iy, a, cx, cy);
+            const double x0 = A.box.lo[0] + cx * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
+            const double y0 = A.box.lo[1] + cy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
+            for (int32_t vb = A.view0; vb < vend; vb += 64 / kViewLanes) {
+                const int32_t view = vb + lane / kViewLanes;
+                TiltCorners T;
+                int32_t jn = 0, j1 = -1;
+                if (view < vend) {
+                    tilt_corners(A.frames[view], x0, x1, y0, y1, T);
+                    if (!tilt_column_range(T, A.rows, A.cols, A.du, A.dv, jn, j1)) j1 = -1;
+                }
+                jn += lane % kViewLanes;
+                int32_t jc = 0, kk = 0, kl = -1;
+                for (;;) {
+                    if (kk > kl && jn <= j1) {
+                        jc = jn;
+                        jn += kViewLanes;
+                        if (!tilt_row_range(T, jc, A.rows, A.cols, A.du, A.dv, kk, kl)) {
+                            kk = 0;
+                            kl = -1;
+                        }
                     }
-                }
-                const bool emit = kk <= kl;
-                if (__ballot(emit || jn <= j1) == 0) break;
-                const uint64_t m = __ballot(emit);
-                if (emit) {
-                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    const Frame& F = A.frames[view];
-                    const double u = centred(jc, A.cols, A.du);
-                    TiltItem t;
-                    t.bx = (F.c[0] - F.s[0]) + u * F.u[0];
-                    t.by = (F.c[1] - F.s[1]) + u * F.u[1];
-                    t.bzc = ((F.c[2] - F.s[2]) + u * F.u[2]) * ipz;
-                    t.evx = F.v[0];
-                    t.evy = F.v[1];
-                    t.evzc = F.v[2] * ipz;
-                    t.wx0 = x0 - F.s[0];
-                    t.wx1 = x1 - F.s[0];
-                    t.wy0 = y0 - F.s[1];
-                    t.wy1 = y1 - F.s[1];
-                    t.szc = (F.s[2] - A.box.lo[2]) * ipz;
-                    t.v0 = centred(kk, A.rows, A.dv);
-                    t.view = view;
-                    t.j = jc;
-                    t.k0 = kk;
-                    t.nrows = kl - kk + 1 < 64 ? kl - kk + 1 : 64;
-                    Q[count + (int32_t)below] = t;
-                    kk += 64;
-                }
-                count += (int32_t)__popcll(m);
-                if (count > kQueue - 64) {
-                    wave_lds_sync();
-                    drain(count);
-                    count = 0;
-                    wave_lds_sync();
+                    const bool emit = kk <= kl;
+                    if (__ballot(emit || jn <= j1) == 0) break;
+                    const uint64_t m = __ballot(emit);
+                    if (emit) {
+                        const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        const Frame& F = A.frames[view];
+                        const double u = centred(jc, A.cols, A.du);
+                        TiltItem t;
+                        t.bx = (F.c[0] - F.s[0]) + u * F.u[0];
+                        t.by = (F.c[1] - F.s[1]) + u * F.u[1];
+                        t.bzc = ((F.c[2] - F.s[2]) + u * F.u[2]) * ipz;
+                        t.evx = F.v[0];
+                        t.evy = F.v[1];
+                        t.evzc = F.v[2] * ipz;
+                        t.wx0 = x0 - F.s[0];
+                        t.wx1 = x1 - F.s[0];
+                        t.wy0 = y0 - F.s[1];
+                        t.wy1 = y1 - F.s[1];
+                        t.szc = (F.s[2] - A.box.lo[2]) * ipz;
+                        t.v0 = centred(kk, A.rows, A.dv);
+                        t.view = view;
+                        t.j = jc;
+                        t.k0 = kk;
+                        t.nrows = kl - kk + 1 < 64 ? kl - kk + 1 : 64;
+                        Q[count + (int32_t)below] = t;
+                        kk += 64;
+                    }
+                    count += (int32_t)__popcll(m);
+                    if (count > kQueue - 64) {
+                        wave_lds_sync();
+                        flush(a);
+                        wave_lds_sync();
+                    }
                 }
             }
         }
         wave_lds_sync();
-        drain(count);
+        flush(P - 1);
     }
     __syncthreads();
     if (live) {
-        const int64_t base = (((int64_t)ix * H + iy) * D + z0) * NB;
-        for (int32_t i = lane; i < n * NB; i += 64)
-            vol[base + i] = accumulate ? vol[base + i] + col[NB + i] : col[NB + i];
+        if constexpr (P == 1) {
+            const int64_t base = (((int64_t)ix * H + iy) * D + z0) * NB;
+            for (int32_t i = lane; i < n * NB; i += 64)
+                vol[base + i] = accumulate ? vol[base + i] + col[NB + i] : col[NB + i];
+        } else {
+            // slot a of z cell i is col[NB (i + 1) + a]; each slot's cell gets its own column
+#pragma unroll
+            for (int32_t a = 0; a < P; ++a) {
+                int32_t cx, cy;
+                orbit_cell(P, dir, W, H, ix, iy, a, cx, cy);
+                const int64_t base = ((int64_t)cx * H + cy) * D + z0;
+                for (int32_t i = lane; i < n; i += 64) {
+                    const float v = col[NB * (i + 1) + a];
+                    vol[base + i] = accumulate ? vol[base + i] + v : v;
+                }
+            }
+        }
     }
 }
 
@@ -1680,15 +1751,25 @@ void trace_launch(const char* kernel, dim3 grid, dim3 block, size_t lds, const c
 }
 
 hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vol,
-                                  float* const* sino, hipStream_t s) {
+                                  float* const* sino, hipStream_t s, int orbit, int dir,
+                                  int64_t slot_stride) {
     const int64_t n = (int64_t)a.nviews * a.rows * a.cols;
     if (n == 0) return hipSuccess;
+    if (orbit != 1 && (a.nb != 1 || (orbit != 2 && orbit != 4) || a.box.n[0] % 2 != 0 ||
+                       (orbit == 4 && a.box.n[0] != a.box.n[1])))
+        return hipErrorInvalidValue;
     Ptrs4 v{};
     MPtrs4 o{};
     for (int m = 0; m < a.nb; ++m) { v.p[m] = vol[m]; o.p[m] = sino[m]; }
-    trace_launch("generic_forward_kernel", dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                 "views %d..%d members %d", a.view0, a.view0 + a.nviews - 1, a.nb);
-    generic_forward_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a, v, o);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    trace_launch("generic_forward_kernel", grid, dim3(256), 0, "views %d..%d members %d orbit %d (turn %d)",
+                 a.view0, a.view0 + a.nviews - 1, a.nb, orbit, dir);
+    switch (orbit) {
+        case 1: generic_forward_kernel<1><<<grid, dim3(256), 0, s>>>(a, v, o, slot_stride, dir); break;
+        case 2: generic_forward_kernel<2><<<grid, dim3(256), 0, s>>>(a, v, o, slot_stride, dir); break;
+        case 4: generic_forward_kernel<4><<<grid, dim3(256), 0, s>>>(a, v, o, slot_stride, dir); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -1852,25 +1933,32 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
 }
 
 hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol, int accumulate,
-                              hipStream_t s) {
-    const int32_t D = a.box.n[2];
-    const int32_t zchunk = gather_zchunk(D, nb);
+                              hipStream_t s, int orbit, int dir) {
+    const int32_t W = a.box.n[0], H = a.box.n[1], D = a.box.n[2];
+    if (orbit != 1 && (nb != 1 || (orbit != 2 && orbit != 4) || W % 2 != 0 ||
+                       (orbit == 4 && H != W) || a.nviews % orbit != 0))
+        return hipErrorInvalidValue;
+    const int slots = orbit > 1 ? orbit : nb;
+    const int32_t zchunk = gather_zchunk(D, slots);
     const int32_t nchunks = (D + zchunk - 1) / zchunk;
-    const uint64_t tasks = (uint64_t)a.box.n[0] * (uint64_t)a.box.n[1] * (uint64_t)nchunks;
-    const bool tiled = a.box.n[0] % 16 == 0 && a.box.n[1] % 32 == 0;
-    const int32_t tx = tiled ? 16 : 1, ty = tiled ? 32 : a.box.n[1];
+    int32_t Wr, Hr;
+    orbit_grid(orbit, W, H, Wr, Hr);
+    const uint64_t tasks = (uint64_t)Wr * (uint64_t)Hr * (uint64_t)nchunks;
+    const bool tiled = Wr % 16 == 0 && Hr % 32 == 0;
+    const int32_t tx = tiled ? 16 : 1, ty = tiled ? 32 : Hr;
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(TiltItem) +
-                                    (size_t)gather_column_floats(zchunk, nb) * sizeof(float));
-    trace_launch("tilt_gather_kernel", grid, dim3(256), lds, "views %d..%d members %d z chunk %d tiles %d x %d",
-                 a.view0, a.view0 + a.nviews - 1, nb, zchunk, tx, ty);
-    switch (nb) {
-        case 1: tilt_gather_kernel<1><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
-        case 2: tilt_gather_kernel<2><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
-        case 4: tilt_gather_kernel<4><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate); break;
-        default: return hipErrorInvalidValue;
-    }
+                                    (size_t)gather_column_floats(zchunk, slots) * sizeof(float));
+    trace_launch("tilt_gather_kernel", grid, dim3(256), lds,
+                 "views %d..%d members %d orbit %d (turn %d) z chunk %d tiles %d x %d",
+                 a.view0, a.view0 + a.nviews - 1, nb, orbit, dir, zchunk, tx, ty);
+#define MBP_TILT(NB_, P_) \
+    if (slots == NB_ && orbit == P_) \
+        tilt_gather_kernel<NB_, P_><<<grid, dim3(256), lds, s>>>(a, ysc, vol, zchunk, nchunks, tx, ty, accumulate, dir)
+    MBP_TILT(1, 1); else MBP_TILT(2, 1); else MBP_TILT(4, 1); else MBP_TILT(2, 2); else MBP_TILT(4, 4);
+    else return hipErrorInvalidValue;
+#undef MBP_TILT
     return hipGetLastError();
 }
 

@@ -39,9 +39,13 @@ struct ColumnLaunch {
     uint32_t pad_;
 };
 
-// Forward: sino[m][ray] for rays of the launch; adjoint: atomically adds into vol.
+// Forward: sino[m][ray] for rays of the launch; adjoint: atomically adds into vol. Forward with
+// orbit 2 or 4 (nb = 1): the launch's views lie among the first q = V / orbit, and each ray's
+// walk also gives the rays of the views q m apart (orbit_cell), stored slot_stride * m
+// elements after it; dir: the quarter turn's sense.
 hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vol,
-                                  float* const* sino, hipStream_t s);
+                                  float* const* sino, hipStream_t s, int orbit = 1, int dir = 0,
+                                  int64_t slot_stride = 0);
 hipError_t launch_generic_adjoint(const GenericLaunch& a, const float* const* sino,
                                   float* const* vol, hipStream_t s);
 // orbit 2 or 4 (nb = 1): the launch's views lie among the first q = V / orbit, and each ray's
@@ -71,9 +75,9 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
                                 float* vol, int accumulate, hipStream_t s, int orbit = 1, int dir = 0);
 // The gather for cone geometries whose detector rows do not run along z: the same pre-pass
 // sinogram (ysc) and output as launch_column_gather, each ray clipped against each cell on
-// its own.
+// its own; orbit and dir as for launch_column_gather.
 hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, float* vol, int accumulate,
-                              hipStream_t s);
+                              hipStream_t s, int orbit = 1, int dir = 0);
 // Per-(view, column) line constants of the gather, for views [a.view0, a.view0 + views)
 // (lines holds views * cols entries).
 hipError_t launch_column_lines(const ColumnLaunch& a, int32_t views, ColLine* lines, hipStream_t s);

@@ -354,20 +354,20 @@ bool tilt_gather(const mbp_plan* p) {
     return p->tilt_capable && p->forced_path == MBP_PATH_AUTO && adjoint_kind(p) == MBP_ADJOINT_GATHER;
 }
 
-// Turn symmetry of the views about the vertical axis through the grid's xy centre, for the
-// gather's shared items (orbit_cell): 4 when view v + V/4 is view v turned a quarter turn for
-// every v (square grid of equal x and y pitch), else 2 when view v + V/2 is view v turned a
-// half turn, else 1; the grid's W must be even (no cell is its own image). *dir: the quarter
-// turn's sense (+1 anticlockwise seen from +z). Turned frames are formed exactly (the turns
-// only swap and negate coordinates relative to the axis) and must match the stored ones within
-// 1e-12 of the frame's extent, far below fp32 rounding, so the shared items give the sums of
-// the unshared ones to rounding. Only for the column gather (rows along z).
+// Turn symmetry of the views about the vertical axis through the grid's xy centre (orbit_cell),
+// a property of the geometry that every operator with a shared form takes: 4 when view
+// v + V/4 is view v turned a quarter turn for every v (square grid of equal x and y pitch),
+// else 2 when view v + V/2 is view v turned a half turn, else 1; the grid's W must be even (no
+// cell is its own image). *dir: the quarter turn's sense (+1 anticlockwise seen from +z).
+// Turned frames are formed exactly (the turns only swap and negate coordinates relative to the
+// axis) and must match the stored ones within 1e-12 of the frame's extent, far below fp32
+// rounding, so the shared forms give the sums of the unshared ones to rounding.
 int32_t find_orbit(const mbp_plan& P, int32_t* dir) {
     *dir = 0;
     const mbp_geometry& g = P.g;
-    if (!P.column_capable || g.W % 2 != 0) return 1;
+    if (g.W % 2 != 0) return 1;
     const double ax = 0.5 * (P.box.lo[0] + P.box.hi[0]), ay = 0.5 * (P.box.lo[1] + P.box.hi[1]);
-    const bool line = g.beam == MBP_PARALLEL3D;   // s is a direction, not a point
+    const bool line = g.beam == MBP_PARALLEL3D || g.beam == MBP_PARALLEL;   // s: a direction
     // whether frame B is frame A turned k quarter turns (k = 1 or -1) or a half turn (k = 2)
     auto turned = [&](const Frame& A, const Frame& B, int k) {
         auto turn = [&](const double* p, bool point, double* out) {
@@ -462,11 +462,16 @@ int run_generic(mbp_plan* p, DeviceState* d, bool adjoint, const float* in, floa
         dst[m] = out + (m0 + m) * (adjoint ? vox : rays);
     }
     const int64_t vb = views_per_launch(p);
-    for (int64_t v0 = 0; v0 < g.views; v0 += vb) {
+    // the forward of one member shares each walk over the views' turn symmetry (as run_column)
+    const int32_t orbit = !adjoint && nb == 1 && p->orbit_enabled ? p->orbit : 1;
+    const int64_t views = g.views / orbit;
+    if (!adjoint) p->last_fwd_orbit = p->last_fwd_orbit ? std::min(p->last_fwd_orbit, orbit) : orbit;
+    for (int64_t v0 = 0; v0 < views; v0 += vb) {
         a.view0 = (int32_t)v0;
-        a.nviews = (int32_t)std::min(vb, g.views - v0);
+        a.nviews = (int32_t)std::min(vb, views - v0);
         hipError_t e = adjoint ? mbp::launch_generic_adjoint(a, src, dst, s)
-                               : mbp::launch_generic_forward(a, src, dst, s);
+                               : mbp::launch_generic_forward(a, src, dst, s, orbit, p->orbit_dir,
+                                                             views * g.rows * g.cols);
         if (e != hipSuccess) return hip_fail(e, adjoint ? "generic adjoint launch" : "generic forward launch");
     }
     return MBP_OK;
@@ -761,7 +766,6 @@ int mbp_project(mbp_plan* plan, const float* volume, int64_t batch, float* sinog
         const int nb = (int)std::min<int64_t>(4, batch - m0);
         rc = run_generic(plan, d, false, volume, sinogram, m0, nb, s);
         if (rc != MBP_OK) return rc;
-        plan->last_fwd_orbit = 1;
         m0 += nb;
     }
     return MBP_OK;
@@ -858,7 +862,7 @@ int backproject_on(mbp_plan* plan, DeviceState* d, const float* sinogram, int64_
                 if (e != hipSuccess) return hip_fail(e, "column line launch");
             }
             // the turn symmetry's shared items: one member, all views in one launch
-            const int32_t orbit = gather && !tilt && nb == 1 && vb == g.views && plan->orbit_enabled
+            const int32_t orbit = gather && nb == 1 && vb == g.views && plan->orbit_enabled
                                       ? plan->orbit : 1;
             if (orbit > 1) {
                 // pre-pass over the first q = V / orbit views with member m the view v + m q;
@@ -878,8 +882,9 @@ int backproject_on(mbp_plan* plan, DeviceState* d, const float* sinogram, int64_
                     if (e != hipSuccess) return hip_fail(e, "column line launch");
                     lines = batch_lines;
                 }
-                e = mbp::launch_column_gather(a, 1, lines, ysc, target, acc_target, s, orbit, plan->orbit_dir);
-                if (e != hipSuccess) return hip_fail(e, "column gather launch");
+                e = tilt ? mbp::launch_tilt_gather(a, 1, ysc, target, acc_target, s, orbit, plan->orbit_dir)
+                         : mbp::launch_column_gather(a, 1, lines, ysc, target, acc_target, s, orbit, plan->orbit_dir);
+                if (e != hipSuccess) return hip_fail(e, tilt ? "tilt gather launch" : "column gather launch");
                 plan->last_orbit = orbit;
             } else if (gather) {
                 // one pre-pass and one gather per view batch; every launch after the first adds

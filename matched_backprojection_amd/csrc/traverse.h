@@ -272,6 +272,48 @@ MBP_HD MBP_INLINE void walk_ray_offsets(const RayWalk& r, int32_t sx, int32_t sy
     visit(off, (float)fmax(r.T - t, 0.0));
 }
 
+// walk_ray_offsets for the rays a turn symmetry of the views relates (orbit_cell): the cell
+// (cx, cy, cz) of the walked ray stands for cell R^m (cx, cy) at the same cz for the ray m steps
+// of the turn later, whose element offset is base[m] + cx * tx[m] + cy * ty[m] + cz * sz
+// (orbit_strides). `visit(offsets, length)` gets the P offsets of each segment.
+template <int P, class Visit>
+MBP_HD MBP_INLINE void walk_ray_orbit(const RayWalk& r, const int32_t (&base)[P], const int32_t (&tx)[P],
+                                      const int32_t (&ty)[P], int32_t sz, Visit& visit) {
+    if (!r.hit) return;
+    int32_t off[P], dx[P], dy[P];
+    for (int m = 0; m < P; ++m) {
+        off[m] = base[m] + r.ax[0].c0 * tx[m] + r.ax[1].c0 * ty[m] + r.ax[2].c0 * sz;
+        dx[m] = r.ax[0].step * tx[m];
+        dy[m] = r.ax[1].step * ty[m];
+    }
+    const int32_t dz = r.ax[2].step * sz;
+    int32_t kx = 0, ky = 0, kz = 0;
+    double nx = r.ax[0].steps > 0 ? r.ax[0].t_first : INFINITY;
+    double ny = r.ax[1].steps > 0 ? r.ax[1].t_first : INFINITY;
+    double nz = r.ax[2].steps > 0 ? r.ax[2].t_first : INFINITY;
+    const int32_t total = r.ax[0].steps + r.ax[1].steps + r.ax[2].steps;
+    double t = 0.0;
+    for (int32_t i = 0; i < total; ++i) {
+        const bool bx = nx <= ny && nx <= nz;
+        const bool by = !bx && ny <= nz;
+        const double tb = bx ? nx : (by ? ny : nz);
+        visit(off, (float)fmax(tb - t, 0.0));
+        t = fmax(t, tb);
+        for (int m = 0; m < P; ++m) off[m] += bx ? dx[m] : (by ? dy[m] : dz);
+        if (bx) {
+            ++kx;
+            nx = kx < r.ax[0].steps ? fma((double)kx, r.ax[0].t_step, r.ax[0].t_first) : INFINITY;
+        } else if (by) {
+            ++ky;
+            ny = ky < r.ax[1].steps ? fma((double)ky, r.ax[1].t_step, r.ax[1].t_first) : INFINITY;
+        } else {
+            ++kz;
+            nz = kz < r.ax[2].steps ? fma((double)kz, r.ax[2].t_step, r.ax[2].t_first) : INFINITY;
+        }
+    }
+    visit(off, (float)fmax(r.T - t, 0.0));
+}
+
 // ------------------------------------------------------------------------------------------
 // Column walk: the rows of one column share their xy line.
 //
@@ -740,6 +782,19 @@ MBP_HD MBP_INLINE void orbit_columns(uint32_t cxy, uint32_t c1, uint32_t WH1, ui
         cell[2 % P] = WH1 - cxy;
         cell[3 % P] = WH1 - c1;
     }
+}
+
+// Element offsets of the turned cells on a volume with element (x, y, z) at x sx + y sy + z sz:
+// cell R^a (cx, cy) lies at base + cx tx + cy ty (+ cz sz), the map being affine in (cx, cy).
+MBP_HD MBP_INLINE void orbit_strides(int32_t P, int32_t dir, int32_t W, int32_t H, int32_t sx,
+                                     int32_t sy, int32_t a, int32_t& base, int32_t& tx, int32_t& ty) {
+    int32_t x0, y0, x1, y1, x2, y2;
+    orbit_cell(P, dir, W, H, 0, 0, a, x0, y0);
+    orbit_cell(P, dir, W, H, 1, 0, a, x1, y1);
+    orbit_cell(P, dir, W, H, 0, 1, a, x2, y2);
+    base = x0 * sx + y0 * sy;
+    tx = (x1 - x0) * sx + (y1 - y0) * sy;
+    ty = (x2 - x0) * sx + (y2 - y0) * sy;
 }
 
 // The cells that stand for the orbits (one per orbit): ix < W / 2 for P = 2 (W even), ix and

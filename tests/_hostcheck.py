@@ -32,7 +32,7 @@ def _load():
             mod.build_hostcheck(sanitize=_SANITIZED)
         lib = ctypes.CDLL(_LIB)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P]
+        lib.mbph_project.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, I64, I64, I64, P, P, P, I, I]
         lib.mbph_backproject.argtypes = [I, P, I, P, P, P, P, I, I, I, D, D, P, P, I64, I64, I64, P]
         lib.mbph_check_rays.argtypes = [I, P, I, P, P, P, I, I, I, D, D, P, I64, P]
         lib.mbph_gather.argtypes = [P, I, P, P, P, I, I, I, D, D, P, I, I, P, P, P, I, I]
@@ -96,8 +96,10 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def project(path: str, geom: dict, traj: dict, vol: np.ndarray):
-    """Replay the forward walk on a (D, H, W) / (H, W) float32 volume."""
+def project(path: str, geom: dict, traj: dict, vol: np.ndarray, orbit: int = 1, turn: int = 0):
+    """Replay the forward walk on a (D, H, W) / (H, W) float32 volume; orbit 2 or 4 (generic
+    walk; turn: the quarter turn's sense): the walks shared over the turn symmetry of the
+    views, as the kernel shares them."""
     lib = _load()
     f, lo, hi, p, n = _common(geom, traj)
     rows = int(geom.get("rows", 1))
@@ -109,7 +111,8 @@ def project(path: str, geom: dict, traj: dict, vol: np.ndarray):
     sx, sy, sz = 1, int(n[0]), int(n[0] * n[1])
     lib.mbph_project(_PATH[path], _ptr(f), _BEAM[geom["beam"]], _ptr(lo), _ptr(hi), _ptr(p),
                      _ptr(n), views, rows, cols, float(geom.get("du", 1.0)), float(geom.get("dv", 1.0)),
-                     _ptr(vol), sx, sy, sz, _ptr(sino), _ptr(counts), ctypes.byref(viol))
+                     _ptr(vol), sx, sy, sz, _ptr(sino), _ptr(counts), ctypes.byref(viol),
+                     int(orbit), int(turn))
     if geom["beam"] not in _BEAMS_3D:
         sino, counts = sino[:, 0], counts[:, 0]
     return sino, counts, int(viol.value)

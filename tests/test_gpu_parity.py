@@ -465,6 +465,54 @@ def test_orbit_pair_parity(torch_dev, mbp, oracle, case):
         plan.close()
 
 
+@pytest.mark.parametrize("case", ["tilted_quarter", "tilted_quarter_clockwise", "tilted_half",
+                                  "fan_quarter", "fan_half"])
+def test_orbit_generic_walk_and_per_row_gather_parity(torch_dev, mbp, oracle, case):
+    """Geometries off the column walk with a turn symmetry: the generic forward walk shares
+    each walk over it (turned element strides), and the per-row gather (the cone tilted in its
+    detector plane) each cell clip; the 2-D fan's adjoint is the generic walk's atomics, which
+    do not share. Both layouts for the cone, the accumulating gather, against the oracle, the
+    unshared operators and the adjoint identity."""
+    from tests.test_hostcheck import _generic_turn_cases
+    torch, dev = torch_dev
+    cfg, traj, P, turn = _generic_turn_cases()[case]
+    geom = geom_of(cfg)
+    x = np.random.default_rng(8).random(cfg.shape).astype(np.float32)
+    ref = oracle.project(geom, traj, x)
+    y = np.random.default_rng(9).random(ref.shape).astype(np.float32)
+    bref = oracle.backproject(geom, traj, y)
+    cone = cfg.beam == "cone"
+    for layout in (("WHD", "DHW") if cone else ("DHW",)):
+        say(f"case generic orbit {case} (P={P}, turn {turn}) layout={layout}")
+        plan = make_plan(mbp, cfg, traj=traj, layout=layout)
+        assert plan.info["orbit"] == P and plan.info["path"] == "generic"
+        xd = to_device_volume(torch, dev, x, layout)
+        yd = torch.from_numpy(y).to(dev)
+        p = plan.project(xd).cpu().numpy().astype(np.float64)
+        assert plan.info["last_forward_orbit"] == P
+        check(p, ref, "shared generic forward")
+        b = plan.backproject(yd).cpu().numpy().astype(np.float64)
+        assert plan.info["last_adjoint_orbit"] == (P if cone else 1)
+        check(b, bref, "per-row gather" if cone else "generic adjoint")
+        if cone:
+            pre = np.random.default_rng(10).random(cfg.shape).astype(np.float32)
+            out = to_device_volume(torch, dev, pre, layout)
+            plan.backproject(yd, out=out, accumulate=True)
+            check(out.cpu().numpy().astype(np.float64), bref + pre.astype(np.float64), "accumulate")
+        lhs = float(np.dot(p.ravel(), y.astype(np.float64).ravel()))
+        rhs = float(np.dot(x.astype(np.float64).ravel(), b.ravel()))
+        say(f"  adjoint identity {abs(lhs - rhs) / abs(lhs):.2e}")
+        assert abs(lhs - rhs) <= RTOL_ADJ * abs(lhs)
+        plan.set_orbit(False)
+        p1 = plan.project(xd).cpu().numpy().astype(np.float64)
+        b1 = plan.backproject(yd).cpu().numpy().astype(np.float64)
+        assert plan.info["last_forward_orbit"] == 1 and plan.info["last_adjoint_orbit"] == 1
+        d, df = rel_l2(b, b1), rel_l2(p, p1)
+        say(f"  shared vs unshared rel-L2: adjoint {d:.2e}, forward {df:.2e}")
+        assert df <= 1e-6 and d <= 1e-6
+        plan.close()
+
+
 def test_view_batches_layouts_batches_and_accumulate(torch_dev, mbp, oracle):
     """Ragged view batches, both layouts, batch sizes 0..5, accumulation, caller workspace."""
     torch, dev = torch_dev
