@@ -686,6 +686,10 @@ constexpr int kGroup = kGatherGroup;
 // of four waves takes at most 40 KiB, so four blocks share a CU's 160 KiB and the register
 // budget, not LDS, sets the occupancy.
 constexpr int kQueue = 80;
+// The tilted gather's queue: 64 items of 88 bytes (5.5 KiB), drained after every round that
+// adds to it; with a column of up to about 4 KiB a block of four waves then takes at most
+// 40 KiB, and four blocks fit a CU.
+constexpr int kTiltQueue = 64;
 // Lanes per view when items are built.
 constexpr int kViewLanes = 4;
 
@@ -1285,10 +1289,13 @@ __device__ __forceinline__ void tilt_clip_walls(const double (&d)[2], const doub
 // P > 1: shared over a turn symmetry of the views as column_gather_kernel is (orbit_cell): the
 // launch's views are the first q = nviews / P, member m of the reordered sinogram is the line
 // of view v + m q, and a wave owns the P cells of an orbit as the NB == P slots of its column.
-// Occupancy: four waves per SIMD for one member or slot; three (168 registers) for two and
-// four, which at four waves spilled 5 and 23 registers per thread.
+// Occupancy: four waves per SIMD (at most 128 vector registers; the LDS of a four-wave block,
+// its columns and 64-item queues, stays within a quarter of the compute unit's for columns
+// of up to 4 KiB). The wave takes one item at a time: preparing two at once, for their fp64
+// chains to interleave, needed 168 registers and held the kernel to three waves per SIMD,
+// which ran slower.
 template <int NB, int P>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 4 : 3)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* __restrict__ vol,
                    int32_t zchunk, int32_t nchunks, int32_t tx, int32_t ty, int32_t accumulate,
                    int32_t dir) {
@@ -1311,7 +1318,7 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
     const int32_t colf = gather_column_floats(zchunk, NB);
     float* const cols = reinterpret_cast<float*>(lds_raw) + wave * colf;
     float* const col = cols + 2 * NB;                   // the guard cell below the chunk
-    TiltItem* Q = reinterpret_cast<TiltItem*>(lds_raw + 4 * (size_t)colf * sizeof(float)) + wave * kQueue;
+    TiltItem* Q = reinterpret_cast<TiltItem*>(lds_raw + 4 * (size_t)colf * sizeof(float)) + wave * kTiltQueue;
     for (int32_t i = lane; i < colf; i += 64) cols[i] = 0.0f;
     __syncthreads();
     if (live) {
@@ -1351,10 +1358,11 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
             constexpr int SH = decltype(shift)::value;
             const int32_t nrows = (int32_t)uniform((uint32_t)it.nrows);
             // the row's ray direction: xy in world units, z in cells per unit parameter
-            const double v = it.v0 + lane_dv;
+            const double v = centred((int32_t)uniform((uint32_t)it.k0), A.rows, A.dv) + lane_dv;
             const double d[2] = {fma(v, it.evx, it.bx), fma(v, it.evy, it.by)};
             const double dzc = fma(v, it.evzc, it.bzc);
-            const double wl[2] = {it.wx0, it.wy0}, wh[2] = {it.wx1, it.wy1};
+            const double wl[2] = {it.wx0, it.wy0};
+            const double wh[2] = {it.wx0 + A.box.pitch[0], it.wy0 + A.box.pitch[1]};
             double t0, t1;
             if (__ballot(d[0] == 0.0 || d[1] == 0.0) == 0) {
                 // no row of the item runs parallel to a wall (the rule): no per-lane branch
@@ -1437,32 +1445,23 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
             for (int m = 0; m < NB; ++m) nz |= w[m] != 0.0f;
             return __ballot(nz) != 0;
         };
-        // Items in queue order, two at a time; the next two items' row values are loaded while
-        // the current ones are summed (the buffers swap roles from step to step). An item whose
-        // rows are all zero adds nothing.
+        // Items in queue order, one at a time; the next item's row values are loaded while the
+        // current one is summed (the buffers swap roles from step to step). An item whose rows
+        // are all zero adds nothing.
         // The queue's items all belong to one cell of the orbit (slot SH = decltype(shift)).
         auto drain = [&](auto shift, int32_t count) __attribute__((always_inline)) {
             if (count == 0) return;
-            float wa[2][NB], wb[2][NB];
-            load_rows(0, wa[0]);
-            if (count > 1) load_rows(1, wa[1]);
+            float wa[NB], wb[NB];
+            load_rows(0, wa);
             int32_t i = 0;
-            auto step = [&](const float (&cur)[2][NB], float (&nxt)[2][NB]) {
-                const bool two_items = i + 1 < count;
-                if (i + 2 < count) load_rows(i + 2, nxt[0]);
-                if (i + 3 < count) load_rows(i + 3, nxt[1]);
-                const bool nz0 = any_nonzero(cur[0]);
-                const bool nz1 = two_items && any_nonzero(cur[1]);
-                if (nz0 || nz1) {
-                    // both preps unconditionally (the last of an odd count preps a copy of its
-                    // predecessor, never committed), so that their instructions can interleave
-                    Row r0, r1;
-                    prep(shift, Q[i], cur[0], r0);
-                    prep(shift, Q[two_items ? i + 1 : i], cur[1], r1);
-                    if (nz0) commit(shift, r0, cur[0]);
-                    if (nz1) commit(shift, r1, cur[1]);
+            auto step = [&](const float (&cur)[NB], float (&nxt)[NB]) {
+                if (i + 1 < count) load_rows(i + 1, nxt);
+                if (any_nonzero(cur)) {
+                    Row r;
+                    prep(shift, Q[i], cur, r);
+                    commit(shift, r, cur);
                 }
-                i += 2;
+                ++i;
                 return i < count;
             };
             while (step(wa, wb) && step(wb, wa)) {
@@ -1532,11 +1531,8 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
                         t.evy = F.v[1];
                         t.evzc = F.v[2] * ipz;
                         t.wx0 = x0 - F.s[0];
-                        t.wx1 = x1 - F.s[0];
                         t.wy0 = y0 - F.s[1];
-                        t.wy1 = y1 - F.s[1];
                         t.szc = (F.s[2] - A.box.lo[2]) * ipz;
-                        t.v0 = centred(kk, A.rows, A.dv);
                         t.view = view;
                         t.j = jc;
                         t.k0 = kk;
@@ -1545,7 +1541,7 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
                         kk += 64;
                     }
                     count += (int32_t)__popcll(m);
-                    if (count > kQueue - 64) {
+                    if (count > kTiltQueue - 64) {
                         wave_lds_sync();
                         flush(a);
                         wave_lds_sync();
@@ -1948,7 +1944,7 @@ hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, f
     const int32_t tx = tiled ? 16 : 1, ty = tiled ? 32 : Hr;
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
-    const size_t lds = (size_t)4 * (kQueue * sizeof(TiltItem) +
+    const size_t lds = (size_t)4 * (kTiltQueue * sizeof(TiltItem) +
                                     (size_t)gather_column_floats(zchunk, slots) * sizeof(float));
     trace_launch("tilt_gather_kernel", grid, dim3(256), lds,
                  "views %d..%d members %d orbit %d (turn %d) z chunk %d tiles %d x %d",

@@ -636,15 +636,14 @@ MBP_HD MBP_INLINE bool tilt_row_range(const TiltCorners& T, int32_t j, int32_t r
 // One item of the tilted gather: rows k0 .. k0 + nrows - 1 (at most 64) of column j in view
 // `view`, with everything its rows share, computed once when the item is built: the column's
 // ray direction at v = 0, b = c - s + u eu (xy components, and z in cells per unit parameter),
-// the view's row axis ev (likewise), the offsets of the cell's four walls from the source
-// (x0 - sx, x1 - sx, y0 - sy, y1 - sy), the source's z in cells above the box, and the row
-// coordinate of row k0 (112 bytes). Row k0 + l's ray direction is b + (v0 + l dv) ev.
+// the view's row axis ev (likewise), the offsets of the cell's lower walls from the source
+// (x0 - sx, y0 - sy; the upper walls lie one pitch further) and the source's z in cells above
+// the box (88 bytes). Row k's ray direction is b + v_k ev, v_k the row's centred coordinate.
 struct TiltItem {
     double bx, by, bzc;
     double evx, evy, evzc;
-    double wx0, wx1, wy0, wy1;
+    double wx0, wy0;
     double szc;
-    double v0;
     int32_t view, j, k0, nrows;
 };
 
