@@ -79,12 +79,30 @@ __global__ void __launch_bounds__(256) generic_forward_kernel(const GenericLaunc
                                                               const Ptrs4 vol, const MPtrs4 sino,
                                                               int64_t slot_stride, int32_t dir) {
     const uint32_t per_view = (uint32_t)A.rows * (uint32_t)A.cols;
-    const uint32_t rid = blockIdx.x * 256u + threadIdx.x;
-    if (rid >= (uint32_t)A.nviews * per_view) return;
-    const uint32_t vl = rid / per_view;
-    uint32_t rem = rid - vl * per_view;
+    uint32_t vl, rem;
     int32_t k, j;
-    generic_pixel(A, rem, k, j);
+    if (A.rows_fast) {
+        // z-fastest volume: a block takes 4 adjacent columns of one 64-row block (wave =
+        // column, lane = row), column quadruples fastest, then row blocks, then views, each
+        // XCD a contiguous range of them, so that the waves running together cross
+        // neighbouring voxel columns at the same heights (against 256 consecutive rows per
+        // block: the tilted 256^3 cone's forward 15.4 -> 14.3 ms)
+        const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
+        const uint32_t rbs = ((uint32_t)A.rows + 63u) / 64u, quads = ((uint32_t)A.cols + 3u) / 4u;
+        const uint32_t cq = blk % quads, rest = blk / quads;
+        const uint32_t rb = rest % rbs;
+        vl = rest / rbs;
+        j = (int32_t)(cq * 4u + (threadIdx.x >> 6));
+        k = (int32_t)(rb * 64u + (threadIdx.x & 63u));
+        if (vl >= (uint32_t)A.nviews || j >= A.cols || k >= A.rows) return;
+        rem = (uint32_t)k * (uint32_t)A.cols + (uint32_t)j;
+    } else {
+        const uint32_t rid = blockIdx.x * 256u + threadIdx.x;
+        if (rid >= (uint32_t)A.nviews * per_view) return;
+        vl = rid / per_view;
+        rem = rid - vl * per_view;
+        generic_pixel(A, rem, k, j);
+    }
     const int32_t view = A.view0 + (int32_t)vl;
     const Frame F = A.frames[view];
     RayWalk r;
@@ -1757,7 +1775,9 @@ hipError_t launch_generic_forward(const GenericLaunch& a, const float* const* vo
     Ptrs4 v{};
     MPtrs4 o{};
     for (int m = 0; m < a.nb; ++m) { v.p[m] = vol[m]; o.p[m] = sino[m]; }
-    const dim3 grid((unsigned)((n + 255) / 256));
+    // rows-fastest launches: one block per (view, 64-row block, 4 adjacent columns)
+    const dim3 grid(a.rows_fast ? (unsigned)((int64_t)a.nviews * ((a.cols + 3) / 4) * ((a.rows + 63) / 64))
+                                : (unsigned)((n + 255) / 256));
     trace_launch("generic_forward_kernel", grid, dim3(256), 0, "views %d..%d members %d orbit %d (turn %d)",
                  a.view0, a.view0 + a.nviews - 1, a.nb, orbit, dir);
     switch (orbit) {
