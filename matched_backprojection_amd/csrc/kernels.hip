@@ -83,15 +83,16 @@ __global__ void __launch_bounds__(256) generic_forward_kernel(const GenericLaunc
     int32_t k, j;
     if (A.rows_fast) {
         // z-fastest volume: a block takes 4 adjacent columns of one 64-row block (wave =
-        // column, lane = row), column quadruples fastest, then row blocks, then views, each
-        // XCD a contiguous range of them, so that the waves running together cross
-        // neighbouring voxel columns at the same heights (against 256 consecutive rows per
-        // block: the tilted 256^3 cone's forward 15.4 -> 14.3 ms)
-        const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
-        const uint32_t rbs = ((uint32_t)A.rows + 63u) / 64u, quads = ((uint32_t)A.cols + 3u) / 4u;
-        const uint32_t cq = blk % quads, rest = blk / quads;
-        const uint32_t rb = rest % rbs;
-        vl = rest / rbs;
+        // column, lane = row), so that its waves cross neighbouring voxel columns at the same
+        // heights; views are the fastest block index, then row blocks, then column
+        // quadruples, dealt round-robin to the XCDs, as in the column forward (against 256
+        // consecutive rows per block: the tilted 256^3 cone's forward 15.4 -> 13.5 ms; with
+        // quadruples fastest and a contiguous range per XCD, 14.3)
+        const uint32_t blk = blockIdx.x;
+        const uint32_t rbs = ((uint32_t)A.rows + 63u) / 64u;
+        vl = blk % (uint32_t)A.nviews;
+        const uint32_t rest = blk / (uint32_t)A.nviews;
+        const uint32_t rb = rest % rbs, cq = rest / rbs;
         j = (int32_t)(cq * 4u + (threadIdx.x >> 6));
         k = (int32_t)(rb * 64u + (threadIdx.x & 63u));
         if (vl >= (uint32_t)A.nviews || j >= A.cols || k >= A.rows) return;
@@ -1035,7 +1036,12 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
-    const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
+    // P == 1: blocks dealt round-robin to the XCDs, as the hardware deals them, so the XCDs work
+    // on neighbouring cells of one tile at a time and share its sinogram lines in the
+    // memory-side cache (the helical batch's adjoint 157.9 -> 132.0 ms); an orbit's blocks
+    // keep one contiguous range of tiles per XCD (round-robin: the 720-view 512^3 cone 90.6
+    // -> 94.6 ms, the 360-view one 69.8 -> 76.5, the 256^3 cone 8.58 -> 8.39)
+    const uint32_t blk = P == 1 ? blockIdx.x : uniform(xcd_remap(blockIdx.x, gridDim.x));
     const uint32_t task = blk * 4u + wave;
     const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
     int32_t Wr, Hr;
@@ -1327,7 +1333,9 @@ tilt_gather_kernel(const ColumnLaunch A, const float* __restrict__ ysc, float* _
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
-    const uint32_t blk = uniform(xcd_remap(blockIdx.x, gridDim.x));
+    // blocks dealt round-robin to the XCDs (against one contiguous range of tiles per XCD: the
+    // tilted 256^3 cone 32.9 -> 32.2 ms)
+    const uint32_t blk = blockIdx.x;
     const uint32_t task = blk * 4u + wave;
     const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
     int32_t Wr, Hr;
