@@ -1036,12 +1036,10 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const int32_t lane = (int32_t)(threadIdx.x & 63u);
-    // P == 1: blocks dealt round-robin to the XCDs, as the hardware deals them, so the XCDs work
-    // on neighbouring cells of one tile at a time and share its sinogram lines in the
-    // memory-side cache (the helical batch's adjoint 157.9 -> 132.0 ms); an orbit's blocks
-    // keep one contiguous range of tiles per XCD (round-robin: the 720-view 512^3 cone 90.6
-    // -> 94.6 ms, the 360-view one 69.8 -> 76.5, the 256^3 cone 8.58 -> 8.39)
-    const uint32_t blk = P == 1 ? blockIdx.x : uniform(xcd_remap(blockIdx.x, gridDim.x));
+    // blocks dealt round-robin to the XCDs, as the hardware deals them: the XCDs work on
+    // neighbouring cells of one tile at a time and share its sinogram lines in the
+    // memory-side cache
+    const uint32_t blk = blockIdx.x;
     const uint32_t task = blk * 4u + wave;
     const int32_t W = A.box.n[0], H = A.box.n[1], D = A.box.n[2];
     int32_t Wr, Hr;
@@ -1931,16 +1929,16 @@ hipError_t launch_column_gather(const ColumnLaunch& a, int nb, const ColLine* li
     int32_t Wr, Hr;
     orbit_grid(orbit, W, H, Wr, Hr);
     const uint64_t tasks = (uint64_t)Wr * (uint64_t)Hr * (uint64_t)nchunks;
-    // tiles of 64 x 8 cells (measured against 16 x 32, 32 x 16, 32 x 32, 64 x 16 and 16 x 64:
-    // 2.5% faster than 16 x 32 on the 512^3 cone), else 16 x 32, else plain y-fastest order.
-    // An orbit's tasks tile the grid of the cells that stand for the orbits, in 8 x 8 tiles:
-    // its lines hold `orbit` views each, and a smaller patch keeps the lines its waves share
-    // in L2 (against 64 x 8: the 256^3 cone -8%, the 360-view 512^3 cone -1%, the 720-view
-    // 512^3 cone unchanged; 16 x 16, 32 x 8, 32 x 16 and 16 x 32 no better)
-    const bool small = orbit > 1 && Wr % 8 == 0 && Hr % 8 == 0;
-    const bool wide = !small && Wr % 64 == 0 && Hr % 8 == 0;
-    const bool tiled = small || wide || (Wr % 16 == 0 && Hr % 32 == 0);
-    const int32_t tx = small ? 8 : wide ? 64 : tiled ? 16 : 1, ty = small || wide ? 8 : tiled ? 32 : Hr;
+    // tiles of 32 x 32 cells (of the orbits' grid for an orbit), else 16 x 32, else plain
+    // y-fastest order; the kernel deals its blocks round-robin to the XCDs, so that all XCDs
+    // work on one tile at a time and share its sinogram lines in the memory-side cache.
+    // Measured against the earlier 8 x 8 orbit tiles (64 x 8 for one slot) with a contiguous
+    // range of tiles per XCD: the 720-view 512^3 cone 90.0 -> 86.6 ms (64 x 64: 85.3), the
+    // 360-view one 69.8 -> 68.1 (64 x 64: 68.6), the 256^3 cone 8.58 -> 7.85 (16 x 16: 7.90),
+    // the helical batch 157.9 -> 130.1 ms (64 x 8: 132.0, 16 x 16: 130.9, 8 x 8: 133.7).
+    const bool big = Wr % 32 == 0 && Hr % 32 == 0;
+    const bool tiled = big || (Wr % 16 == 0 && Hr % 32 == 0);
+    const int32_t tx = big ? 32 : tiled ? 16 : 1, ty = tiled ? 32 : Hr;
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kQueue * sizeof(GatherItem) +
@@ -1974,11 +1972,11 @@ hipError_t launch_tilt_gather(const ColumnLaunch& a, int nb, const float* ysc, f
     int32_t Wr, Hr;
     orbit_grid(orbit, W, H, Wr, Hr);
     const uint64_t tasks = (uint64_t)Wr * (uint64_t)Hr * (uint64_t)nchunks;
-    // an orbit's cells in 8 x 8 tiles, as in the column gather (the tilted 256^3 cone: 33.0
-    // against 33.5 ms with 16 x 32), else 16 x 32, else plain y-fastest order
-    const bool small = orbit > 1 && Wr % 8 == 0 && Hr % 8 == 0;
-    const bool tiled = small || (Wr % 16 == 0 && Hr % 32 == 0);
-    const int32_t tx = small ? 8 : tiled ? 16 : 1, ty = small ? 8 : tiled ? 32 : Hr;
+    // tiles of 32 x 32 cells, as in the column gather (the tilted 256^3 cone: 31.9 ms, against
+    // 32.2 with 8 x 8 and 33.5 with 16 x 32), else 16 x 32, else plain y-fastest order
+    const bool big = Wr % 32 == 0 && Hr % 32 == 0;
+    const bool tiled = big || (Wr % 16 == 0 && Hr % 32 == 0);
+    const int32_t tx = big ? 32 : tiled ? 16 : 1, ty = tiled ? 32 : Hr;
     if (tasks == 0) return hipSuccess;
     const dim3 grid((unsigned)((tasks + 3) / 4));
     const size_t lds = (size_t)4 * (kTiltQueue * sizeof(TiltItem) +
