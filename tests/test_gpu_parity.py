@@ -666,13 +666,14 @@ def _sample_rays(cfg, n, rng):
 
 def _unit_z_columns(cfg):
     """(x, y) of the xy cells whose whole z column is compared: the gathers' unit of work is
-    one z column, and their cells are dealt in tiles (64 x 8 for the column gather when the
-    grid holds them, else 16 x 32; 16 x 32 for the per-row gather; with a turn symmetry, 8 x 8
-    tiles of the quadrant or half whose cells stand for the orbits); the columns sit on the
-    volume's faces, on both sides of the first tile edges of every tiling in x and y, on both
-    sides of the midlines where the orbits' images meet, and on the images of those cells."""
+    one z column, and their cells are dealt in tiles (32 x 32 for both gathers when the grid
+    holds them, else 16 x 32; with a turn symmetry, tiles of the quadrant or half whose cells
+    stand for the orbits; earlier tilings took 64 x 8 and 8 x 8, whose edges stay sampled);
+    the columns sit on the volume's faces, on both sides of the first tile edges of every
+    tiling in x and y, on both sides of the midlines where the orbits' images meet, and on the
+    images of those cells."""
     D, H, W = cfg.shape
-    xs = sorted({min(x, W - 1) for x in (0, 15, 16, 63, 64, W - 1)})
+    xs = sorted({min(x, W - 1) for x in (0, 15, 16, 31, 32, 63, 64, W - 1)})
     ys = sorted({min(y, H - 1) for y in (0, 7, 8, 31, 32, H - 1)})
     cells = {(x, y) for x in xs for y in ys}
     for x, y in ((7, 7), (8, 8), (7, 8), (W // 2 - 1, H // 2 - 1), (W // 2, H // 2),
