@@ -302,22 +302,33 @@ __device__ __forceinline__ ColumnTask column_task(const ColumnLaunch& A) {
 // The forward's waves: a block takes 4 adjacent detector columns of one 64-row block and view
 // (one wave per column), so the waves on one compute unit cross the same voxel columns at the
 // same heights and share their cache lines (against 4 row blocks of one column: c3 -5%, the
-// 360-view 512^3 cone -3%). Views are the fastest block index, then row blocks, then column
-// quadruples, and the blocks are dealt round-robin to the XCDs as the hardware deals them:
-// the blocks running at one time on all XCDs take one column quadruple's row blocks over
-// consecutive views, which cross the same voxels from nearby angles, so the XCDs share those
-// voxels' lines in the memory-side cache. Against row blocks fastest, then quadruples, then
-// views, each XCD a contiguous range: the 720-view 512^3 cone 71.3 -> 65.7 ms, c3 6.22 ->
-// 5.97, the 360-view 512^3 cone 50.9 -> 50.3 (row blocks slowest, views fastest: 65.6, 6.21,
-// 53.3; row blocks slowest, quadruples fastest, each XCD a range: 70.3, 6.58, 58.9).
+// 360-view 512^3 cone -3%). The views are taken in groups of kForwardViewGroup (the last
+// group holding the rest); inside a group the views are the fastest block index, then row
+// blocks, then column quadruples, and the blocks are dealt round-robin to the XCDs as the
+// hardware deals them. The blocks running at one time on all XCDs then take a few column
+// quadruples over the group's consecutive views, which cross the same voxels from nearby
+// angles (and, on a helix, at nearby heights), so the XCDs share those voxels' lines in the
+// memory-side cache. Measured (the 720-view 512^3 cone, c3, the 360-view 512^3 cone, the
+// helical batch, ms): row blocks fastest, then quadruples, then views, each XCD a contiguous
+// range 71.3 / 6.22 / 50.9 / 46.5; all views fastest, round-robin 65.5 / 5.95 / 50.5 / 43.8;
+// groups of 16 views 65.6 / 5.96 / 47.6 / 32.0 (kept); the same with quadruples before row
+// blocks 65.3 / 6.26 / 52.5 / 32.1; groups of 8 views 65.3 / 6.17 / 53.8 / 33.4; of 32 views
+// 66.0 / 6.34 / 53.0 / 33.6 (both with quadruples before row blocks).
+constexpr uint32_t kForwardViewGroup = 16;
 __device__ __forceinline__ ColumnTask forward_task(const ColumnLaunch& A) {
     ColumnTask t;
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t blk = blockIdx.x;
-    const uint32_t nv = (uint32_t)A.nviews;
-    const uint32_t vl = blk % nv, rest = blk / nv;
-    const uint32_t rb = rest % (uint32_t)A.row_blocks, cq = rest / (uint32_t)A.row_blocks;
+    const uint32_t nv = (uint32_t)A.nviews, rbs = (uint32_t)A.row_blocks;
+    const uint32_t per_view = ((uint32_t)A.cols + 3u) / 4u * rbs;     // blocks per view
+    const uint32_t nfull = nv / kForwardViewGroup, full = nfull * kForwardViewGroup * per_view;
+    // the group and the block's place in it; the last group holds nv mod kForwardViewGroup views
+    const uint32_t grp = blk < full ? blk / (kForwardViewGroup * per_view) : nfull;
+    const uint32_t r = blk < full ? blk % (kForwardViewGroup * per_view) : blk - full;
+    const uint32_t gs = blk < full ? kForwardViewGroup : nv - nfull * kForwardViewGroup;
+    const uint32_t vl = grp * kForwardViewGroup + r % gs, rest = r / gs;
+    const uint32_t rb = rest % rbs, cq = rest / rbs;
     t.col = (int32_t)(cq * 4u + wave);
     t.view = A.view0 + (int32_t)vl;
     t.row = (int32_t)(rb * 64u + lane);
