@@ -315,20 +315,29 @@ __device__ __forceinline__ ColumnTask column_task(const ColumnLaunch& A) {
 // blocks 65.3 / 6.26 / 52.5 / 32.1; groups of 8 views 65.3 / 6.17 / 53.8 / 33.4; of 32 views
 // 66.0 / 6.34 / 53.0 / 33.6 (both with quadruples before row blocks).
 constexpr uint32_t kForwardViewGroup = 16;
+
+// Block blk's (view, row block, column quadruple) in that order: groups of kForwardViewGroup
+// views (the last group holding the rest), inside a group views fastest, then row blocks,
+// then quadruples. A bijection of [0, nv * rbs * quads).
+__device__ __forceinline__ void view_group_block(uint32_t blk, uint32_t nv, uint32_t rbs, uint32_t quads,
+                                                 uint32_t& vl, uint32_t& rb, uint32_t& cq) {
+    const uint32_t per_view = quads * rbs;                            // blocks per view
+    const uint32_t nfull = nv / kForwardViewGroup, full = nfull * kForwardViewGroup * per_view;
+    const uint32_t grp = blk < full ? blk / (kForwardViewGroup * per_view) : nfull;
+    const uint32_t r = blk < full ? blk % (kForwardViewGroup * per_view) : blk - full;
+    const uint32_t gs = blk < full ? kForwardViewGroup : nv - nfull * kForwardViewGroup;
+    vl = grp * kForwardViewGroup + r % gs;
+    const uint32_t rest = r / gs;
+    rb = rest % rbs;
+    cq = rest / rbs;
+}
 __device__ __forceinline__ ColumnTask forward_task(const ColumnLaunch& A) {
     ColumnTask t;
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t blk = blockIdx.x;
-    const uint32_t nv = (uint32_t)A.nviews, rbs = (uint32_t)A.row_blocks;
-    const uint32_t per_view = ((uint32_t)A.cols + 3u) / 4u * rbs;     // blocks per view
-    const uint32_t nfull = nv / kForwardViewGroup, full = nfull * kForwardViewGroup * per_view;
-    // the group and the block's place in it; the last group holds nv mod kForwardViewGroup views
-    const uint32_t grp = blk < full ? blk / (kForwardViewGroup * per_view) : nfull;
-    const uint32_t r = blk < full ? blk % (kForwardViewGroup * per_view) : blk - full;
-    const uint32_t gs = blk < full ? kForwardViewGroup : nv - nfull * kForwardViewGroup;
-    const uint32_t vl = grp * kForwardViewGroup + r % gs, rest = r / gs;
-    const uint32_t rb = rest % rbs, cq = rest / rbs;
+    uint32_t vl, rb, cq;
+    view_group_block(blockIdx.x, (uint32_t)A.nviews, (uint32_t)A.row_blocks,
+                     ((uint32_t)A.cols + 3u) / 4u, vl, rb, cq);
     t.col = (int32_t)(cq * 4u + wave);
     t.view = A.view0 + (int32_t)vl;
     t.row = (int32_t)(rb * 64u + lane);
