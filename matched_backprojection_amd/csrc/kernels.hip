@@ -319,6 +319,7 @@ constexpr uint32_t kForwardViewGroup = 16;
 // Block blk's (view, row block, column quadruple) in that order: groups of kForwardViewGroup
 // views (the last group holding the rest), inside a group views fastest, then row blocks,
 // then quadruples. A bijection of [0, nv * rbs * quads).
+static_assert(kForwardViewGroup == 16, "the view pairing below deals 16 views to 8 XCDs");
 __device__ __forceinline__ void view_group_block(uint32_t blk, uint32_t nv, uint32_t rbs, uint32_t quads,
                                                  uint32_t& vl, uint32_t& rb, uint32_t& cq) {
     const uint32_t per_view = quads * rbs;                            // blocks per view
@@ -326,7 +327,14 @@ __device__ __forceinline__ void view_group_block(uint32_t blk, uint32_t nv, uint
     const uint32_t grp = blk < full ? blk / (kForwardViewGroup * per_view) : nfull;
     const uint32_t r = blk < full ? blk % (kForwardViewGroup * per_view) : blk - full;
     const uint32_t gs = blk < full ? kForwardViewGroup : nv - nfull * kForwardViewGroup;
-    vl = grp * kForwardViewGroup + r % gs;
+    // in a full group, block r mod 8 runs on XCD r mod 8 (the hardware deals blocks
+    // round-robin to the 8 XCDs and a group starts at a multiple of 8): XCD x takes the
+    // adjacent views 2x and 2x + 1, which share more of their lines in its L2 (against views
+    // x and x + 8: the 720-view 512^3 cone 65.4 -> 65.0 ms, c3 5.97 -> 5.92, the 360-view
+    // 512^3 cone 48.0 -> 47.3, the helical batch 31.9 -> 30.8)
+    uint32_t g = r % gs;
+    if (gs == kForwardViewGroup) g = (g % 8u) * 2u + g / 8u;
+    vl = grp * kForwardViewGroup + g;
     const uint32_t rest = r / gs;
     rb = rest % rbs;
     cq = rest / rbs;
