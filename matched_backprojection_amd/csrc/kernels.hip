@@ -311,7 +311,8 @@ __device__ __forceinline__ ColumnTask column_task(const ColumnLaunch& A) {
 // memory-side cache. Measured (the 720-view 512^3 cone, c3, the 360-view 512^3 cone, the
 // helical batch, ms): row blocks fastest, then quadruples, then views, each XCD a contiguous
 // range 71.3 / 6.22 / 50.9 / 46.5; all views fastest, round-robin 65.5 / 5.95 / 50.5 / 43.8;
-// groups of 16 views 65.6 / 5.96 / 47.6 / 32.0 (kept); the same with quadruples before row
+// groups of 16 views 65.6 / 5.96 / 47.6 / 32.0 (kept, with the XCD pairing of view_group_block:
+// 65.0 / 5.92 / 47.3 / 30.8); the same with quadruples before row
 // blocks 65.3 / 6.26 / 52.5 / 32.1; groups of 8 views 65.3 / 6.17 / 53.8 / 33.4; of 32 views
 // 66.0 / 6.34 / 53.0 / 33.6 (both with quadruples before row blocks).
 constexpr uint32_t kForwardViewGroup = 16;
