@@ -961,6 +961,7 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         const float r = __builtin_amdgcn_rcpf((float)ext);
         const float f = fminf((float)num * r, 1.0f);
         const float g = mul_legacy((float)__builtin_elementwise_sub_sat(ext, num), r);
+        const float fd = f * dt, gd = g * dt;
         lds_float* dst;
         if constexpr (NB == 1) {
             const int32_t ad = shl_add<2>(fb, abase);
@@ -972,9 +973,8 @@ __device__ __forceinline__ void gather_fast_group(const GatherItem& it, int32_t 
         float qa[NB], qb[NB];
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
-            const float q = dt * w[c][(m + NB - SH) % NB];
-            qa[m] = f * q;
-            qb[m] = g * q;
+            qa[m] = fd * w[c][(m + NB - SH) % NB];
+            qb[m] = gd * w[c][(m + NB - SH) % NB];
         }
         // cells are moved through their own vector type, so that the compiler knows their
         // alignment (4 * NB bytes) and moves each with one access
@@ -1086,6 +1086,9 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
     GatherItem* Q = reinterpret_cast<GatherItem*>(lds_raw + 4 * (size_t)colf * sizeof(float)) + wave * kQueue;
     for (int32_t i = lane; i < colf; i += 64) cols[i] = 0.0f;
     __syncthreads();
+    // lanes per view when items are built: two for one slot (the helical batch: 125.8 against
+    // 129.1 ms with four), four for an orbit (the 512^3 cone: 87.8 against 90.9 with two)
+    constexpr int VL = P == 1 ? 2 : kViewLanes;
     if (live) {
         const bool line = A.beam == BEAM_PARALLEL;
         const int32_t S = gather_stride(A.rows);
@@ -1178,8 +1181,8 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
             }
         };
 
-        // Items: kViewLanes lanes take one view of a round of 64 / kViewLanes and walk its
-        // candidate columns, lane r of a view taking candidates j0 + r, j0 + r + kViewLanes, ...;
+        // Items: VL lanes take one view of a round of 64 / VL and walk its
+        // candidate columns, lane r of a view taking candidates j0 + r, j0 + r + VL, ...;
         // the crossings found are appended to the queue in lane order. A round spans few
         // views, so the sinogram lines the concurrently running waves of a tile read stay few
         // enough to share L2. With an orbit, the slots' cells take their turns, each over the
@@ -1204,8 +1207,8 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
             orbit_cell(P, dir, W, H, ix, iy, a, cx, cy);
             const double x0 = A.box.lo[0] + cx * A.box.pitch[0], x1 = x0 + A.box.pitch[0];
             const double y0 = A.box.lo[1] + cy * A.box.pitch[1], y1 = y0 + A.box.pitch[1];
-            for (int32_t vb = A.view0; vb < vend; vb += 64 / kViewLanes) {
-                const int32_t view = vb + lane / kViewLanes;
+            for (int32_t vb = A.view0; vb < vend; vb += 64 / VL) {
+                const int32_t view = vb + lane / VL;
                 int32_t jn = 0, j1 = -1;
                 if (view < vend &&
                     !cell_column_range(A.frames[view], A.beam, A.cols, A.du, x0, x1, y0, y1, jn, j1)) {
@@ -1213,7 +1216,7 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                     j1 = -1;
                 }
                 if (view >= vend) j1 = -1;
-                jn += lane % kViewLanes;
+                jn += lane % VL;
                 while (__ballot(jn <= j1) != 0) {
                     GatherItem it;
                     bool hit = false;
@@ -1221,7 +1224,7 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
                         const int32_t yoff = (view - A.view0) * A.cols + jn;
                         hit = gather_item(lines[yoff], line, x0, x1, y0, y1, S, A.rows, rows_pad, yoff,
                                           it, in_lo, in_hi);
-                        jn += kViewLanes;
+                        jn += VL;
                     }
                     const uint64_t m = __ballot(hit);
                     if (hit) {
