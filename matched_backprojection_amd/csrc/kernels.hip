@@ -1086,9 +1086,10 @@ column_gather_kernel(const ColumnLaunch A, const ColLine* __restrict__ lines,
     GatherItem* Q = reinterpret_cast<GatherItem*>(lds_raw + 4 * (size_t)colf * sizeof(float)) + wave * kQueue;
     for (int32_t i = lane; i < colf; i += 64) cols[i] = 0.0f;
     __syncthreads();
-    // lanes per view when items are built: two for one slot (the helical batch: 125.8 against
-    // 129.1 ms with four), four for an orbit (the 512^3 cone: 87.8 against 90.9 with two)
-    constexpr int VL = P == 1 ? 2 : kViewLanes;
+    // lanes per view when items are built: one for one slot (the helical batch: 123.5 ms,
+    // against 125.8 with two and 129.1 with four), four for an orbit (the 512^3 cone: 87.8
+    // against 90.9 with two)
+    constexpr int VL = P == 1 ? 1 : kViewLanes;
     if (live) {
         const bool line = A.beam == BEAM_PARALLEL;
         const int32_t S = gather_stride(A.rows);
